@@ -179,3 +179,20 @@ def test_pages_quantization_steps():
         step = (change[-1] - change[0]) / (change.size - 1)   # mean code width
         assert round(step, case["digits"]) == case["printed_step_px"]
         assert step == pytest.approx(W / 65535, rel=2e-3)
+
+
+def test_sh_colour_uses_view_direction_from_camera_centre():
+    """Colour = max(0, sum_k sh_k Y_k(d) + 0.5) with d the unit vector from the
+    camera's position (the look-at eye, not the translation column) to the mean."""
+    rng = np.random.default_rng(17)
+    eye = np.array([1.5, -2.0, 4.0])
+    vm = workloads.lookat_viewmat(eye, target=(0.2, 0.1, -0.3))
+    mu = rng.uniform(-0.5, 0.5, size=(8, 3))
+    sh = rng.normal(0, 0.6, size=(8, 16, 3))
+    pc = project_camera(mu, np.tile([1.0, 0, 0, 0], (8, 1)), np.full((8, 3), -3.0), np.zeros(8),
+                        sh, vm, intrinsics(300, 300, 256, 256), 256, 256, 3)
+    d = (mu - eye) / np.linalg.norm(mu - eye, axis=1, keepdims=True)
+    Y = oracle.sh_basis(3, d)
+    raw = np.einsum("nk,nkc->nc", Y, sh) + 0.5
+    np.testing.assert_allclose(pc["rgb"], np.maximum(raw, 0.0), atol=1e-12)
+    assert np.any(raw < 0)          # the clamp is exercised
