@@ -1,0 +1,14 @@
+"""Differentiable 16x16-tile Gaussian rasterizer for MI355X (gfx950).
+
+The compute path is the HIP library ``libgs.so`` (C ABI in include/gs.h);
+this package is its thin ctypes binding plus the build script.
+"""
+from ._lib import (GS_OK, GS_E_INVALID, GS_E_CAPACITY, GS_E_WORKSPACE, GS_E_OVERFLOW, GS_E_HIP,
+                   GS_E_DEVICE, EXPORTS, GsError, Rasterizer, Scene, Projected, Intersected,
+                   load, status_str, pad_n, tiles, gs_project, gs_intersect, gs_rasterize_fwd,
+                   gs_rasterize_bwd, gs_project_bwd)
+
+__all__ = ["GS_OK", "GS_E_INVALID", "GS_E_CAPACITY", "GS_E_WORKSPACE", "GS_E_OVERFLOW",
+           "GS_E_HIP", "GS_E_DEVICE", "EXPORTS", "GsError", "Rasterizer", "Scene", "Projected",
+           "Intersected", "load", "status_str", "pad_n", "tiles", "gs_project", "gs_intersect",
+           "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd"]

@@ -1,0 +1,327 @@
+"""ctypes binding of libgs (include/gs.h).
+
+Argument marshalling only: every step of the rasterizer runs in the HIP
+kernels of libgs.so. PyTorch supplies device memory and the stream.
+The functions named like the C entry points pass tensors through as raw
+pointers; ``Rasterizer`` adds growth-only buffer management on top
+(capacities and workspaces only grow, as the pages' pooled buffers do).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgs.so")
+
+GS_OK, GS_E_INVALID, GS_E_CAPACITY, GS_E_WORKSPACE, GS_E_OVERFLOW, GS_E_HIP, GS_E_DEVICE = \
+    0, -1, -2, -3, -4, -5, -6
+MASK_GROUP = 128
+TILE = 16
+ROW = 10
+
+EXPORTS = ("gs_status_str", "gs_version", "gs_pad_n", "gs_project_workspace_bytes",
+           "gs_intersect_workspace_bytes", "gs_project", "gs_intersect", "gs_rasterize_fwd",
+           "gs_rasterize_bwd", "gs_project_bwd")
+
+_lib = None
+
+c_vp, c_i32, c_i64, c_u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+P_i64 = ctypes.POINTER(ctypes.c_int64)
+P_u64 = ctypes.POINTER(ctypes.c_uint64)
+
+
+class GsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+        self.status = status
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libgs.so (built in place by build.py). Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"libgs.so not built at {p}: run "
+                          "`python -m gaussian_splatting_differentiable_project_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.gs_status_str.restype = ctypes.c_char_p
+    lib.gs_status_str.argtypes = [ctypes.c_int]
+    lib.gs_version.restype = ctypes.c_int
+    lib.gs_pad_n.restype = c_i64
+    lib.gs_pad_n.argtypes = [c_i64]
+    lib.gs_project_workspace_bytes.restype = c_u64
+    lib.gs_project_workspace_bytes.argtypes = [c_i64, c_i32]
+    lib.gs_intersect_workspace_bytes.restype = c_u64
+    lib.gs_intersect_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i64, c_i64]
+    lib.gs_project.restype = ctypes.c_int
+    lib.gs_project.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
+        [c_vp] * 3 + [c_vp, c_vp, c_i64, c_vp, c_u64, P_i64, P_i64]
+    lib.gs_intersect.restype = ctypes.c_int
+    lib.gs_intersect.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i64, c_vp, c_vp, P_i64, c_vp, c_u64,
+                                 c_vp, c_i64, c_vp, c_vp, P_i64, P_u64]
+    lib.gs_rasterize_fwd.restype = ctypes.c_int
+    lib.gs_rasterize_fwd.argtypes = [c_vp, c_i32, c_i32, c_i32] + [c_vp] * 6
+    lib.gs_rasterize_bwd.restype = ctypes.c_int
+    lib.gs_rasterize_bwd.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i64] + [c_vp] * 8
+    lib.gs_project_bwd.restype = ctypes.c_int
+    lib.gs_project_bwd.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
+        [c_vp] * 3 + [c_vp] * 5 + [c_i32]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().gs_status_str(int(status)).decode()
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def pad_n(N: int) -> int:
+    return int(load().gs_pad_n(N))
+
+
+def tiles(W: int, H: int) -> tuple[int, int]:
+    return (W + TILE - 1) // TILE, (H + TILE - 1) // TILE
+
+
+# ---------------------------------------------------------------------------
+# Direct bindings, one per C entry point.
+
+def gs_project(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, sh, viewmats,
+               Ks, mask, wg_count, wg_scan, screen, aabb16, screen_capacity, workspace,
+               workspace_bytes, stream=None):
+    """Returns (status, nnz, cam_offsets list)."""
+    nnz = ctypes.c_int64(-1)
+    cam = (ctypes.c_int64 * (C + 1))()
+    st = load().gs_project(_stream(stream), N, C, W, H, sh_degree, _ptr(means), _ptr(quats),
+                           _ptr(log_scales), _ptr(opacity_logits), _ptr(sh), _ptr(viewmats),
+                           _ptr(Ks), _ptr(mask), _ptr(wg_count), _ptr(wg_scan), _ptr(screen),
+                           _ptr(aabb16), screen_capacity, _ptr(workspace), workspace_bytes,
+                           ctypes.byref(nnz), cam)
+    return st, nnz.value, list(cam)
+
+
+def gs_intersect(C, W, H, nnz, screen, aabb16, cam_offsets, workspace, workspace_bytes,
+                 flatten_ids, isect_capacity, tile_offsets, sorted_keys=None, stream=None):
+    """Returns (status, n_isects, workspace_needed)."""
+    cam = (ctypes.c_int64 * (C + 1))(*[int(x) for x in cam_offsets])
+    n_is = ctypes.c_int64(-1)
+    need = ctypes.c_uint64(0)
+    st = load().gs_intersect(_stream(stream), C, W, H, nnz, _ptr(screen), _ptr(aabb16), cam,
+                             _ptr(workspace), workspace_bytes, _ptr(flatten_ids), isect_capacity,
+                             _ptr(tile_offsets), _ptr(sorted_keys), ctypes.byref(n_is),
+                             ctypes.byref(need))
+    return st, n_is.value, need.value
+
+
+def gs_rasterize_fwd(C, W, H, screen, flatten_ids, tile_offsets, out_rgb, out_T, last_ids,
+                     stream=None):
+    return load().gs_rasterize_fwd(_stream(stream), C, W, H, _ptr(screen), _ptr(flatten_ids),
+                                   _ptr(tile_offsets), _ptr(out_rgb), _ptr(out_T),
+                                   _ptr(last_ids))
+
+
+def gs_rasterize_bwd(C, W, H, nnz, screen, flatten_ids, tile_offsets, out_T, last_ids, v_rgb,
+                     v_T, v_screen, stream=None):
+    return load().gs_rasterize_bwd(_stream(stream), C, W, H, nnz, _ptr(screen),
+                                   _ptr(flatten_ids), _ptr(tile_offsets), _ptr(out_T),
+                                   _ptr(last_ids), _ptr(v_rgb), _ptr(v_T), _ptr(v_screen))
+
+
+def gs_project_bwd(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, sh,
+                   viewmats, Ks, mask, wg_scan, v_screen, v_means, v_quats, v_log_scales,
+                   v_opacity_logits, v_sh, accumulate=0, stream=None):
+    return load().gs_project_bwd(_stream(stream), N, C, W, H, sh_degree, _ptr(means), _ptr(quats),
+                                 _ptr(log_scales), _ptr(opacity_logits), _ptr(sh),
+                                 _ptr(viewmats), _ptr(Ks), _ptr(mask), _ptr(wg_scan),
+                                 _ptr(v_screen), _ptr(v_means), _ptr(v_quats),
+                                 _ptr(v_log_scales), _ptr(v_opacity_logits), _ptr(v_sh),
+                                 int(accumulate))
+
+
+# ---------------------------------------------------------------------------
+# Buffer-managing front end.
+
+@dataclass
+class Scene:
+    """Device-resident fp32 inputs of one step (SoA, contiguous)."""
+    N: int
+    C: int
+    W: int
+    H: int
+    sh_degree: int
+    means: torch.Tensor
+    quats: torch.Tensor
+    log_scales: torch.Tensor
+    opacity_logits: torch.Tensor
+    sh: torch.Tensor
+    viewmats: torch.Tensor
+    Ks: torch.Tensor
+
+    @staticmethod
+    def from_numpy(sc: dict, device="cuda") -> "Scene":
+        f = lambda k: torch.from_numpy(sc[k]).to(device=device, dtype=torch.float32).contiguous()
+        return Scene(sc["N"], sc["C"], sc["W"], sc["H"], sc["sh_degree"], f("means"), f("quats"),
+                     f("log_scales"), f("opacity_logits"), f("sh"), f("viewmats"), f("Ks"))
+
+
+@dataclass
+class Projected:
+    nnz: int
+    cam_offsets: list
+    mask: torch.Tensor
+    wg_count: torch.Tensor
+    wg_scan: torch.Tensor
+    screen: torch.Tensor   # [nnz, 10] view
+    aabb16: torch.Tensor   # [nnz, 2] view
+
+
+@dataclass
+class Intersected:
+    n_isects: int
+    flatten_ids: torch.Tensor  # [n_isects] view
+    tile_offsets: torch.Tensor  # [C*T+1]
+    sorted_keys: torch.Tensor | None
+
+
+def _grow(buf, numel, dtype, device, slack=1.0):
+    if buf is None or buf.numel() < numel:
+        n = max(int(numel * slack), 1)
+        return torch.empty(n, dtype=dtype, device=device)
+    return buf
+
+
+class Rasterizer:
+    """Runs the five library calls with growth-only device buffers."""
+
+    def __init__(self, device="cuda", slack: float = 1.1):
+        load()
+        self.device = torch.device(device)
+        self.slack = slack
+        self._screen = self._aabb = self._pws = self._iws = self._ids = self._vscreen = None
+        self._keys = None
+
+    def _check(self, st, where):
+        if st != GS_OK:
+            raise GsError(st, where)
+
+    def project(self, s: Scene) -> Projected:
+        Np = pad_n(s.N)
+        dev = self.device
+        mask = torch.empty(max(s.C * Np // 64, 1), dtype=torch.int64, device=dev)
+        wg_count = torch.empty(max(s.C * Np // MASK_GROUP, 1), dtype=torch.int32, device=dev)
+        wg_scan = torch.empty_like(wg_count)
+        wsb = int(load().gs_project_workspace_bytes(s.N, s.C))
+        self._pws = _grow(self._pws, wsb, torch.uint8, dev)
+        for _ in range(3):
+            cap = 0 if self._screen is None else self._screen.numel() // ROW
+            st, nnz, cam = gs_project(s.N, s.C, s.W, s.H, s.sh_degree, s.means, s.quats,
+                                      s.log_scales, s.opacity_logits, s.sh, s.viewmats, s.Ks,
+                                      mask, wg_count, wg_scan, self._screen, self._aabb, cap,
+                                      self._pws, self._pws.numel())
+            if st == GS_E_CAPACITY:
+                self._screen = _grow(None, nnz * ROW, torch.float32, dev, self.slack)
+                self._aabb = _grow(None, (self._screen.numel() // ROW) * 2, torch.int32, dev)
+                continue
+            self._check(st, "gs_project")
+            return Projected(nnz, cam, mask, wg_count, wg_scan,
+                             self._screen[: nnz * ROW].view(nnz, ROW) if nnz else
+                             torch.empty(0, ROW, device=dev),
+                             self._aabb[: nnz * 2].view(nnz, 2) if nnz else
+                             torch.empty(0, 2, dtype=torch.int32, device=dev))
+        raise GsError(GS_E_CAPACITY, "gs_project")
+
+    def intersect(self, s: Scene, p: Projected, want_keys: bool = False) -> Intersected:
+        dev = self.device
+        tx, ty = tiles(s.W, s.H)
+        n_tiles = s.C * tx * ty
+        tile_offsets = torch.empty(n_tiles + 1, dtype=torch.int64, device=dev)
+        if self._iws is None:
+            self._iws = _grow(None, int(load().gs_intersect_workspace_bytes(s.C, s.W, s.H, p.nnz, 0)),
+                              torch.uint8, dev, self.slack)
+        for _ in range(4):
+            cap = 0 if self._ids is None else self._ids.numel()
+            keys = None
+            if want_keys:
+                keys = _grow(self._keys, max(cap, 1), torch.int64, dev)
+                self._keys = keys
+            st, n_is, need = gs_intersect(s.C, s.W, s.H, p.nnz, p.screen, p.aabb16, p.cam_offsets,
+                                          self._iws, self._iws.numel(), self._ids, cap,
+                                          tile_offsets, keys)
+            if st == GS_E_WORKSPACE:
+                self._iws = _grow(None, need, torch.uint8, dev, self.slack)
+                continue
+            if st == GS_E_CAPACITY:
+                self._ids = _grow(None, n_is, torch.int32, dev, self.slack)
+                if want_keys:
+                    self._keys = _grow(None, self._ids.numel(), torch.int64, dev)
+                continue
+            self._check(st, "gs_intersect")
+            return Intersected(n_is, self._ids[:n_is] if n_is else
+                               torch.empty(0, dtype=torch.int32, device=dev), tile_offsets,
+                               keys[:n_is] if keys is not None else None)
+        raise GsError(GS_E_CAPACITY, "gs_intersect")
+
+    def rasterize_fwd(self, s: Scene, p: Projected, it: Intersected):
+        dev = self.device
+        rgb = torch.empty(s.C, s.H, s.W, 3, device=dev)
+        T = torch.empty(s.C, s.H, s.W, device=dev)
+        last = torch.empty(s.C, s.H, s.W, dtype=torch.int32, device=dev)
+        self._check(gs_rasterize_fwd(s.C, s.W, s.H, p.screen, it.flatten_ids, it.tile_offsets,
+                                     rgb, T, last), "gs_rasterize_fwd")
+        return rgb, T, last
+
+    def rasterize_bwd(self, s: Scene, p: Projected, it: Intersected, out_T, last, v_rgb, v_T=None):
+        dev = self.device
+        self._vscreen = _grow(self._vscreen, max(p.nnz * ROW, 1), torch.float32, dev, self.slack)
+        v = self._vscreen[: p.nnz * ROW].view(p.nnz, ROW) if p.nnz else \
+            torch.empty(0, ROW, device=dev)
+        self._check(gs_rasterize_bwd(s.C, s.W, s.H, p.nnz, p.screen, it.flatten_ids,
+                                     it.tile_offsets, out_T, last, v_rgb, v_T, v),
+                    "gs_rasterize_bwd")
+        return v
+
+    def project_bwd(self, s: Scene, p: Projected, v_screen, grads=None, accumulate=False):
+        dev = self.device
+        K = (s.sh_degree + 1) ** 2
+        if grads is None:
+            grads = dict(v_means=torch.empty(s.N, 3, device=dev),
+                         v_quats=torch.empty(s.N, 4, device=dev),
+                         v_log_scales=torch.empty(s.N, 3, device=dev),
+                         v_opacity_logits=torch.empty(s.N, device=dev),
+                         v_sh=torch.empty(s.N, K, 3, device=dev))
+        self._check(gs_project_bwd(s.N, s.C, s.W, s.H, s.sh_degree, s.means, s.quats,
+                                   s.log_scales, s.opacity_logits, s.sh, s.viewmats, s.Ks, p.mask,
+                                   p.wg_scan, v_screen, grads["v_means"], grads["v_quats"],
+                                   grads["v_log_scales"], grads["v_opacity_logits"],
+                                   grads["v_sh"], 1 if accumulate else 0), "gs_project_bwd")
+        return grads
+
+    def step(self, s: Scene, v_rgb, v_T=None):
+        """One whole pass: project, intersect, raster forward and backward,
+        projection backward. Returns everything the passes produced."""
+        p = self.project(s)
+        it = self.intersect(s, p)
+        rgb, T, last = self.rasterize_fwd(s, p, it)
+        v_screen = self.rasterize_bwd(s, p, it, T, last, v_rgb, v_T)
+        grads = self.project_bwd(s, p, v_screen)
+        return dict(proj=p, isect=it, rgb=rgb, T=T, last=last, v_screen=v_screen, grads=grads)

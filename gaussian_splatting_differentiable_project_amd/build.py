@@ -1,0 +1,51 @@
+"""Build libgs.so (HIP, gfx950) in place with hipcc.
+
+Usage: python -m gaussian_splatting_differentiable_project_amd.build
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libgs.so")
+
+SOURCES = ["gs_api.hip", "gs_project.hip", "gs_project_bwd.hip", "gs_sort.hip",
+           "gs_intersect.hip", "gs_raster.hip"]
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",
+    "-munsafe-fp-atomics",
+    # keep the compiler from forming packed fp32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found: the HIP toolchain is required to build libgs")
+    return exe
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libgs.so next to this file; returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in proc.stderr.splitlines() if noise not in l and "(ignoring feature)" not in l)
+    if proc.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + err)
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

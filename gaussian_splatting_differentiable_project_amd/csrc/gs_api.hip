@@ -1,0 +1,369 @@
+// C ABI of libgs: argument checks, workspace layout and the host-side
+// sequencing of the kernels on the caller's stream.
+//
+// Error protocol ([VRAM] "The 4 GiB rule and the 2^31 limit"): totals
+// are computed exactly in 64 bits on the device and read back once per
+// call; the host checks them against the caller's capacities before any
+// kernel writes a buffer sized by them, and returns the required size
+// instead of writing past an allocation.
+#include <cstdlib>
+#include <cstring>
+
+#include "gs_internal.h"
+
+using namespace gs;
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+inline uint64_t align_up(uint64_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool check_env() {
+  static const bool on = [] {
+    const char* v = std::getenv("GS_CHECK");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t tiles_x_of(int W) { return (W + kTile - 1) / kTile; }
+int64_t tiles_y_of(int H) { return (H + kTile - 1) / kTile; }
+
+int bits_for(uint64_t n_values) {  // bits needed to hold values 0..n_values-1
+  int b = 0;
+  while (b < 64 && (n_values - 1) >> b) ++b;
+  return b;
+}
+
+// Bump layout of a workspace: offsets are computed the same way for
+// sizing (base == nullptr) and for carving.
+struct Carver {
+  char* base;
+  uint64_t off = 0;
+  template <typename T>
+  T* take(uint64_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+// ---- gs_project workspace ----
+struct ProjectWs {
+  uint64_t* total;
+  int* err;
+  uint32_t* ticket;
+  int64_t* cam_off;   // [C+1]
+  uint64_t* lookback;  // scan of the group counts
+  uint64_t bytes;
+};
+
+ProjectWs carve_project(void* base, int64_t n_groups, int32_t C) {
+  Carver cv{static_cast<char*>(base)};
+  ProjectWs w{};
+  w.total = cv.take<uint64_t>(1);
+  w.err = cv.take<int>(1);
+  w.ticket = cv.take<uint32_t>(1);
+  w.cam_off = cv.take<int64_t>(uint64_t(C) + 1);
+  w.lookback = cv.take<uint64_t>((uint64_t(n_groups) + kScanTile - 1) / kScanTile + 1);
+  w.bytes = cv.off;
+  return w;
+}
+
+// ---- gs_intersect workspace ----
+struct IsectWs {
+  uint64_t* total;
+  uint64_t* total2;
+  int* err;
+  uint32_t* tickets;    // [32]: 0 scan, 1..4 depth passes, 8..15 tile passes
+  uint64_t* hist_depth; // [4][256]
+  uint64_t* hist_tile;  // [4][256]
+  int64_t* cam_off;     // [C+1]
+  uint32_t *dkeys_a, *dkeys_b, *dvals_a, *dvals_b, *cnt;
+  uint64_t* offs;
+  uint64_t* scan_lb;
+  uint64_t zero_words;  // u32 words to zero from `total` up to cam_off
+  uint64_t* sort_lb;    // [max blocks][256]
+  uint64_t sort_lb_words;
+  uint64_t phase1_bytes;  // enough to count (I still unknown)
+  uint32_t *tkeys_a, *tkeys_b, *tvals;
+  uint64_t bytes;
+};
+
+IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects) {
+  Carver cv{static_cast<char*>(base)};
+  IsectWs w{};
+  w.total = cv.take<uint64_t>(1);
+  w.total2 = cv.take<uint64_t>(1);
+  w.err = cv.take<int>(1);
+  w.tickets = cv.take<uint32_t>(32);
+  w.hist_depth = cv.take<uint64_t>(4 * kRadix);
+  w.hist_tile = cv.take<uint64_t>(4 * kRadix);
+  w.zero_words = cv.off / 4;
+  w.cam_off = cv.take<int64_t>(uint64_t(C) + 1);
+  const uint64_t n = uint64_t(nnz);
+  w.dkeys_a = cv.take<uint32_t>(n);
+  w.dkeys_b = cv.take<uint32_t>(n);
+  w.dvals_a = cv.take<uint32_t>(n);
+  w.dvals_b = cv.take<uint32_t>(n);
+  w.cnt = cv.take<uint32_t>(n);
+  w.offs = cv.take<uint64_t>(n);
+  w.scan_lb = cv.take<uint64_t>((n + kScanTile - 1) / kScanTile + 1);
+  const uint64_t nb1 = sort_blocks(n);
+  w.phase1_bytes = cv.off + align_up(nb1 * kRadix * sizeof(uint64_t));
+  const uint64_t I = n_isects > 0 ? uint64_t(n_isects) : 0;
+  const uint64_t nb = nb1 > sort_blocks(I) ? nb1 : sort_blocks(I);
+  w.sort_lb_words = nb * kRadix * 2;
+  w.sort_lb = cv.take<uint64_t>(nb * kRadix);
+  w.tkeys_a = cv.take<uint32_t>(I);
+  w.tkeys_b = cv.take<uint32_t>(I);
+  w.tvals = cv.take<uint32_t>(I);
+  w.bytes = cv.off;
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_E_HIP; }
+
+#define GS_TRY(expr)                            \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return GS_E_HIP;      \
+  } while (0)
+
+int check_device_error(const int* err, hipStream_t s) {
+  if (!check_env()) return GS_OK;
+  int h = 0;
+  GS_TRY(hipMemcpyAsync(&h, err, sizeof(int), hipMemcpyDeviceToHost, s));
+  GS_TRY(hipStreamSynchronize(s));
+  return h ? GS_E_DEVICE : GS_OK;
+}
+
+bool valid_image(int32_t C, int32_t W, int32_t H) {
+  return C >= 1 && W >= 1 && H >= 1 && W <= 65535 && H <= 65535;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gs_status_str(int status) {
+  switch (status) {
+    case GS_OK: return "ok";
+    case GS_E_INVALID: return "invalid argument";
+    case GS_E_CAPACITY: return "output capacity too small";
+    case GS_E_WORKSPACE: return "workspace too small";
+    case GS_E_OVERFLOW: return "count exceeds its storage type";
+    case GS_E_HIP: return "HIP runtime error";
+    case GS_E_DEVICE: return "kernel reported an internal error";
+    default: return "unknown status";
+  }
+}
+
+int gs_version(void) { return 100; }
+
+int64_t gs_pad_n(int64_t N) { return N <= 0 ? 0 : ((N + kMaskGroup - 1) / kMaskGroup) * kMaskGroup; }
+
+uint64_t gs_project_workspace_bytes(int64_t N, int32_t C) {
+  if (N < 0 || C < 1) return 0;
+  return carve_project(nullptr, int64_t(C) * gs_pad_n(N) / kMaskGroup, C).bytes;
+}
+
+uint64_t gs_intersect_workspace_bytes(int32_t C, int32_t W, int32_t H, int64_t nnz,
+                                      int64_t n_isects) {
+  (void)W;
+  (void)H;
+  if (C < 1 || nnz < 0) return 0;
+  return carve_isect(nullptr, C, nnz, n_isects).bytes;
+}
+
+int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t sh_degree,
+               const float* means, const float* quats, const float* log_scales,
+               const float* opacity_logits, const float* sh, const float* viewmats,
+               const float* Ks, uint64_t* mask, uint32_t* wg_count, uint32_t* wg_scan,
+               float* screen, uint32_t* aabb16, int64_t screen_capacity, void* workspace,
+               uint64_t workspace_bytes, int64_t* nnz_out, int64_t* cam_offsets_out) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N < 0 || !valid_image(C, W, H) || sh_degree < 0 || sh_degree > 3 || !nnz_out ||
+      screen_capacity < 0)
+    return GS_E_INVALID;
+  if (N > 0 && (!means || !quats || !log_scales || !opacity_logits || !sh || !viewmats || !Ks ||
+                !mask || !wg_count || !wg_scan || !workspace))
+    return GS_E_INVALID;
+  if (!aligned(quats, 16) || !aligned(screen, 8) || !aligned(aabb16, 8) ||
+      !aligned(workspace, kAlign) || !aligned(mask, 8))
+    return GS_E_INVALID;
+  const int64_t Np = gs_pad_n(N);
+  const int64_t n_groups = int64_t(C) * Np / kMaskGroup;
+  const ProjectWs ws = carve_project(workspace, n_groups, C);
+  if (!workspace || workspace_bytes < ws.bytes) return GS_E_WORKSPACE;
+
+  ProjectArgs a{};
+  a.N = N, a.N_pad = Np, a.C = C, a.W = W, a.H = H, a.deg = sh_degree;
+  a.means = means, a.quats = quats, a.log_scales = log_scales, a.opacity_logits = opacity_logits;
+  a.sh = sh, a.viewmats = viewmats, a.Ks = Ks;
+  a.norm = sh_norm_table();
+  a.qsx = float(kQ16) / float(W);
+  a.qsy = float(kQ16) / float(H);
+
+  GS_TRY(launch_fill_u32(workspace, 0u, ws.bytes / 4, s));
+  GS_TRY(launch_project_mask(a, mask, wg_count, s));
+  GS_TRY(launch_scan_u32(wg_count, nullptr, uint64_t(n_groups), wg_scan, nullptr, ws.total,
+                         ws.lookback, ws.ticket, ws.err, s));
+  GS_TRY(launch_cam_offsets(wg_scan, Np / kMaskGroup, C, ws.total, ws.cam_off, s));
+  int64_t host_off[1 + 1024];
+  int64_t* off_h = host_off;
+  int64_t* heap = nullptr;
+  if (C + 1 > 1025) {
+    heap = static_cast<int64_t*>(std::malloc(sizeof(int64_t) * (C + 1)));
+    if (!heap) return GS_E_INVALID;
+    off_h = heap;
+  }
+  hipError_t e = hipMemcpyAsync(off_h, ws.cam_off, sizeof(int64_t) * (C + 1),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    std::free(heap);
+    return GS_E_HIP;
+  }
+  const int64_t nnz = off_h[C];
+  *nnz_out = nnz;
+  if (cam_offsets_out) std::memcpy(cam_offsets_out, off_h, sizeof(int64_t) * (C + 1));
+  std::free(heap);
+  if (nnz >= (int64_t(1) << 31)) return GS_E_OVERFLOW;
+  if (nnz > screen_capacity) return GS_E_CAPACITY;
+  if (nnz > 0 && (!screen || !aabb16)) return GS_E_INVALID;
+  GS_TRY(launch_project_compact(a, mask, wg_scan, screen, aabb16, s));
+  return check_device_error(ws.err, s);
+}
+
+int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, const float* screen,
+                 const uint32_t* aabb16, const int64_t* cam_offsets, void* workspace,
+                 uint64_t workspace_bytes, uint32_t* flatten_ids, int64_t isect_capacity,
+                 int64_t* tile_offsets, uint64_t* sorted_keys, int64_t* n_isects_out,
+                 uint64_t* workspace_needed_out) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!valid_image(C, W, H) || nnz < 0 || !n_isects_out || !workspace_needed_out ||
+      !tile_offsets || !cam_offsets || isect_capacity < 0)
+    return GS_E_INVALID;
+  if (nnz > 0 && (!screen || !aabb16)) return GS_E_INVALID;
+  if (!aligned(aabb16, 8) || !aligned(workspace, kAlign)) return GS_E_INVALID;
+  *n_isects_out = -1;
+  if (nnz >= (int64_t(1) << 31)) return GS_E_OVERFLOW;
+  for (int c = 0; c < C; ++c)
+    if (cam_offsets[c] < 0 || cam_offsets[c] > cam_offsets[c + 1]) return GS_E_INVALID;
+  if (cam_offsets[0] != 0 || cam_offsets[C] != nnz) return GS_E_INVALID;
+  const uint64_t n_tiles = uint64_t(C) * uint64_t(tiles_x_of(W) * tiles_y_of(H));
+  if (n_tiles >= (uint64_t(1) << 32)) return GS_E_OVERFLOW;
+
+  IsectWs ws = carve_isect(workspace, C, nnz, 0);
+  *workspace_needed_out = ws.phase1_bytes;
+  if (!workspace || workspace_bytes < ws.phase1_bytes) return GS_E_WORKSPACE;
+
+  // Phase 1: depth keys, per-slot tile counts and their exact 64-bit total.
+  GS_TRY(launch_fill_u32(workspace, 0u, ws.zero_words, s));
+  GS_TRY(hipMemcpyAsync(ws.cam_off, cam_offsets, sizeof(int64_t) * (C + 1),
+                        hipMemcpyHostToDevice, s));
+  GS_TRY(launch_isect_prep(uint64_t(nnz), screen, aabb16, W, H, ws.dkeys_a, ws.dvals_a, ws.cnt,
+                           ws.total, s));
+  uint64_t I = 0;
+  GS_TRY(hipMemcpyAsync(&I, ws.total, sizeof(uint64_t), hipMemcpyDeviceToHost, s));
+  GS_TRY(hipStreamSynchronize(s));
+  *n_isects_out = int64_t(I);
+  if (I >= (uint64_t(1) << 62)) return GS_E_OVERFLOW;
+  ws = carve_isect(workspace, C, nnz, int64_t(I));
+  *workspace_needed_out = ws.bytes;
+  if (int64_t(I) > isect_capacity) return GS_E_CAPACITY;
+  if (workspace_bytes < ws.bytes) return GS_E_WORKSPACE;
+  if (I > 0 && !flatten_ids) return GS_E_INVALID;
+
+  if (I == 0) {
+    GS_TRY(launch_fill_u32(tile_offsets, 0u, 2 * (n_tiles + 1), s));
+    return GS_OK;
+  }
+
+  GS_TRY(launch_fill_u32(ws.sort_lb, 0u, ws.sort_lb_words, s));
+  GS_TRY(launch_fill_u32(ws.scan_lb, 0u, 2 * ((uint64_t(nnz) + kScanTile - 1) / kScanTile + 1), s));
+  // Phase 2: stable sort of the slots by depth.
+  SortScratch sd{ws.hist_depth, ws.sort_lb, ws.tickets + 1, ws.err};
+  GS_TRY(launch_sort_histogram(ws.dkeys_a, uint64_t(nnz), 0, 32, sd, s));
+  bool in_b = false;
+  GS_TRY(launch_sort_passes(ws.dkeys_a, ws.dvals_a, ws.dkeys_b, ws.dvals_b, uint64_t(nnz), 0, 32,
+                            sd, 1, &in_b, s));
+  const uint32_t* order = in_b ? ws.dvals_b : ws.dvals_a;
+
+  // Phase 3: entry offsets in depth order, then emit (tile id, slot).
+  GS_TRY(launch_scan_u32(ws.cnt, order, uint64_t(nnz), nullptr, ws.offs, ws.total2, ws.scan_lb,
+                         ws.tickets, ws.err, s));
+  const int tbits = bits_for(n_tiles);
+  const int passes = sort_passes(tbits);
+  // the final pass must land its values in flatten_ids
+  uint32_t* v_first = (passes & 1) ? ws.tvals : flatten_ids;
+  uint32_t* v_second = (passes & 1) ? flatten_ids : ws.tvals;
+  GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.offs, ws.cam_off, C, W, H, I,
+                           ws.tkeys_a, v_first, s));
+
+  // Phase 4: stable sort of the entries by tile id.
+  SortScratch st{ws.hist_tile, ws.sort_lb, ws.tickets + 8, ws.err};
+  GS_TRY(launch_sort_histogram(ws.tkeys_a, I, 0, tbits, st, s));
+  GS_TRY(launch_sort_passes(ws.tkeys_a, v_first, ws.tkeys_b, v_second, I, 0, tbits, st, 8, &in_b,
+                            s));
+  const uint32_t* tkeys = in_b ? ws.tkeys_b : ws.tkeys_a;
+
+  // Phase 5: per-tile ranges (and the composed 64-bit keys on request).
+  GS_TRY(launch_tile_ranges(tkeys, I, n_tiles, tile_offsets, s));
+  if (sorted_keys) GS_TRY(launch_compose_keys(tkeys, flatten_ids, screen, I, sorted_keys, s));
+  return check_device_error(ws.err, s);
+}
+
+int gs_rasterize_fwd(void* stream, int32_t C, int32_t W, int32_t H, const float* screen,
+                     const uint32_t* flatten_ids, const int64_t* tile_offsets, float* out_rgb,
+                     float* out_T, int32_t* last_ids) {
+  if (!valid_image(C, W, H) || !tile_offsets || !out_rgb || !out_T || !last_ids)
+    return GS_E_INVALID;
+  if (!aligned(screen, 8)) return GS_E_INVALID;
+  return hip_status(launch_raster_fwd(C, W, H, screen, flatten_ids, tile_offsets, out_rgb, out_T,
+                                      last_ids, static_cast<hipStream_t>(stream)));
+}
+
+int gs_rasterize_bwd(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz,
+                     const float* screen, const uint32_t* flatten_ids, const int64_t* tile_offsets,
+                     const float* out_T, const int32_t* last_ids, const float* v_rgb,
+                     const float* v_T, float* v_screen) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!valid_image(C, W, H) || nnz < 0 || !tile_offsets || !out_T || !last_ids || !v_rgb)
+    return GS_E_INVALID;
+  if (nnz > 0 && !v_screen) return GS_E_INVALID;
+  if (!aligned(screen, 8)) return GS_E_INVALID;
+  GS_TRY(launch_fill_u32(v_screen, 0u, uint64_t(nnz) * kRow, s));
+  return hip_status(launch_raster_bwd(C, W, H, screen, flatten_ids, tile_offsets, out_T, last_ids,
+                                      v_rgb, v_T, v_screen, s));
+}
+
+int gs_project_bwd(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t sh_degree,
+                   const float* means, const float* quats, const float* log_scales,
+                   const float* opacity_logits, const float* sh, const float* viewmats,
+                   const float* Ks, const uint64_t* mask, const uint32_t* wg_scan,
+                   const float* v_screen, float* v_means, float* v_quats, float* v_log_scales,
+                   float* v_opacity_logits, float* v_sh, int32_t accumulate) {
+  if (N < 0 || !valid_image(C, W, H) || sh_degree < 0 || sh_degree > 3) return GS_E_INVALID;
+  if (N == 0) return GS_OK;
+  if (!means || !quats || !log_scales || !opacity_logits || !sh || !viewmats || !Ks || !mask ||
+      !wg_scan || !v_means || !v_quats || !v_log_scales || !v_opacity_logits || !v_sh)
+    return GS_E_INVALID;
+  if (!aligned(quats, 16) || !aligned(v_quats, 16) || !aligned(v_screen, 8)) return GS_E_INVALID;
+  ProjectArgs a{};
+  a.N = N, a.N_pad = gs_pad_n(N), a.C = C, a.W = W, a.H = H, a.deg = sh_degree;
+  a.means = means, a.quats = quats, a.log_scales = log_scales, a.opacity_logits = opacity_logits;
+  a.sh = sh, a.viewmats = viewmats, a.Ks = Ks;
+  a.norm = sh_norm_table();
+  a.qsx = float(kQ16) / float(W);
+  a.qsy = float(kQ16) / float(H);
+  return hip_status(launch_project_bwd(a, mask, wg_scan, v_screen, v_means, v_quats, v_log_scales,
+                                       v_opacity_logits, v_sh, accumulate,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// Shared constants and wave64 helpers of the gfx950 kernels.
+//
+// The geometry constants live in one header because the visibility pass
+// and the compaction pass must agree on them: both map bit b of the
+// 64-bit mask word w to pair 64 w + b and both launch GS_MASK_GROUP lanes
+// per work-group ([VRAM] "Bitmask compaction": the block size is a shared
+// constant, otherwise the bit-to-word mapping silently shifts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gs.h"
+
+namespace gs {
+
+constexpr int kWave = 64;                  // CDNA wavefront width
+constexpr int kMaskGroup = GS_MASK_GROUP;  // 128 pairs = 2 waves
+constexpr int kTile = GS_TILE;             // 16 x 16 pixels
+constexpr int kTilePix = kTile * kTile;
+constexpr int kRow = GS_ROW;               // floats per screen row
+constexpr float kNear = 0.01f;
+constexpr float kBlur = 0.3f;              // px^2 added to the 2D covariance
+constexpr float kAlphaMax = 0.99f;
+constexpr float kAlphaMin = 1.0f / 255.0f;
+constexpr float kTStop = 1e-4f;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kQ16 = 65535u;          // 16-bit box grid steps
+
+// Radix sort geometry: 8-bit digits, 256 lanes, 16 keys per lane.
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kSortThreads = 256;
+constexpr int kSortItems = 16;
+constexpr int kSortTile = kSortThreads * kSortItems;  // 4096 keys per block
+
+// Scan geometry (decoupled look-back): 256 lanes x 16 values.
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 16;
+constexpr int kScanTile = kScanThreads * kScanItems;
+
+// Look-back words: [63:62] status, [61:56] epoch tag, [55:0] value.
+constexpr uint64_t kLbAgg = 1ull << 62;
+constexpr uint64_t kLbPrefix = 2ull << 62;
+constexpr uint64_t kLbValueMask = (1ull << 56) - 1;
+constexpr uint32_t kSpinLimit = 1u << 24;  // bounded waits: a bug reports, never hangs
+
+__device__ __forceinline__ uint64_t lb_word(uint64_t status, uint32_t tag, uint64_t v) {
+  return status | (uint64_t(tag & 63u) << 56) | (v & kLbValueMask);
+}
+__device__ __forceinline__ uint32_t lb_tag(uint64_t w) { return uint32_t(w >> 56) & 63u; }
+__device__ __forceinline__ uint64_t lb_status(uint64_t w) { return w & (3ull << 62); }
+
+__device__ __forceinline__ void lb_store(uint64_t* p, uint64_t w) {
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t lb_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive prefix of everything before block `blk` for one counter of a
+// decoupled look-back chain. `lb` is indexed [block * stride]. The block's
+// own aggregate must already be published. Spins are bounded: on timeout
+// *err is set and 0 is returned (the caller's output is then garbage but
+// every wave still exits).
+__device__ __forceinline__ uint64_t lookback_prefix(const uint64_t* lb, int64_t blk,
+                                                    int64_t stride, uint32_t tag,
+                                                    int* err) {
+  uint64_t acc = 0;
+  int64_t p = blk - 1;
+  uint32_t spins = 0;
+  while (p >= 0) {
+    uint64_t w = lb_load(lb + p * stride);
+    if (lb_tag(w) != tag || lb_status(w) == 0) {
+      if (++spins > kSpinLimit) {
+        atomicOr(err, 1);
+        return 0;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    acc += w & kLbValueMask;
+    if (lb_status(w) == kLbPrefix) break;
+    --p;
+  }
+  return acc;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = __lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Sum of a float over the 64 lanes; every lane gets the total.
+// Row sums (16 lanes) by DPP row rotations, then the four row sums by
+// readlane.
+__device__ __forceinline__ float wave_sum(float v) {
+  int x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false));  // row_ror:8
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x124, 0xf, 0xf, false));  // row_ror:4
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x122, 0xf, 0xf, false));  // row_ror:2
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x121, 0xf, 0xf, false));  // row_ror:1
+  x = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Inclusive prefix sum of a uint64 over the 64 lanes (shuffle-based).
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  const int l = __lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint64_t t = __shfl_up(v, o, kWave);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  const int l = __lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t t = __shfl_up(v, o, kWave);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+}  // namespace gs

@@ -1,0 +1,85 @@
+// Host-side launchers shared between the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gs_projmath.h"
+
+namespace gs {
+
+struct ProjectArgs {
+  int64_t N, N_pad;
+  int32_t C, W, H, deg;
+  const float *means, *quats, *log_scales, *opacity_logits, *sh, *viewmats, *Ks;
+  ShNorm norm;
+  float qsx, qsy;  // 65535 / W, 65535 / H in fp32
+};
+
+ShNorm sh_norm_table();
+
+hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, uint32_t* wg_count,
+                               hipStream_t s);
+hipError_t launch_project_compact(const ProjectArgs& a, const uint64_t* mask,
+                                  const uint32_t* wg_scan, float* screen, uint32_t* aabb16,
+                                  hipStream_t s);
+hipError_t launch_project_bwd(const ProjectArgs& a, const uint64_t* mask,
+                              const uint32_t* wg_scan, const float* v_screen, float* v_means,
+                              float* v_quats, float* v_log_scales, float* v_opacity_logits,
+                              float* v_sh, int accumulate, hipStream_t s);
+
+// Exclusive scan of n uint32 values (optionally gathered through idx) into
+// uint32 or uint64 outputs; the total is written to *total (device).
+// Scratch: lookback[ceil(n / kScanTile)] + one ticket; both must be zero.
+hipError_t launch_scan_u32(const uint32_t* in, const uint32_t* idx, uint64_t n, uint32_t* out32,
+                           uint64_t* out64, uint64_t* total, uint64_t* lookback,
+                           uint32_t* ticket, int* err, hipStream_t s);
+
+hipError_t launch_fill_u32(void* p, uint32_t v, uint64_t n_words, hipStream_t s);
+
+// Stable LSD radix sort, one 8-bit digit per pass, of uint32 keys with
+// uint32 values, over the bit range [bit0, bit0 + bits).
+struct SortScratch {
+  uint64_t* hist;      // [passes][256], zeroed; becomes the digit starts
+  uint64_t* lookback;  // [blocks][256], zeroed
+  uint32_t* tickets;   // [passes], zeroed
+  int* err;
+};
+int sort_passes(int bits);
+uint64_t sort_blocks(uint64_t n);
+// Histograms of every digit of `keys` (adds into sc.hist).
+hipError_t launch_sort_histogram(const uint32_t* keys, uint64_t n, int bit0, int bits,
+                                 const SortScratch& sc, hipStream_t s);
+// Runs all passes (look-back epoch tags tag0, tag0+1, ...); the result ends
+// in (keys_a, vals_a) when the pass count is even, else in (keys_b, vals_b),
+// which *in_b reports.
+hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys_b,
+                              uint32_t* vals_b, uint64_t n, int bit0, int bits,
+                              const SortScratch& sc, uint32_t tag0, bool* in_b, hipStream_t s);
+
+// Intersection stages (gs_intersect.hip).
+hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* aabb16, int W,
+                             int H, uint32_t* dkeys, uint32_t* dvals, uint32_t* cnt,
+                             uint64_t* total, hipStream_t s);
+hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
+                             const uint64_t* offs, const int64_t* cam_off, int C, int W, int H,
+                             uint64_t cap, uint32_t* tkeys, uint32_t* tvals, hipStream_t s);
+hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
+                              hipStream_t s);
+hipError_t launch_compose_keys(const uint32_t* tkeys, const uint32_t* ids, const float* screen,
+                               uint64_t n, uint64_t* out, hipStream_t s);
+
+// Rasterization (gs_raster.hip).
+hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uint32_t* ids,
+                             const int64_t* toff, float* out_rgb, float* out_T, int32_t* last_ids,
+                             hipStream_t s);
+hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uint32_t* ids,
+                             const int64_t* toff, const float* out_T, const int32_t* last_ids,
+                             const float* v_rgb, const float* v_T, float* v_screen,
+                             hipStream_t s);
+
+// First slot of every camera from the group scan (gs_project.hip).
+hipError_t launch_cam_offsets(const uint32_t* wg_scan, int64_t groups_per_cam, int C,
+                              const uint64_t* total, int64_t* out, hipStream_t s);
+
+}  // namespace gs

@@ -1,0 +1,170 @@
+// Tile intersection: count, emit, tile ranges.
+//
+// [VRAM] "The 4 GiB rule and the 2^31 limit": the exact number of
+// (splat, tile) intersections is accumulated in 64 bits and checked on
+// the host before anything is sized by it, the emit pass never writes
+// past the real allocation, and every buffer whose length follows nnz or
+// n_isects is addressed with 64-bit offsets. [VRAM] "16-bit packed AABB":
+// the tile rectangle is decoded from the 16-bit box codes. [BWD] section 4:
+// the tile offsets are kept for the backward.
+//
+// The sort is factored: slots are first sorted by their 32-bit depth key
+// (nnz elements), intersections are then emitted in that order and sorted
+// stably by tile id alone. Because each slot meets a tile at most once,
+// the result is exactly the stable sort of (tile << 32) | depth keys in
+// slot order, with a fraction of the bytes moved per intersection.
+#include "gs_internal.h"
+
+namespace gs {
+
+namespace {
+
+struct TileRect {
+  uint32_t tx0, ty0, tx1, ty1;  // [tx0, tx1) x [ty0, ty1)
+};
+
+// Decoded edge = q * extent / 65535, so with 16-pixel tiles the first tile
+// is floor(q0 * extent / (16 * 65535)) and the end is the ceiling of the
+// same for q1: integer arithmetic only.
+__device__ __forceinline__ TileRect rect_of(uint2 box, uint32_t W, uint32_t H) {
+  constexpr uint64_t D = uint64_t(kTile) * kQ16;
+  const uint64_t qx0 = box.x & 0xFFFFu, qy0 = box.x >> 16;
+  const uint64_t qx1 = box.y & 0xFFFFu, qy1 = box.y >> 16;
+  TileRect r;
+  r.tx0 = uint32_t(qx0 * W / D);
+  r.ty0 = uint32_t(qy0 * H / D);
+  r.tx1 = uint32_t((qx1 * W + D - 1) / D);
+  r.ty1 = uint32_t((qy1 * H + D - 1) / D);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t rect_count(const TileRect& r) {
+  const uint32_t wx = r.tx1 > r.tx0 ? r.tx1 - r.tx0 : 0u;
+  const uint32_t wy = r.ty1 > r.ty0 ? r.ty1 - r.ty0 : 0u;
+  return wx * wy;
+}
+
+// Per slot: depth key bits and identity value for the depth sort, tile
+// count, and the exact 64-bit total (one atomic per work-group).
+__global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* __restrict__ screen,
+                                                   const uint2* __restrict__ aabb16, uint32_t W,
+                                                   uint32_t H, uint32_t* __restrict__ dkeys,
+                                                   uint32_t* __restrict__ dvals,
+                                                   uint32_t* __restrict__ cnt, uint64_t* total) {
+  __shared__ uint64_t s_w[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t i = uint64_t(blockIdx.x) * 256 + tid;
+  uint64_t n = 0;
+  if (i < nnz) {
+    dkeys[i] = __float_as_uint(screen[i * kRow + 6]);
+    dvals[i] = uint32_t(i);
+    const uint32_t k = rect_count(rect_of(aabb16[i], W, H));
+    cnt[i] = k;
+    n = k;
+  }
+  const uint64_t incl = wave_incl_scan_u64(n);
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    const uint64_t b = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    if (b) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)b);
+  }
+}
+
+// Intersections of the slots in depth order: position i of the depth sort
+// holds slot order[i], whose entries start at offs[i]. Writes are clamped
+// to `cap` entries.
+__global__ __launch_bounds__(256) void k_isect_emit(
+    uint64_t nnz, const uint32_t* __restrict__ order, const uint2* __restrict__ aabb16,
+    const uint64_t* __restrict__ offs, const int64_t* __restrict__ cam_off, int C, uint32_t W,
+    uint32_t H, uint32_t tiles_x, uint32_t T, uint64_t cap, uint32_t* __restrict__ tkeys,
+    uint32_t* __restrict__ tvals) {
+  const uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= nnz) return;
+  const uint32_t s = order[i];
+  // camera of slot s: cameras own consecutive slot ranges
+  int lo = 0, hi = C - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (int64_t(s) >= cam_off[mid]) lo = mid; else hi = mid - 1;
+  }
+  const uint32_t tbase = uint32_t(lo) * T;
+  const TileRect r = rect_of(aabb16[s], W, H);
+  uint64_t o = offs[i];
+  for (uint32_t ty = r.ty0; ty < r.ty1; ++ty)
+    for (uint32_t tx = r.tx0; tx < r.tx1; ++tx) {
+      if (o < cap) {
+        tkeys[o] = tbase + ty * tiles_x + tx;
+        tvals[o] = s;
+      }
+      ++o;
+    }
+}
+
+// tile_offsets[t] = first sorted position whose tile id is >= t.
+__global__ __launch_bounds__(256) void k_tile_ranges(const uint32_t* __restrict__ tkeys,
+                                                    uint64_t n, uint64_t n_tiles,
+                                                    int64_t* __restrict__ toff) {
+  const uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i > n) return;
+  // ids are < n_tiles by construction; the clamps only keep the writes
+  // inside toff[0..n_tiles] whatever the keys hold
+  uint64_t cur = i < n ? tkeys[i] : n_tiles;
+  cur = cur < n_tiles ? cur : n_tiles;
+  int64_t prev = i > 0 ? int64_t(tkeys[i - 1]) : -1;
+  prev = prev < int64_t(n_tiles) ? prev : int64_t(n_tiles);
+  for (int64_t t = prev + 1; t <= int64_t(cur); ++t) toff[t] = int64_t(i);
+}
+
+__global__ __launch_bounds__(256) void k_compose_keys(const uint32_t* __restrict__ tkeys,
+                                                     const uint32_t* __restrict__ ids,
+                                                     const float* __restrict__ screen, uint64_t n,
+                                                     uint64_t* __restrict__ out) {
+  const uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t s = ids[i];
+  out[i] = (uint64_t(tkeys[i]) << 32) | __float_as_uint(screen[uint64_t(s) * kRow + 6]);
+}
+
+inline uint32_t grid_for(uint64_t n) { return uint32_t((n + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* aabb16, int W,
+                             int H, uint32_t* dkeys, uint32_t* dvals, uint32_t* cnt,
+                             uint64_t* total, hipStream_t s) {
+  if (nnz == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_isect_prep, dim3(grid_for(nnz)), dim3(256), 0, s, nnz, screen,
+                     reinterpret_cast<const uint2*>(aabb16), uint32_t(W), uint32_t(H), dkeys,
+                     dvals, cnt, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
+                             const uint64_t* offs, const int64_t* cam_off, int C, int W, int H,
+                             uint64_t cap, uint32_t* tkeys, uint32_t* tvals, hipStream_t s) {
+  if (nnz == 0) return hipSuccess;
+  const uint32_t tiles_x = uint32_t((W + kTile - 1) / kTile);
+  const uint32_t T = tiles_x * uint32_t((H + kTile - 1) / kTile);
+  hipLaunchKernelGGL(k_isect_emit, dim3(grid_for(nnz)), dim3(256), 0, s, nnz, order,
+                     reinterpret_cast<const uint2*>(aabb16), offs, cam_off, C, uint32_t(W),
+                     uint32_t(H), tiles_x, T, cap, tkeys, tvals);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_tile_ranges, dim3(grid_for(n + 1)), dim3(256), 0, s, tkeys, n, n_tiles,
+                     toff);
+  return hipGetLastError();
+}
+
+hipError_t launch_compose_keys(const uint32_t* tkeys, const uint32_t* ids, const float* screen,
+                               uint64_t n, uint64_t* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_compose_keys, dim3(grid_for(n)), dim3(256), 0, s, tkeys, ids, screen, n,
+                     out);
+  return hipGetLastError();
+}
+
+}  // namespace gs

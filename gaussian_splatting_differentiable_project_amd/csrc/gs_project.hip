@@ -1,0 +1,190 @@
+// Packed projection: visibility bitmask pass and compaction pass.
+//
+// [VRAM] "Bitmask compaction": the first pass projects every (camera,
+// Gaussian) pair and ORs the visibility predicate into work-group bit
+// words, writing one popcount per work-group; a scan over the C*N/128
+// counts follows; the second pass re-projects only the survivors and
+// recovers each one's exact output slot as (scanned count of earlier
+// work-groups) + (set bits before this lane).
+//
+// gfx950 mapping: a 128-lane work-group is two wave64s; each wave's
+// ballot *is* one 64-bit mask word, so the bit words need no shared
+// memory at all. Threads are Gaussian-major (lane = Gaussian, loop over
+// cameras), so the parameters are read once per Gaussian, not C times.
+#include <cmath>
+
+#include "gs_internal.h"
+
+namespace gs {
+
+namespace {
+
+__device__ __forceinline__ void zero_local(GaussLocal& G) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) G.mu[i] = 0.f, G.s[i] = 1.f;
+  G.qn = 1.f;
+  G.qh[0] = 1.f, G.qh[1] = G.qh[2] = G.qh[3] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) G.Rq[i] = G.M[i] = (i % 4 == 0) ? 1.f : 0.f;
+}
+
+__global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint64_t* mask,
+                                                             uint32_t* wg_count) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t g = int64_t(blockIdx.x) * kMaskGroup + tid;
+  const bool valid = g < a.N;
+  GaussLocal G;
+  if (valid)
+    gauss_local(a.means, a.quats, a.log_scales, g, G);
+  else
+    zero_local(G);
+  __shared__ uint32_t pc[2][2];
+  const float Wf = float(a.W), Hf = float(a.H);
+  for (int c = 0; c < a.C; ++c) {
+    const Camera k = load_camera(a.viewmats, a.Ks, c);
+    PairFwd P;
+    pair_fwd(k, G, Wf, Hf, P);
+    const uint64_t word = __ballot(valid && P.visible);
+    const int64_t p0 = int64_t(c) * a.N_pad + int64_t(blockIdx.x) * kMaskGroup;
+    if (lane == 0) {
+      mask[p0 / 64 + wave] = word;
+      pc[c & 1][wave] = uint32_t(__popcll(word));
+    }
+    __syncthreads();
+    if (tid == 0) wg_count[p0 / kMaskGroup] = pc[c & 1][0] + pc[c & 1][1];
+  }
+}
+
+template <int DEG>
+__global__ __launch_bounds__(kMaskGroup) void k_project_compact(ProjectArgs a,
+                                                                const uint64_t* __restrict__ mask,
+                                                                const uint32_t* __restrict__ wg_scan,
+                                                                float* __restrict__ screen,
+                                                                uint32_t* __restrict__ aabb16) {
+  constexpr int K = (DEG + 1) * (DEG + 1);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t g = int64_t(blockIdx.x) * kMaskGroup + tid;
+  const uint64_t lt = lanemask_lt();
+  // Which cameras see this Gaussian (mask words are wave-uniform loads).
+  bool any = false;
+  for (int c = 0; c < a.C; ++c) {
+    const int64_t p0 = int64_t(c) * a.N_pad + int64_t(blockIdx.x) * kMaskGroup;
+    const uint64_t mine = mask[p0 / 64 + wave];
+    any |= ((mine >> lane) & 1ull) != 0;
+  }
+  if (!any) return;
+  GaussLocal G;
+  gauss_local(a.means, a.quats, a.log_scales, g, G);
+  const float opac = 1.f / (1.f + expf(-a.opacity_logits[g]));
+  float shc[K * 3];
+  const float* shg = a.sh + g * (K * 3);
+#pragma unroll
+  for (int i = 0; i < K * 3; ++i) shc[i] = shg[i];
+  const float Wf = float(a.W), Hf = float(a.H);
+  for (int c = 0; c < a.C; ++c) {
+    const int64_t p0 = int64_t(c) * a.N_pad + int64_t(blockIdx.x) * kMaskGroup;
+    const uint64_t w0 = mask[p0 / 64], w1 = mask[p0 / 64 + 1];
+    const uint64_t mine = wave ? w1 : w0;
+    if (!((mine >> lane) & 1ull)) continue;
+    const int64_t slot = int64_t(wg_scan[p0 / kMaskGroup]) + (wave ? __popcll(w0) : 0) +
+                         __popcll(mine & lt);
+    const Camera k = load_camera(a.viewmats, a.Ks, c);
+    PairFwd P;
+    pair_fwd(k, G, Wf, Hf, P);
+    // colour toward the camera centre
+    float dx = G.mu[0] - k.cc[0], dy = G.mu[1] - k.cc[1], dz = G.mu[2] - k.cc[2];
+    const float inv = 1.f / sqrtf(dx * dx + dy * dy + dz * dz);
+    dx *= inv, dy *= inv, dz *= inv;
+    float Y[K];
+    sh_basis<DEG>(a.norm, dx, dy, dz, Y);
+    float rgb[3];
+#pragma unroll
+    for (int ch = 0; ch < 3; ++ch) {
+      float acc = 0.5f;
+#pragma unroll
+      for (int kk = 0; kk < K; ++kk) acc = fmaf(Y[kk], shc[3 * kk + ch], acc);
+      rgb[ch] = fmaxf(acc, 0.f);
+    }
+    float2* row = reinterpret_cast<float2*>(screen + slot * kRow);
+    row[0] = make_float2(P.u, P.v);
+    row[1] = make_float2(P.ca, P.cb);
+    row[2] = make_float2(P.cc, opac);
+    row[3] = make_float2(P.z, rgb[0]);
+    row[4] = make_float2(rgb[1], rgb[2]);
+    // 16-bit box: min edges round down, max edges round up, on the grid
+    // of 65535 steps over [0, extent].
+    const float fx0 = fminf(fmaxf(floorf(P.x0 * a.qsx), 0.f), 65535.f);
+    const float fy0 = fminf(fmaxf(floorf(P.y0 * a.qsy), 0.f), 65535.f);
+    const float fx1 = fminf(fmaxf(ceilf(P.x1 * a.qsx), 0.f), 65535.f);
+    const float fy1 = fminf(fmaxf(ceilf(P.y1 * a.qsy), 0.f), 65535.f);
+    uint2 box;
+    box.x = uint32_t(fx0) | (uint32_t(fy0) << 16);
+    box.y = uint32_t(fx1) | (uint32_t(fy1) << 16);
+    reinterpret_cast<uint2*>(aabb16)[slot] = box;
+  }
+}
+
+__global__ void k_cam_offsets(const uint32_t* __restrict__ wg_scan, int64_t groups_per_cam, int C,
+                              const uint64_t* __restrict__ total, int64_t* __restrict__ out) {
+  const int c = threadIdx.x + blockIdx.x * blockDim.x;
+  if (c > C) return;
+  if (c == C || groups_per_cam == 0)
+    out[c] = c == 0 ? 0 : int64_t(*total);
+  else
+    out[c] = int64_t(wg_scan[int64_t(c) * groups_per_cam]);
+}
+
+}  // namespace
+
+hipError_t launch_cam_offsets(const uint32_t* wg_scan, int64_t groups_per_cam, int C,
+                              const uint64_t* total, int64_t* out, hipStream_t s) {
+  const int n = C + 1;
+  hipLaunchKernelGGL(k_cam_offsets, dim3((n + 255) / 256), dim3(256), 0, s, wg_scan,
+                     groups_per_cam, C, total, out);
+  return hipGetLastError();
+}
+
+ShNorm sh_norm_table() {
+  // N_{l,m} = sqrt((2l+1)/(4 pi) * (l-m)!/(l+m)!), times sqrt(2) if m > 0.
+  const double pi = 3.14159265358979323846;
+  auto fact = [](int n) {
+    double f = 1.0;
+    for (int i = 2; i <= n; ++i) f *= i;
+    return f;
+  };
+  ShNorm t{};
+  int idx = 0;
+  for (int l = 0; l <= 3; ++l)
+    for (int m = 0; m <= l; ++m) {
+      double v = std::sqrt((2.0 * l + 1.0) / (4.0 * pi) * fact(l - m) / fact(l + m));
+      if (m > 0) v *= std::sqrt(2.0);
+      t.n[idx++] = float(v);
+    }
+  return t;
+}
+
+hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, uint32_t* wg_count,
+                               hipStream_t s) {
+  const int64_t blocks = a.N_pad / kMaskGroup;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_project_mask, dim3(uint32_t(blocks)), dim3(kMaskGroup), 0, s, a, mask,
+                     wg_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_compact(const ProjectArgs& a, const uint64_t* mask,
+                                  const uint32_t* wg_scan, float* screen, uint32_t* aabb16,
+                                  hipStream_t s) {
+  const int64_t blocks = a.N_pad / kMaskGroup;
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid{uint32_t(blocks)}, block{uint32_t(kMaskGroup)};
+  switch (a.deg) {
+    case 0: hipLaunchKernelGGL(k_project_compact<0>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;
+    case 1: hipLaunchKernelGGL(k_project_compact<1>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;
+    case 2: hipLaunchKernelGGL(k_project_compact<2>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;
+    default: hipLaunchKernelGGL(k_project_compact<3>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gs

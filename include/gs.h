@@ -1,0 +1,232 @@
+/*
+ * gs.h -- C ABI of libgs, a differentiable 16x16-tile Gaussian rasterizer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages on a 3D Gaussian Splatting trainer):
+ *  [VRAM]  "Spirula Studio VRAM deep dive: the splat x img category and
+ *          bitmask compaction, training ten million Gaussians in 8 GB"
+ *  [BWD]   "How Spirula Studio's backward pass sends image gradients back
+ *          to every Gaussian"
+ *  [PROF]  "3D Gaussian Splatting profiling guide: reading every step of
+ *          Spirula Studio with SS_PROFILE=1"
+ *  [GSPLAT] a deployment blog on the gsplat CUDA library, section 2.3
+ *          (a C API over caller-owned device pointers loaded by ctypes).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer is a DEVICE pointer unless its comment says (host).
+ *  - Every buffer is owned by the caller; the library allocates no device
+ *    memory and keeps no state between calls ([GSPLAT] 2.3: memory
+ *    lifetimes belong to the caller).
+ *  - `stream` is a hipStream_t passed as void*; all work is enqueued on it.
+ *    gs_project and gs_intersect each block the host once on `stream` to
+ *    read one 64-bit total (the host-side check of [VRAM] "The 4 GiB rule
+ *    and the 2^31 limit"); the other calls return without waiting.
+ *  - Inputs are fp32, structure-of-arrays:
+ *      means[N][3], quats[N][4] as (w,x,y,z) (need not be unit length),
+ *      log_scales[N][3], opacity_logits[N], sh[N][K][3] with
+ *      K = (sh_degree+1)^2 ordered l = 0..deg, m = -l..l,
+ *      viewmats[C][4][4] row-major world->camera (x right, y down,
+ *      z forward), Ks[C][3][3] pinhole intrinsics. All C cameras share one
+ *      W x H image size.
+ *  - Pair index p = c * N_pad + g (camera-major), N_pad = N rounded up to
+ *    GS_MASK_GROUP. A "slot" is the rank of a visible pair in p order.
+ *  - A screen row ([VRAM] per-element cost table, proj.screen, 40 bytes) is
+ *    10 floats: u, v, conic_a, conic_b, conic_c, opacity, depth z, r, g, b.
+ *  - Returns GS_OK (0) or a negative status; no call aborts or prints.
+ *    On an error nothing is written past any stated capacity.
+ */
+#ifndef GS_H
+#define GS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  GS_OK = 0,
+  GS_E_INVALID = -1,   /* null required pointer or out-of-range argument */
+  GS_E_CAPACITY = -2,  /* an output is too small; required count returned */
+  GS_E_WORKSPACE = -3, /* workspace too small; required bytes returned */
+  GS_E_OVERFLOW = -4,  /* a count exceeds the width of its storage type */
+  GS_E_HIP = -5,       /* HIP runtime error (launch, copy, sync) */
+  GS_E_DEVICE = -6     /* a kernel reported an internal error */
+};
+
+#define GS_TILE 16        /* tiles are 16 x 16 pixels */
+#define GS_MASK_GROUP 128 /* pairs per visibility work-group ([VRAM]
+                             "Bitmask compaction": one popcount per
+                             128-lane work-group) */
+#define GS_ROW 10         /* floats per screen row */
+
+/* Text of a status code (static storage). */
+const char* gs_status_str(int status);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gs_version(void);
+
+/* ---------------------------------------------------------------------
+ * Buffer sizes (host only, no GPU work).
+ *
+ * gs_pad_n: N_pad = ceil(N / 128) * 128.
+ * Sizes for gs_project, counted in elements:
+ *   mask      uint64[C * N_pad / 64]    (bit p%64 of word p/64 = pair p)
+ *   wg_count  uint32[C * N_pad / 128]   (popcount of each 128-pair group)
+ *   wg_scan   uint32[C * N_pad / 128]   (its exclusive prefix sum)
+ * These are the [VRAM] cost-table rows proj.mask (C*N/8 bytes) and
+ * proj.block_count / proj.scan (C*N/32 bytes each).
+ * gs_project_workspace_bytes: device scratch needed by gs_project.
+ * gs_intersect_workspace_bytes: device scratch needed by gs_intersect for
+ * nnz visible pairs producing n_isects (tile, pair) intersections.
+ * ------------------------------------------------------------------- */
+int64_t gs_pad_n(int64_t N);
+uint64_t gs_project_workspace_bytes(int64_t N, int32_t C);
+uint64_t gs_intersect_workspace_bytes(int32_t C, int32_t W, int32_t H,
+                                      int64_t nnz, int64_t n_isects);
+
+/* ---------------------------------------------------------------------
+ * gs_project -- packed projection of C cameras x N Gaussians.
+ * [VRAM] "Bitmask compaction" and "16-bit packed AABB".
+ *
+ * Pass 1 tests every (camera, Gaussian) pair for visibility (depth beyond
+ * the near plane and a 3-sigma screen box that overlaps the image), ORs
+ * the predicate into bit-words with wavefront ballots and writes one
+ * popcount per 128-pair group. A scan of those counts gives each group's
+ * first slot and nnz. Pass 2 re-projects only visible pairs and writes
+ * screen row `slot` = scan of earlier groups + set bits before the pair:
+ *   screen[nnz][10] fp32: u, v, conic (a,b,c) of the inverse 2D covariance
+ *     (EWA projection plus 0.3 px blur), sigmoid(opacity_logit), camera
+ *     depth z, RGB from the SH coefficients toward the camera centre
+ *     (max(0, sum + 0.5)).
+ *   aabb16[nnz][2] uint32: the 3-sigma box clamped to the image on a
+ *     uniform 65535-step grid over [0, W] x [0, H], min edges rounded
+ *     down and max edges rounded up: word0 = qx0 | qy0 << 16,
+ *     word1 = qx1 | qy1 << 16.
+ *
+ * Outputs: mask, wg_count, wg_scan (sizes above); screen and aabb16 with
+ * room for screen_capacity rows; (host) *nnz_out; (host, nullable)
+ * cam_offsets_out[C+1]: first slot of each camera, cam_offsets_out[C]=nnz.
+ * workspace: device scratch of gs_project_workspace_bytes(N, C) bytes.
+ * Errors: GS_E_INVALID for N < 0, C < 1, W or H outside [1, 65535],
+ * sh_degree outside [0, 3], or a null required pointer.
+ * GS_E_CAPACITY when nnz > screen_capacity: *nnz_out and mask, wg_count,
+ * wg_scan are valid, screen/aabb16 are untouched. GS_E_OVERFLOW when
+ * nnz >= 2^31 (slots are 31-bit).
+ * ------------------------------------------------------------------- */
+int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
+               int32_t sh_degree, const float* means, const float* quats,
+               const float* log_scales, const float* opacity_logits,
+               const float* sh, const float* viewmats, const float* Ks,
+               uint64_t* mask, uint32_t* wg_count, uint32_t* wg_scan,
+               float* screen, uint32_t* aabb16, int64_t screen_capacity,
+               void* workspace, uint64_t workspace_bytes,
+               int64_t* nnz_out, int64_t* cam_offsets_out);
+
+/* ---------------------------------------------------------------------
+ * gs_intersect -- (tile, pair) intersections, sorted per tile by depth.
+ * [VRAM] "The 4 GiB rule and the 2^31 limit" (exact 64-bit total checked
+ * on the host before anything is sized by it; 64-bit addressing for every
+ * buffer sized by nnz or n_isects), the cost-table row isect.ids_a/b
+ * (keys (tile_id << 32) | depth); [BWD] section 4 (tile offsets and the
+ * flattened intersection list kept for the backward).
+ *
+ * A pair's tile rectangle comes from its aabb16 words with integer
+ * arithmetic: tx0 = floor(qx0*W / (16*65535)), tx1 = ceil(qx1*W /
+ * (16*65535)) (exclusive), same for y with H. Its key for tile
+ * (tx, ty) of camera c is (c*T + ty*ceil(W/16) + tx) << 32 | bits(z) with
+ * T = ceil(W/16)*ceil(H/16) and z the fp32 depth of its screen row. The
+ * result equals a stable sort of those 64-bit keys emitted slot by slot:
+ * within a tile, entries are ordered by depth, then by slot.
+ *
+ * Inputs: screen[nnz][10], aabb16[nnz][2] from gs_project, and (host)
+ * cam_offsets[C+1] (first slot of every camera).
+ * Outputs: flatten_ids[n_isects] (uint32 slot of every sorted entry,
+ * capacity isect_capacity); tile_offsets[C*T+1] int64 (entries of global
+ * tile t are flatten_ids[tile_offsets[t] .. tile_offsets[t+1]));
+ * sorted_keys[n_isects] (nullable: the sorted 64-bit keys);
+ * (host) *n_isects_out; (host) *workspace_needed_out.
+ * Errors: GS_E_INVALID as for gs_project or nnz < 0;
+ * GS_E_OVERFLOW if nnz >= 2^31; GS_E_CAPACITY if n_isects >
+ * isect_capacity; GS_E_WORKSPACE if workspace_bytes is short (the bytes
+ * needed are returned; before the count is known this is the lower bound
+ * for counting, after it the full amount). Call again after growing.
+ * ------------------------------------------------------------------- */
+int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz,
+                 const float* screen, const uint32_t* aabb16,
+                 const int64_t* cam_offsets, void* workspace,
+                 uint64_t workspace_bytes, uint32_t* flatten_ids,
+                 int64_t isect_capacity, int64_t* tile_offsets,
+                 uint64_t* sorted_keys, int64_t* n_isects_out,
+                 uint64_t* workspace_needed_out);
+
+/* ---------------------------------------------------------------------
+ * gs_rasterize_fwd -- per-tile front-to-back alpha compositing.
+ * [PROF] kernel rasterize_fwd; [BWD] section 4 (what the forward saves).
+ *
+ * For every pixel (centre (j+0.5, i+0.5)) of camera c, over the entries of
+ * its tile in sorted order: d = (u - px, v - py),
+ * sigma = (a dx^2 + c dy^2)/2 + b dx dy, alpha = min(0.99, o exp(-sigma));
+ * entries with sigma < 0 or alpha < 1/255 are skipped; if
+ * T*(1-alpha) < 1e-4 the walk stops before that entry; otherwise
+ * rgb += colour*alpha*T and T *= 1-alpha.
+ * Outputs (all C x H x W, row-major): out_rgb[C][H][W][3] (premultiplied,
+ * no background), out_T[C][H][W] final transmittance, last_ids[C][H][W]
+ * local index (within the tile's list) of the last composited entry, -1 if
+ * none. Errors: GS_E_INVALID.
+ * ------------------------------------------------------------------- */
+int gs_rasterize_fwd(void* stream, int32_t C, int32_t W, int32_t H,
+                     const float* screen, const uint32_t* flatten_ids,
+                     const int64_t* tile_offsets, float* out_rgb,
+                     float* out_T, int32_t* last_ids);
+
+/* ---------------------------------------------------------------------
+ * gs_rasterize_bwd -- gradient of L = <v_rgb, out_rgb> + <v_T, out_T>
+ * with respect to every screen row. [BWD] section 4
+ * (rasterize_to_pixels_3dgs_bwd: the pixel gradient is split over the
+ * Gaussians on that pixel in proportion to their alpha contribution, in
+ * blend order, and summed with atomics into the fp32 screen gradients).
+ *
+ * Walks each pixel's entries back to front from last_ids, recovering the
+ * transmittance before entry i as T_{i+1} / (1 - alpha_i). Writes
+ * v_screen[nnz][10] fp32 (zeroed by this call first; the depth column is
+ * 0). v_T may be null (taken as zero). Entries whose alpha hit the 0.99
+ * clamp get no opacity or position/conic gradient. Summation order is not
+ * fixed (float atomics), so results vary in the last bits run to run.
+ * ------------------------------------------------------------------- */
+int gs_rasterize_bwd(void* stream, int32_t C, int32_t W, int32_t H,
+                     int64_t nnz, const float* screen,
+                     const uint32_t* flatten_ids, const int64_t* tile_offsets,
+                     const float* out_T, const int32_t* last_ids,
+                     const float* v_rgb, const float* v_T, float* v_screen);
+
+/* ---------------------------------------------------------------------
+ * gs_project_bwd -- screen-row gradients to parameter gradients.
+ * [BWD] section 5 (projection_3dgs_backward: the chain rule through the
+ * intrinsics and extrinsics; gradients are fp32) and section 6 (only the
+ * first sub-batch zeroes the accumulators).
+ *
+ * For each Gaussian, over every camera whose mask bit is set, reads
+ * v_screen[slot] (slot from wg_scan and the mask, as gs_project assigned
+ * it) and applies the exact chain rule of the projection: means (camera
+ * transform, the Jacobian's dependence on the camera-space point and the
+ * SH view direction), raw quaternions (through normalisation), log-scales,
+ * opacity logits and SH coefficients (zero where the colour clamp at 0 is
+ * active). Nothing flows through the radius, box or visibility test.
+ * Outputs v_means[N][3], v_quats[N][4], v_log_scales[N][3],
+ * v_opacity_logits[N], v_sh[N][K][3]: overwritten when accumulate == 0
+ * (zeros for Gaussians visible nowhere), added to when accumulate != 0.
+ * ------------------------------------------------------------------- */
+int gs_project_bwd(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
+                   int32_t sh_degree, const float* means, const float* quats,
+                   const float* log_scales, const float* opacity_logits,
+                   const float* sh, const float* viewmats, const float* Ks,
+                   const uint64_t* mask, const uint32_t* wg_scan,
+                   const float* v_screen, float* v_means, float* v_quats,
+                   float* v_log_scales, float* v_opacity_logits, float* v_sh,
+                   int32_t accumulate);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_H */

@@ -1,0 +1,132 @@
+"""Parity helpers: run the HIP path through its C ABI and compare with the
+oracle, excluding the decisions an fp32 kernel cannot reproduce from an
+fp64 reference ("fragile" items, decided from the oracle's own values).
+
+Tolerances (the pages' rasterizer targets):
+* mask, nnz, per-tile counts and sorted order: bit-exact on non-fragile
+  pairs and pixels;
+* images: max-abs 1e-4 on non-fragile pixels;
+* gradients: relative L2 1e-3 per tensor.
+
+Fragility windows (readings): a pair is fragile if, in fp64, its depth is
+within a relative 1e-5 of the near plane, a box edge is within TAU_PX of
+the image border it is tested against, or a box edge scaled to the 16-bit
+grid lies within TAU_PX (in codes) of a grid point that decides a tile
+crossing. TAU_PX = max(1e-5 px, 8 ulp32 of the coordinate) -- the
+literal 1e-5 px is below fp32 resolution past 128 px. A pixel is fragile
+if any entry it evaluates has alpha within a relative 1e-4 of 1/255, if
+its stop test is within a relative 1e-3 of 1e-4, or if its tile is
+touched by a fragile pair.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import raster as oraster
+from oracle.intersect import TILE, tile_rects_from_aabb16
+
+IMG_TOL = 1e-4
+GRAD_TOL = 1e-3
+Q16 = 65535
+
+
+def ulp32(x):
+    x = np.abs(np.asarray(x, np.float64)).astype(np.float32)
+    return (np.nextafter(x, np.float32(np.inf)) - x).astype(np.float64)
+
+
+def tau_px(coord):
+    return np.maximum(1e-5, 8.0 * ulp32(np.maximum(np.abs(coord), 1.0)))
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def unpack_mask(words: np.ndarray, n_pairs: int) -> np.ndarray:
+    w = np.asarray(words).view(np.uint64)
+    bits = (w[:, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)
+    return bits.astype(bool).ravel()[:n_pairs]
+
+
+def _tile_fragile_edge(e, extent, is_min, tau):
+    """Does moving edge e by +-tau change the tile its 16-bit code decides?"""
+    s = np.float32(Q16) / np.float32(extent)
+    lo = (np.asarray(e - tau, np.float64)).astype(np.float32) * s
+    hi = (np.asarray(e + tau, np.float64)).astype(np.float32) * s
+    f = np.floor if is_min else np.ceil
+    qlo = np.clip(f(lo), 0, Q16).astype(np.int64)
+    qhi = np.clip(f(hi), 0, Q16).astype(np.int64)
+    D = TILE * Q16
+    if is_min:
+        return (qlo * extent) // D != (qhi * extent) // D
+    return -((-(qlo * extent)) // D) != -((-(qhi * extent)) // D)
+
+
+def fragile_pairs(scene: dict, proj) -> np.ndarray:
+    """Boolean [C * N_pad]: pairs whose visibility, tile rect or key an fp32
+    kernel may decide differently from the fp64 oracle."""
+    N, C, W, H, Np = scene["N"], scene["C"], scene["W"], scene["H"], proj.N_pad
+    frag = np.zeros(C * Np, bool)
+    for c in range(C):
+        pc = oracle.project_camera(scene["means"], scene["quats"], scene["log_scales"],
+                                   scene["opacity_logits"], scene["sh"], scene["viewmats"][c],
+                                   scene["Ks"][c], W, H, scene["sh_degree"])
+        u, v, r, z = pc["u"], pc["v"], pc["r"], pc["z"]
+        f = np.abs(z - oracle.project.NEAR) <= 1e-5 * oracle.project.NEAR
+        with np.errstate(invalid="ignore"):
+            for a, ext in ((u, W), (v, H)):
+                t = tau_px(np.abs(a) + r)
+                f |= np.abs(a + r) <= t          # box max edge vs 0
+                f |= np.abs(a - r - ext) <= t    # box min edge vs extent
+                lo = np.maximum(a - r, 0.0)
+                hi = np.minimum(a + r, float(ext))
+                vis = pc["visible"]
+                f |= vis & _tile_fragile_edge(lo, ext, True, t)
+                f |= vis & _tile_fragile_edge(hi, ext, False, t)
+        f |= ~np.isfinite(u) | ~np.isfinite(v)
+        frag[c * Np: c * Np + N] = f & (z > 0)
+    return frag
+
+
+def fragile_pixels(screen, flatten_ids, tile_offsets, C, W, H, tiles_touched=None):
+    """Boolean [C, H, W]: pixels whose composite crosses a threshold within
+    the fragility window (evaluated by the oracle's own walk)."""
+    tiles_x = (W + TILE - 1) // TILE
+    T_per = tiles_x * ((H + TILE - 1) // TILE)
+    out = np.zeros((C, H, W), bool)
+    screen = np.asarray(screen, np.float64)
+    for t in range(C * T_per):
+        c, tl = divmod(t, T_per)
+        ii, jj = oraster._tile_pixels(tl, tiles_x, W, H)
+        if tiles_touched is not None and tiles_touched[t]:
+            out[c, ii, jj] = True
+            continue
+        ids = np.asarray(flatten_ids[int(tile_offsets[t]):int(tile_offsets[t + 1])], np.int64)
+        if ids.size == 0:
+            continue
+        rows = screen[ids]
+        _, _, _, _, rec = oraster._walk_tile(rows, jj + 0.5, ii + 0.5, record=True)
+        a = rec["alpha"]
+        reached = np.ones_like(a, bool)
+        bad = reached & (np.abs(a - oraster.ALPHA_MIN) <= 1e-4 * oraster.ALPHA_MIN)
+        Tn = rec["Tb"] * (1.0 - a)
+        bad |= (a >= oraster.ALPHA_MIN) & (np.abs(Tn - oraster.T_STOP) <= 1e-3 * oraster.T_STOP)
+        out[c, ii, jj] = bad.any(axis=1)
+    return out
+
+
+def to_dev(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def u32_as_i32(a):
+    return np.ascontiguousarray(np.asarray(a, np.uint32)).view(np.int32)
