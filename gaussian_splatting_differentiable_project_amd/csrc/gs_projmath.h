@@ -121,8 +121,18 @@ struct PairFwd {
 __device__ __forceinline__ void pair_fwd(const Camera& k, const GaussLocal& G, float Wimg,
                                          float Himg, PairFwd& P) {
   const float mx = G.mu[0], my = G.mu[1], mz = G.mu[2];
-  P.x = fmaf(k.R[0], mx, fmaf(k.R[1], my, fmaf(k.R[2], mz, k.t[0])));
-  P.y = fmaf(k.R[3], mx, fmaf(k.R[4], my, fmaf(k.R[5], mz, k.t[1])));
+  // The screen position is computed in fp64 and rounded once: the 40-byte
+  // row stores it in fp32, and an fp32 evaluation of fx x / z + cx would
+  // add several ulps at the image edges (about 5e-4 px at 1000 px).
+  const double dmx = mx, dmy = my, dmz = mz;
+  const double xd = fma(double(k.R[0]), dmx, fma(double(k.R[1]), dmy, fma(double(k.R[2]), dmz, double(k.t[0]))));
+  const double yd = fma(double(k.R[3]), dmx, fma(double(k.R[4]), dmy, fma(double(k.R[5]), dmz, double(k.t[1]))));
+  const double zd = fma(double(k.R[6]), dmx, fma(double(k.R[7]), dmy, fma(double(k.R[8]), dmz, double(k.t[2]))));
+  const double izd = 1.0 / zd;
+  P.u = float(fma(double(k.fx), xd * izd, double(k.cx)));
+  P.v = float(fma(double(k.fy), yd * izd, double(k.cy)));
+  P.x = float(xd);
+  P.y = float(yd);
   P.z = depth_z32(k, mx, my, mz);
   const float z = P.z;
   const float iz = 1.f / z;
@@ -148,8 +158,6 @@ __device__ __forceinline__ void pair_fwd(const Camera& k, const GaussLocal& G, f
   P.ca = P.S11 * idet;
   P.cb = -P.S01 * idet;
   P.cc = P.S00 * idet;
-  P.u = fmaf(k.fx, P.x * iz, k.cx);
-  P.v = fmaf(k.fy, P.y * iz, k.cy);
   const float mid = 0.5f * (P.S00 + P.S11);
   const float lam = mid + sqrtf(fmaxf(0.f, mid * mid - P.det));
   P.r = 3.f * sqrtf(lam);

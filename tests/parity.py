@@ -14,9 +14,10 @@ the image border it is tested against, or a box edge scaled to the 16-bit
 grid lies within TAU_PX (in codes) of a grid point that decides a tile
 crossing. TAU_PX = max(1e-5 px, 8 ulp32 of the coordinate) -- the
 literal 1e-5 px is below fp32 resolution past 128 px. A pixel is fragile
-if any entry it evaluates has alpha within a relative 1e-4 of 1/255, if
-its stop test is within a relative 1e-3 of 1e-4, or if its tile is
-touched by a fragile pair.
+if any entry it reaches has alpha within a relative 2e-5 of 1/255 (the
+fp32 error of sigma near the threshold is a few 1e-6), if its stop test
+is within a relative 1e-4 of 1e-4 (T is a product of up to hundreds of
+rounded factors), or if its tile is touched by a fragile pair.
 """
 from __future__ import annotations
 
@@ -25,10 +26,13 @@ import torch
 
 import oracle
 from oracle import raster as oraster
-from oracle.intersect import TILE, tile_rects_from_aabb16
+from oracle.intersect import TILE
+from oracle.project import NEAR
 
 IMG_TOL = 1e-4
 GRAD_TOL = 1e-3
+ALPHA_WIN = 2e-5   # relative window around alpha = 1/255
+T_WIN = 1e-4       # relative window around the T = 1e-4 stop
 Q16 = 65535
 
 
@@ -78,7 +82,7 @@ def fragile_pairs(scene: dict, proj) -> np.ndarray:
                                    scene["opacity_logits"], scene["sh"], scene["viewmats"][c],
                                    scene["Ks"][c], W, H, scene["sh_degree"])
         u, v, r, z = pc["u"], pc["v"], pc["r"], pc["z"]
-        f = np.abs(z - oracle.project.NEAR) <= 1e-5 * oracle.project.NEAR
+        f = np.abs(z - NEAR) <= 1e-5 * NEAR
         with np.errstate(invalid="ignore"):
             for a, ext in ((u, W), (v, H)):
                 t = tau_px(np.abs(a) + r)
@@ -113,10 +117,14 @@ def fragile_pixels(screen, flatten_ids, tile_offsets, C, W, H, tiles_touched=Non
         rows = screen[ids]
         _, _, _, _, rec = oraster._walk_tile(rows, jj + 0.5, ii + 0.5, record=True)
         a = rec["alpha"]
-        reached = np.ones_like(a, bool)
-        bad = reached & (np.abs(a - oraster.ALPHA_MIN) <= 1e-4 * oraster.ALPHA_MIN)
         Tn = rec["Tb"] * (1.0 - a)
-        bad |= (a >= oraster.ALPHA_MIN) & (np.abs(Tn - oraster.T_STOP) <= 1e-3 * oraster.T_STOP)
+        # entries a pixel reaches: up to and including the one that stops it
+        stops = (a >= oraster.ALPHA_MIN) & (Tn < oraster.T_STOP) & ~rec["comp"]
+        first = np.where(stops.any(1), stops.argmax(1), a.shape[1])
+        reached = np.arange(a.shape[1])[None, :] <= first[:, None]
+        bad = reached & (np.abs(a - oraster.ALPHA_MIN) <= ALPHA_WIN * oraster.ALPHA_MIN)
+        bad |= reached & (a >= oraster.ALPHA_MIN) & \
+            (np.abs(Tn - oraster.T_STOP) <= T_WIN * oraster.T_STOP)
         out[c, ii, jj] = bad.any(axis=1)
     return out
 
