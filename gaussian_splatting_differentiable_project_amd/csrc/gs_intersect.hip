@@ -53,14 +53,15 @@ __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* _
                                                    uint32_t* __restrict__ cnt, uint64_t* total) {
   __shared__ uint64_t s_w[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint64_t i = uint64_t(blockIdx.x) * 256 + tid;
   uint64_t n = 0;
-  if (i < nnz) {
+  // grid-stride, so few blocks contend for the one 64-bit total
+  const uint64_t stride = uint64_t(gridDim.x) * 256;
+  for (uint64_t i = uint64_t(blockIdx.x) * 256 + tid; i < nnz; i += stride) {
     dkeys[i] = __float_as_uint(screen[i * kRow + 6]);
     dvals[i] = uint32_t(i);
     const uint32_t k = rect_count(rect_of(aabb16[i], W, H));
     cnt[i] = k;
-    n = k;
+    n += k;
   }
   const uint64_t incl = wave_incl_scan_u64(n);
   if (lane == 63) s_w[wave] = incl;
@@ -134,7 +135,9 @@ hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* 
                              int H, uint32_t* dkeys, uint32_t* dvals, uint32_t* cnt,
                              uint64_t* total, hipStream_t s) {
   if (nnz == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_isect_prep, dim3(grid_for(nnz)), dim3(256), 0, s, nnz, screen,
+  uint32_t blocks = grid_for(nnz);
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(k_isect_prep, dim3(blocks), dim3(256), 0, s, nnz, screen,
                      reinterpret_cast<const uint2*>(aabb16), uint32_t(W), uint32_t(H), dkeys,
                      dvals, cnt, total);
   return hipGetLastError();

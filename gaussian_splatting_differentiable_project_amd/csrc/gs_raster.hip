@@ -15,22 +15,53 @@
 // gradient over the PPT pixels of a lane, then over the wave with DPP row
 // rotations, and issues one fp32 atomic per field per wave -- and only
 // for waves where some pixel actually composited the entry.
+#include <cstdlib>
+
 #include "gs_internal.h"
 
 namespace gs {
 
 namespace {
 
-__device__ __forceinline__ float fast_exp_neg(float s) {
-  // exp(-s) through the hardware base-2 exponential
-  return __builtin_amdgcn_exp2f(-s * kLog2e);
+// Per-entry constants staged in LDS. The conic's diagonal is stored
+// halved and the opacity as log2, so that
+//   sigma = a' dx^2 + c' dy^2 + b dx dy   (a' = a/2, c' = c/2)
+//   raw   = exp2(log2(o) - sigma log2(e)) = o exp(-sigma)
+// costs six multiply/adds and one exponential per pixel. The forward and
+// the backward evaluate exactly the same expressions (explicit fused
+// operations, no contraction freedom), so they take the same skip
+// decisions on every (pixel, entry).
+struct Staged {
+  float4 a;  // u, v, a', c'
+  float4 b;  // b, log2(o), r, g
+  float2 c;  // blue, 1/o
+};
+
+__device__ __forceinline__ Staged stage_row(const float* __restrict__ screen, uint32_t s) {
+  const float2* r = reinterpret_cast<const float2*>(screen + int64_t(s) * kRow);
+  const float2 r0 = r[0], r1 = r[1], r2 = r[2], r3 = r[3], r4 = r[4];
+  Staged e;
+  e.a = make_float4(r0.x, r0.y, 0.5f * r1.x, 0.5f * r2.x);
+  e.b = make_float4(r1.y, __builtin_amdgcn_logf(r2.y), r3.y, r4.x);
+  e.c = make_float2(r4.y, __builtin_amdgcn_rcpf(r2.y));
+  return e;
 }
 
-// sigma = (a dx^2 + c dy^2) / 2 + b dx dy, written with explicit fused
-// operations only, so the forward and the backward (separate kernels)
-// round it identically and take the same skip decisions.
-__device__ __forceinline__ float splat_sigma(float a, float b, float c, float dx, float dy) {
-  return fmaf(b * dx, dy, 0.5f * fmaf(a, dx * dx, c * (dy * dy)));
+struct Eval {
+  float dx, dy, dxx, dyy, dxy, raw, alpha;
+};
+
+__device__ __forceinline__ Eval eval_splat(const float4& A, const float4& Bv, float px, float py) {
+  Eval e;
+  e.dx = A.x - px;
+  e.dy = A.y - py;
+  e.dxx = e.dx * e.dx;
+  e.dyy = e.dy * e.dy;
+  e.dxy = e.dx * e.dy;
+  const float sig = fmaf(A.z, e.dxx, fmaf(A.w, e.dyy, Bv.x * e.dxy));
+  e.raw = __builtin_amdgcn_exp2f(fmaf(-sig, kLog2e, Bv.y));
+  e.alpha = fminf(kAlphaMax, e.raw);
+  return e;
 }
 
 template <int PPT>
@@ -40,9 +71,9 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
     float* __restrict__ out_rgb, float* __restrict__ out_T, int32_t* __restrict__ last_ids) {
   constexpr int NT = kTilePix / PPT;
   constexpr int B = NT;
-  __shared__ float4 s_a[B];  // u, v, conic a, conic b
-  __shared__ float4 s_b[B];  // conic c, opacity, r, g
-  __shared__ float s_c[B];   // b
+  __shared__ float4 s_a[B];
+  __shared__ float4 s_b[B];
+  __shared__ float s_c[B];
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.x;
   const int c = int(t / T);
@@ -53,7 +84,6 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
   float px[PPT], py[PPT], Tr[PPT], cr[PPT], cg[PPT], cb[PPT];
   int last[PPT];
   bool live[PPT];
-  int64_t pix[PPT];
   bool inside[PPT];
 #pragma unroll
   for (int k = 0; k < PPT; ++k) {
@@ -63,7 +93,6 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
     live[k] = inside[k];
     px[k] = float(X) + 0.5f;
     py[k] = float(Yp) + 0.5f;
-    pix[k] = (int64_t(c) * H + Yp) * W + X;
     Tr[k] = 1.f;
     cr[k] = cg[k] = cb[k] = 0.f;
     last[k] = -1;
@@ -75,35 +104,31 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
     for (int k = 0; k < PPT; ++k) any_live |= live[k];
     if (__syncthreads_count(any_live) == 0) break;
     if (b0 + tid < end) {
-      const uint32_t s = ids[b0 + tid];
-      const float2* r = reinterpret_cast<const float2*>(screen + int64_t(s) * kRow);
-      const float2 r0 = r[0], r1 = r[1], r2 = r[2], r3 = r[3], r4 = r[4];
-      s_a[tid] = make_float4(r0.x, r0.y, r1.x, r1.y);
-      s_b[tid] = make_float4(r2.x, r2.y, r3.y, r4.x);
-      s_c[tid] = r4.y;
+      const Staged e = stage_row(screen, ids[b0 + tid]);
+      s_a[tid] = e.a;
+      s_b[tid] = e.b;
+      s_c[tid] = e.c.x;
     }
     __syncthreads();
     const int nb = int((end - b0) < B ? (end - b0) : B);
+    const int lid0 = int(b0 - start);
     for (int j = 0; j < nb; ++j) {
       const float4 A = s_a[j], Bv = s_b[j];
       const float cblue = s_c[j];
-      const int lid = int(b0 - start) + j;
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
-        const float dx = A.x - px[k], dy = A.y - py[k];
-        const float sig = splat_sigma(A.z, A.w, Bv.x, dx, dy);
-        const float alpha = fminf(kAlphaMax, Bv.y * fast_exp_neg(sig));
-        const float Tn = Tr[k] * (1.f - alpha);
-        const bool use = live[k] && sig >= 0.f && alpha >= kAlphaMin;
+        const Eval e = eval_splat(A, Bv, px[k], py[k]);
+        const float Tn = Tr[k] * (1.f - e.alpha);
+        const bool use = live[k] && e.alpha >= kAlphaMin;
         const bool stop = use && Tn < kTStop;
         if (stop) live[k] = false;
         if (use && !stop) {
-          const float w = alpha * Tr[k];
+          const float w = e.alpha * Tr[k];
           cr[k] = fmaf(Bv.z, w, cr[k]);
           cg[k] = fmaf(Bv.w, w, cg[k]);
           cb[k] = fmaf(cblue, w, cb[k]);
           Tr[k] = Tn;
-          last[k] = lid;
+          last[k] = lid0 + j;
         }
       }
     }
@@ -111,12 +136,78 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
 #pragma unroll
   for (int k = 0; k < PPT; ++k) {
     if (!inside[k]) continue;
-    out_rgb[3 * pix[k] + 0] = cr[k];
-    out_rgb[3 * pix[k] + 1] = cg[k];
-    out_rgb[3 * pix[k] + 2] = cb[k];
-    out_T[pix[k]] = Tr[k];
-    last_ids[pix[k]] = last[k];
+    const int p = tid + k * NT;
+    const int64_t pix = (int64_t(c) * H + ty * kTile + (p >> 4)) * W + tx * kTile + (p & 15);
+    out_rgb[3 * pix + 0] = cr[k];
+    out_rgb[3 * pix + 1] = cg[k];
+    out_rgb[3 * pix + 2] = cb[k];
+    out_T[pix] = Tr[k];
+    last_ids[pix] = last[k];
   }
+}
+
+// DPP lane permutations inside 16-lane rows (all lanes active).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowMirror = 0x140;      // lane reads 15 - l within its row
+constexpr int kDppRowHalfMirror = 0x141;  // lane reads 7 - l within its half-row
+constexpr int kDppXor2 = 0x4E;            // quad_perm [2,3,0,1]
+constexpr int kDppXor1 = 0xB1;            // quad_perm [1,0,3,2]
+
+// Sum nine per-lane values over the wave and add the totals to
+// dst[field] with one atomic instruction. Transposed reduction: at each
+// step a lane pairs with a partner differing in one lane bit and keeps the
+// sums of half of the remaining values (9 -> 5 -> 3 -> 2 -> 1), so a lane
+// ends with one value summed over its 16-lane row; two exchanges across
+// rows finish the sum. Lanes 0..15 then hold: lane -> value index
+// 0,1,2,-,3,4,-,-,5,6,7,-,8,-,-,- (value index -> screen field
+// 0,1,2,3,4,5,7,8,9). Must be called with all 64 lanes active.
+__device__ __forceinline__ void wave_reduce9_atomic(const float (&v)[9], float* dst) {
+  // Every DPP read is evaluated by all lanes before any select: a DPP
+  // inside a conditional would read lanes that are switched off.
+  const int lane = __lane_id();
+  bool hi = (lane & 8) != 0;
+  float w1[5];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo_s = v[k] + dpp<kDppRowMirror>(v[k]);
+    const float hi_s = v[5 + k] + dpp<kDppRowMirror>(v[5 + k]);
+    w1[k] = hi ? hi_s : lo_s;
+  }
+  {
+    const float lo_s = v[4] + dpp<kDppRowMirror>(v[4]);
+    w1[4] = hi ? 0.f : lo_s;
+  }
+  hi = (lane & 4) != 0;
+  float w2[3];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float lo_s = w1[k] + dpp<kDppRowHalfMirror>(w1[k]);
+    const float hi_s = w1[3 + k] + dpp<kDppRowHalfMirror>(w1[3 + k]);
+    w2[k] = hi ? hi_s : lo_s;
+  }
+  {
+    const float lo_s = w1[2] + dpp<kDppRowHalfMirror>(w1[2]);
+    w2[2] = hi ? 0.f : lo_s;
+  }
+  hi = (lane & 2) != 0;
+  const float s30 = w2[0] + dpp<kDppXor2>(w2[0]);
+  const float s31 = w2[1] + dpp<kDppXor2>(w2[1]);
+  const float s32 = w2[2] + dpp<kDppXor2>(w2[2]);
+  const float w3_0 = hi ? s32 : s30;
+  const float w3_1 = hi ? 0.f : s31;
+  hi = (lane & 1) != 0;
+  const float s40 = w3_0 + dpp<kDppXor1>(w3_0);
+  const float s41 = w3_1 + dpp<kDppXor1>(w3_1);
+  float w4 = hi ? s41 : s40;
+  w4 += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, w4), 0x401F));
+  w4 += __shfl_xor(w4, 32, kWave);
+  constexpr uint64_t kFieldPlus1 = 0xa098600540321ull;  // 4 bits per lane 0..15
+  const int f = lane < 16 ? int((kFieldPlus1 >> (4 * lane)) & 15u) - 1 : -1;
+  if (f >= 0) atomicAdd(dst + f, w4);
 }
 
 template <int PPT>
@@ -127,9 +218,9 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
     const float* __restrict__ v_rgb, const float* __restrict__ v_T, float* __restrict__ v_screen) {
   constexpr int NT = kTilePix / PPT;
   constexpr int B = NT;
-  __shared__ float4 s_a[B];  // u, v, conic a, conic b
-  __shared__ float4 s_b[B];  // conic c, opacity, r, g
-  __shared__ float s_c[B];   // b
+  __shared__ float4 s_a[B];
+  __shared__ float4 s_b[B];
+  __shared__ float2 s_c[B];
   __shared__ uint32_t s_id[B];
   __shared__ int s_max;
   const int tid = threadIdx.x;
@@ -140,8 +231,10 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
   const int64_t start = toff[t], end = toff[t + 1];
   if (tid == 0) s_max = -1;
 
-  float px[PPT], py[PPT], Tc[PPT], S0[PPT], S1[PPT], S2[PPT], g0[PPT], g1[PPT], g2[PPT],
-      gTT[PPT];
+  // Per pixel: current transmittance (walking back to front), the running
+  // dot product P = g . sum_{later} colour alpha T, the upstream colour
+  // gradient g and the T gradient term g_T T_final.
+  float px[PPT], py[PPT], Tc[PPT], Pd[PPT], g0[PPT], g1[PPT], g2[PPT], gTT[PPT];
   int last[PPT];
   int my_max = -1;
 #pragma unroll
@@ -151,7 +244,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
     const bool in = X < W && Yp < H;
     px[k] = float(X) + 0.5f;
     py[k] = float(Yp) + 0.5f;
-    S0[k] = S1[k] = S2[k] = 0.f;
+    Pd[k] = 0.f;
     if (in) {
       const int64_t pix = (int64_t(c) * H + Yp) * W + X;
       Tc[k] = out_T[pix];
@@ -180,76 +273,56 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
     __syncthreads();
     if (tid < nb) {
       const uint32_t s = ids[b_start + tid];
-      const float2* r = reinterpret_cast<const float2*>(screen + int64_t(s) * kRow);
-      const float2 r0 = r[0], r1 = r[1], r2 = r[2], r3 = r[3], r4 = r[4];
-      s_a[tid] = make_float4(r0.x, r0.y, r1.x, r1.y);
-      s_b[tid] = make_float4(r2.x, r2.y, r3.y, r4.x);
-      s_c[tid] = r4.y;
+      const Staged e = stage_row(screen, s);
+      s_a[tid] = e.a;
+      s_b[tid] = e.b;
+      s_c[tid] = e.c;
       s_id[tid] = s;
     }
     __syncthreads();
+    const int lid0 = int(b_start - start);
     for (int j = nb - 1; j >= 0; --j) {
       const float4 A = s_a[j], Bv = s_b[j];
-      const float cblue = s_c[j];
-      const int lid = int(b_start - start) + j;
-      float gu = 0.f, gv = 0.f, ga = 0.f, gb = 0.f, gc = 0.f, go = 0.f, gr = 0.f, gg = 0.f,
-            gbl = 0.f;
+      const float2 Cv = s_c[j];
+      const int lid = lid0 + j;
+      // per-lane sums over its pixels: first moments and second moments of
+      // (dx, dy) weighted by dL/dsigma, sum of dL/dalpha raw, colour grads
+      float mx = 0.f, my = 0.f, mxx = 0.f, mxy = 0.f, myy = 0.f, mo = 0.f;
+      float gr = 0.f, gg = 0.f, gbl = 0.f;
       bool any = false;
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
-        const float dx = A.x - px[k], dy = A.y - py[k];
-        const float sig = splat_sigma(A.z, A.w, Bv.x, dx, dy);
-        const float ex = fast_exp_neg(sig);
-        const float raw = Bv.y * ex;
-        const float alpha = fminf(kAlphaMax, raw);
-        const bool use = lid <= last[k] && sig >= 0.f && alpha >= kAlphaMin;
-        if (use) {
+        const Eval e = eval_splat(A, Bv, px[k], py[k]);
+        if (lid <= last[k] && e.alpha >= kAlphaMin) {
           any = true;
-          const float om = 1.f / (1.f - alpha);
+          const float om = __builtin_amdgcn_rcpf(1.f - e.alpha);
           const float Ti = Tc[k] * om;
-          const float w = alpha * Ti;
+          const float w = e.alpha * Ti;
           gr = fmaf(w, g0[k], gr);
           gg = fmaf(w, g1[k], gg);
           gbl = fmaf(w, g2[k], gbl);
-          const float va = g0[k] * (Bv.z * Ti - S0[k] * om) + g1[k] * (Bv.w * Ti - S1[k] * om) +
-                           g2[k] * (cblue * Ti - S2[k] * om) - gTT[k] * om;
-          S0[k] = fmaf(Bv.z, w, S0[k]);
-          S1[k] = fmaf(Bv.w, w, S1[k]);
-          S2[k] = fmaf(cblue, w, S2[k]);
+          const float gc = fmaf(g2[k], Cv.x, fmaf(g1[k], Bv.w, g0[k] * Bv.z));
+          const float va = fmaf(Ti, gc, -(Pd[k] + gTT[k]) * om);
+          Pd[k] = fmaf(w, gc, Pd[k]);
           Tc[k] = Ti;
-          if (raw <= kAlphaMax) {
-            const float vs = -va * alpha;
-            go = fmaf(va, ex, go);
-            gu = fmaf(vs, A.z * dx + A.w * dy, gu);
-            gv = fmaf(vs, A.w * dx + Bv.x * dy, gv);
-            ga = fmaf(vs, 0.5f * dx * dx, ga);
-            gb = fmaf(vs, dx * dy, gb);
-            gc = fmaf(vs, 0.5f * dy * dy, gc);
+          if (e.raw <= kAlphaMax) {
+            const float vs = -va * e.alpha;
+            mo = fmaf(va, e.raw, mo);
+            mx = fmaf(vs, e.dx, mx);
+            my = fmaf(vs, e.dy, my);
+            mxx = fmaf(vs, e.dxx, mxx);
+            mxy = fmaf(vs, e.dxy, mxy);
+            myy = fmaf(vs, e.dyy, myy);
           }
         }
       }
       if (__ballot(any) != 0ull) {
-        gu = wave_sum(gu);
-        gv = wave_sum(gv);
-        ga = wave_sum(ga);
-        gb = wave_sum(gb);
-        gc = wave_sum(gc);
-        go = wave_sum(go);
-        gr = wave_sum(gr);
-        gg = wave_sum(gg);
-        gbl = wave_sum(gbl);
-        if ((tid & 63) == 0) {
-          float* dst = v_screen + int64_t(s_id[j]) * kRow;
-          atomicAdd(dst + 0, gu);
-          atomicAdd(dst + 1, gv);
-          atomicAdd(dst + 2, ga);
-          atomicAdd(dst + 3, gb);
-          atomicAdd(dst + 4, gc);
-          atomicAdd(dst + 5, go);
-          atomicAdd(dst + 7, gr);
-          atomicAdd(dst + 8, gg);
-          atomicAdd(dst + 9, gbl);
-        }
+        // dsigma/du = a dx + b dy, dsigma/dv = b dx + c dy, dsigma/da = dx^2/2,
+        // dsigma/db = dx dy, dsigma/dc = dy^2/2, dalpha/do = exp(-sigma)
+        const float a2 = A.z + A.z, c2 = A.w + A.w;
+        const float vals[9] = {fmaf(a2, mx, Bv.x * my), fmaf(Bv.x, mx, c2 * my), 0.5f * mxx, mxy,
+                               0.5f * myy, mo * Cv.y, gr, gg, gbl};
+        wave_reduce9_atomic(vals, v_screen + int64_t(s_id[j]) * kRow);
       }
     }
   }
@@ -257,18 +330,33 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
 
 }  // namespace
 
+// Pixels per lane of the forward and backward tiles (1, 2 or 4, i.e. 4, 2
+// or 1 wave per tile). GS_RASTER_PPT_FWD / GS_RASTER_PPT_BWD override the
+// defaults for launch-shape sweeps.
+int ppt_from_env(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v) return dflt;
+  const int p = std::atoi(v);
+  return (p == 1 || p == 2 || p == 4) ? p : dflt;
+}
+
 constexpr int kFwdPPT = 1;
-constexpr int kBwdPPT = 1;
+constexpr int kBwdPPT = 4;
 
 hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uint32_t* ids,
                              const int64_t* toff, float* out_rgb, float* out_T, int32_t* last_ids,
                              hipStream_t s) {
+  static const int ppt = ppt_from_env("GS_RASTER_PPT_FWD", kFwdPPT);
   const int tiles_x = (W + kTile - 1) / kTile, tiles_y = (H + kTile - 1) / kTile;
   const int T = tiles_x * tiles_y;
   const int64_t blocks = int64_t(C) * T;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_raster_fwd<kFwdPPT>, dim3(uint32_t(blocks)), dim3(kTilePix / kFwdPPT), 0, s,
-                     screen, ids, toff, W, H, tiles_x, T, out_rgb, out_T, last_ids);
+  const dim3 grid{uint32_t(blocks)};
+#define GS_FWD(P)                                                                            \
+  hipLaunchKernelGGL(k_raster_fwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, W, H, \
+                     tiles_x, T, out_rgb, out_T, last_ids)
+  if (ppt == 4) GS_FWD(4); else if (ppt == 2) GS_FWD(2); else GS_FWD(1);
+#undef GS_FWD
   return hipGetLastError();
 }
 
@@ -276,12 +364,17 @@ hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uin
                              const int64_t* toff, const float* out_T, const int32_t* last_ids,
                              const float* v_rgb, const float* v_T, float* v_screen,
                              hipStream_t s) {
+  static const int ppt = ppt_from_env("GS_RASTER_PPT_BWD", kBwdPPT);
   const int tiles_x = (W + kTile - 1) / kTile, tiles_y = (H + kTile - 1) / kTile;
   const int T = tiles_x * tiles_y;
   const int64_t blocks = int64_t(C) * T;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_raster_bwd<kBwdPPT>, dim3(uint32_t(blocks)), dim3(kTilePix / kBwdPPT), 0, s,
-                     screen, ids, toff, W, H, tiles_x, T, out_T, last_ids, v_rgb, v_T, v_screen);
+  const dim3 grid{uint32_t(blocks)};
+#define GS_BWD(P)                                                                             \
+  hipLaunchKernelGGL(k_raster_bwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, W, H,  \
+                     tiles_x, T, out_T, last_ids, v_rgb, v_T, v_screen)
+  if (ppt == 4) GS_BWD(4); else if (ppt == 2) GS_BWD(2); else GS_BWD(1);
+#undef GS_BWD
   return hipGetLastError();
 }
 

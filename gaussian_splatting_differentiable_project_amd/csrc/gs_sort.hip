@@ -269,7 +269,7 @@ hipError_t launch_sort_histogram(const uint32_t* keys, uint64_t n, int bit0, int
                                  const SortScratch& sc, hipStream_t s) {
   if (n == 0) return hipSuccess;
   uint64_t blocks = (n + 256 * 16 - 1) / (256 * 16);
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 512) blocks = 512;  // few blocks: fewer global atomics per bin
   hipLaunchKernelGGL(k_sort_hist, dim3(uint32_t(blocks)), dim3(256), 0, s, keys, n, bit0,
                      sort_passes(bits), sc.hist);
   return hipGetLastError();
