@@ -2,15 +2,19 @@
 
 A step is one pass of the whole path on one seeded synthetic scene:
 gs_project -> gs_intersect -> gs_rasterize_fwd -> gs_rasterize_bwd ->
-gs_project_bwd, with fixed upstream image gradients, inputs resident in
-HBM. Prints one JSON line.
+gs_project_bwd, with fixed upstream image gradients and every input
+resident in HBM before the timed region starts. Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
-       [--no-cpu-baseline]
+       [--no-cpu-baseline] [--calibrate-copy MIB]
+
+--calibrate-copy runs only a plain device-to-device copy of MIB MiB (for
+scaling the FETCH_SIZE / WRITE_SIZE hardware counters to bytes).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,8 +27,26 @@ import numpy as np  # noqa: E402
 
 import workloads  # noqa: E402
 
-HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
-FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector peak
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector peak, TFLOP/s
+CSRC = os.path.join(ROOT, "gaussian_splatting_differentiable_project_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+KERNELS = ["k_project_mask", "k_scan", "k_cam_offsets", "k_project_compact", "k_fill_u32",
+           "k_isect_prep", "k_sort_hist", "k_digit_base", "k_onesweep", "k_isect_emit",
+           "k_tile_ranges", "k_raster_fwd", "k_raster_bwd", "k_project_bwd"]
+KERNEL_SOURCE = {"k_raster_fwd": "gs_raster.hip", "k_raster_bwd": "gs_raster.hip",
+                 "k_project_mask": "gs_project.hip", "k_project_compact": "gs_project.hip",
+                 "k_project_bwd": "gs_project_bwd.hip", "k_onesweep": "gs_sort.hip",
+                 "k_isect_emit": "gs_intersect.hip"}
+
+# Flops of one (pixel, entry) evaluation in the raster kernels: the alpha
+# test every evaluation needs (dx, dy, three products, the quadratic form,
+# the exponent, the clamp: 14), plus the compositing (forward: 9) or the
+# gradient terms (backward: 35) of an entry that is composited.
+FLOPS_EVAL = 14
+FLOPS_FWD_COMPOSITE = 9
+FLOPS_BWD_COMPOSITE = 35
 
 
 def parse():
@@ -34,90 +56,128 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-sample-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     return ap.parse_args()
 
 
-def algorithmic_bytes(spec, nnz, n_isects, V, tile_passes, depth_passes=4):
-    """Bytes each stage must move (see the design notes): parameters read
-    once per Gaussian, 40 B rows, 8 B boxes, 4 B keys and ids per pass."""
+def source_sha(kernel: str) -> str | None:
+    f = KERNEL_SOURCE.get(kernel)
+    if f is None:
+        return None
+    h = hashlib.sha256()
+    for name in (f, "gs_common.h", "gs_projmath.h", "gs_internal.h"):
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes):
+    """Algorithmic HBM bytes of one launch of an HBM-bound kernel."""
     N, C, K = spec.n, spec.n_cams, spec.K
     Np = ((N + 127) // 128) * 128
     pairs = C * Np
-    px = C * spec.width * spec.height
-    b = {}
-    b["project"] = (40 * N + pairs / 8 + 4 * pairs / 128          # mask pass
-                    + pairs / 8 + 2 * 4 * pairs / 128 + (44 + 12 * K) * V + 48 * nnz)
-    b["intersect"] = (48 * nnz                                      # prep
-                      + depth_passes * 16 * nnz + 8 * nnz           # depth sort
-                      + 16 * nnz                                    # gather + scan
-                      + 16 * nnz + 8 * n_isects                     # emit
-                      + 4 * n_isects + tile_passes * 16 * n_isects  # tile sort
-                      + 4 * n_isects)                               # ranges
-    b["raster_fwd"] = 40 * nnz + 4 * n_isects + 20 * px
-    b["raster_bwd"] = 80 * nnz + 4 * n_isects + 24 * px
-    b["project_bwd"] = (44 + 12 * K) * (V + N) + 40 * nnz + pairs / 8 + 4 * pairs / 128
-    return b
+    if kernel == "k_project_mask":   # 40 B of geometry per Gaussian; mask bits + counts
+        return 40 * N + pairs / 8 + 4 * pairs / 128
+    if kernel == "k_project_compact":  # mask + scan; params + SH of visible; 48 B out per pair
+        return pairs / 8 + 4 * pairs / 128 + (44 + 12 * K) * V + 48 * nnz
+    if kernel == "k_project_bwd":    # params + SH read and grads written per Gaussian
+        return (44 + 12 * K) * (V + N) + 40 * nnz + pairs / 8 + 4 * pairs / 128
+    if kernel == "k_onesweep":       # one tile-id pass: 8 B read + 8 B written per entry
+        return 16 * n_isects
+    if kernel == "k_isect_emit":     # order, box, offset per pair; 8 B per entry
+        return 16 * nnz + 8 * n_isects
+    return None
+
+
+def raster_work(last_ids, W, H):
+    """(evaluations walked by the backward, upper bound of composited
+    evaluations): the backward walks every tile from its largest last id,
+    256 pixels per entry; a pixel composites at most last + 1 entries."""
+    import torch
+    C = last_ids.shape[0]
+    tx, ty = (W + 15) // 16, (H + 15) // 16
+    pad = torch.full((C, ty * 16, tx * 16), -1, dtype=torch.int32, device=last_ids.device)
+    pad[:, :H, :W] = last_ids
+    per_tile = pad.view(C, ty, 16, tx, 16).amax(dim=(2, 4)).to(torch.int64) + 1
+    walked = int(per_tile.sum().item()) * 256
+    comp = int((last_ids.to(torch.int64) + 1).sum().item())
+    return walked, comp
 
 
 def cpu_baseline(sc, spec, seconds):
-    """The fp64 oracle on a bounded sample of the same scene, scaled to a
-    whole step: projection (+ its backward) on a seeded subset of the
-    Gaussians, raster fwd/bwd on a seeded subset of tiles."""
+    """The fp64 oracle on a bounded sample of the same scene, single-threaded:
+    projection, intersection/sort and projection backward on the whole
+    scene, raster forward + backward on a seeded random sample of tiles,
+    scaled to all tiles."""
+    from threadpoolctl import threadpool_limits
+
     import oracle
     from oracle.intersect import intersect as o_intersect
+    from oracle.project import Projection
     rng = np.random.default_rng(0)
-    N = sc["N"]
-    t0 = time.perf_counter()
-    n_sub = min(N, 50_000)
-    idx = np.sort(rng.choice(N, n_sub, replace=False))
-    sub = dict(sc)
-    for k in ("means", "quats", "log_scales", "opacity_logits", "sh"):
-        sub[k] = sc[k][idx]
-    sub["N"] = n_sub
-    proj = oracle.project(sub)
-    t_proj = time.perf_counter() - t0
-    t1 = time.perf_counter()
-    isect = o_intersect(proj, sc["W"], sc["H"])
-    t_isect = time.perf_counter() - t1
-    n_tiles = isect.tile_offsets.size - 1
-    # raster on a tile sample from the full scene's tile lists is too costly
-    # to build; use the subset's lists, scaled by the entry count ratio
-    counts = np.diff(isect.tile_offsets)
-    order = rng.permutation(n_tiles)
-    t2 = time.perf_counter()
-    done_entries, tiles_done = 0, []
-    for t in order:
-        tiles_done.append(int(t))
-        done_entries += int(counts[t])
-        if time.perf_counter() - t2 > seconds * 0.5:
-            break
-        oracle.rasterize_fwd(proj.screen, isect.flatten_ids, isect.tile_offsets, sc["C"],
-                             sc["W"], sc["H"], tiles=[int(t)])
-        oracle.rasterize_bwd(proj.screen, isect.flatten_ids, isect.tile_offsets, sc["C"],
-                             sc["W"], sc["H"], sc["v_rgb"], sc["v_T"], tiles=[int(t)])
-    t_raster = time.perf_counter() - t2
-    scale_g = N / n_sub
-    ent_full_est = counts.sum() * scale_g
-    per_entry = t_raster / max(done_entries, 1)
-    est = (t_proj * 2 + t_isect) * scale_g + per_entry * ent_full_est
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        proj = oracle.project(sc)
+        proj.screen = proj.screen.astype(np.float32).astype(np.float64)
+        t_proj = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        isect = o_intersect(proj, sc["W"], sc["H"])
+        t_isect = time.perf_counter() - t0
+        n_tiles = isect.tile_offsets.size - 1
+        order = rng.permutation(n_tiles)
+        t0 = time.perf_counter()
+        done = 0
+        for t in order:
+            oracle.rasterize_fwd(proj.screen, isect.flatten_ids, isect.tile_offsets, sc["C"],
+                                 sc["W"], sc["H"], tiles=[int(t)])
+            oracle.rasterize_bwd(proj.screen, isect.flatten_ids, isect.tile_offsets, sc["C"],
+                                 sc["W"], sc["H"], sc["v_rgb"], sc["v_T"], tiles=[int(t)])
+            done += 1
+            if time.perf_counter() - t0 > seconds:
+                break
+        t_raster = (time.perf_counter() - t0) * n_tiles / done
+        # projection backward on a seeded sample of visible pairs, scaled
+        n_pb = min(proj.nnz, 100_000)
+        pick = np.sort(rng.choice(proj.nnz, n_pb, replace=False)) if n_pb else np.zeros(0, int)
+        sub = Projection(**{**proj.__dict__, "cam": proj.cam[pick],
+                             "gauss": proj.gauss[pick]})
+        t0 = time.perf_counter()
+        oracle.project_bwd(sc, sub, np.zeros((n_pb, 10)))
+        t_pbwd = (time.perf_counter() - t0) * proj.nnz / max(n_pb, 1)
+    est = t_proj + t_isect + t_raster + t_pbwd
     return dict(value=1.0 / est, unit="steps/s", cores=1, kind="oracle",
-                sample=(f"fp64 NumPy oracle: projection on {n_sub} of {N} Gaussians "
-                        f"(x2 for its backward), intersect+sort of those, raster fwd+bwd on "
-                        f"{len(tiles_done)} tiles ({done_entries} entries); scaled linearly to "
-                        f"the full scene (est. {est:.1f} s/step)"))
+                sample=(f"fp64 NumPy oracle, one thread: projection ({t_proj:.1f} s) and intersect + "
+                        f"stable sort ({t_isect:.1f} s) on the whole scene; projection backward on "
+                        f"{n_pb} of {proj.nnz} seeded random visible pairs scaled to all "
+                        f"({t_pbwd:.1f} s); raster fwd+bwd on {done} of {n_tiles} seeded random "
+                        f"tiles scaled to all tiles ({t_raster:.0f} s); est. {est:.0f} s/step"))
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib * 2**20 // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": mib, "bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4,
+                      "copies": 3}))
 
 
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "one GPU only: this build has no multi-GPU path; use --gpus 1"}))
         sys.exit(2)
     import torch
 
     import gaussian_splatting_differentiable_project_amd as gsd
     gsd.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.calibrate_copy:
+        calibrate_copy(a.calibrate_copy)
+        return
     spec = workloads.CONFIGS[a.config]
     sc = workloads.make_scene(spec)
     s = gsd.Scene.from_numpy(sc, "cuda")
@@ -125,7 +185,6 @@ def main():
     v_T = torch.from_numpy(sc["v_T"]).cuda()
     r = gsd.Rasterizer("cuda")
     stream = torch.cuda.current_stream()
-
     stages = ["project", "intersect", "raster_fwd", "raster_bwd", "project_bwd"]
 
     def step(ev=None):
@@ -143,33 +202,77 @@ def main():
         mark(4)
         r.project_bwd(s, p, vs)
         mark(5)
-        return p, it
+        return p, it, last
 
     for _ in range(a.warmup):
-        p, it = step()
+        step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+
+    # per-kernel breakdown (not the headline timing): every kernel timed
+    n_bd = 3
+    gsd.profile_reset()
+    gsd.profile_enable(None)
+    bd_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_bd)]
+    for k in range(n_bd):
+        step(bd_ev[k])
+    torch.cuda.synchronize()
+    gsd.profile_disable()
+    kernel_ms = {}
+    for kn in KERNELS:
+        n, ms = gsd.profile_query(kn)
+        if n:
+            kernel_ms[kn] = ms / n_bd
+    stage_ms = {st: float(np.mean([bd_ev[k][i].elapsed_time(bd_ev[k][i + 1]) for k in range(n_bd)]))
+                for i, st in enumerate(stages)}
+    dom = max(kernel_ms, key=kernel_ms.get)
+    gsd.profile_reset()
+
+    # timed region: events only around the dominant kernel, on its stream
+    gsd.profile_enable(dom)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(a.steps):
-        p, it = step(evs[k])
+    for _ in range(a.steps):
+        p, it, last = step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage_ms = {st: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(a.steps)]))
-                for i, st in enumerate(stages)}
+    gsd.profile_disable()
+    n_dom, dom_ms_total = gsd.profile_query(dom)
+    gsd.profile_reset()
+    dom_ms = dom_ms_total / max(n_dom, 1)
+    launches_per_step = n_dom / a.steps
+
     ms_per_step = wall * 1e3 / a.steps
     steps_s = a.steps / wall
     nnz, n_is = p.nnz, it.n_isects
-    V = int((p.mask.cpu().numpy().view(np.uint64) != 0).sum())  # placeholder, refined below
     vis = np.unpackbits(p.mask.cpu().numpy().view(np.uint8), bitorder="little").astype(bool)
     Np = gsd.pad_n(spec.n)
-    V = int(vis.reshape(spec.n_cams, Np).any(0).sum())
+    V = int(vis[: spec.n_cams * Np].reshape(spec.n_cams, Np).any(0).sum())
     tx, ty = gsd.tiles(spec.width, spec.height)
     tile_bits = max(1, int(np.ceil(np.log2(max(spec.n_cams * tx * ty, 2)))))
     tile_passes = (tile_bits + 7) // 8
-    bytes_ = algorithmic_bytes(spec, nnz, n_is, V, tile_passes)
-    hbm = {st: bytes_[st] / (stage_ms[st] * 1e-3) / 1e9 for st in stages}
-    dom = max(stages, key=lambda st: stage_ms[st])
+    walked, comp = raster_work(last, spec.width, spec.height)
+
+    if dom in ("k_raster_bwd", "k_raster_fwd"):
+        per_comp = FLOPS_BWD_COMPOSITE if dom == "k_raster_bwd" else FLOPS_FWD_COMPOSITE
+        work = FLOPS_EVAL * walked + per_comp * comp
+        achieved = work / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "kernel": dom, "achieved": achieved, "peak": FP32_VECTOR_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_TFLOPS,
+                "flops_per_launch": work, "evaluations_walked": walked,
+                "composited_upper_bound": comp, "launch_ms": dom_ms}
+    else:
+        byt = hbm_bytes(dom, spec, nnz, n_is, V, tile_passes)
+        achieved = byt / (dom_ms * 1e-3) / 1e9 if byt else None
+        roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+                "bytes_per_launch": byt, "launch_ms": dom_ms}
+    roof["traffic"] = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        ent = tr.get(dom)
+        if ent and ent.get("workload") == spec.name and ent.get("source_sha") == source_sha(dom):
+            roof["traffic"] = ent["hbm_bytes_per_launch"]
+
     out = {
         "metric": "fwd+bwd rasterizer steps/s and M visible pairs/s at 1 MI355X; % HBM peak",
         "value": steps_s,
@@ -191,12 +294,16 @@ def main():
         "n_isects": n_is,
         "visible_gaussians": V,
         "stage_ms": stage_ms,
-        "stage_algorithmic_GBps": hbm,
-        "stage_hbm_frac": {st: hbm[st] / HBM_PEAK_GBS for st in stages},
-        "roofline": {"bound": "hbm", "stage": dom, "achieved": hbm[dom], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": hbm[dom] / HBM_PEAK_GBS,
-                     "traffic": None},
+        "kernel_ms_per_step": kernel_ms,
+        "dominant_launches_per_step": launches_per_step,
+        "roofline": roof,
     }
+    hb = {}
+    for kn, ms in kernel_ms.items():
+        byt = hbm_bytes(kn, spec, nnz, n_is, V, tile_passes)
+        if byt and kn != "k_onesweep":
+            hb[kn] = byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    out["hbm_frac_by_kernel"] = hb
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(sc, spec, a.cpu_sample_seconds)
     print(json.dumps(out))

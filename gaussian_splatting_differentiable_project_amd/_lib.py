@@ -25,7 +25,8 @@ ROW = 10
 
 EXPORTS = ("gs_status_str", "gs_version", "gs_pad_n", "gs_project_workspace_bytes",
            "gs_intersect_workspace_bytes", "gs_project", "gs_intersect", "gs_rasterize_fwd",
-           "gs_rasterize_bwd", "gs_project_bwd")
+           "gs_rasterize_bwd", "gs_project_bwd", "gs_profile_enable", "gs_profile_disable",
+           "gs_profile_reset", "gs_profile_query")
 
 _lib = None
 
@@ -72,9 +73,37 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gs_project_bwd.restype = ctypes.c_int
     lib.gs_project_bwd.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
         [c_vp] * 3 + [c_vp] * 5 + [c_i32]
+    lib.gs_profile_enable.restype = ctypes.c_int
+    lib.gs_profile_enable.argtypes = [ctypes.c_char_p]
+    lib.gs_profile_disable.restype = ctypes.c_int
+    lib.gs_profile_reset.restype = ctypes.c_int
+    lib.gs_profile_query.restype = ctypes.c_int
+    lib.gs_profile_query.argtypes = [ctypes.c_char_p, P_i64, ctypes.POINTER(ctypes.c_double)]
     if path is None:
         _lib = lib
     return lib
+
+
+def profile_enable(filter: str | None = None) -> None:
+    load().gs_profile_enable(filter.encode() if filter else None)
+
+
+def profile_disable() -> None:
+    load().gs_profile_disable()
+
+
+def profile_reset() -> None:
+    load().gs_profile_reset()
+
+
+def profile_query(kernel: str) -> tuple[int, float]:
+    """(launches, total milliseconds) recorded for one kernel name."""
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    st = load().gs_profile_query(kernel.encode(), ctypes.byref(n), ctypes.byref(ms))
+    if st != GS_OK:
+        raise GsError(st, "gs_profile_query")
+    return n.value, ms.value
 
 
 def status_str(status: int) -> str:

@@ -8,6 +8,22 @@
 
 namespace gs {
 
+// Records a HIP event pair around one kernel launch on stream s when
+// gs_profile_enable() is on and the name matches its filter.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t a_{}, b_{};
+  bool on_ = false;
+};
+
 struct ProjectArgs {
   int64_t N, N_pad;
   int32_t C, W, H, deg;

@@ -137,6 +137,7 @@ hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* 
   if (nnz == 0) return hipSuccess;
   uint32_t blocks = grid_for(nnz);
   if (blocks > 1024) blocks = 1024;
+  ProfScope prof("k_isect_prep", s);
   hipLaunchKernelGGL(k_isect_prep, dim3(blocks), dim3(256), 0, s, nnz, screen,
                      reinterpret_cast<const uint2*>(aabb16), uint32_t(W), uint32_t(H), dkeys,
                      dvals, cnt, total);
@@ -149,6 +150,7 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
   if (nnz == 0) return hipSuccess;
   const uint32_t tiles_x = uint32_t((W + kTile - 1) / kTile);
   const uint32_t T = tiles_x * uint32_t((H + kTile - 1) / kTile);
+  ProfScope prof("k_isect_emit", s);
   hipLaunchKernelGGL(k_isect_emit, dim3(grid_for(nnz)), dim3(256), 0, s, nnz, order,
                      reinterpret_cast<const uint2*>(aabb16), offs, cam_off, C, uint32_t(W),
                      uint32_t(H), tiles_x, T, cap, tkeys, tvals);
@@ -157,6 +159,7 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
 
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
                               hipStream_t s) {
+  ProfScope prof("k_tile_ranges", s);
   hipLaunchKernelGGL(k_tile_ranges, dim3(grid_for(n + 1)), dim3(256), 0, s, tkeys, n, n_tiles,
                      toff);
   return hipGetLastError();
@@ -165,6 +168,7 @@ hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tile
 hipError_t launch_compose_keys(const uint32_t* tkeys, const uint32_t* ids, const float* screen,
                                uint64_t n, uint64_t* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
+  ProfScope prof("k_compose_keys", s);
   hipLaunchKernelGGL(k_compose_keys, dim3(grid_for(n)), dim3(256), 0, s, tkeys, ids, screen, n,
                      out);
   return hipGetLastError();

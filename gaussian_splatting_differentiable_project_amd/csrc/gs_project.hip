@@ -139,6 +139,7 @@ __global__ void k_cam_offsets(const uint32_t* __restrict__ wg_scan, int64_t grou
 hipError_t launch_cam_offsets(const uint32_t* wg_scan, int64_t groups_per_cam, int C,
                               const uint64_t* total, int64_t* out, hipStream_t s) {
   const int n = C + 1;
+  ProfScope prof("k_cam_offsets", s);
   hipLaunchKernelGGL(k_cam_offsets, dim3((n + 255) / 256), dim3(256), 0, s, wg_scan,
                      groups_per_cam, C, total, out);
   return hipGetLastError();
@@ -167,6 +168,7 @@ hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, uint32_t* w
                                hipStream_t s) {
   const int64_t blocks = a.N_pad / kMaskGroup;
   if (blocks == 0) return hipSuccess;
+  ProfScope prof("k_project_mask", s);
   hipLaunchKernelGGL(k_project_mask, dim3(uint32_t(blocks)), dim3(kMaskGroup), 0, s, a, mask,
                      wg_count);
   return hipGetLastError();
@@ -178,6 +180,7 @@ hipError_t launch_project_compact(const ProjectArgs& a, const uint64_t* mask,
   const int64_t blocks = a.N_pad / kMaskGroup;
   if (blocks == 0) return hipSuccess;
   const dim3 grid{uint32_t(blocks)}, block{uint32_t(kMaskGroup)};
+  ProfScope prof("k_project_compact", s);
   switch (a.deg) {
     case 0: hipLaunchKernelGGL(k_project_compact<0>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;
     case 1: hipLaunchKernelGGL(k_project_compact<1>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;

@@ -227,6 +227,7 @@ hipError_t launch_project_bwd(const ProjectArgs& a, const uint64_t* mask,
 #define GS_LAUNCH_PB(D)                                                                      \
   hipLaunchKernelGGL(k_project_bwd<D>, grid, block, 0, s, a, mask, wg_scan, v_screen, v_means, \
                      v_quats, v_log_scales, v_opacity_logits, v_sh, accumulate)
+  ProfScope prof("k_project_bwd", s);
   switch (a.deg) {
     case 0: GS_LAUNCH_PB(0); break;
     case 1: GS_LAUNCH_PB(1); break;

@@ -355,6 +355,7 @@ hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uin
 #define GS_FWD(P)                                                                            \
   hipLaunchKernelGGL(k_raster_fwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, W, H, \
                      tiles_x, T, out_rgb, out_T, last_ids)
+  ProfScope prof("k_raster_fwd", s);
   if (ppt == 4) GS_FWD(4); else if (ppt == 2) GS_FWD(2); else GS_FWD(1);
 #undef GS_FWD
   return hipGetLastError();
@@ -373,6 +374,7 @@ hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uin
 #define GS_BWD(P)                                                                             \
   hipLaunchKernelGGL(k_raster_bwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, W, H,  \
                      tiles_x, T, out_T, last_ids, v_rgb, v_T, v_screen)
+  ProfScope prof("k_raster_bwd", s);
   if (ppt == 4) GS_BWD(4); else if (ppt == 2) GS_BWD(2); else GS_BWD(1);
 #undef GS_BWD
   return hipGetLastError();

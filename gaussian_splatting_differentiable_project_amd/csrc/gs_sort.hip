@@ -236,6 +236,7 @@ hipError_t launch_fill_u32(void* p, uint32_t v, uint64_t n_words, hipStream_t s)
   if (n_words == 0) return hipSuccess;
   uint64_t blocks = (n_words + 255) / 256;
   if (blocks > 8192) blocks = 8192;
+  ProfScope prof("k_fill_u32", s);
   hipLaunchKernelGGL(k_fill_u32, dim3(uint32_t(blocks)), dim3(256), 0, s,
                      static_cast<uint32_t*>(p), v, n_words);
   return hipGetLastError();
@@ -247,6 +248,7 @@ hipError_t launch_scan_u32(const uint32_t* in, const uint32_t* idx, uint64_t n, 
   if (n == 0) return hipSuccess;
   const uint64_t blocks = (n + kScanTile - 1) / kScanTile;
   const dim3 grid{uint32_t(blocks)}, block{uint32_t(kScanThreads)};
+  ProfScope prof("k_scan", s);
   if (idx) {
     if (out64)
       hipLaunchKernelGGL((k_scan<true, true>), grid, block, 0, s, in, idx, n, out32, out64, total, lookback, ticket, err);
@@ -270,6 +272,7 @@ hipError_t launch_sort_histogram(const uint32_t* keys, uint64_t n, int bit0, int
   if (n == 0) return hipSuccess;
   uint64_t blocks = (n + 256 * 16 - 1) / (256 * 16);
   if (blocks > 512) blocks = 512;  // few blocks: fewer global atomics per bin
+  ProfScope prof("k_sort_hist", s);
   hipLaunchKernelGGL(k_sort_hist, dim3(uint32_t(blocks)), dim3(256), 0, s, keys, n, bit0,
                      sort_passes(bits), sc.hist);
   return hipGetLastError();
@@ -282,12 +285,16 @@ hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys
   const int passes = sort_passes(bits);
   *in_b = (passes & 1) != 0;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_digit_base, dim3(passes), dim3(256), 0, s, sc.hist);
+  {
+    ProfScope prof("k_digit_base", s);
+    hipLaunchKernelGGL(k_digit_base, dim3(passes), dim3(256), 0, s, sc.hist);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t blocks = sort_blocks(n);
   uint32_t *ki = keys_a, *vi = vals_a, *ko = keys_b, *vo = vals_b;
   for (int p = 0; p < passes; ++p) {
+    ProfScope prof("k_onesweep", s);
     hipLaunchKernelGGL(k_onesweep, dim3(uint32_t(blocks)), dim3(kSortThreads), 0, s, ki, vi, ko,
                        vo, n, bit0 + kRadixBits * p, sc.hist + p * kRadix, sc.lookback,
                        sc.tickets + p, tag0 + uint32_t(p), sc.err);

@@ -225,6 +225,29 @@ int gs_project_bwd(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
                    float* v_log_scales, float* v_opacity_logits, float* v_sh,
                    int32_t accumulate);
 
+/* ---------------------------------------------------------------------
+ * Per-kernel timing (opt-in; a HIP event pair around each launch of a
+ * kernel whose name contains `filter`, on the stream it runs on).
+ * [PROF] sections 3-4 describe the trainer's own per-kernel GPU timing
+ * report; this is the library's counterpart for benchmarks.
+ *
+ * gs_profile_enable: start recording (filter NULL or "" = every kernel).
+ * gs_profile_disable: stop recording (recorded events are kept).
+ * gs_profile_reset: wait for and release every recorded event.
+ * gs_profile_query: for the kernel named exactly `kernel` (e.g.
+ *   "k_raster_bwd"), wait for its recorded launches and return their
+ *   count and summed duration in milliseconds (host out-params).
+ * Kernel names: k_project_mask, k_scan, k_cam_offsets, k_project_compact,
+ * k_fill_u32, k_isect_prep, k_sort_hist, k_digit_base, k_onesweep,
+ * k_isect_emit, k_tile_ranges, k_compose_keys, k_raster_fwd,
+ * k_raster_bwd, k_project_bwd. Recording adds host overhead per launch
+ * and is not meant to stay on in production.
+ * ------------------------------------------------------------------- */
+int gs_profile_enable(const char* filter);
+int gs_profile_disable(void);
+int gs_profile_reset(void);
+int gs_profile_query(const char* kernel, int64_t* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

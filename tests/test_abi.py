@@ -35,7 +35,9 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"gs_status_str", "gs_version", "gs_pad_n", "gs_project_workspace_bytes",
                           "gs_intersect_workspace_bytes", "gs_project", "gs_intersect",
-                          "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd"}
+                          "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd",
+                          "gs_profile_enable", "gs_profile_disable", "gs_profile_reset",
+                          "gs_profile_query"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
