@@ -24,6 +24,13 @@ class ProfScope {
   bool on_ = false;
 };
 
+// A dispatch's work-item count per dimension is 32-bit: a grid of
+// blocks x threads >= 2^32 would silently wrap. Launchers that size their
+// grid by the data check it with this before launching.
+inline bool fits_dispatch(uint64_t blocks, uint64_t threads_per_block) {
+  return blocks * (threads_per_block ? threads_per_block : 256) < (uint64_t(1) << 32);
+}
+
 struct ProjectArgs {
   int64_t N, N_pad;
   int32_t C, W, H, deg;

@@ -103,31 +103,40 @@ __global__ __launch_bounds__(256) void k_isect_emit(
 }
 
 // tile_offsets[t] = first sorted position whose tile id is >= t.
+// Grid-stride over the n + 1 boundaries: a dispatch's work-item count is
+// a 32-bit quantity, and n_isects can exceed 2^32.
 __global__ __launch_bounds__(256) void k_tile_ranges(const uint32_t* __restrict__ tkeys,
                                                     uint64_t n, uint64_t n_tiles,
                                                     int64_t* __restrict__ toff) {
-  const uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i > n) return;
-  // ids are < n_tiles by construction; the clamps only keep the writes
-  // inside toff[0..n_tiles] whatever the keys hold
-  uint64_t cur = i < n ? tkeys[i] : n_tiles;
-  cur = cur < n_tiles ? cur : n_tiles;
-  int64_t prev = i > 0 ? int64_t(tkeys[i - 1]) : -1;
-  prev = prev < int64_t(n_tiles) ? prev : int64_t(n_tiles);
-  for (int64_t t = prev + 1; t <= int64_t(cur); ++t) toff[t] = int64_t(i);
+  const uint64_t stride = uint64_t(gridDim.x) * 256;
+  for (uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x; i <= n; i += stride) {
+    // ids are < n_tiles by construction; the clamps only keep the writes
+    // inside toff[0..n_tiles] whatever the keys hold
+    uint64_t cur = i < n ? tkeys[i] : n_tiles;
+    cur = cur < n_tiles ? cur : n_tiles;
+    int64_t prev = i > 0 ? int64_t(tkeys[i - 1]) : -1;
+    prev = prev < int64_t(n_tiles) ? prev : int64_t(n_tiles);
+    for (int64_t t = prev + 1; t <= int64_t(cur); ++t) toff[t] = int64_t(i);
+  }
 }
 
 __global__ __launch_bounds__(256) void k_compose_keys(const uint32_t* __restrict__ tkeys,
                                                      const uint32_t* __restrict__ ids,
                                                      const float* __restrict__ screen, uint64_t n,
                                                      uint64_t* __restrict__ out) {
-  const uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= n) return;
-  const uint32_t s = ids[i];
-  out[i] = (uint64_t(tkeys[i]) << 32) | __float_as_uint(screen[uint64_t(s) * kRow + 6]);
+  const uint64_t stride = uint64_t(gridDim.x) * 256;
+  for (uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) {
+    const uint32_t s = ids[i];
+    out[i] = (uint64_t(tkeys[i]) << 32) | __float_as_uint(screen[uint64_t(s) * kRow + 6]);
+  }
 }
 
 inline uint32_t grid_for(uint64_t n) { return uint32_t((n + 255) / 256); }
+// Blocks for a grid-stride loop over n elements.
+inline uint32_t grid_stride_blocks(uint64_t n) {
+  const uint64_t b = (n + 255) / 256;
+  return uint32_t(b < 65536 ? (b ? b : 1) : 65536);
+}
 
 }  // namespace
 
@@ -148,6 +157,7 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
                              const uint64_t* offs, const int64_t* cam_off, int C, int W, int H,
                              uint64_t cap, uint32_t* tkeys, uint32_t* tvals, hipStream_t s) {
   if (nnz == 0) return hipSuccess;
+  if (!fits_dispatch(grid_for(nnz), 256)) return hipErrorInvalidConfiguration;
   const uint32_t tiles_x = uint32_t((W + kTile - 1) / kTile);
   const uint32_t T = tiles_x * uint32_t((H + kTile - 1) / kTile);
   ProfScope prof("k_isect_emit", s);
@@ -160,7 +170,7 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
                               hipStream_t s) {
   ProfScope prof("k_tile_ranges", s);
-  hipLaunchKernelGGL(k_tile_ranges, dim3(grid_for(n + 1)), dim3(256), 0, s, tkeys, n, n_tiles,
+  hipLaunchKernelGGL(k_tile_ranges, dim3(grid_stride_blocks(n + 1)), dim3(256), 0, s, tkeys, n, n_tiles,
                      toff);
   return hipGetLastError();
 }
@@ -169,7 +179,7 @@ hipError_t launch_compose_keys(const uint32_t* tkeys, const uint32_t* ids, const
                                uint64_t n, uint64_t* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
   ProfScope prof("k_compose_keys", s);
-  hipLaunchKernelGGL(k_compose_keys, dim3(grid_for(n)), dim3(256), 0, s, tkeys, ids, screen, n,
+  hipLaunchKernelGGL(k_compose_keys, dim3(grid_stride_blocks(n)), dim3(256), 0, s, tkeys, ids, screen, n,
                      out);
   return hipGetLastError();
 }

@@ -19,13 +19,14 @@ namespace gs {
 
 namespace {
 
-__device__ __forceinline__ void zero_local(GaussLocal& G) {
+template <typename T>
+__device__ __forceinline__ void zero_local(GaussLocal<T>& G) {
 #pragma unroll
-  for (int i = 0; i < 3; ++i) G.mu[i] = 0.f, G.s[i] = 1.f;
-  G.qn = 1.f;
-  G.qh[0] = 1.f, G.qh[1] = G.qh[2] = G.qh[3] = 0.f;
+  for (int i = 0; i < 3; ++i) G.mu[i] = 0.f, G.s[i] = T(1);
+  G.qn = T(1);
+  G.qh[0] = T(1), G.qh[1] = G.qh[2] = G.qh[3] = T(0);
 #pragma unroll
-  for (int i = 0; i < 9; ++i) G.Rq[i] = G.M[i] = (i % 4 == 0) ? 1.f : 0.f;
+  for (int i = 0; i < 9; ++i) G.Rq[i] = G.M[i] = (i % 4 == 0) ? T(1) : T(0);
 }
 
 __global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint64_t* mask,
@@ -33,16 +34,20 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t g = int64_t(blockIdx.x) * kMaskGroup + tid;
   const bool valid = g < a.N;
-  GaussLocal G;
+  // The projection is evaluated in fp64 (full rate on gfx950; this pass
+  // is bound by memory, not arithmetic) and only its results are rounded,
+  // so visibility is decided as the exact arithmetic decides it except at
+  // ties.
+  GaussLocal<double> G;
   if (valid)
     gauss_local(a.means, a.quats, a.log_scales, g, G);
   else
     zero_local(G);
   __shared__ uint32_t pc[2][2];
-  const float Wf = float(a.W), Hf = float(a.H);
+  const double Wf = double(a.W), Hf = double(a.H);
   for (int c = 0; c < a.C; ++c) {
     const Camera k = load_camera(a.viewmats, a.Ks, c);
-    PairFwd P;
+    PairFwd<double> P;
     pair_fwd(k, G, Wf, Hf, P);
     const uint64_t word = __ballot(valid && P.visible);
     const int64_t p0 = int64_t(c) * a.N_pad + int64_t(blockIdx.x) * kMaskGroup;
@@ -73,14 +78,15 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_compact(ProjectArgs a,
     any |= ((mine >> lane) & 1ull) != 0;
   }
   if (!any) return;
-  GaussLocal G;
+  // fp64 arithmetic, rounded once into the fp32 row (see the mask pass)
+  GaussLocal<double> G;
   gauss_local(a.means, a.quats, a.log_scales, g, G);
-  const float opac = 1.f / (1.f + expf(-a.opacity_logits[g]));
+  const float opac = float(1.0 / (1.0 + exp(-double(a.opacity_logits[g]))));
   float shc[K * 3];
   const float* shg = a.sh + g * (K * 3);
 #pragma unroll
   for (int i = 0; i < K * 3; ++i) shc[i] = shg[i];
-  const float Wf = float(a.W), Hf = float(a.H);
+  const double Wf = double(a.W), Hf = double(a.H);
   for (int c = 0; c < a.C; ++c) {
     const int64_t p0 = int64_t(c) * a.N_pad + int64_t(blockIdx.x) * kMaskGroup;
     const uint64_t w0 = mask[p0 / 64], w1 = mask[p0 / 64 + 1];
@@ -89,34 +95,36 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_compact(ProjectArgs a,
     const int64_t slot = int64_t(wg_scan[p0 / kMaskGroup]) + (wave ? __popcll(w0) : 0) +
                          __popcll(mine & lt);
     const Camera k = load_camera(a.viewmats, a.Ks, c);
-    PairFwd P;
+    PairFwd<double> P;
     pair_fwd(k, G, Wf, Hf, P);
     // colour toward the camera centre
-    float dx = G.mu[0] - k.cc[0], dy = G.mu[1] - k.cc[1], dz = G.mu[2] - k.cc[2];
-    const float inv = 1.f / sqrtf(dx * dx + dy * dy + dz * dz);
+    double dx = double(G.mu[0]) - k.cc[0], dy = double(G.mu[1]) - k.cc[1],
+           dz = double(G.mu[2]) - k.cc[2];
+    const double inv = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
     dx *= inv, dy *= inv, dz *= inv;
-    float Y[K];
+    double Y[K];
     sh_basis<DEG>(a.norm, dx, dy, dz, Y);
     float rgb[3];
 #pragma unroll
     for (int ch = 0; ch < 3; ++ch) {
-      float acc = 0.5f;
+      double acc = 0.5;
 #pragma unroll
-      for (int kk = 0; kk < K; ++kk) acc = fmaf(Y[kk], shc[3 * kk + ch], acc);
-      rgb[ch] = fmaxf(acc, 0.f);
+      for (int kk = 0; kk < K; ++kk) acc = fma(Y[kk], double(shc[3 * kk + ch]), acc);
+      rgb[ch] = float(fmax(acc, 0.0));
     }
     float2* row = reinterpret_cast<float2*>(screen + slot * kRow);
-    row[0] = make_float2(P.u, P.v);
-    row[1] = make_float2(P.ca, P.cb);
-    row[2] = make_float2(P.cc, opac);
-    row[3] = make_float2(P.z, rgb[0]);
+    row[0] = make_float2(float(P.u), float(P.v));
+    row[1] = make_float2(float(P.ca), float(P.cb));
+    row[2] = make_float2(float(P.cc), opac);
+    row[3] = make_float2(P.z32, rgb[0]);
     row[4] = make_float2(rgb[1], rgb[2]);
     // 16-bit box: min edges round down, max edges round up, on the grid
-    // of 65535 steps over [0, extent].
-    const float fx0 = fminf(fmaxf(floorf(P.x0 * a.qsx), 0.f), 65535.f);
-    const float fy0 = fminf(fmaxf(floorf(P.y0 * a.qsy), 0.f), 65535.f);
-    const float fx1 = fminf(fmaxf(ceilf(P.x1 * a.qsx), 0.f), 65535.f);
-    const float fy1 = fminf(fmaxf(ceilf(P.y1 * a.qsy), 0.f), 65535.f);
+    // of 65535 steps over [0, extent]; the edge is taken in fp32 and scaled
+    // in fp32 (a float deciding an integer code: one fixed precision).
+    const float fx0 = fminf(fmaxf(floorf(float(P.x0) * a.qsx), 0.f), 65535.f);
+    const float fy0 = fminf(fmaxf(floorf(float(P.y0) * a.qsy), 0.f), 65535.f);
+    const float fx1 = fminf(fmaxf(ceilf(float(P.x1) * a.qsx), 0.f), 65535.f);
+    const float fy1 = fminf(fmaxf(ceilf(float(P.y1) * a.qsy), 0.f), 65535.f);
     uint2 box;
     box.x = uint32_t(fx0) | (uint32_t(fy0) << 16);
     box.y = uint32_t(fx1) | (uint32_t(fy1) << 16);
@@ -159,7 +167,7 @@ ShNorm sh_norm_table() {
     for (int m = 0; m <= l; ++m) {
       double v = std::sqrt((2.0 * l + 1.0) / (4.0 * pi) * fact(l - m) / fact(l + m));
       if (m > 0) v *= std::sqrt(2.0);
-      t.n[idx++] = float(v);
+      t.n[idx++] = v;
     }
   return t;
 }
@@ -168,6 +176,7 @@ hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, uint32_t* w
                                hipStream_t s) {
   const int64_t blocks = a.N_pad / kMaskGroup;
   if (blocks == 0) return hipSuccess;
+  if (!fits_dispatch(uint64_t(blocks), kMaskGroup)) return hipErrorInvalidConfiguration;
   ProfScope prof("k_project_mask", s);
   hipLaunchKernelGGL(k_project_mask, dim3(uint32_t(blocks)), dim3(kMaskGroup), 0, s, a, mask,
                      wg_count);
@@ -179,6 +188,7 @@ hipError_t launch_project_compact(const ProjectArgs& a, const uint64_t* mask,
                                   hipStream_t s) {
   const int64_t blocks = a.N_pad / kMaskGroup;
   if (blocks == 0) return hipSuccess;
+  if (!fits_dispatch(uint64_t(blocks), kMaskGroup)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)}, block{uint32_t(kMaskGroup)};
   ProfScope prof("k_project_compact", s);
   switch (a.deg) {

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_bwd(
     any |= ((mask[p0 / 64 + wave] >> lane) & 1ull) != 0;
   }
 
-  GaussLocal G;
+  GaussLocal<float> G;
   float o = 0.f;
   if (any) {
     gauss_local(a.means, a.quats, a.log_scales, g, G);
@@ -69,8 +69,8 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_bwd(
       const float vrgb[3] = {r3.y, r4.x, r4.y};
 
       const Camera k = load_camera(a.viewmats, a.Ks, c);
-      PairFwd P;
-      pair_fwd(k, G, Wf, Hf, P);
+      PairFwd<float> P;
+      pair_fwd<float>(k, G, Wf, Hf, P);
 
       // colour = max(0, sum_k sh_k Y_k(d) + 0.5), d = (mu - cc) / |mu - cc|
       float dx = G.mu[0] - k.cc[0], dy = G.mu[1] - k.cc[1], dz = G.mu[2] - k.cc[2];
@@ -223,6 +223,7 @@ hipError_t launch_project_bwd(const ProjectArgs& a, const uint64_t* mask,
                               float* v_sh, int accumulate, hipStream_t s) {
   const int64_t blocks = a.N_pad / kMaskGroup;
   if (blocks == 0) return hipSuccess;
+  if (!fits_dispatch(uint64_t(blocks), kMaskGroup)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)}, block{uint32_t(kMaskGroup)};
 #define GS_LAUNCH_PB(D)                                                                      \
   hipLaunchKernelGGL(k_project_bwd<D>, grid, block, 0, s, a, mask, wg_scan, v_screen, v_means, \

@@ -351,6 +351,7 @@ hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uin
   const int T = tiles_x * tiles_y;
   const int64_t blocks = int64_t(C) * T;
   if (blocks == 0) return hipSuccess;
+  if (!fits_dispatch(uint64_t(blocks), kTilePix)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)};
 #define GS_FWD(P)                                                                            \
   hipLaunchKernelGGL(k_raster_fwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, W, H, \
@@ -370,6 +371,7 @@ hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uin
   const int T = tiles_x * tiles_y;
   const int64_t blocks = int64_t(C) * T;
   if (blocks == 0) return hipSuccess;
+  if (!fits_dispatch(uint64_t(blocks), kTilePix)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)};
 #define GS_BWD(P)                                                                             \
   hipLaunchKernelGGL(k_raster_bwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, W, H,  \

@@ -247,6 +247,7 @@ hipError_t launch_scan_u32(const uint32_t* in, const uint32_t* idx, uint64_t n, 
                            uint32_t* ticket, int* err, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const uint64_t blocks = (n + kScanTile - 1) / kScanTile;
+  if (!fits_dispatch(blocks, kScanThreads)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)}, block{uint32_t(kScanThreads)};
   ProfScope prof("k_scan", s);
   if (idx) {
@@ -292,6 +293,7 @@ hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t blocks = sort_blocks(n);
+  if (!fits_dispatch(blocks, kSortThreads)) return hipErrorInvalidConfiguration;
   uint32_t *ki = keys_a, *vi = vals_a, *ko = keys_b, *vo = vals_b;
   for (int p = 0; p < passes; ++p) {
     ProfScope prof("k_onesweep", s);

@@ -52,6 +52,28 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
 
 
+def compare_rows(rg, ro):
+    """GPU screen rows vs the oracle's fp32-stored rows of the same pairs.
+    Both sides evaluate the projection in fp64 and round once, so every
+    value agrees to within one fp32 ulp (of the conic's scale for the
+    conic, of max(|x|, 0.5) for colours); depth bits are exact. Returns
+    the largest differences in ulps."""
+    rg = np.asarray(rg, np.float64)
+    ro = np.asarray(ro, np.float64)
+    out = {}
+    for j, name in ((0, "u"), (1, "v"), (5, "opacity")):
+        d = np.abs(rg[:, j] - ro[:, j]) / ulp32(ro[:, j])
+        out[name] = float(d.max(initial=0))
+    cs = ulp32(np.maximum(np.abs(ro[:, 2]), np.abs(ro[:, 4])))
+    out["conic"] = float((np.abs(rg[:, 2:5] - ro[:, 2:5]) / cs[:, None]).max(initial=0))
+    out["rgb"] = float((np.abs(rg[:, 7:] - ro[:, 7:]) / ulp32(np.maximum(np.abs(ro[:, 7:]), 0.5))).max(initial=0))
+    np.testing.assert_array_equal(rg[:, 6].astype(np.float32).view(np.uint32),
+                                  ro[:, 6].astype(np.float32).view(np.uint32))
+    assert out["u"] <= 1 and out["v"] <= 1 and out["opacity"] <= 1, out
+    assert out["conic"] <= 2 and out["rgb"] <= 1, out
+    return out
+
+
 def unpack_mask(words: np.ndarray, n_pairs: int) -> np.ndarray:
     w = np.asarray(words).view(np.uint64)
     bits = (w[:, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)
