@@ -1,0 +1,190 @@
+"""Edge cases of the C ABI on the GPU: empty and invisible scenes, the
+capacity / workspace protocol (required sizes returned, nothing written
+past a capacity), degenerate images, saturated splats, null optional
+inputs, and run-to-run determinism of everything but the atomics."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import parity as P
+from tests.helpers import intrinsics, make_scene_from
+
+pytestmark = pytest.mark.gpu
+
+gsd = pytest.importorskip("gaussian_splatting_differentiable_project_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return gsd.load()
+
+
+def compare_full(sc, tag):
+    """Whole step on the GPU vs the oracle (fp32 rows), no exclusions
+    needed on these hand-built scenes beyond the fragility windows."""
+    L, grads_o, ref = oracle.loss_and_grads(sc, rows32=True)
+    r = gsd.Rasterizer()
+    out = r.step(gsd.Scene.from_numpy(sc), P.to_dev(sc["v_rgb"]), P.to_dev(sc["v_T"]))
+    torch.cuda.synchronize()
+    assert out["proj"].nnz == ref["proj"].nnz
+    fpx = P.fragile_pixels(ref["proj"].screen, ref["isect"].flatten_ids, ref["isect"].tile_offsets,
+                           sc["C"], sc["W"], sc["H"])
+    ok = ~fpx
+    e = np.abs(out["rgb"].cpu().numpy() - ref["rgb"])[ok].max(initial=0)
+    eT = np.abs(out["T"].cpu().numpy() - ref["T"])[ok].max(initial=0)
+    errs = {k: P.rel_l2(out["grads"][k].cpu().numpy(), grads_o[k]) for k in grads_o}
+    print(f"{tag}: nnz={out['proj'].nnz} isects={out['isect'].n_isects} rgb={e:.2e} T={eT:.2e} {errs}")
+    assert e <= P.IMG_TOL and eT <= P.IMG_TOL
+    assert max(errs.values()) <= P.GRAD_TOL
+    np.testing.assert_array_equal(out["last"].cpu().numpy()[ok], ref["last"][ok])
+    return out, ref
+
+
+def test_empty_scene(lib):
+    sc = make_scene_from(np.zeros((0, 3)), np.zeros((0, 4)), np.zeros((0, 3)), np.zeros(0),
+                         np.zeros((0, 1, 3)), workloads.lookat_viewmat((0, 0, 5)),
+                         intrinsics(40, 40, 33, 20), 33, 20, 0)
+    r = gsd.Rasterizer()
+    out = r.step(gsd.Scene.from_numpy(sc), P.to_dev(sc["v_rgb"]), P.to_dev(sc["v_T"]))
+    torch.cuda.synchronize()
+    assert out["proj"].nnz == 0 and out["isect"].n_isects == 0
+    assert int(out["isect"].tile_offsets.abs().sum()) == 0
+    assert torch.all(out["T"] == 1) and torch.all(out["rgb"] == 0) and torch.all(out["last"] == -1)
+    for g in out["grads"].values():
+        assert g.numel() == 0
+
+
+def test_nothing_visible(lib):
+    rng = np.random.default_rng(3)
+    n = 300
+    means = rng.uniform(-1, 1, (n, 3))
+    means[:, 2] = 9.0          # behind a camera at z = 5 looking at the origin
+    sc = make_scene_from(means, rng.normal(size=(n, 4)), np.full((n, 3), -2.0), rng.normal(size=n),
+                         rng.normal(size=(n, 4, 3)) * 0.1, workloads.lookat_viewmat((0, 0, 5)),
+                         intrinsics(40, 40, 40, 30), 40, 30, 1)
+    r = gsd.Rasterizer()
+    out = r.step(gsd.Scene.from_numpy(sc), P.to_dev(sc["v_rgb"]), P.to_dev(sc["v_T"]))
+    torch.cuda.synchronize()
+    assert out["proj"].nnz == 0 and out["isect"].n_isects == 0
+    assert torch.all(out["T"] == 1) and torch.all(out["last"] == -1)
+    for g in out["grads"].values():
+        assert torch.all(g == 0)
+
+
+def test_capacity_and_workspace_protocol(lib):
+    sc = workloads.make_scene(workloads.SMALL["sh1-odd-n"])
+    s = gsd.Scene.from_numpy(sc)
+    N, C, W, H = s.N, s.C, s.W, s.H
+    Np = gsd.pad_n(N)
+    mask = torch.empty(C * Np // 64, dtype=torch.int64, device="cuda")
+    wgc = torch.empty(C * Np // 128, dtype=torch.int32, device="cuda")
+    wgs = torch.empty_like(wgc)
+    wsb = lib.gs_project_workspace_bytes(N, C)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    canary = 0x7FC0DEAD
+    screen = torch.full((64 * 10 + 16,), 0, dtype=torch.int32, device="cuda").fill_(canary)
+    aabb = torch.full((64 * 2 + 16,), canary, dtype=torch.int32, device="cuda")
+    # too small: the required count comes back, the outputs stay untouched
+    st, nnz, cam = gsd.gs_project(N, C, W, H, s.sh_degree, s.means, s.quats, s.log_scales,
+                                  s.opacity_logits, s.sh, s.viewmats, s.Ks, mask, wgc, wgs,
+                                  screen, aabb, 64, ws, wsb)
+    torch.cuda.synchronize()
+    assert st == gsd.GS_E_CAPACITY and nnz > 64
+    assert torch.all(screen == canary) and torch.all(aabb == canary)
+    # short workspace
+    st2, _, _ = gsd.gs_project(N, C, W, H, s.sh_degree, s.means, s.quats, s.log_scales,
+                               s.opacity_logits, s.sh, s.viewmats, s.Ks, mask, wgc, wgs,
+                               screen, aabb, 64, ws, wsb - 1)
+    assert st2 == gsd.GS_E_WORKSPACE
+    # exact capacity, with canaries past the end
+    screen = torch.full((nnz * 10 + 64,), canary, dtype=torch.int32, device="cuda")
+    aabb = torch.full((nnz * 2 + 64,), canary, dtype=torch.int32, device="cuda")
+    st, nnz2, cam = gsd.gs_project(N, C, W, H, s.sh_degree, s.means, s.quats, s.log_scales,
+                                   s.opacity_logits, s.sh, s.viewmats, s.Ks, mask, wgc, wgs,
+                                   screen, aabb, nnz, ws, wsb)
+    torch.cuda.synchronize()
+    assert st == 0 and nnz2 == nnz and cam[-1] == nnz
+    assert torch.all(screen[nnz * 10:] == canary) and torch.all(aabb[nnz * 2:] == canary)
+    rows = screen[: nnz * 10].view(torch.float32).view(nnz, 10)
+    box = aabb[: nnz * 2].view(nnz, 2)
+    # intersect: workspace protocol, then capacity protocol
+    tx, ty = gsd.tiles(W, H)
+    toff = torch.empty(C * tx * ty + 1, dtype=torch.int64, device="cuda")
+    small_ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    st, n_is, need = gsd.gs_intersect(C, W, H, nnz, rows, box, cam, small_ws, 256, None, 0, toff)
+    assert st == gsd.GS_E_WORKSPACE and need > 256
+    ws1 = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ids = torch.full((16,), canary, dtype=torch.int32, device="cuda")
+    st, n_is, need2 = gsd.gs_intersect(C, W, H, nnz, rows, box, cam, ws1, need, ids, 8, toff)
+    torch.cuda.synchronize()
+    assert st == gsd.GS_E_CAPACITY and n_is > 8 and torch.all(ids == canary)
+    ws2 = torch.empty(need2, dtype=torch.uint8, device="cuda")
+    ids = torch.full((n_is + 64,), canary, dtype=torch.int32, device="cuda")
+    st, n_is2, _ = gsd.gs_intersect(C, W, H, nnz, rows, box, cam, ws2, need2, ids, n_is, toff)
+    torch.cuda.synchronize()
+    assert st == 0 and n_is2 == n_is and int(toff[-1]) == n_is
+    assert torch.all(ids[n_is:] == canary)
+    # a workspace short by one byte is refused
+    st, _, _ = gsd.gs_intersect(C, W, H, nnz, rows, box, cam, ws2, need2 - 1, ids, n_is, toff)
+    assert st == gsd.GS_E_WORKSPACE
+    # invalid camera offsets
+    bad = list(cam)
+    bad[-1] = nnz + 1
+    st, _, _ = gsd.gs_intersect(C, W, H, nnz, rows, box, bad, ws2, need2, ids, n_is, toff)
+    assert st == gsd.GS_E_INVALID
+
+
+@pytest.mark.parametrize("W,H", [(1, 1), (16, 16), (17, 5)])
+def test_tiny_images(lib, W, H):
+    spec = workloads.SceneSpec("tiny-image", 400, 2, 1, W, H, 20.0 * max(W, H) / 16, 1.0, -2.5, 0.4,
+                               5.0, seed=77)
+    compare_full(workloads.make_scene(spec), f"{W}x{H}")
+
+
+def test_saturated_splats(lib):
+    """Large, nearly opaque splats over the whole image: the 0.99 clamp and
+    the early stop decide most pixels."""
+    rng = np.random.default_rng(5)
+    n = 90
+    means = rng.uniform(-0.6, 0.6, (n, 3))
+    sc = make_scene_from(means, rng.normal(size=(n, 4)), rng.normal(-0.8, 0.2, (n, 3)),
+                         np.full(n, 6.0), rng.normal(size=(n, 9, 3)) * 0.2,
+                         workloads.lookat_viewmat((0, 0, 5)), intrinsics(60, 60, 70, 50), 70, 50, 2)
+    out, ref = compare_full(sc, "saturated")
+    assert (ref["T"] < 1e-3).mean() > 0.15   # the early stop decides many pixels
+
+
+def test_null_vT_is_zero(lib):
+    sc = workloads.make_scene(workloads.SMALL["sh2-dense"])
+    r = gsd.Rasterizer()
+    s = gsd.Scene.from_numpy(sc)
+    p = r.project(s)
+    it = r.intersect(s, p)
+    rgb, T, last = r.rasterize_fwd(s, p, it)
+    v1 = r.rasterize_bwd(s, p, it, T, last, P.to_dev(sc["v_rgb"]), None).clone()
+    v2 = r.rasterize_bwd(s, p, it, T, last, P.to_dev(sc["v_rgb"]),
+                         torch.zeros(s.C, s.H, s.W, device="cuda")).clone()
+    torch.cuda.synchronize()
+    assert P.rel_l2(v1.cpu().numpy(), v2.cpu().numpy()) < 1e-6
+
+
+def test_forward_and_sort_are_deterministic(lib):
+    sc = workloads.make_scene(workloads.SMALL["multicam"])
+    outs = []
+    for _ in range(2):
+        r = gsd.Rasterizer()
+        s = gsd.Scene.from_numpy(sc)
+        p = r.project(s)
+        it = r.intersect(s, p, want_keys=True)
+        rgb, T, last = r.rasterize_fwd(s, p, it)
+        torch.cuda.synchronize()
+        outs.append([x.cpu().numpy().copy() for x in (p.mask, p.screen, p.aabb16, it.flatten_ids,
+                                                      it.sorted_keys, it.tile_offsets, rgb, T, last)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
