@@ -64,6 +64,63 @@ __device__ __forceinline__ Eval eval_splat(const float4& A, const float4& Bv, fl
   return e;
 }
 
+// Can the entry reach alpha >= 1/255 at any pixel centre of the tile?
+// alpha >= 1/255  <=>  sigma <= ln(255 o); sigma is a convex quadratic in
+// the pixel position, so its minimum over the rectangle of pixel centres
+// is 0 if the splat centre is inside, else the least of the four edge
+// minima (a 1-D quadratic clamped to the edge). Entries that fail are
+// skipped for the whole tile; the margin in sigma (1e-3 plus 1e-4
+// relative) is far above the rounding of either side of the comparison,
+// so no entry that any pixel would composite is ever skipped.
+__device__ __forceinline__ bool reaches_tile(const Staged& e, float x0, float x1, float y0,
+                                             float y1) {
+  const float u = e.a.x, v = e.a.y, ha = e.a.z, hc = e.a.w, b = e.b.x;
+  const float cut = (e.b.y + 7.99435343f) * 0.69314718f;  // ln(255 o)
+  if (u >= x0 && u <= x1 && v >= y0 && v <= y1) return true;
+  // sigma(dx, dy) = ha dx^2 + hc dy^2 + b dx dy with dx = u - px, dy = v - py
+  auto q = [&](float dx, float dy) { return fmaf(ha * dx, dx, fmaf(hc * dy, dy, b * dx * dy)); };
+  const float ia = 0.5f / ha, ic = 0.5f / hc;
+  float m = 3.4e38f;
+  {  // vertical edges px = x0, x1: best dy = -b dx / (2 hc), clamped
+    const float dxa = u - x0, dxb = u - x1;
+    const float dya = fminf(fmaxf(-b * dxa * ic, v - y1), v - y0);
+    const float dyb = fminf(fmaxf(-b * dxb * ic, v - y1), v - y0);
+    m = fminf(m, fminf(q(dxa, dya), q(dxb, dyb)));
+  }
+  {  // horizontal edges py = y0, y1
+    const float dya = v - y0, dyb = v - y1;
+    const float dxa = fminf(fmaxf(-b * dya * ia, u - x1), u - x0);
+    const float dxb = fminf(fmaxf(-b * dyb * ia, u - x1), u - x0);
+    m = fminf(m, fminf(q(dxa, dya), q(dxb, dyb)));
+  }
+  return m <= cut + 1e-3f + 1e-4f * fabsf(cut);
+}
+
+// Order-preserving compaction of a batch staged by all NT lanes: lanes with
+// keep write their entry to the next free LDS slot. Returns the count.
+template <int NT>
+__device__ __forceinline__ int compact_slot(bool keep, int* s_wcnt, int* pos) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t bal = __ballot(keep);
+  const int mine = __popcll(bal & lanemask_lt());
+  if constexpr (NT <= kWave) {
+    *pos = mine;
+    return __popcll(bal);
+  } else {
+    if (lane == 0) s_wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+      const int c = s_wcnt[w];
+      off += w < wave ? c : 0;
+      tot += c;
+    }
+    *pos = off + mine;
+    return tot;
+  }
+}
+
 template <int PPT>
 __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
     const float* __restrict__ screen, const uint32_t* __restrict__ ids,
@@ -74,6 +131,8 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
   __shared__ float4 s_a[B];
   __shared__ float4 s_b[B];
   __shared__ float s_c[B];
+  __shared__ int s_lid[B];
+  __shared__ int s_wcnt[NT / kWave];
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.x;
   const int c = int(t / T);
@@ -98,23 +157,32 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
     last[k] = -1;
   }
 
+  const float tx0 = float(tx * kTile) + 0.5f, ty0 = float(ty * kTile) + 0.5f;
+  const float tx1 = fminf(tx0 + 15.f, float(W) - 0.5f), ty1 = fminf(ty0 + 15.f, float(H) - 0.5f);
   for (int64_t b0 = start; b0 < end; b0 += B) {
     bool any_live = false;
 #pragma unroll
     for (int k = 0; k < PPT; ++k) any_live |= live[k];
     if (__syncthreads_count(any_live) == 0) break;
+    Staged e;
+    bool keep = false;
     if (b0 + tid < end) {
-      const Staged e = stage_row(screen, ids[b0 + tid]);
-      s_a[tid] = e.a;
-      s_b[tid] = e.b;
-      s_c[tid] = e.c.x;
+      e = stage_row(screen, ids[b0 + tid]);
+      keep = reaches_tile(e, tx0, tx1, ty0, ty1);
+    }
+    int pos;
+    const int nb = compact_slot<NT>(keep, s_wcnt, &pos);
+    if (keep) {
+      s_a[pos] = e.a;
+      s_b[pos] = e.b;
+      s_c[pos] = e.c.x;
+      s_lid[pos] = int(b0 - start) + tid;
     }
     __syncthreads();
-    const int nb = int((end - b0) < B ? (end - b0) : B);
-    const int lid0 = int(b0 - start);
     for (int j = 0; j < nb; ++j) {
       const float4 A = s_a[j], Bv = s_b[j];
       const float cblue = s_c[j];
+      const int lid = s_lid[j];
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
         const Eval e = eval_splat(A, Bv, px[k], py[k]);
@@ -128,7 +196,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
           cg[k] = fmaf(Bv.w, w, cg[k]);
           cb[k] = fmaf(cblue, w, cb[k]);
           Tr[k] = Tn;
-          last[k] = lid0 + j;
+          last[k] = lid;
         }
       }
     }
@@ -222,6 +290,8 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
   __shared__ float4 s_b[B];
   __shared__ float2 s_c[B];
   __shared__ uint32_t s_id[B];
+  __shared__ int s_lid[B];
+  __shared__ int s_wcnt[NT / kWave];
   __shared__ int s_max;
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.x;
@@ -267,24 +337,34 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
   if (n_used <= 0 || end <= start) return;
   const int64_t stop_at = start + n_used;
 
+  const float tx0 = float(tx * kTile) + 0.5f, ty0 = float(ty * kTile) + 0.5f;
+  const float tx1 = fminf(tx0 + 15.f, float(W) - 0.5f), ty1 = fminf(ty0 + 15.f, float(H) - 0.5f);
   for (int64_t b_end = stop_at; b_end > start; b_end -= B) {
     const int64_t b_start = (b_end - start) > B ? b_end - B : start;
-    const int nb = int(b_end - b_start);
+    const int n_in = int(b_end - b_start);
     __syncthreads();
-    if (tid < nb) {
-      const uint32_t s = ids[b_start + tid];
-      const Staged e = stage_row(screen, s);
-      s_a[tid] = e.a;
-      s_b[tid] = e.b;
-      s_c[tid] = e.c;
-      s_id[tid] = s;
+    Staged e;
+    uint32_t sid = 0;
+    bool keep = false;
+    if (tid < n_in) {
+      sid = ids[b_start + tid];
+      e = stage_row(screen, sid);
+      keep = reaches_tile(e, tx0, tx1, ty0, ty1);
+    }
+    int pos;
+    const int nb = compact_slot<NT>(keep, s_wcnt, &pos);
+    if (keep) {
+      s_a[pos] = e.a;
+      s_b[pos] = e.b;
+      s_c[pos] = e.c;
+      s_id[pos] = sid;
+      s_lid[pos] = int(b_start - start) + tid;
     }
     __syncthreads();
-    const int lid0 = int(b_start - start);
     for (int j = nb - 1; j >= 0; --j) {
       const float4 A = s_a[j], Bv = s_b[j];
       const float2 Cv = s_c[j];
-      const int lid = lid0 + j;
+      const int lid = s_lid[j];
       // per-lane sums over its pixels: first moments and second moments of
       // (dx, dy) weighted by dL/dsigma, sum of dL/dalpha raw, colour grads
       float mx = 0.f, my = 0.f, mxx = 0.f, mxy = 0.f, myy = 0.f, mo = 0.f;

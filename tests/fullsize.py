@@ -207,40 +207,63 @@ def gpu_tile_counts_from_boxes(aabb_dev, cam_offsets, C, W, H):
 
 
 def raster_tiles(o: OracleScene, tiles, sc, with_bwd=False):
-    """Oracle raster over the given global tiles using compact lists:
-    returns (rgb, T, last, fragile pixel mask) per tile and, with_bwd, the
-    screen gradients of every slot on those tiles (dict slot -> row)."""
+    """Oracle raster over the given global tiles using compact lists.
+
+    Returns (tiles, rgb, T, last, fragile pixel mask, screen gradients,
+    composited slots): images are full-size arrays, NaN outside the tiles;
+    the gradients (with_bwd) map every slot on those tiles to its row;
+    composited slots are those the oracle's walk composites at >= 1 pixel.
+    """
     C, W, H = o.C, o.W, o.H
-    lists = {int(t): o.tile_list(t) for t in tiles}
-    uniq = np.unique(np.concatenate([l for l in lists.values()] + [np.zeros(0, np.int64)]))
+    order = sorted(int(t) for t in tiles)
+    lists = {t: o.tile_list(t) for t in order}
+    uniq = np.unique(np.concatenate([lists[t] for t in order] + [np.zeros(0, np.int64)]))
     local = {int(s): k for k, s in enumerate(uniq)}
     rows = o.rows[uniq].astype(np.float64)
-    n_tiles = C * o.T
-    offs = np.zeros(n_tiles + 1, np.int64)
-    order = sorted(lists)
-    counts = np.zeros(n_tiles, np.int64)
-    for t in order:
-        counts[t] = lists[t].size
-    offs[1:] = np.cumsum(counts)
-    flat = np.zeros(int(offs[-1]), np.int64)
-    for t in order:
-        flat[offs[t]:offs[t + 1]] = [local[int(s)] for s in lists[t]]
-    rgb, T, last, _ = oracle.rasterize_fwd(rows, flat, offs, C, W, H, tiles=order)
-    frag_px = P.fragile_pixels(rows, flat, offs, C, W, H,
-                               tiles_touched=None) if len(order) else None
-    # pixels a fragile pair can reach with alpha >= 1/255 are fragile too
+    rgb = np.full((C, H, W, 3), np.nan)
+    Tm = np.full((C, H, W), np.nan)
+    last = np.full((C, H, W), -2, np.int64)
+    frag_px = np.zeros((C, H, W), bool)
+    composited = set()
     for t in order:
         c, tl = divmod(t, o.T)
         ii, jj = oraster._tile_pixels(tl, o.tiles_x, W, H)
-        fr = [int(s) for s in lists[t] if o.frag[o.pairs[s]]]
-        for s in fr:
-            u, v, a, b, cc, op = (float(x) for x in o.rows[s, :6])
-            dx, dy = u - (jj + 0.5), v - (ii + 0.5)
-            al = op * np.exp(-(0.5 * (a * dx * dx + cc * dy * dy) + b * dx * dy))
-            hit = al >= oraster.ALPHA_MIN * (1 - 1e-3)
-            frag_px[c, ii[hit], jj[hit]] = True
+        ids = np.array([local[int(s)] for s in lists[t]], np.int64)
+        if ids.size == 0:
+            rgb[c, ii, jj] = 0.0
+            Tm[c, ii, jj] = 1.0
+            last[c, ii, jj] = -1
+            continue
+        Cc, Tt, ll, _, rec = oraster._walk_tile(rows[ids], jj + 0.5, ii + 0.5, record=True)
+        rgb[c, ii, jj] = Cc
+        Tm[c, ii, jj] = Tt
+        last[c, ii, jj] = ll
+        a = rec["alpha"]
+        Tn = rec["Tb"] * (1.0 - a)
+        stops = (a >= oraster.ALPHA_MIN) & (Tn < oraster.T_STOP) & ~rec["comp"]
+        first = np.where(stops.any(1), stops.argmax(1), a.shape[1])
+        reached = np.arange(a.shape[1])[None, :] <= first[:, None]
+        bad = reached & (np.abs(a - oraster.ALPHA_MIN) <= P.ALPHA_WIN * oraster.ALPHA_MIN)
+        bad |= reached & (a >= oraster.ALPHA_MIN) & \
+            (np.abs(Tn - oraster.T_STOP) <= P.T_WIN * oraster.T_STOP)
+        fp = bad.any(1)
+        # pixels a fragile pair reaches with alpha >= 1/255
+        for k, s in enumerate(lists[t]):
+            if o.frag[o.pairs[s]]:
+                fp |= reached[:, k] & (a[:, k] >= oraster.ALPHA_MIN * (1 - 1e-3))
+        frag_px[c, ii, jj] = fp
+        composited.update(int(s) for s in lists[t][rec["comp"].any(0)])
     vs = None
     if with_bwd:
+        n_tiles = C * o.T
+        counts = np.zeros(n_tiles, np.int64)
+        for t in order:
+            counts[t] = lists[t].size
+        offs = np.zeros(n_tiles + 1, np.int64)
+        offs[1:] = np.cumsum(counts)
+        flat = np.zeros(int(offs[-1]), np.int64)
+        for t in order:
+            flat[offs[t]:offs[t + 1]] = [local[int(s)] for s in lists[t]]
         g = oracle.rasterize_bwd(rows, flat, offs, C, W, H, sc["v_rgb"], sc["v_T"], tiles=order)
         vs = {int(s): g[local[int(s)]] for s in uniq}
-    return order, rgb, T, last, frag_px, vs
+    return order, rgb, Tm, last, frag_px, vs, composited
