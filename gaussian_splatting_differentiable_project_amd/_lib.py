@@ -65,11 +65,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
         [c_vp] * 3 + [c_vp, c_vp, c_i64, c_vp, c_u64, P_i64, P_i64]
     lib.gs_intersect.restype = ctypes.c_int
     lib.gs_intersect.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i64, c_vp, c_vp, P_i64, c_vp, c_u64,
-                                 c_vp, c_i64, c_vp, c_vp, P_i64, P_u64]
+                                 c_vp, c_i64, c_vp, c_vp, c_vp, P_i64, P_u64]
     lib.gs_rasterize_fwd.restype = ctypes.c_int
-    lib.gs_rasterize_fwd.argtypes = [c_vp, c_i32, c_i32, c_i32] + [c_vp] * 6
+    lib.gs_rasterize_fwd.argtypes = [c_vp, c_i32, c_i32, c_i32] + [c_vp] * 7
     lib.gs_rasterize_bwd.restype = ctypes.c_int
-    lib.gs_rasterize_bwd.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i64] + [c_vp] * 8
+    lib.gs_rasterize_bwd.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i64] + [c_vp] * 9
     lib.gs_project_bwd.restype = ctypes.c_int
     lib.gs_project_bwd.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
         [c_vp] * 3 + [c_vp] * 5 + [c_i32]
@@ -150,30 +150,33 @@ def gs_project(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, 
 
 
 def gs_intersect(C, W, H, nnz, screen, aabb16, cam_offsets, workspace, workspace_bytes,
-                 flatten_ids, isect_capacity, tile_offsets, sorted_keys=None, stream=None):
+                 flatten_ids, isect_capacity, tile_offsets, sorted_keys=None, tile_order=None,
+                 stream=None):
     """Returns (status, n_isects, workspace_needed)."""
     cam = (ctypes.c_int64 * (C + 1))(*[int(x) for x in cam_offsets])
     n_is = ctypes.c_int64(-1)
     need = ctypes.c_uint64(0)
     st = load().gs_intersect(_stream(stream), C, W, H, nnz, _ptr(screen), _ptr(aabb16), cam,
                              _ptr(workspace), workspace_bytes, _ptr(flatten_ids), isect_capacity,
-                             _ptr(tile_offsets), _ptr(sorted_keys), ctypes.byref(n_is),
+                             _ptr(tile_offsets), _ptr(sorted_keys), _ptr(tile_order),
+                             ctypes.byref(n_is),
                              ctypes.byref(need))
     return st, n_is.value, need.value
 
 
-def gs_rasterize_fwd(C, W, H, screen, flatten_ids, tile_offsets, out_rgb, out_T, last_ids,
-                     stream=None):
+def gs_rasterize_fwd(C, W, H, screen, flatten_ids, tile_offsets, tile_order, out_rgb, out_T,
+                     last_ids, stream=None):
     return load().gs_rasterize_fwd(_stream(stream), C, W, H, _ptr(screen), _ptr(flatten_ids),
-                                   _ptr(tile_offsets), _ptr(out_rgb), _ptr(out_T),
-                                   _ptr(last_ids))
+                                   _ptr(tile_offsets), _ptr(tile_order), _ptr(out_rgb),
+                                   _ptr(out_T), _ptr(last_ids))
 
 
-def gs_rasterize_bwd(C, W, H, nnz, screen, flatten_ids, tile_offsets, out_T, last_ids, v_rgb,
-                     v_T, v_screen, stream=None):
+def gs_rasterize_bwd(C, W, H, nnz, screen, flatten_ids, tile_offsets, tile_order, out_T,
+                     last_ids, v_rgb, v_T, v_screen, stream=None):
     return load().gs_rasterize_bwd(_stream(stream), C, W, H, nnz, _ptr(screen),
-                                   _ptr(flatten_ids), _ptr(tile_offsets), _ptr(out_T),
-                                   _ptr(last_ids), _ptr(v_rgb), _ptr(v_T), _ptr(v_screen))
+                                   _ptr(flatten_ids), _ptr(tile_offsets), _ptr(tile_order),
+                                   _ptr(out_T), _ptr(last_ids), _ptr(v_rgb), _ptr(v_T),
+                                   _ptr(v_screen))
 
 
 def gs_project_bwd(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, sh,
@@ -230,6 +233,7 @@ class Intersected:
     flatten_ids: torch.Tensor  # [n_isects] view
     tile_offsets: torch.Tensor  # [C*T+1]
     sorted_keys: torch.Tensor | None
+    tile_order: torch.Tensor | None = None  # [C*T] raster launch order, longest tiles first
 
 
 def _grow(buf, numel, dtype, device, slack=1.0):
@@ -279,11 +283,15 @@ class Rasterizer:
                              torch.empty(0, 2, dtype=torch.int32, device=dev))
         raise GsError(GS_E_CAPACITY, "gs_project")
 
-    def intersect(self, s: Scene, p: Projected, want_keys: bool = False) -> Intersected:
+    def intersect(self, s: Scene, p: Projected, want_keys: bool = False,
+                  ordered: bool = True) -> Intersected:
+        """ordered: also return the heavy-first launch order the raster
+        calls then use (without it they run tiles in id order)."""
         dev = self.device
         tx, ty = tiles(s.W, s.H)
         n_tiles = s.C * tx * ty
         tile_offsets = torch.empty(n_tiles + 1, dtype=torch.int64, device=dev)
+        order = torch.empty(n_tiles, dtype=torch.int32, device=dev) if ordered else None
         if self._iws is None:
             self._iws = _grow(None, int(load().gs_intersect_workspace_bytes(s.C, s.W, s.H, p.nnz, 0)),
                               torch.uint8, dev, self.slack)
@@ -295,7 +303,7 @@ class Rasterizer:
                 self._keys = keys
             st, n_is, need = gs_intersect(s.C, s.W, s.H, p.nnz, p.screen, p.aabb16, p.cam_offsets,
                                           self._iws, self._iws.numel(), self._ids, cap,
-                                          tile_offsets, keys)
+                                          tile_offsets, keys, order)
             if st == GS_E_WORKSPACE:
                 self._iws = _grow(None, need, torch.uint8, dev, self.slack)
                 continue
@@ -307,7 +315,7 @@ class Rasterizer:
             self._check(st, "gs_intersect")
             return Intersected(n_is, self._ids[:n_is] if n_is else
                                torch.empty(0, dtype=torch.int32, device=dev), tile_offsets,
-                               keys[:n_is] if keys is not None else None)
+                               keys[:n_is] if keys is not None else None, order)
         raise GsError(GS_E_CAPACITY, "gs_intersect")
 
     def rasterize_fwd(self, s: Scene, p: Projected, it: Intersected):
@@ -316,7 +324,7 @@ class Rasterizer:
         T = torch.empty(s.C, s.H, s.W, device=dev)
         last = torch.empty(s.C, s.H, s.W, dtype=torch.int32, device=dev)
         self._check(gs_rasterize_fwd(s.C, s.W, s.H, p.screen, it.flatten_ids, it.tile_offsets,
-                                     rgb, T, last), "gs_rasterize_fwd")
+                                     it.tile_order, rgb, T, last), "gs_rasterize_fwd")
         return rgb, T, last
 
     def rasterize_bwd(self, s: Scene, p: Projected, it: Intersected, out_T, last, v_rgb, v_T=None):
@@ -325,7 +333,7 @@ class Rasterizer:
         v = self._vscreen[: p.nnz * ROW].view(p.nnz, ROW) if p.nnz else \
             torch.empty(0, ROW, device=dev)
         self._check(gs_rasterize_bwd(s.C, s.W, s.H, p.nnz, p.screen, it.flatten_ids,
-                                     it.tile_offsets, out_T, last, v_rgb, v_T, v),
+                                     it.tile_offsets, it.tile_order, out_T, last, v_rgb, v_T, v),
                     "gs_rasterize_bwd")
         return v
 

@@ -81,6 +81,7 @@ struct IsectWs {
   uint32_t* tickets;    // [32]: 0 scan, 1..4 depth passes, 8..15 tile passes
   uint64_t* hist_depth; // [4][256]
   uint64_t* hist_tile;  // [4][256]
+  uint64_t* hist_order; // [4][256]
   int64_t* cam_off;     // [C+1]
   uint32_t *dkeys_a, *dkeys_b, *dvals_a, *dvals_b, *cnt;
   uint64_t* offs;
@@ -90,10 +91,11 @@ struct IsectWs {
   uint64_t sort_lb_words;
   uint64_t phase1_bytes;  // enough to count (I still unknown)
   uint32_t *tkeys_a, *tkeys_b, *tvals;
+  uint32_t *ord_keys_a, *ord_keys_b, *ord_vals_b;  // launch-order sort of the tiles
   uint64_t bytes;
 };
 
-IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects) {
+IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects, uint64_t n_tiles) {
   Carver cv{static_cast<char*>(base)};
   IsectWs w{};
   w.total = cv.take<uint64_t>(1);
@@ -102,6 +104,7 @@ IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects) {
   w.tickets = cv.take<uint32_t>(32);
   w.hist_depth = cv.take<uint64_t>(4 * kRadix);
   w.hist_tile = cv.take<uint64_t>(4 * kRadix);
+  w.hist_order = cv.take<uint64_t>(4 * kRadix);
   w.zero_words = cv.off / 4;
   w.cam_off = cv.take<int64_t>(uint64_t(C) + 1);
   const uint64_t n = uint64_t(nnz);
@@ -112,7 +115,11 @@ IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects) {
   w.cnt = cv.take<uint32_t>(n);
   w.offs = cv.take<uint64_t>(n);
   w.scan_lb = cv.take<uint64_t>((n + kScanTile - 1) / kScanTile + 1);
-  const uint64_t nb1 = sort_blocks(n);
+  w.ord_keys_a = cv.take<uint32_t>(n_tiles);
+  w.ord_keys_b = cv.take<uint32_t>(n_tiles);
+  w.ord_vals_b = cv.take<uint32_t>(n_tiles);
+  uint64_t nb1 = sort_blocks(n);
+  if (sort_blocks(n_tiles) > nb1) nb1 = sort_blocks(n_tiles);
   w.phase1_bytes = cv.off + align_up(nb1 * kRadix * sizeof(uint64_t));
   const uint64_t I = n_isects > 0 ? uint64_t(n_isects) : 0;
   const uint64_t nb = nb1 > sort_blocks(I) ? nb1 : sort_blocks(I);
@@ -173,10 +180,9 @@ uint64_t gs_project_workspace_bytes(int64_t N, int32_t C) {
 
 uint64_t gs_intersect_workspace_bytes(int32_t C, int32_t W, int32_t H, int64_t nnz,
                                       int64_t n_isects) {
-  (void)W;
-  (void)H;
-  if (C < 1 || nnz < 0) return 0;
-  return carve_isect(nullptr, C, nnz, n_isects).bytes;
+  if (C < 1 || nnz < 0 || W < 1 || H < 1) return 0;
+  const uint64_t n_tiles = uint64_t(C) * uint64_t(tiles_x_of(W) * tiles_y_of(H));
+  return carve_isect(nullptr, C, nnz, n_isects, n_tiles).bytes;
 }
 
 int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t sh_degree,
@@ -242,8 +248,8 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t
 int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, const float* screen,
                  const uint32_t* aabb16, const int64_t* cam_offsets, void* workspace,
                  uint64_t workspace_bytes, uint32_t* flatten_ids, int64_t isect_capacity,
-                 int64_t* tile_offsets, uint64_t* sorted_keys, int64_t* n_isects_out,
-                 uint64_t* workspace_needed_out) {
+                 int64_t* tile_offsets, uint64_t* sorted_keys, uint32_t* tile_order,
+                 int64_t* n_isects_out, uint64_t* workspace_needed_out) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!valid_image(C, W, H) || nnz < 0 || !n_isects_out || !workspace_needed_out ||
       !tile_offsets || !cam_offsets || isect_capacity < 0)
@@ -258,7 +264,7 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   const uint64_t n_tiles = uint64_t(C) * uint64_t(tiles_x_of(W) * tiles_y_of(H));
   if (n_tiles >= (uint64_t(1) << 32)) return GS_E_OVERFLOW;
 
-  IsectWs ws = carve_isect(workspace, C, nnz, 0);
+  IsectWs ws = carve_isect(workspace, C, nnz, 0, n_tiles);
   *workspace_needed_out = ws.phase1_bytes;
   if (!workspace || workspace_bytes < ws.phase1_bytes) return GS_E_WORKSPACE;
 
@@ -273,7 +279,7 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   GS_TRY(hipStreamSynchronize(s));
   *n_isects_out = int64_t(I);
   if (I >= (uint64_t(1) << 62)) return GS_E_OVERFLOW;
-  ws = carve_isect(workspace, C, nnz, int64_t(I));
+  ws = carve_isect(workspace, C, nnz, int64_t(I), n_tiles);
   *workspace_needed_out = ws.bytes;
   if (int64_t(I) > isect_capacity) return GS_E_CAPACITY;
   if (workspace_bytes < ws.bytes) return GS_E_WORKSPACE;
@@ -281,6 +287,7 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
 
   if (I == 0) {
     GS_TRY(launch_fill_u32(tile_offsets, 0u, 2 * (n_tiles + 1), s));
+    if (tile_order) GS_TRY(launch_tile_order_keys(tile_offsets, n_tiles, ws.ord_keys_a, tile_order, s));
     return GS_OK;
   }
 
@@ -315,31 +322,41 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   // Phase 5: per-tile ranges (and the composed 64-bit keys on request).
   GS_TRY(launch_tile_ranges(tkeys, I, n_tiles, tile_offsets, s));
   if (sorted_keys) GS_TRY(launch_compose_keys(tkeys, flatten_ids, screen, I, sorted_keys, s));
+  // Phase 6: launch order for the raster calls, longest tiles first (a
+  // stable sort of 16-bit inverted counts: two even passes end in tile_order).
+  if (tile_order) {
+    GS_TRY(launch_tile_order_keys(tile_offsets, n_tiles, ws.ord_keys_a, tile_order, s));
+    SortScratch so{ws.hist_order, ws.sort_lb, ws.tickets + 16, ws.err};
+    GS_TRY(launch_sort_histogram(ws.ord_keys_a, n_tiles, 0, 16, so, s));
+    GS_TRY(launch_sort_passes(ws.ord_keys_a, tile_order, ws.ord_keys_b, ws.ord_vals_b, n_tiles, 0,
+                              16, so, 16, &in_b, s));
+  }
   return check_device_error(ws.err, s);
 }
 
 int gs_rasterize_fwd(void* stream, int32_t C, int32_t W, int32_t H, const float* screen,
-                     const uint32_t* flatten_ids, const int64_t* tile_offsets, float* out_rgb,
-                     float* out_T, int32_t* last_ids) {
+                     const uint32_t* flatten_ids, const int64_t* tile_offsets,
+                     const uint32_t* tile_order, float* out_rgb, float* out_T,
+                     int32_t* last_ids) {
   if (!valid_image(C, W, H) || !tile_offsets || !out_rgb || !out_T || !last_ids)
     return GS_E_INVALID;
   if (!aligned(screen, 8)) return GS_E_INVALID;
-  return hip_status(launch_raster_fwd(C, W, H, screen, flatten_ids, tile_offsets, out_rgb, out_T,
-                                      last_ids, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_raster_fwd(C, W, H, screen, flatten_ids, tile_offsets, tile_order,
+                                      out_rgb, out_T, last_ids, static_cast<hipStream_t>(stream)));
 }
 
 int gs_rasterize_bwd(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz,
                      const float* screen, const uint32_t* flatten_ids, const int64_t* tile_offsets,
-                     const float* out_T, const int32_t* last_ids, const float* v_rgb,
-                     const float* v_T, float* v_screen) {
+                     const uint32_t* tile_order, const float* out_T, const int32_t* last_ids,
+                     const float* v_rgb, const float* v_T, float* v_screen) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!valid_image(C, W, H) || nnz < 0 || !tile_offsets || !out_T || !last_ids || !v_rgb)
     return GS_E_INVALID;
   if (nnz > 0 && !v_screen) return GS_E_INVALID;
   if (!aligned(screen, 8)) return GS_E_INVALID;
   GS_TRY(launch_fill_u32(v_screen, 0u, uint64_t(nnz) * kRow, s));
-  return hip_status(launch_raster_bwd(C, W, H, screen, flatten_ids, tile_offsets, out_T, last_ids,
-                                      v_rgb, v_T, v_screen, s));
+  return hip_status(launch_raster_bwd(C, W, H, screen, flatten_ids, tile_offsets, tile_order, out_T,
+                                      last_ids, v_rgb, v_T, v_screen, s));
 }
 
 int gs_project_bwd(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t sh_degree,

@@ -89,17 +89,19 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
                              uint64_t cap, uint32_t* tkeys, uint32_t* tvals, hipStream_t s);
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
                               hipStream_t s);
+hipError_t launch_tile_order_keys(const int64_t* toff, uint64_t n_tiles, uint32_t* keys,
+                                  uint32_t* vals, hipStream_t s);
 hipError_t launch_compose_keys(const uint32_t* tkeys, const uint32_t* ids, const float* screen,
                                uint64_t n, uint64_t* out, hipStream_t s);
 
 // Rasterization (gs_raster.hip).
 hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uint32_t* ids,
-                             const int64_t* toff, float* out_rgb, float* out_T, int32_t* last_ids,
-                             hipStream_t s);
+                             const int64_t* toff, const uint32_t* order, float* out_rgb,
+                             float* out_T, int32_t* last_ids, hipStream_t s);
 hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uint32_t* ids,
-                             const int64_t* toff, const float* out_T, const int32_t* last_ids,
-                             const float* v_rgb, const float* v_T, float* v_screen,
-                             hipStream_t s);
+                             const int64_t* toff, const uint32_t* order, const float* out_T,
+                             const int32_t* last_ids, const float* v_rgb, const float* v_T,
+                             float* v_screen, hipStream_t s);
 
 // First slot of every camera from the group scan (gs_project.hip).
 hipError_t launch_cam_offsets(const uint32_t* wg_scan, int64_t groups_per_cam, int C,

@@ -131,6 +131,20 @@ __global__ __launch_bounds__(256) void k_compose_keys(const uint32_t* __restrict
   }
 }
 
+// Keys for the raster launch order: tiles with more entries first (the
+// key is 0xFFFF minus the entry count, saturated), values are tile ids.
+__global__ __launch_bounds__(256) void k_tile_order_keys(const int64_t* __restrict__ toff,
+                                                        uint64_t n_tiles,
+                                                        uint32_t* __restrict__ keys,
+                                                        uint32_t* __restrict__ vals) {
+  const uint64_t stride = uint64_t(gridDim.x) * 256;
+  for (uint64_t t = uint64_t(blockIdx.x) * 256 + threadIdx.x; t < n_tiles; t += stride) {
+    const int64_t n = toff[t + 1] - toff[t];
+    keys[t] = 0xFFFFu - uint32_t(n < 0xFFFF ? n : 0xFFFF);
+    vals[t] = uint32_t(t);
+  }
+}
+
 inline uint32_t grid_for(uint64_t n) { return uint32_t((n + 255) / 256); }
 // Blocks for a grid-stride loop over n elements.
 inline uint32_t grid_stride_blocks(uint64_t n) {
@@ -172,6 +186,15 @@ hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tile
   ProfScope prof("k_tile_ranges", s);
   hipLaunchKernelGGL(k_tile_ranges, dim3(grid_stride_blocks(n + 1)), dim3(256), 0, s, tkeys, n, n_tiles,
                      toff);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_order_keys(const int64_t* toff, uint64_t n_tiles, uint32_t* keys,
+                                  uint32_t* vals, hipStream_t s) {
+  if (n_tiles == 0) return hipSuccess;
+  ProfScope prof("k_tile_order_keys", s);
+  hipLaunchKernelGGL(k_tile_order_keys, dim3(grid_stride_blocks(n_tiles)), dim3(256), 0, s, toff,
+                     n_tiles, keys, vals);
   return hipGetLastError();
 }
 

@@ -64,36 +64,53 @@ __device__ __forceinline__ Eval eval_splat(const float4& A, const float4& Bv, fl
   return e;
 }
 
-// Can the entry reach alpha >= 1/255 at any pixel centre of the tile?
-// alpha >= 1/255  <=>  sigma <= ln(255 o); sigma is a convex quadratic in
-// the pixel position, so its minimum over the rectangle of pixel centres
-// is 0 if the splat centre is inside, else the least of the four edge
-// minima (a 1-D quadratic clamped to the edge). Entries that fail are
-// skipped for the whole tile; the margin in sigma (1e-3 plus 1e-4
-// relative) is far above the rounding of either side of the comparison,
-// so no entry that any pixel would composite is ever skipped.
-__device__ __forceinline__ bool reaches_tile(const Staged& e, float x0, float x1, float y0,
-                                             float y1) {
+// Minimum of the entry's sigma over the rectangle [x0,x1] x [y0,y1] of
+// pixel centres: sigma is a convex quadratic in the pixel position, so the
+// minimum is 0 if the splat centre is inside, else the least of the four
+// edge minima (a 1-D quadratic clamped to the edge).
+__device__ __forceinline__ float rect_min_sigma(const Staged& e, float x0, float x1, float y0,
+                                                float y1) {
   const float u = e.a.x, v = e.a.y, ha = e.a.z, hc = e.a.w, b = e.b.x;
-  const float cut = (e.b.y + 7.99435343f) * 0.69314718f;  // ln(255 o)
-  if (u >= x0 && u <= x1 && v >= y0 && v <= y1) return true;
+  if (u >= x0 && u <= x1 && v >= y0 && v <= y1) return 0.f;
   // sigma(dx, dy) = ha dx^2 + hc dy^2 + b dx dy with dx = u - px, dy = v - py
   auto q = [&](float dx, float dy) { return fmaf(ha * dx, dx, fmaf(hc * dy, dy, b * dx * dy)); };
   const float ia = 0.5f / ha, ic = 0.5f / hc;
-  float m = 3.4e38f;
-  {  // vertical edges px = x0, x1: best dy = -b dx / (2 hc), clamped
-    const float dxa = u - x0, dxb = u - x1;
-    const float dya = fminf(fmaxf(-b * dxa * ic, v - y1), v - y0);
-    const float dyb = fminf(fmaxf(-b * dxb * ic, v - y1), v - y0);
-    m = fminf(m, fminf(q(dxa, dya), q(dxb, dyb)));
+  const float dxa = u - x0, dxb = u - x1;
+  const float dya_v = fminf(fmaxf(-b * dxa * ic, v - y1), v - y0);
+  const float dyb_v = fminf(fmaxf(-b * dxb * ic, v - y1), v - y0);
+  const float dya = v - y0, dyb = v - y1;
+  const float dxa_h = fminf(fmaxf(-b * dya * ia, u - x1), u - x0);
+  const float dxb_h = fminf(fmaxf(-b * dyb * ia, u - x1), u - x0);
+  return fminf(fminf(q(dxa, dya_v), q(dxb, dyb_v)), fminf(q(dxa_h, dya), q(dxb_h, dyb)));
+}
+
+// Largest sigma at which the entry still reaches alpha >= 1/255:
+// alpha >= 1/255  <=>  sigma <= ln(255 o). The margin (1e-3 plus 1e-4
+// relative) is far above the rounding on either side of the comparison,
+// so a test against it never skips anything a pixel would composite.
+__device__ __forceinline__ float reach_limit(const Staged& e) {
+  const float cut = (e.b.y + 7.99435343f) * 0.69314718f;  // ln(255 o)
+  return cut + 1e-3f + 1e-4f * fabsf(cut);
+}
+
+// Can the entry reach alpha >= 1/255 anywhere in the tile?
+__device__ __forceinline__ bool reaches_tile(const Staged& e, float x0, float x1, float y0,
+                                             float ylast) {
+  return rect_min_sigma(e, x0, x1, y0, fminf(y0 + 15.f, ylast)) <= reach_limit(e);
+}
+
+// Which 4-row strips of the tile can the entry reach (bit k = rows
+// 4k..4k+3)? Entries and strips that fail are skipped.
+__device__ __forceinline__ uint32_t reach_mask(const Staged& e, float x0, float x1, float y0,
+                                               float ylast) {
+  const float lim = reach_limit(e);
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float s0 = y0 + 4.f * k;
+    if (s0 <= ylast && rect_min_sigma(e, x0, x1, s0, fminf(s0 + 3.f, ylast)) <= lim) m |= 1u << k;
   }
-  {  // horizontal edges py = y0, y1
-    const float dya = v - y0, dyb = v - y1;
-    const float dxa = fminf(fmaxf(-b * dya * ia, u - x1), u - x0);
-    const float dxb = fminf(fmaxf(-b * dyb * ia, u - x1), u - x0);
-    m = fminf(m, fminf(q(dxa, dya), q(dxb, dyb)));
-  }
-  return m <= cut + 1e-3f + 1e-4f * fabsf(cut);
+  return m;
 }
 
 // Order-preserving compaction of a batch staged by all NT lanes: lanes with
@@ -124,17 +141,19 @@ __device__ __forceinline__ int compact_slot(bool keep, int* s_wcnt, int* pos) {
 template <int PPT>
 __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
     const float* __restrict__ screen, const uint32_t* __restrict__ ids,
-    const int64_t* __restrict__ toff, int W, int H, int tiles_x, int T,
-    float* __restrict__ out_rgb, float* __restrict__ out_T, int32_t* __restrict__ last_ids) {
+    const int64_t* __restrict__ toff, const uint32_t* __restrict__ order, int W, int H,
+    int tiles_x, int T, float* __restrict__ out_rgb, float* __restrict__ out_T,
+    int32_t* __restrict__ last_ids) {
   constexpr int NT = kTilePix / PPT;
   constexpr int B = NT;
   __shared__ float4 s_a[B];
   __shared__ float4 s_b[B];
   __shared__ float s_c[B];
   __shared__ int s_lid[B];
+  __shared__ uint32_t s_reach[B];
   __shared__ int s_wcnt[NT / kWave];
   const int tid = threadIdx.x;
-  const int64_t t = blockIdx.x;
+  const int64_t t = order ? int64_t(order[blockIdx.x]) : int64_t(blockIdx.x);
   const int c = int(t / T);
   const int tl = int(t - int64_t(c) * T);
   const int ty = tl / tiles_x, tx = tl - ty * tiles_x;
@@ -158,33 +177,38 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
   }
 
   const float tx0 = float(tx * kTile) + 0.5f, ty0 = float(ty * kTile) + 0.5f;
-  const float tx1 = fminf(tx0 + 15.f, float(W) - 0.5f), ty1 = fminf(ty0 + 15.f, float(H) - 0.5f);
+  const float tx1 = fminf(tx0 + 15.f, float(W) - 0.5f), ylast = float(H) - 0.5f;
+  const int wave = tid >> 6;
   for (int64_t b0 = start; b0 < end; b0 += B) {
     bool any_live = false;
 #pragma unroll
     for (int k = 0; k < PPT; ++k) any_live |= live[k];
     if (__syncthreads_count(any_live) == 0) break;
     Staged e;
-    bool keep = false;
+    uint32_t reach = 0;
     if (b0 + tid < end) {
       e = stage_row(screen, ids[b0 + tid]);
-      keep = reaches_tile(e, tx0, tx1, ty0, ty1);
+      reach = reach_mask(e, tx0, tx1, ty0, ylast);
     }
     int pos;
-    const int nb = compact_slot<NT>(keep, s_wcnt, &pos);
-    if (keep) {
+    const int nb = compact_slot<NT>(reach != 0, s_wcnt, &pos);
+    if (reach) {
       s_a[pos] = e.a;
       s_b[pos] = e.b;
       s_c[pos] = e.c.x;
       s_lid[pos] = int(b0 - start) + tid;
+      s_reach[pos] = reach;
     }
     __syncthreads();
     for (int j = 0; j < nb; ++j) {
+      const uint32_t rm = s_reach[j];
       const float4 A = s_a[j], Bv = s_b[j];
       const float cblue = s_c[j];
       const int lid = s_lid[j];
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
+        // pixel k of this wave lies in strip wave + k * (waves per tile)
+        if (!((rm >> (wave + k * (NT / kWave))) & 1u)) continue;
         const Eval e = eval_splat(A, Bv, px[k], py[k]);
         const float Tn = Tr[k] * (1.f - e.alpha);
         const bool use = live[k] && e.alpha >= kAlphaMin;
@@ -281,8 +305,8 @@ __device__ __forceinline__ void wave_reduce9_atomic(const float (&v)[9], float* 
 template <int PPT>
 __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
     const float* __restrict__ screen, const uint32_t* __restrict__ ids,
-    const int64_t* __restrict__ toff, int W, int H, int tiles_x, int T,
-    const float* __restrict__ out_T, const int32_t* __restrict__ last_ids,
+    const int64_t* __restrict__ toff, const uint32_t* __restrict__ order, int W, int H,
+    int tiles_x, int T, const float* __restrict__ out_T, const int32_t* __restrict__ last_ids,
     const float* __restrict__ v_rgb, const float* __restrict__ v_T, float* __restrict__ v_screen) {
   constexpr int NT = kTilePix / PPT;
   constexpr int B = NT;
@@ -294,7 +318,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
   __shared__ int s_wcnt[NT / kWave];
   __shared__ int s_max;
   const int tid = threadIdx.x;
-  const int64_t t = blockIdx.x;
+  const int64_t t = order ? int64_t(order[blockIdx.x]) : int64_t(blockIdx.x);
   const int c = int(t / T);
   const int tl = int(t - int64_t(c) * T);
   const int ty = tl / tiles_x, tx = tl - ty * tiles_x;
@@ -338,7 +362,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
   const int64_t stop_at = start + n_used;
 
   const float tx0 = float(tx * kTile) + 0.5f, ty0 = float(ty * kTile) + 0.5f;
-  const float tx1 = fminf(tx0 + 15.f, float(W) - 0.5f), ty1 = fminf(ty0 + 15.f, float(H) - 0.5f);
+  const float tx1 = fminf(tx0 + 15.f, float(W) - 0.5f), ylast = float(H) - 0.5f;
   for (int64_t b_end = stop_at; b_end > start; b_end -= B) {
     const int64_t b_start = (b_end - start) > B ? b_end - B : start;
     const int n_in = int(b_end - b_start);
@@ -349,7 +373,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
     if (tid < n_in) {
       sid = ids[b_start + tid];
       e = stage_row(screen, sid);
-      keep = reaches_tile(e, tx0, tx1, ty0, ty1);
+      keep = reaches_tile(e, tx0, tx1, ty0, ylast);
     }
     int pos;
     const int nb = compact_slot<NT>(keep, s_wcnt, &pos);
@@ -424,8 +448,8 @@ constexpr int kFwdPPT = 1;
 constexpr int kBwdPPT = 4;
 
 hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uint32_t* ids,
-                             const int64_t* toff, float* out_rgb, float* out_T, int32_t* last_ids,
-                             hipStream_t s) {
+                             const int64_t* toff, const uint32_t* order, float* out_rgb,
+                             float* out_T, int32_t* last_ids, hipStream_t s) {
   static const int ppt = ppt_from_env("GS_RASTER_PPT_FWD", kFwdPPT);
   const int tiles_x = (W + kTile - 1) / kTile, tiles_y = (H + kTile - 1) / kTile;
   const int T = tiles_x * tiles_y;
@@ -434,8 +458,8 @@ hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uin
   if (!fits_dispatch(uint64_t(blocks), kTilePix)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)};
 #define GS_FWD(P)                                                                            \
-  hipLaunchKernelGGL(k_raster_fwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, W, H, \
-                     tiles_x, T, out_rgb, out_T, last_ids)
+  hipLaunchKernelGGL(k_raster_fwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, order, \
+                     W, H, tiles_x, T, out_rgb, out_T, last_ids)
   ProfScope prof("k_raster_fwd", s);
   if (ppt == 4) GS_FWD(4); else if (ppt == 2) GS_FWD(2); else GS_FWD(1);
 #undef GS_FWD
@@ -443,9 +467,9 @@ hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uin
 }
 
 hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uint32_t* ids,
-                             const int64_t* toff, const float* out_T, const int32_t* last_ids,
-                             const float* v_rgb, const float* v_T, float* v_screen,
-                             hipStream_t s) {
+                             const int64_t* toff, const uint32_t* order, const float* out_T,
+                             const int32_t* last_ids, const float* v_rgb, const float* v_T,
+                             float* v_screen, hipStream_t s) {
   static const int ppt = ppt_from_env("GS_RASTER_PPT_BWD", kBwdPPT);
   const int tiles_x = (W + kTile - 1) / kTile, tiles_y = (H + kTile - 1) / kTile;
   const int T = tiles_x * tiles_y;
@@ -454,8 +478,8 @@ hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uin
   if (!fits_dispatch(uint64_t(blocks), kTilePix)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)};
 #define GS_BWD(P)                                                                             \
-  hipLaunchKernelGGL(k_raster_bwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, W, H,  \
-                     tiles_x, T, out_T, last_ids, v_rgb, v_T, v_screen)
+  hipLaunchKernelGGL(k_raster_bwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, order, \
+                     W, H, tiles_x, T, out_T, last_ids, v_rgb, v_T, v_screen)
   ProfScope prof("k_raster_bwd", s);
   if (ppt == 4) GS_BWD(4); else if (ppt == 2) GS_BWD(2); else GS_BWD(1);
 #undef GS_BWD

@@ -144,6 +144,9 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
  * capacity isect_capacity); tile_offsets[C*T+1] int64 (entries of global
  * tile t are flatten_ids[tile_offsets[t] .. tile_offsets[t+1]));
  * sorted_keys[n_isects] (nullable: the sorted 64-bit keys);
+ * tile_order[C*T] (nullable: every global tile id once, ordered by
+ * decreasing entry count, ties by tile id -- a launch order for the
+ * raster calls so that the longest tiles start first);
  * (host) *n_isects_out; (host) *workspace_needed_out.
  * Errors: GS_E_INVALID as for gs_project or nnz < 0;
  * GS_E_OVERFLOW if nnz >= 2^31; GS_E_CAPACITY if n_isects >
@@ -156,8 +159,8 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz,
                  const int64_t* cam_offsets, void* workspace,
                  uint64_t workspace_bytes, uint32_t* flatten_ids,
                  int64_t isect_capacity, int64_t* tile_offsets,
-                 uint64_t* sorted_keys, int64_t* n_isects_out,
-                 uint64_t* workspace_needed_out);
+                 uint64_t* sorted_keys, uint32_t* tile_order,
+                 int64_t* n_isects_out, uint64_t* workspace_needed_out);
 
 /* ---------------------------------------------------------------------
  * gs_rasterize_fwd -- per-tile front-to-back alpha compositing.
@@ -165,10 +168,12 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz,
  *
  * For every pixel (centre (j+0.5, i+0.5)) of camera c, over the entries of
  * its tile in sorted order: d = (u - px, v - py),
- * sigma = (a dx^2 + c dy^2)/2 + b dx dy, alpha = min(0.99, o exp(-sigma));
- * entries with sigma < 0 or alpha < 1/255 are skipped; if
- * T*(1-alpha) < 1e-4 the walk stops before that entry; otherwise
- * rgb += colour*alpha*T and T *= 1-alpha.
+ * sigma = (a dx^2 + c dy^2)/2 + b dx dy (>= 0: the conic is positive
+ * definite), alpha = min(0.99, o exp(-sigma)); entries with
+ * alpha < 1/255 are skipped; if T*(1-alpha) < 1e-4 the walk stops before
+ * that entry; otherwise rgb += colour*alpha*T and T *= 1-alpha.
+ * tile_order (nullable) is the order in which tiles are launched (from
+ * gs_intersect; null = tile id order); it changes no result.
  * Outputs (all C x H x W, row-major): out_rgb[C][H][W][3] (premultiplied,
  * no background), out_T[C][H][W] final transmittance, last_ids[C][H][W]
  * local index (within the tile's list) of the last composited entry, -1 if
@@ -176,8 +181,8 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz,
  * ------------------------------------------------------------------- */
 int gs_rasterize_fwd(void* stream, int32_t C, int32_t W, int32_t H,
                      const float* screen, const uint32_t* flatten_ids,
-                     const int64_t* tile_offsets, float* out_rgb,
-                     float* out_T, int32_t* last_ids);
+                     const int64_t* tile_offsets, const uint32_t* tile_order,
+                     float* out_rgb, float* out_T, int32_t* last_ids);
 
 /* ---------------------------------------------------------------------
  * gs_rasterize_bwd -- gradient of L = <v_rgb, out_rgb> + <v_T, out_T>
@@ -190,14 +195,16 @@ int gs_rasterize_fwd(void* stream, int32_t C, int32_t W, int32_t H,
  * transmittance before entry i as T_{i+1} / (1 - alpha_i). Writes
  * v_screen[nnz][10] fp32 (zeroed by this call first; the depth column is
  * 0). v_T may be null (taken as zero). Entries whose alpha hit the 0.99
- * clamp get no opacity or position/conic gradient. Summation order is not
- * fixed (float atomics), so results vary in the last bits run to run.
+ * clamp get no opacity or position/conic gradient. tile_order as for
+ * gs_rasterize_fwd. Summation order is not fixed (float atomics), so
+ * results vary in the last bits run to run.
  * ------------------------------------------------------------------- */
 int gs_rasterize_bwd(void* stream, int32_t C, int32_t W, int32_t H,
                      int64_t nnz, const float* screen,
                      const uint32_t* flatten_ids, const int64_t* tile_offsets,
-                     const float* out_T, const int32_t* last_ids,
-                     const float* v_rgb, const float* v_T, float* v_screen);
+                     const uint32_t* tile_order, const float* out_T,
+                     const int32_t* last_ids, const float* v_rgb,
+                     const float* v_T, float* v_screen);
 
 /* ---------------------------------------------------------------------
  * gs_project_bwd -- screen-row gradients to parameter gradients.

@@ -182,6 +182,19 @@ def check_sort_order(toff, ids, screen_dev, chunk=1 << 27):
         del pos, tile, slot, key
 
 
+def check_launch_order(order, toff):
+    """The heavy-first launch order, by its defining properties (which fix
+    it uniquely): a permutation of the tile ids along which the saturated
+    entry count never increases and equal counts keep increasing ids."""
+    n = toff.numel() - 1
+    o = order.to(torch.int64) & 0xFFFFFFFF
+    assert o.numel() == n
+    assert torch.equal(torch.sort(o).values, torch.arange(n, device=o.device)), "not a permutation"
+    cnt = torch.diff(toff).clamp(max=0xFFFF)[o]
+    ok = (cnt[1:] < cnt[:-1]) | ((cnt[1:] == cnt[:-1]) & (o[1:] > o[:-1]))
+    assert bool(ok.all()), "launch order violated"
+
+
 def gpu_tile_counts_from_boxes(aabb_dev, cam_offsets, C, W, H):
     """Per-tile entry counts implied by the GPU's own 16-bit boxes: each
     slot adds one to every tile of its rectangle (2-D difference array)."""

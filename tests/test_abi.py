@@ -79,13 +79,13 @@ def test_invalid_arguments_need_no_gpu(lib):
     st = lib.gs_project(None, 10, 1, 10, 10, 4, *([None] * 7), None, None, None, None, None, 0,
                         None, 0, ctypes.byref(nnz), cam)
     assert st == gsd.GS_E_INVALID
-    assert lib.gs_rasterize_fwd(None, 0, 10, 10, None, None, None, None, None, None) == \
+    assert lib.gs_rasterize_fwd(None, 0, 10, 10, None, None, None, None, None, None, None) == \
         gsd.GS_E_INVALID
     n_is = ctypes.c_int64(0)
     need = ctypes.c_uint64(0)
     # nnz >= 2^31 overflows the 31-bit slot ids
     cam2 = (ctypes.c_int64 * 2)(0, 1 << 31)
-    st = lib.gs_intersect(None, 1, 16, 16, 1 << 31, 8, 8, cam2, None, 0, None, 0, 8, None,
+    st = lib.gs_intersect(None, 1, 16, 16, 1 << 31, 8, 8, cam2, None, 0, None, 0, 8, None, None,
                           ctypes.byref(n_is), ctypes.byref(need))
     assert st == gsd.GS_E_OVERFLOW
 

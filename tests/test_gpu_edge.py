@@ -55,6 +55,8 @@ def test_empty_scene(lib):
     torch.cuda.synchronize()
     assert out["proj"].nnz == 0 and out["isect"].n_isects == 0
     assert int(out["isect"].tile_offsets.abs().sum()) == 0
+    # every tile empty: the launch order is the identity
+    assert torch.equal(out["isect"].tile_order.long().cpu(), torch.arange(3 * 2))
     assert torch.all(out["T"] == 1) and torch.all(out["rgb"] == 0) and torch.all(out["last"] == -1)
     for g in out["grads"].values():
         assert g.numel() == 0

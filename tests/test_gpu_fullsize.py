@@ -62,6 +62,7 @@ def test_fullsize_scene(cid):
                                        spec.height)
     assert torch.equal(cnt, torch.diff(it.tile_offsets)), "per-tile counts differ from the boxes"
     log(f"[{spec.name}] sort order and per-tile counts hold over all {it.n_isects} entries")
+    F.check_launch_order(it.tile_order, it.tile_offsets)
 
     # projection: every pair
     o = F.OracleScene(sc)

@@ -109,19 +109,30 @@ def test_intersect_sort_bit_exact(lib, name):
     ids = torch.empty(max(isect.n_isects, 1), dtype=torch.int32, device="cuda")
     keys = torch.empty(max(isect.n_isects, 1), dtype=torch.int64, device="cuda")
     toff = torch.empty(n_tiles + 1, dtype=torch.int64, device="cuda")
+    order = torch.empty(n_tiles, dtype=torch.int32, device="cuda")
     st, n_is, need = gsd.gs_intersect(C, W, H, proj.nnz, screen, aabb, cam, ws, ws_bytes, ids,
-                                      ids.numel(), toff, keys)
+                                      ids.numel(), toff, keys, order)
     torch.cuda.synchronize()
     assert st == 0, gsd.status_str(st)
     assert n_is == isect.n_isects
     np.testing.assert_array_equal(toff.cpu().numpy(), isect.tile_offsets)
     np.testing.assert_array_equal(ids.cpu().numpy()[:n_is].view(np.uint32), isect.flatten_ids)
     np.testing.assert_array_equal(keys.cpu().numpy()[:n_is].view(np.uint64), isect.sorted_keys)
+    np.testing.assert_array_equal(order.cpu().numpy(), launch_order(isect.tile_offsets))
 
 
+def launch_order(tile_offsets):
+    """The raster launch order the library documents: tiles by decreasing
+    entry count (saturated at 65535), ties by increasing tile id."""
+    cnt = np.minimum(np.diff(tile_offsets), 0xFFFF)
+    return np.argsort(-cnt, kind="stable").astype(np.int32)
+
+
+@pytest.mark.parametrize("ordered", [False, True], ids=["id-order", "heavy-first"])
 @pytest.mark.parametrize("name", SCENES)
-def test_raster_fwd_stage(lib, name):
-    """Stage-isolated forward: oracle rows (fp32) and oracle tile lists in."""
+def test_raster_fwd_stage(lib, name, ordered):
+    """Stage-isolated forward: oracle rows (fp32) and oracle tile lists in,
+    tiles launched in id order or in the heavy-first order."""
     sc, _, ref = reference(name)
     proj, isect = ref["proj"], ref["isect"]
     C, W, H = sc["C"], sc["W"], sc["H"]
@@ -131,8 +142,9 @@ def test_raster_fwd_stage(lib, name):
     rgb = torch.empty(C, H, W, 3, device="cuda")
     T = torch.empty(C, H, W, device="cuda")
     last = torch.empty(C, H, W, dtype=torch.int32, device="cuda")
+    order = P.to_dev(launch_order(isect.tile_offsets)) if ordered else None
     st = gsd.gs_rasterize_fwd(C, W, H, P.to_dev(rows32), P.to_dev(P.u32_as_i32(isect.flatten_ids)),
-                              P.to_dev(isect.tile_offsets), rgb, T, last)
+                              P.to_dev(isect.tile_offsets), order, rgb, T, last)
     torch.cuda.synchronize()
     assert st == 0
     frag = P.fragile_pixels(rows32, isect.flatten_ids, isect.tile_offsets, C, W, H)
@@ -146,8 +158,9 @@ def test_raster_fwd_stage(lib, name):
     np.testing.assert_array_equal(lg[ok], last_o[ok])
 
 
+@pytest.mark.parametrize("ordered", [False, True], ids=["id-order", "heavy-first"])
 @pytest.mark.parametrize("name", SCENES)
-def test_raster_bwd_stage(lib, name):
+def test_raster_bwd_stage(lib, name, ordered):
     sc, _, ref = reference(name)
     proj, isect = ref["proj"], ref["isect"]
     C, W, H = sc["C"], sc["W"], sc["H"]
@@ -163,9 +176,10 @@ def test_raster_bwd_stage(lib, name):
     rgb = torch.empty(C, H, W, 3, device="cuda")
     T = torch.empty(C, H, W, device="cuda")
     last = torch.empty(C, H, W, dtype=torch.int32, device="cuda")
-    assert gsd.gs_rasterize_fwd(C, W, H, d_rows, d_ids, d_toff, rgb, T, last) == 0
+    order = P.to_dev(launch_order(isect.tile_offsets)) if ordered else None
+    assert gsd.gs_rasterize_fwd(C, W, H, d_rows, d_ids, d_toff, order, rgb, T, last) == 0
     v_screen = torch.empty(proj.nnz, 10, device="cuda")
-    st = gsd.gs_rasterize_bwd(C, W, H, proj.nnz, d_rows, d_ids, d_toff, T, last,
+    st = gsd.gs_rasterize_bwd(C, W, H, proj.nnz, d_rows, d_ids, d_toff, order, T, last,
                               P.to_dev(sc["v_rgb"]), P.to_dev(sc["v_T"]), v_screen)
     torch.cuda.synchronize()
     assert st == 0
