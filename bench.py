@@ -33,11 +33,11 @@ CSRC = os.path.join(ROOT, "gaussian_splatting_differentiable_project_amd", "csrc
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 KERNELS = ["k_project_mask", "k_scan", "k_cam_offsets", "k_project_compact", "k_fill_u32",
-           "k_isect_prep", "k_sort_hist", "k_digit_base", "k_onesweep", "k_isect_emit",
+           "k_isect_prep", "k_radix_count", "k_radix_scan", "k_radix_scatter", "k_isect_emit",
            "k_tile_ranges", "k_tile_order_keys", "k_raster_fwd", "k_raster_bwd", "k_project_bwd"]
 KERNEL_SOURCE = {"k_raster_fwd": "gs_raster.hip", "k_raster_bwd": "gs_raster.hip",
                  "k_project_mask": "gs_project.hip", "k_project_compact": "gs_project.hip",
-                 "k_project_bwd": "gs_project_bwd.hip", "k_onesweep": "gs_sort.hip",
+                 "k_project_bwd": "gs_project_bwd.hip", "k_radix_scatter": "gs_sort.hip",
                  "k_isect_emit": "gs_intersect.hip"}
 
 # Flops of one (pixel, entry) evaluation in the raster kernels: the alpha
@@ -82,8 +82,9 @@ def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes):
         return pairs / 8 + 4 * pairs / 128 + (44 + 12 * K) * V + 48 * nnz
     if kernel == "k_project_bwd":    # params + SH read and grads written per Gaussian
         return (44 + 12 * K) * (V + N) + 40 * nnz + pairs / 8 + 4 * pairs / 128
-    if kernel == "k_onesweep":       # one tile-id pass: 8 B read + 8 B written per entry
-        return 16 * n_isects
+    if kernel == "k_radix_scatter":  # mean over the step's passes: 8 B read + 8 B written per key
+        tiles = C * ((spec.width + 15) // 16) * ((spec.height + 15) // 16)
+        return 16 * (4 * nnz + tile_passes * n_isects + 2 * tiles) / (4 + tile_passes + 2)
     if kernel == "k_isect_emit":     # order, box, offset per pair; 8 B per entry
         return 16 * nnz + 8 * n_isects
     return None
@@ -301,8 +302,17 @@ def main():
     hb = {}
     for kn, ms in kernel_ms.items():
         byt = hbm_bytes(kn, spec, nnz, n_is, V, tile_passes)
-        if byt and kn != "k_onesweep":
+        if byt:
             hb[kn] = byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    # the whole sort (depth passes over the pairs, tile passes over the
+    # entries, launch-order passes over the tiles; each pass reads and
+    # writes a 4 B key and a 4 B value per element) against the time of all
+    # its kernels: counting, scan and scatter
+    sort_ms = sum(kernel_ms.get(k, 0.0) for k in ("k_radix_count", "k_radix_scan",
+                                                  "k_radix_scatter"))
+    sort_bytes = 16 * (4 * nnz + tile_passes * n_is + 2 * spec.n_cams * tx * ty)
+    if sort_ms > 0:
+        hb["sort (all radix kernels)"] = sort_bytes / (sort_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     out["hbm_frac_by_kernel"] = hb
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(sc, spec, a.cpu_sample_seconds)

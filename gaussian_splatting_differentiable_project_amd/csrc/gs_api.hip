@@ -3,9 +3,10 @@
 //
 // Error protocol ([VRAM] "The 4 GiB rule and the 2^31 limit"): totals
 // are computed exactly in 64 bits on the device and read back once per
-// call; the host checks them against the caller's capacities before any
-// kernel writes a buffer sized by them, and returns the required size
-// instead of writing past an allocation.
+// call; the host checks them against the caller's capacities before it
+// queues any kernel whose size depends on them, and returns the required
+// size instead of writing past an allocation. Kernels queued before the
+// check (the compaction) clamp their writes to the capacity themselves.
 #include <cstdlib>
 #include <cstring>
 
@@ -74,62 +75,94 @@ ProjectWs carve_project(void* base, int64_t n_groups, int32_t C) {
 }
 
 // ---- gs_intersect workspace ----
+// Layout: the words that must start at zero come first (one fill), then
+// every array the first phase needs (sized by nnz and the tile count),
+// then the entry arrays sized by n_isects.
 struct IsectWs {
-  uint64_t* total;
-  uint64_t* total2;
+  uint64_t* total;      // n_isects (prep)
+  uint64_t* total2;     // same total again (gather scan)
   int* err;
-  uint32_t* tickets;    // [32]: 0 scan, 1..4 depth passes, 8..15 tile passes
-  uint64_t* hist_depth; // [4][256]
-  uint64_t* hist_tile;  // [4][256]
-  uint64_t* hist_order; // [4][256]
+  uint32_t* ticket;     // gather scan
+  uint64_t* scan_lb;    // gather scan look-back
+  uint64_t zero_words;  // u32 words to clear, from the start
   int64_t* cam_off;     // [C+1]
   uint32_t *dkeys_a, *dkeys_b, *dvals_a, *dvals_b, *cnt;
   uint64_t* offs;
-  uint64_t* scan_lb;
-  uint64_t zero_words;  // u32 words to zero from `total` up to cam_off
-  uint64_t* sort_lb;    // [max blocks][256]
-  uint64_t sort_lb_words;
+  uint32_t *ord_keys_a, *ord_keys_b, *ord_vals_b;  // launch-order sort of the tiles
+  void* sort;           // radix sort scratch (fixed size)
   uint64_t phase1_bytes;  // enough to count (I still unknown)
   uint32_t *tkeys_a, *tkeys_b, *tvals;
-  uint32_t *ord_keys_a, *ord_keys_b, *ord_vals_b;  // launch-order sort of the tiles
   uint64_t bytes;
 };
 
 IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects, uint64_t n_tiles) {
   Carver cv{static_cast<char*>(base)};
   IsectWs w{};
+  const uint64_t n = uint64_t(nnz);
   w.total = cv.take<uint64_t>(1);
   w.total2 = cv.take<uint64_t>(1);
   w.err = cv.take<int>(1);
-  w.tickets = cv.take<uint32_t>(32);
-  w.hist_depth = cv.take<uint64_t>(4 * kRadix);
-  w.hist_tile = cv.take<uint64_t>(4 * kRadix);
-  w.hist_order = cv.take<uint64_t>(4 * kRadix);
+  w.ticket = cv.take<uint32_t>(1);
+  w.scan_lb = cv.take<uint64_t>((n + kScanTile - 1) / kScanTile + 1);
   w.zero_words = cv.off / 4;
   w.cam_off = cv.take<int64_t>(uint64_t(C) + 1);
-  const uint64_t n = uint64_t(nnz);
   w.dkeys_a = cv.take<uint32_t>(n);
   w.dkeys_b = cv.take<uint32_t>(n);
   w.dvals_a = cv.take<uint32_t>(n);
   w.dvals_b = cv.take<uint32_t>(n);
   w.cnt = cv.take<uint32_t>(n);
   w.offs = cv.take<uint64_t>(n);
-  w.scan_lb = cv.take<uint64_t>((n + kScanTile - 1) / kScanTile + 1);
   w.ord_keys_a = cv.take<uint32_t>(n_tiles);
   w.ord_keys_b = cv.take<uint32_t>(n_tiles);
   w.ord_vals_b = cv.take<uint32_t>(n_tiles);
-  uint64_t nb1 = sort_blocks(n);
-  if (sort_blocks(n_tiles) > nb1) nb1 = sort_blocks(n_tiles);
-  w.phase1_bytes = cv.off + align_up(nb1 * kRadix * sizeof(uint64_t));
+  w.sort = cv.take<char>(sort_scratch_bytes());
+  w.phase1_bytes = cv.off;
   const uint64_t I = n_isects > 0 ? uint64_t(n_isects) : 0;
-  const uint64_t nb = nb1 > sort_blocks(I) ? nb1 : sort_blocks(I);
-  w.sort_lb_words = nb * kRadix * 2;
-  w.sort_lb = cv.take<uint64_t>(nb * kRadix);
   w.tkeys_a = cv.take<uint32_t>(I);
   w.tkeys_b = cv.take<uint32_t>(I);
   w.tvals = cv.take<uint32_t>(I);
   w.bytes = cv.off;
   return w;
+}
+
+// Page-locked host words for the device-to-host readback of each call,
+// one set per thread and device (never freed: the process owns them).
+// A call records an event after the copy and waits on that event only,
+// so the kernels queued behind the copy keep the device busy while the
+// host checks the totals.
+struct HostStage {
+  int64_t* buf = nullptr;
+  uint64_t words = 0;
+  hipEvent_t ev = nullptr;
+};
+constexpr int kMaxDevices = 64;
+thread_local HostStage tl_stage[kMaxDevices];
+
+hipError_t host_stage(uint64_t words, HostStage** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  HostStage& h = tl_stage[dev];
+  if (!h.ev) {
+    e = hipEventCreateWithFlags(&h.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  if (h.words < words) {
+    if (h.buf) {
+      e = hipHostFree(h.buf);
+      if (e != hipSuccess) return e;
+      h.buf = nullptr;
+      h.words = 0;
+    }
+    void* p = nullptr;
+    e = hipHostMalloc(&p, words * sizeof(int64_t), hipHostMallocDefault);
+    if (e != hipSuccess) return e;
+    h.buf = static_cast<int64_t*>(p);
+    h.words = words;
+  }
+  *out = &h;
+  return hipSuccess;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_E_HIP; }
@@ -214,34 +247,29 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t
   a.qsx = float(kQ16) / float(W);
   a.qsy = float(kQ16) / float(H);
 
+  if (screen_capacity > 0 && (!screen || !aabb16)) return GS_E_INVALID;
+  a.cap = screen_capacity;
+
+  HostStage* hs = nullptr;
+  GS_TRY(host_stage(uint64_t(C) + 1, &hs));
   GS_TRY(launch_fill_u32(workspace, 0u, ws.bytes / 4, s));
   GS_TRY(launch_project_mask(a, mask, wg_count, s));
   GS_TRY(launch_scan_u32(wg_count, nullptr, uint64_t(n_groups), wg_scan, nullptr, ws.total,
                          ws.lookback, ws.ticket, ws.err, s));
   GS_TRY(launch_cam_offsets(wg_scan, Np / kMaskGroup, C, ws.total, ws.cam_off, s));
-  int64_t host_off[1 + 1024];
-  int64_t* off_h = host_off;
-  int64_t* heap = nullptr;
-  if (C + 1 > 1025) {
-    heap = static_cast<int64_t*>(std::malloc(sizeof(int64_t) * (C + 1)));
-    if (!heap) return GS_E_INVALID;
-    off_h = heap;
-  }
-  hipError_t e = hipMemcpyAsync(off_h, ws.cam_off, sizeof(int64_t) * (C + 1),
-                                hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) {
-    std::free(heap);
-    return GS_E_HIP;
-  }
-  const int64_t nnz = off_h[C];
+  GS_TRY(hipMemcpyAsync(hs->buf, ws.cam_off, sizeof(int64_t) * (C + 1), hipMemcpyDeviceToHost, s));
+  GS_TRY(hipEventRecord(hs->ev, s));
+  // The compaction needs no host decision: slots at or past the capacity
+  // are not written, so it is queued before the host reads the count.
+  const hipError_t e = launch_project_compact(a, mask, wg_scan, screen, aabb16, s);
+  // wait even after an error: the copy into the staging words must land
+  const hipError_t e2 = hipEventSynchronize(hs->ev);
+  if (e != hipSuccess || e2 != hipSuccess) return GS_E_HIP;
+  const int64_t nnz = hs->buf[C];
   *nnz_out = nnz;
-  if (cam_offsets_out) std::memcpy(cam_offsets_out, off_h, sizeof(int64_t) * (C + 1));
-  std::free(heap);
+  if (cam_offsets_out) std::memcpy(cam_offsets_out, hs->buf, sizeof(int64_t) * (C + 1));
   if (nnz >= (int64_t(1) << 31)) return GS_E_OVERFLOW;
   if (nnz > screen_capacity) return GS_E_CAPACITY;
-  if (nnz > 0 && (!screen || !aabb16)) return GS_E_INVALID;
-  GS_TRY(launch_project_compact(a, mask, wg_scan, screen, aabb16, s));
   return check_device_error(ws.err, s);
 }
 
@@ -267,6 +295,9 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   IsectWs ws = carve_isect(workspace, C, nnz, 0, n_tiles);
   *workspace_needed_out = ws.phase1_bytes;
   if (!workspace || workspace_bytes < ws.phase1_bytes) return GS_E_WORKSPACE;
+  const SortScratch sc = sort_scratch(ws.sort);
+  HostStage* hs = nullptr;
+  GS_TRY(host_stage(1, &hs));
 
   // Phase 1: depth keys, per-slot tile counts and their exact 64-bit total.
   GS_TRY(launch_fill_u32(workspace, 0u, ws.zero_words, s));
@@ -274,9 +305,22 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
                         hipMemcpyHostToDevice, s));
   GS_TRY(launch_isect_prep(uint64_t(nnz), screen, aabb16, W, H, ws.dkeys_a, ws.dvals_a, ws.cnt,
                            ws.total, s));
-  uint64_t I = 0;
-  GS_TRY(hipMemcpyAsync(&I, ws.total, sizeof(uint64_t), hipMemcpyDeviceToHost, s));
-  GS_TRY(hipStreamSynchronize(s));
+  GS_TRY(hipMemcpyAsync(hs->buf, ws.total, sizeof(uint64_t), hipMemcpyDeviceToHost, s));
+  GS_TRY(hipEventRecord(hs->ev, s));
+  // Phase 2 needs only nnz-sized memory, so it is queued before the host
+  // waits for the total: a stable sort of the slots by depth, then the
+  // entry offsets of the slots in depth order.
+  bool in_b = false;
+  hipError_t e = launch_sort_passes(ws.dkeys_a, ws.dvals_a, ws.dkeys_b, ws.dvals_b, uint64_t(nnz),
+                                    0, 32, sc, &in_b, s);
+  const uint32_t* order = in_b ? ws.dvals_b : ws.dvals_a;
+  if (e == hipSuccess)
+    e = launch_scan_u32(ws.cnt, order, uint64_t(nnz), nullptr, ws.offs, ws.total2, ws.scan_lb,
+                        ws.ticket, ws.err, s);
+  // wait even after an error: the copy into the staging words must land
+  const hipError_t e2 = hipEventSynchronize(hs->ev);
+  if (e != hipSuccess || e2 != hipSuccess) return GS_E_HIP;
+  const uint64_t I = uint64_t(hs->buf[0]);
   *n_isects_out = int64_t(I);
   if (I >= (uint64_t(1) << 62)) return GS_E_OVERFLOW;
   ws = carve_isect(workspace, C, nnz, int64_t(I), n_tiles);
@@ -287,49 +331,29 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
 
   if (I == 0) {
     GS_TRY(launch_fill_u32(tile_offsets, 0u, 2 * (n_tiles + 1), s));
-    if (tile_order) GS_TRY(launch_tile_order_keys(tile_offsets, n_tiles, ws.ord_keys_a, tile_order, s));
-    return GS_OK;
+  } else {
+    // Phase 3: emit (tile id, slot) in depth order.
+    const int tbits = bits_for(n_tiles);
+    const int passes = sort_passes(tbits);
+    // the final pass must land its values in flatten_ids
+    uint32_t* v_first = (passes & 1) ? ws.tvals : flatten_ids;
+    uint32_t* v_second = (passes & 1) ? flatten_ids : ws.tvals;
+    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.offs, ws.cam_off, C, W, H, I,
+                             ws.tkeys_a, v_first, s));
+    // Phase 4: stable sort of the entries by tile id.
+    GS_TRY(launch_sort_passes(ws.tkeys_a, v_first, ws.tkeys_b, v_second, I, 0, tbits, sc, &in_b,
+                              s));
+    const uint32_t* tkeys = in_b ? ws.tkeys_b : ws.tkeys_a;
+    // Phase 5: per-tile ranges (and the composed 64-bit keys on request).
+    GS_TRY(launch_tile_ranges(tkeys, I, n_tiles, tile_offsets, s));
+    if (sorted_keys) GS_TRY(launch_compose_keys(tkeys, flatten_ids, screen, I, sorted_keys, s));
   }
-
-  GS_TRY(launch_fill_u32(ws.sort_lb, 0u, ws.sort_lb_words, s));
-  GS_TRY(launch_fill_u32(ws.scan_lb, 0u, 2 * ((uint64_t(nnz) + kScanTile - 1) / kScanTile + 1), s));
-  // Phase 2: stable sort of the slots by depth.
-  SortScratch sd{ws.hist_depth, ws.sort_lb, ws.tickets + 1, ws.err};
-  GS_TRY(launch_sort_histogram(ws.dkeys_a, uint64_t(nnz), 0, 32, sd, s));
-  bool in_b = false;
-  GS_TRY(launch_sort_passes(ws.dkeys_a, ws.dvals_a, ws.dkeys_b, ws.dvals_b, uint64_t(nnz), 0, 32,
-                            sd, 1, &in_b, s));
-  const uint32_t* order = in_b ? ws.dvals_b : ws.dvals_a;
-
-  // Phase 3: entry offsets in depth order, then emit (tile id, slot).
-  GS_TRY(launch_scan_u32(ws.cnt, order, uint64_t(nnz), nullptr, ws.offs, ws.total2, ws.scan_lb,
-                         ws.tickets, ws.err, s));
-  const int tbits = bits_for(n_tiles);
-  const int passes = sort_passes(tbits);
-  // the final pass must land its values in flatten_ids
-  uint32_t* v_first = (passes & 1) ? ws.tvals : flatten_ids;
-  uint32_t* v_second = (passes & 1) ? flatten_ids : ws.tvals;
-  GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.offs, ws.cam_off, C, W, H, I,
-                           ws.tkeys_a, v_first, s));
-
-  // Phase 4: stable sort of the entries by tile id.
-  SortScratch st{ws.hist_tile, ws.sort_lb, ws.tickets + 8, ws.err};
-  GS_TRY(launch_sort_histogram(ws.tkeys_a, I, 0, tbits, st, s));
-  GS_TRY(launch_sort_passes(ws.tkeys_a, v_first, ws.tkeys_b, v_second, I, 0, tbits, st, 8, &in_b,
-                            s));
-  const uint32_t* tkeys = in_b ? ws.tkeys_b : ws.tkeys_a;
-
-  // Phase 5: per-tile ranges (and the composed 64-bit keys on request).
-  GS_TRY(launch_tile_ranges(tkeys, I, n_tiles, tile_offsets, s));
-  if (sorted_keys) GS_TRY(launch_compose_keys(tkeys, flatten_ids, screen, I, sorted_keys, s));
   // Phase 6: launch order for the raster calls, longest tiles first (a
-  // stable sort of 16-bit inverted counts: two even passes end in tile_order).
+  // stable sort of 16-bit inverted counts: two passes end in tile_order).
   if (tile_order) {
     GS_TRY(launch_tile_order_keys(tile_offsets, n_tiles, ws.ord_keys_a, tile_order, s));
-    SortScratch so{ws.hist_order, ws.sort_lb, ws.tickets + 16, ws.err};
-    GS_TRY(launch_sort_histogram(ws.ord_keys_a, n_tiles, 0, 16, so, s));
     GS_TRY(launch_sort_passes(ws.ord_keys_a, tile_order, ws.ord_keys_b, ws.ord_vals_b, n_tiles, 0,
-                              16, so, 16, &in_b, s));
+                              16, sc, &in_b, s));
   }
   return check_device_error(ws.err, s);
 }

@@ -31,8 +31,7 @@ constexpr uint32_t kQ16 = 65535u;          // 16-bit box grid steps
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kSortThreads = 256;
-constexpr int kSortItems = 16;
-constexpr int kSortTile = kSortThreads * kSortItems;  // 4096 keys per block
+constexpr int kSortChunks = 1024;  // count/scatter blocks per pass: 4 per CU, all resident
 
 // Scan geometry (decoupled look-back): 256 lanes x 16 values.
 constexpr int kScanThreads = 256;

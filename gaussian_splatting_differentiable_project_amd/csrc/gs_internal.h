@@ -37,6 +37,7 @@ struct ProjectArgs {
   const float *means, *quats, *log_scales, *opacity_logits, *sh, *viewmats, *Ks;
   ShNorm norm;
   float qsx, qsy;  // 65535 / W, 65535 / H in fp32
+  int64_t cap;     // compaction: slots at or past this are not written
 };
 
 ShNorm sh_norm_table();
@@ -61,24 +62,22 @@ hipError_t launch_scan_u32(const uint32_t* in, const uint32_t* idx, uint64_t n, 
 hipError_t launch_fill_u32(void* p, uint32_t v, uint64_t n_words, hipStream_t s);
 
 // Stable LSD radix sort, one 8-bit digit per pass, of uint32 keys with
-// uint32 values, over the bit range [bit0, bit0 + bits).
+// uint32 values, over the bit range [bit0, bit0 + bits). The scratch has
+// a fixed size (sort_scratch_bytes) whatever n is, needs no clearing, and
+// serves one sort at a time on a stream.
 struct SortScratch {
-  uint64_t* hist;      // [passes][256], zeroed; becomes the digit starts
-  uint64_t* lookback;  // [blocks][256], zeroed
-  uint32_t* tickets;   // [passes], zeroed
-  int* err;
+  uint64_t* total;  // [256] keys per digit
+  uint64_t* base;   // [kSortChunks][256] start of each chunk's run per digit (before the digit base)
+  uint32_t* cnt;    // [kSortChunks][256] per-chunk digit counts
 };
 int sort_passes(int bits);
-uint64_t sort_blocks(uint64_t n);
-// Histograms of every digit of `keys` (adds into sc.hist).
-hipError_t launch_sort_histogram(const uint32_t* keys, uint64_t n, int bit0, int bits,
-                                 const SortScratch& sc, hipStream_t s);
-// Runs all passes (look-back epoch tags tag0, tag0+1, ...); the result ends
-// in (keys_a, vals_a) when the pass count is even, else in (keys_b, vals_b),
-// which *in_b reports.
+uint64_t sort_scratch_bytes();
+SortScratch sort_scratch(void* base);
+// Runs all passes; the result ends in (keys_a, vals_a) when the pass count
+// is even, else in (keys_b, vals_b), which *in_b reports.
 hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys_b,
                               uint32_t* vals_b, uint64_t n, int bit0, int bits,
-                              const SortScratch& sc, uint32_t tag0, bool* in_b, hipStream_t s);
+                              const SortScratch& sc, bool* in_b, hipStream_t s);
 
 // Intersection stages (gs_intersect.hip).
 hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* aabb16, int W,

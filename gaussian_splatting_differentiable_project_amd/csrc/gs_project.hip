@@ -94,6 +94,7 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_compact(ProjectArgs a,
     if (!((mine >> lane) & 1ull)) continue;
     const int64_t slot = int64_t(wg_scan[p0 / kMaskGroup]) + (wave ? __popcll(w0) : 0) +
                          __popcll(mine & lt);
+    if (slot >= a.cap) continue;  // past the caller's capacity: counted, not written
     const Camera k = load_camera(a.viewmats, a.Ks, c);
     PairFwd<double> P;
     pair_fwd(k, G, Wf, Hf, P);

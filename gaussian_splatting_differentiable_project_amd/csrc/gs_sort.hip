@@ -5,17 +5,24 @@
 // and 64-bit addressing for buffers sized by n_isects. The sort orders the
 // (tile_id << 32) | depth keys of the [VRAM] cost table (isect.ids_a/b).
 //
-// Both use a single-pass decoupled look-back: a block takes a ticket (so
-// every block it waits on is already running), publishes its aggregate,
-// then sums predecessors' aggregates until it meets an inclusive prefix.
-// Each look-back word packs status, an epoch tag and a 56-bit value into
-// one 64-bit atomic, so stale words from an earlier pass are never read as
-// ready and one zero-fill per call serves every pass.
+// The scan is single-pass with a decoupled look-back: a block takes a
+// ticket (so every block it waits on is already running), publishes its
+// aggregate, then sums predecessors' aggregates until it meets an
+// inclusive prefix. Each look-back word packs status, an epoch tag and a
+// 56-bit value into one 64-bit atomic.
 //
-// The radix pass follows the one-sweep scheme: one 8-bit digit per pass,
-// 4096 keys per 256-lane block. Ranks inside a wave come from eight
-// ballots (lanes with equal digits), per-wave counters live in LDS, the
-// block reorders its keys in LDS and writes each digit run contiguously.
+// The radix passes do not use a look-back. With 256 digit counters per
+// block, a look-back walk moves 2 KB per predecessor through the
+// cross-die coherent path, and on this chip that traffic and its latency
+// cost about half of every pass. Each pass is reduce-then-scan instead:
+// the keys are split into at most 1024 contiguous chunks (one resident
+// block each), a counting kernel writes per-chunk digit counts, a tiny
+// kernel turns them into each chunk's start per digit, and the scatter
+// kernel walks its chunk tile by tile with running per-digit cursors.
+// Inside a tile, ranks come from eight ballots (lanes with equal digits),
+// per-wave counters live in LDS, and the tile is reordered in LDS so each
+// digit run is written contiguously. Stability: tiles are taken in order
+// within a chunk and chunks in order within a digit.
 #include "gs_internal.h"
 
 namespace gs {
@@ -25,24 +32,6 @@ namespace {
 __global__ void k_fill_u32(uint32_t* p, uint32_t v, uint64_t n) {
   const uint64_t stride = uint64_t(gridDim.x) * blockDim.x;
   for (uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
-}
-
-// Exclusive block scan of one uint32 per lane over 256 lanes.
-__device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t* s_tmp /*[4]*/,
-                                                        uint32_t* total) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t incl = wave_incl_scan_u32(v);
-  if (lane == 63) s_tmp[wave] = incl;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t t = s_tmp[w];
-    off += (w < wave) ? t : 0u;
-    tot += t;
-  }
-  *total = tot;
-  return off + incl - v;
 }
 
 template <bool GATHER, bool OUT64>
@@ -106,127 +95,187 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint32_t* __restric
   }
 }
 
-// Histograms of `passes` consecutive 8-bit digits starting at bit0.
-__global__ __launch_bounds__(256) void k_sort_hist(const uint32_t* __restrict__ keys, uint64_t n,
-                                                   int bit0, int passes, uint64_t* hist) {
-  __shared__ uint32_t s_h[4][kRadix];
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) s_h[p][tid] = 0;
-  __syncthreads();
-  const uint64_t stride = uint64_t(gridDim.x) * 256;
-  for (uint64_t e = uint64_t(blockIdx.x) * 256 + tid; e < n; e += stride) {
-    const uint32_t k = keys[e];
-    for (int p = 0; p < passes; ++p) atomicAdd(&s_h[p][(k >> (bit0 + kRadixBits * p)) & 255u], 1u);
-  }
-  __syncthreads();
-  for (int p = 0; p < passes; ++p)
-    if (s_h[p][tid]) atomicAdd(reinterpret_cast<unsigned long long*>(hist + p * kRadix + tid),
-                               (unsigned long long)s_h[p][tid]);
-}
-
-// In place: hist[p][d] -> exclusive prefix over d (start of digit d).
-__global__ __launch_bounds__(256) void k_digit_base(uint64_t* hist) {
-  __shared__ uint64_t s_w[4];
+__device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* s_w /*[4]*/,
+                                                        uint64_t* total) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  uint64_t* h = hist + blockIdx.x * kRadix;
-  const uint64_t v = h[tid];
   const uint64_t incl = wave_incl_scan_u64(v);
   if (lane == 63) s_w[wave] = incl;
   __syncthreads();
-  uint64_t off = 0;
-  for (int w = 0; w < wave; ++w) off += s_w[w];
-  h[tid] = off + incl - v;
+  uint64_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint64_t t = s_w[w];
+    off += (w < wave) ? t : 0ull;
+    tot += t;
+  }
+  *total = tot;
+  return off + incl - v;
 }
 
-__global__ __launch_bounds__(kSortThreads) void k_onesweep(
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s_w, uint32_t* total) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint32_t incl = wave_incl_scan_u32(v);
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t t = s_w[w];
+    off += (w < wave) ? t : 0u;
+    tot += t;
+  }
+  *total = tot;
+  return off + incl - v;
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(kSortThreads) void k_radix_count(const uint32_t* __restrict__ keys, uint64_t n,
+                                                    int shift, uint64_t ct,
+                                                    uint32_t* __restrict__ cnt) {
+  constexpr uint64_t TILE = uint64_t(kSortThreads) * ITEMS;
+  __shared__ uint32_t s_h[4][256];
+  const int tid = threadIdx.x, wave = tid >> 6;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) s_h[w][tid] = 0;
+  __syncthreads();
+  const uint64_t e0 = uint64_t(blockIdx.x) * ct * TILE;
+  uint64_t e1 = e0 + ct * TILE;
+  if (e1 > n) e1 = n;
+  for (uint64_t b = e0; b < e1; b += TILE) {
+    uint32_t k[ITEMS];
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const uint64_t e = b + uint64_t(i) * kSortThreads + tid;
+      k[i] = e < e1 ? keys[e] : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const uint64_t e = b + uint64_t(i) * kSortThreads + tid;
+      if (e < e1) atomicAdd(&s_h[wave][(k[i] >> shift) & 255u], 1u);
+    }
+  }
+  __syncthreads();
+  cnt[uint64_t(blockIdx.x) * 256 + tid] = s_h[0][tid] + s_h[1][tid] + s_h[2][tid] + s_h[3][tid];
+}
+
+// One block per digit: exclusive prefix over chunks, and the digit total.
+__global__ __launch_bounds__(kSortThreads) void k_radix_scan(const uint32_t* __restrict__ cnt, uint32_t P,
+                                                   uint64_t* __restrict__ base_rel,
+                                                   uint64_t* __restrict__ total) {
+  __shared__ uint64_t s_w[4];
+  const int tid = threadIdx.x, d = blockIdx.x;
+  const uint32_t per = (P + kSortThreads - 1) / kSortThreads;
+  const uint32_t r0 = tid * per, r1 = min(P, r0 + per);
+  uint64_t sum = 0;
+  for (uint32_t r = r0; r < r1; ++r) sum += cnt[uint64_t(r) * 256 + d];
+  uint64_t tot;
+  uint64_t run = block_excl_scan_u64(sum, s_w, &tot);
+  for (uint32_t r = r0; r < r1; ++r) {
+    base_rel[uint64_t(r) * 256 + d] = run;
+    run += cnt[uint64_t(r) * 256 + d];
+  }
+  if (tid == 0) total[d] = tot;
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint64_t n, int shift,
-    const uint64_t* __restrict__ digit_base, uint64_t* lb, uint32_t* ticket, uint32_t tag,
-    int* err) {
-  __shared__ uint32_t s_blk;
-  __shared__ uint32_t s_whist[4][kRadix];
-  __shared__ uint32_t s_lstart[kRadix];
-  __shared__ int64_t s_gstart[kRadix];
-  __shared__ uint32_t s_tmp[4];
-  __shared__ uint32_t s_keys[kSortTile];
-  __shared__ uint32_t s_vals[kSortTile];
+    uint64_t ct, const uint64_t* __restrict__ base_rel, const uint64_t* __restrict__ total) {
+  constexpr int TILE = kSortThreads * ITEMS;
+  __shared__ int64_t s_gstart[256];
+  __shared__ uint32_t s_whist[4][256];
+  __shared__ uint32_t s_lstart[256];
+  __shared__ uint64_t s_w64[4];
+  __shared__ uint32_t s_w32[4];
+  __shared__ uint32_t s_keys[TILE];
+  __shared__ uint32_t s_vals[TILE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) s_whist[w][tid] = 0;
-  if (tid == 0) s_blk = atomicAdd(ticket, 1u);
-  __syncthreads();
-  const uint64_t blk = s_blk;
-  const uint64_t base = blk * kSortTile;
+  uint64_t run;  // next output position of digit tid
+  {
+    uint64_t tot;
+    const uint64_t db = block_excl_scan_u64(total[tid], s_w64, &tot);
+    run = db + base_rel[uint64_t(blockIdx.x) * 256 + tid];
+  }
   const uint64_t lt = lanemask_lt();
-
-  uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+  const uint64_t e0 = uint64_t(blockIdx.x) * ct * TILE;
+  uint64_t e1 = e0 + ct * uint64_t(TILE);
+  if (e1 > n) e1 = n;
+  uint32_t key[ITEMS], val[ITEMS];
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
-    const uint64_t e = base + uint64_t(wave) * (kSortItems * kWave) + i * kWave + lane;
-    const bool valid = e < n;
-    key[i] = valid ? keys_in[e] : 0u;
-    val[i] = valid ? vals_in[e] : 0u;
-    const uint32_t d = (key[i] >> shift) & 255u;
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < kRadixBits; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t bb = __ballot(bit);
-      peers &= bit ? bb : ~bb;
-    }
-    const uint32_t before = s_whist[wave][d];
-    const uint32_t r = uint32_t(__popcll(peers & lt));
-    if (valid && r == 0) s_whist[wave][d] = before + uint32_t(__popcll(peers));
-    rank[i] = before + r;
+  for (int i = 0; i < ITEMS; ++i) {
+    const uint64_t e = e0 + uint64_t(wave) * (ITEMS * kWave) + i * kWave + lane;
+    key[i] = e < e1 ? keys_in[e] : 0u;
+    val[i] = e < e1 ? vals_in[e] : 0u;
   }
-  __syncthreads();
-
-  // lane tid owns digit tid: wave offsets, block total, look-back, starts
-  const uint32_t c0 = s_whist[0][tid], c1 = s_whist[1][tid], c2 = s_whist[2][tid],
-                 c3 = s_whist[3][tid];
-  const uint32_t cnt = c0 + c1 + c2 + c3;
-  s_whist[0][tid] = 0;
-  s_whist[1][tid] = c0;
-  s_whist[2][tid] = c0 + c1;
-  s_whist[3][tid] = c0 + c1 + c2;
-  uint64_t prefix = 0;
-  uint64_t* my_lb = lb + blk * kRadix + tid;
-  if (blk == 0) {
-    lb_store(my_lb, lb_word(kLbPrefix, tag, cnt));
-  } else {
-    lb_store(my_lb, lb_word(kLbAgg, tag, cnt));
-    prefix = lookback_prefix(lb + tid, int64_t(blk), kRadix, tag, err);
-    lb_store(my_lb, lb_word(kLbPrefix, tag, prefix + cnt));
-  }
-  uint32_t tot;
-  const uint32_t lstart = block_excl_scan_256(cnt, s_tmp, &tot);
-  s_lstart[tid] = lstart;
-  s_gstart[tid] = int64_t(digit_base[tid] + prefix) - int64_t(lstart);
-  __syncthreads();
-
+  for (uint64_t base = e0; base < e1; base += TILE) {
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
-    const uint64_t e = base + uint64_t(wave) * (kSortItems * kWave) + i * kWave + lane;
-    if (e < n) {
+    for (int w = 0; w < 4; ++w) s_whist[w][tid] = 0;
+    __syncthreads();
+    uint32_t rank[ITEMS];
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const uint64_t e = base + uint64_t(wave) * (ITEMS * kWave) + i * kWave + lane;
+      const bool valid = e < e1;
       const uint32_t d = (key[i] >> shift) & 255u;
-      const uint32_t pos = s_lstart[d] + s_whist[wave][d] + rank[i];
-      s_keys[pos] = key[i];
-      s_vals[pos] = val[i];
-    }
-  }
-  __syncthreads();
-  const uint64_t cnt_blk = (n - base) < uint64_t(kSortTile) ? (n - base) : uint64_t(kSortTile);
+      uint64_t peers = __ballot(valid);
 #pragma unroll
-  for (int j = 0; j < kSortItems; ++j) {
-    const uint32_t li = uint32_t(j * kSortThreads + tid);
-    if (li < cnt_blk) {
-      const uint32_t k = s_keys[li];
-      const uint32_t d = (k >> shift) & 255u;
-      const uint64_t g = uint64_t(s_gstart[d] + int64_t(li));
-      keys_out[g] = k;
-      vals_out[g] = s_vals[li];
+      for (int b = 0; b < kRadixBits; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bb = __ballot(bit);
+        peers &= bit ? bb : ~bb;
+      }
+      const uint32_t before = s_whist[wave][d];
+      const uint32_t r = uint32_t(__popcll(peers & lt));
+      if (valid && r == 0) s_whist[wave][d] = before + uint32_t(__popcll(peers));
+      rank[i] = before + r;
     }
+    __syncthreads();
+    const uint32_t c0 = s_whist[0][tid], c1 = s_whist[1][tid], c2 = s_whist[2][tid],
+                   c3 = s_whist[3][tid];
+    const uint32_t cnt = c0 + c1 + c2 + c3;
+    s_whist[0][tid] = 0;
+    s_whist[1][tid] = c0;
+    s_whist[2][tid] = c0 + c1;
+    s_whist[3][tid] = c0 + c1 + c2;
+    uint32_t tot;
+    const uint32_t lstart = block_excl_scan_u32(cnt, s_w32, &tot);
+    s_lstart[tid] = lstart;
+    s_gstart[tid] = int64_t(run) - int64_t(lstart);
+    run += cnt;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const uint64_t e = base + uint64_t(wave) * (ITEMS * kWave) + i * kWave + lane;
+      if (e < e1) {
+        const uint32_t d = (key[i] >> shift) & 255u;
+        const uint32_t pos = s_lstart[d] + s_whist[wave][d] + rank[i];
+        s_keys[pos] = key[i];
+        s_vals[pos] = val[i];
+      }
+    }
+    __syncthreads();
+    // the next tile's loads overlap this tile's scatter
+    const uint64_t nb = base + TILE;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const uint64_t e = nb + uint64_t(wave) * (ITEMS * kWave) + i * kWave + lane;
+      key[i] = e < e1 ? keys_in[e] : 0u;
+      val[i] = e < e1 ? vals_in[e] : 0u;
+    }
+    const uint64_t cnt_blk = (e1 - base) < uint64_t(TILE) ? (e1 - base) : uint64_t(TILE);
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const uint32_t li = uint32_t(j * kSortThreads + tid);
+      if (li < cnt_blk) {
+        const uint32_t k = s_keys[li];
+        const uint32_t d = (k >> shift) & 255u;
+        const uint64_t g = uint64_t(s_gstart[d] + int64_t(li));
+        keys_out[g] = k;
+        vals_out[g] = s_vals[li];
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -266,44 +315,85 @@ hipError_t launch_scan_u32(const uint32_t* in, const uint32_t* idx, uint64_t n, 
 
 int sort_passes(int bits) { return bits <= 0 ? 1 : (bits + kRadixBits - 1) / kRadixBits; }
 
-uint64_t sort_blocks(uint64_t n) { return (n + kSortTile - 1) / kSortTile; }
+namespace {
 
-hipError_t launch_sort_histogram(const uint32_t* keys, uint64_t n, int bit0, int bits,
-                                 const SortScratch& sc, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  uint64_t blocks = (n + 256 * 16 - 1) / (256 * 16);
-  if (blocks > 512) blocks = 512;  // few blocks: fewer global atomics per bin
-  ProfScope prof("k_sort_hist", s);
-  hipLaunchKernelGGL(k_sort_hist, dim3(uint32_t(blocks)), dim3(256), 0, s, keys, n, bit0,
-                     sort_passes(bits), sc.hist);
-  return hipGetLastError();
+struct SortPlan {
+  int items;       // keys per lane per tile
+  uint64_t ct;     // tiles per chunk
+  uint32_t P;      // chunks (= blocks of the count and scatter kernels)
+};
+
+// Small inputs take small tiles so that enough blocks run; large inputs
+// take 4096-key tiles and at most kSortChunks chunks (all resident).
+SortPlan sort_plan(uint64_t n) {
+  SortPlan p{};
+  p.items = n < (uint64_t(1) << 21) ? 4 : n < (uint64_t(1) << 25) ? 8 : 16;
+  const uint64_t tile = uint64_t(kSortThreads) * p.items;
+  const uint64_t tiles = (n + tile - 1) / tile;
+  p.ct = (tiles + kSortChunks - 1) / kSortChunks;
+  p.P = uint32_t((tiles + p.ct - 1) / p.ct);
+  return p;
+}
+
+template <int ITEMS>
+void launch_pass(const SortPlan& pl, const uint32_t* ki, const uint32_t* vi, uint32_t* ko,
+                 uint32_t* vo, uint64_t n, int shift, const SortScratch& sc, hipStream_t s) {
+  {
+    ProfScope prof("k_radix_count", s);
+    hipLaunchKernelGGL(k_radix_count<ITEMS>, dim3(pl.P), dim3(kSortThreads), 0, s, ki, n, shift,
+                       pl.ct, sc.cnt);
+  }
+  {
+    ProfScope prof("k_radix_scan", s);
+    hipLaunchKernelGGL(k_radix_scan, dim3(kRadix), dim3(kSortThreads), 0, s, sc.cnt, pl.P,
+                       sc.base, sc.total);
+  }
+  {
+    ProfScope prof("k_radix_scatter", s);
+    hipLaunchKernelGGL(k_radix_scatter<ITEMS>, dim3(pl.P), dim3(kSortThreads), 0, s, ki, vi, ko,
+                       vo, n, shift, pl.ct, sc.base, sc.total);
+  }
+}
+
+}  // namespace
+
+uint64_t sort_scratch_bytes() {
+  return uint64_t(kSortChunks) * kRadix * (sizeof(uint32_t) + sizeof(uint64_t)) +
+         kRadix * sizeof(uint64_t);
+}
+
+SortScratch sort_scratch(void* base) {
+  SortScratch sc;
+  sc.total = static_cast<uint64_t*>(base);
+  sc.base = sc.total + kRadix;
+  sc.cnt = reinterpret_cast<uint32_t*>(sc.base + uint64_t(kSortChunks) * kRadix);
+  return sc;
 }
 
 hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys_b,
                               uint32_t* vals_b, uint64_t n, int bit0, int bits,
-                              const SortScratch& sc, uint32_t tag0, bool* in_b,
-                              hipStream_t s) {
+                              const SortScratch& sc, bool* in_b, hipStream_t s) {
   const int passes = sort_passes(bits);
   *in_b = (passes & 1) != 0;
   if (n == 0) return hipSuccess;
-  {
-    ProfScope prof("k_digit_base", s);
-    hipLaunchKernelGGL(k_digit_base, dim3(passes), dim3(256), 0, s, sc.hist);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const uint64_t blocks = sort_blocks(n);
-  if (!fits_dispatch(blocks, kSortThreads)) return hipErrorInvalidConfiguration;
+  const SortPlan pl = sort_plan(n);
   uint32_t *ki = keys_a, *vi = vals_a, *ko = keys_b, *vo = vals_b;
   for (int p = 0; p < passes; ++p) {
-    ProfScope prof("k_onesweep", s);
-    hipLaunchKernelGGL(k_onesweep, dim3(uint32_t(blocks)), dim3(kSortThreads), 0, s, ki, vi, ko,
-                       vo, n, bit0 + kRadixBits * p, sc.hist + p * kRadix, sc.lookback,
-                       sc.tickets + p, tag0 + uint32_t(p), sc.err);
-    e = hipGetLastError();
+    const int shift = bit0 + kRadixBits * p;
+    if (pl.items == 4)
+      launch_pass<4>(pl, ki, vi, ko, vo, n, shift, sc, s);
+    else if (pl.items == 8)
+      launch_pass<8>(pl, ki, vi, ko, vo, n, shift, sc, s);
+    else
+      launch_pass<16>(pl, ki, vi, ko, vo, n, shift, sc, s);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    uint32_t* t = ki; ki = ko; ko = t;
-    t = vi; vi = vo; vo = t;
+    uint32_t* t = ki;
+    ki = ko;
+    ko = t;
+    t = vi;
+    vi = vo;
+    vo = t;
   }
   return hipSuccess;
 }

@@ -15,12 +15,17 @@
  * Conventions shared by every entry point
  *  - Every pointer is a DEVICE pointer unless its comment says (host).
  *  - Every buffer is owned by the caller; the library allocates no device
- *    memory and keeps no state between calls ([GSPLAT] 2.3: memory
+ *    memory and keeps no device state between calls ([GSPLAT] 2.3: memory
  *    lifetimes belong to the caller).
  *  - `stream` is a hipStream_t passed as void*; all work is enqueued on it.
- *    gs_project and gs_intersect each block the host once on `stream` to
- *    read one 64-bit total (the host-side check of [VRAM] "The 4 GiB rule
- *    and the 2^31 limit"); the other calls return without waiting.
+ *    gs_project and gs_intersect each block the host once, on an event
+ *    recorded after the copy of a 64-bit total, for the host-side check of
+ *    [VRAM] "The 4 GiB rule and the 2^31 limit"; work that does not depend
+ *    on that total is queued before the wait, and work sized by it after.
+ *    The other calls return without waiting. The stream must belong to
+ *    the current device. Each calling thread keeps a few page-locked
+ *    host words and one event per device for these reads (held until the
+ *    process ends).
  *  - Inputs are fp32, structure-of-arrays:
  *      means[N][3], quats[N][4] as (w,x,y,z) (need not be unit length),
  *      log_scales[N][3], opacity_logits[N], sh[N][K][3] with
@@ -33,7 +38,8 @@
  *  - A screen row ([VRAM] per-element cost table, proj.screen, 40 bytes) is
  *    10 floats: u, v, conic_a, conic_b, conic_c, opacity, depth z, r, g, b.
  *  - Returns GS_OK (0) or a negative status; no call aborts or prints.
- *    On an error nothing is written past any stated capacity.
+ *    On an error nothing is written past any stated capacity; what lies
+ *    within a capacity is then unspecified.
  */
 #ifndef GS_H
 #define GS_H
@@ -109,9 +115,11 @@ uint64_t gs_intersect_workspace_bytes(int32_t C, int32_t W, int32_t H,
  * workspace: device scratch of gs_project_workspace_bytes(N, C) bytes.
  * Errors: GS_E_INVALID for N < 0, C < 1, W or H outside [1, 65535],
  * sh_degree outside [0, 3], or a null required pointer.
- * GS_E_CAPACITY when nnz > screen_capacity: *nnz_out and mask, wg_count,
- * wg_scan are valid, screen/aabb16 are untouched. GS_E_OVERFLOW when
- * nnz >= 2^31 (slots are 31-bit).
+ * GS_E_CAPACITY when nnz > screen_capacity: *nnz_out, cam_offsets_out and
+ * mask, wg_count, wg_scan are valid; rows at slots below the capacity may
+ * have been written, nothing at or past it (the compaction runs before
+ * the host sees nnz and skips slots >= screen_capacity). GS_E_OVERFLOW
+ * when nnz >= 2^31 (slots are 31-bit).
  * ------------------------------------------------------------------- */
 int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
                int32_t sh_degree, const float* means, const float* quats,
@@ -150,9 +158,10 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
  * (host) *n_isects_out; (host) *workspace_needed_out.
  * Errors: GS_E_INVALID as for gs_project or nnz < 0;
  * GS_E_OVERFLOW if nnz >= 2^31; GS_E_CAPACITY if n_isects >
- * isect_capacity; GS_E_WORKSPACE if workspace_bytes is short (the bytes
- * needed are returned; before the count is known this is the lower bound
- * for counting, after it the full amount). Call again after growing.
+ * isect_capacity (flatten_ids, tile_offsets, sorted_keys and tile_order
+ * are then not written); GS_E_WORKSPACE if workspace_bytes is short (the
+ * bytes needed are returned; before the count is known this is the lower
+ * bound for counting, after it the full amount). Call again after growing.
  * ------------------------------------------------------------------- */
 int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz,
                  const float* screen, const uint32_t* aabb16,

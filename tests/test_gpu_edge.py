@@ -92,13 +92,18 @@ def test_capacity_and_workspace_protocol(lib):
     canary = 0x7FC0DEAD
     screen = torch.full((64 * 10 + 16,), 0, dtype=torch.int32, device="cuda").fill_(canary)
     aabb = torch.full((64 * 2 + 16,), canary, dtype=torch.int32, device="cuda")
-    # too small: the required count comes back, the outputs stay untouched
+    # too small: the required count comes back, nothing is written past the capacity
     st, nnz, cam = gsd.gs_project(N, C, W, H, s.sh_degree, s.means, s.quats, s.log_scales,
                                   s.opacity_logits, s.sh, s.viewmats, s.Ks, mask, wgc, wgs,
                                   screen, aabb, 64, ws, wsb)
     torch.cuda.synchronize()
-    assert st == gsd.GS_E_CAPACITY and nnz > 64
-    assert torch.all(screen == canary) and torch.all(aabb == canary)
+    assert st == gsd.GS_E_CAPACITY and nnz > 64 and cam[-1] == nnz
+    assert torch.all(screen[64 * 10:] == canary) and torch.all(aabb[64 * 2:] == canary)
+    # capacity 0 with no buffers at all is a valid way to ask for the count
+    st0, nnz0, _ = gsd.gs_project(N, C, W, H, s.sh_degree, s.means, s.quats, s.log_scales,
+                                  s.opacity_logits, s.sh, s.viewmats, s.Ks, mask, wgc, wgs,
+                                  None, None, 0, ws, wsb)
+    assert st0 == gsd.GS_E_CAPACITY and nnz0 == nnz
     # short workspace
     st2, _, _ = gsd.gs_project(N, C, W, H, s.sh_degree, s.means, s.quats, s.log_scales,
                                s.opacity_logits, s.sh, s.viewmats, s.Ks, mask, wgc, wgs,
