@@ -33,7 +33,7 @@ CSRC = os.path.join(ROOT, "gaussian_splatting_differentiable_project_amd", "csrc
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 KERNELS = ["k_project_mask", "k_scan", "k_cam_offsets", "k_project_compact", "k_fill_u32",
-           "k_isect_prep", "k_radix_count", "k_radix_scan", "k_radix_scatter", "k_isect_emit",
+           "k_isect_prep", "k_radix_count", "k_radix_scatter", "k_isect_emit",
            "k_tile_ranges", "k_tile_order_keys", "k_raster_fwd", "k_raster_bwd", "k_project_bwd"]
 KERNEL_SOURCE = {"k_raster_fwd": "gs_raster.hip", "k_raster_bwd": "gs_raster.hip",
                  "k_project_mask": "gs_project.hip", "k_project_compact": "gs_project.hip",
@@ -303,13 +303,14 @@ def main():
     for kn, ms in kernel_ms.items():
         byt = hbm_bytes(kn, spec, nnz, n_is, V, tile_passes)
         if byt:
+            if kn == "k_radix_scatter":   # per-launch mean; ms is the step's sum
+                byt *= 4 + tile_passes + 2
             hb[kn] = byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     # the whole sort (depth passes over the pairs, tile passes over the
     # entries, launch-order passes over the tiles; each pass reads and
     # writes a 4 B key and a 4 B value per element) against the time of all
-    # its kernels: counting, scan and scatter
-    sort_ms = sum(kernel_ms.get(k, 0.0) for k in ("k_radix_count", "k_radix_scan",
-                                                  "k_radix_scatter"))
+    # its kernels: counting and scatter
+    sort_ms = sum(kernel_ms.get(k, 0.0) for k in ("k_radix_count", "k_radix_scatter"))
     sort_bytes = 16 * (4 * nnz + tile_passes * n_is + 2 * spec.n_cams * tx * ty)
     if sort_ms > 0:
         hb["sort (all radix kernels)"] = sort_bytes / (sort_ms * 1e-3) / 1e9 / HBM_PEAK_GBS

@@ -80,16 +80,15 @@ ProjectWs carve_project(void* base, int64_t n_groups, int32_t C) {
 // then the entry arrays sized by n_isects.
 struct IsectWs {
   uint64_t* total;      // n_isects (prep)
-  uint64_t* total2;     // same total again (gather scan)
   int* err;
-  uint32_t* ticket;     // gather scan
-  uint64_t* scan_lb;    // gather scan look-back
+  uint32_t* ticket;     // emit blocks
+  uint64_t* scan_lb;    // emit look-back
+  uint64_t* sort_grp;   // radix sort group totals
   uint64_t zero_words;  // u32 words to clear, from the start
   int64_t* cam_off;     // [C+1]
-  uint32_t *dkeys_a, *dkeys_b, *dvals_a, *dvals_b, *cnt;
-  uint64_t* offs;
+  uint32_t *dkeys_a, *dkeys_b, *dvals_a, *dvals_b;
   uint32_t *ord_keys_a, *ord_keys_b, *ord_vals_b;  // launch-order sort of the tiles
-  void* sort;           // radix sort scratch (fixed size)
+  uint32_t* sort_cnt;   // radix sort chunk counts (fixed size)
   uint64_t phase1_bytes;  // enough to count (I still unknown)
   uint32_t *tkeys_a, *tkeys_b, *tvals;
   uint64_t bytes;
@@ -100,22 +99,20 @@ IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects, uint64
   IsectWs w{};
   const uint64_t n = uint64_t(nnz);
   w.total = cv.take<uint64_t>(1);
-  w.total2 = cv.take<uint64_t>(1);
   w.err = cv.take<int>(1);
   w.ticket = cv.take<uint32_t>(1);
-  w.scan_lb = cv.take<uint64_t>((n + kScanTile - 1) / kScanTile + 1);
+  w.scan_lb = cv.take<uint64_t>(isect_emit_lookback_words(n));
+  w.sort_grp = cv.take<uint64_t>(sort_groups_bytes() / sizeof(uint64_t));
   w.zero_words = cv.off / 4;
   w.cam_off = cv.take<int64_t>(uint64_t(C) + 1);
   w.dkeys_a = cv.take<uint32_t>(n);
   w.dkeys_b = cv.take<uint32_t>(n);
   w.dvals_a = cv.take<uint32_t>(n);
   w.dvals_b = cv.take<uint32_t>(n);
-  w.cnt = cv.take<uint32_t>(n);
-  w.offs = cv.take<uint64_t>(n);
   w.ord_keys_a = cv.take<uint32_t>(n_tiles);
   w.ord_keys_b = cv.take<uint32_t>(n_tiles);
   w.ord_vals_b = cv.take<uint32_t>(n_tiles);
-  w.sort = cv.take<char>(sort_scratch_bytes());
+  w.sort_cnt = cv.take<uint32_t>(sort_counts_bytes() / sizeof(uint32_t));
   w.phase1_bytes = cv.off;
   const uint64_t I = n_isects > 0 ? uint64_t(n_isects) : 0;
   w.tkeys_a = cv.take<uint32_t>(I);
@@ -295,7 +292,9 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   IsectWs ws = carve_isect(workspace, C, nnz, 0, n_tiles);
   *workspace_needed_out = ws.phase1_bytes;
   if (!workspace || workspace_bytes < ws.phase1_bytes) return GS_E_WORKSPACE;
-  const SortScratch sc = sort_scratch(ws.sort);
+  SortScratch sc;
+  sc.cnt = ws.sort_cnt;
+  sc.grp = ws.sort_grp;
   HostStage* hs = nullptr;
   GS_TRY(host_stage(1, &hs));
 
@@ -303,20 +302,16 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   GS_TRY(launch_fill_u32(workspace, 0u, ws.zero_words, s));
   GS_TRY(hipMemcpyAsync(ws.cam_off, cam_offsets, sizeof(int64_t) * (C + 1),
                         hipMemcpyHostToDevice, s));
-  GS_TRY(launch_isect_prep(uint64_t(nnz), screen, aabb16, W, H, ws.dkeys_a, ws.dvals_a, ws.cnt,
-                           ws.total, s));
+  GS_TRY(launch_isect_prep(uint64_t(nnz), screen, aabb16, W, H, ws.dkeys_a, ws.dvals_a, ws.total,
+                           s));
   GS_TRY(hipMemcpyAsync(hs->buf, ws.total, sizeof(uint64_t), hipMemcpyDeviceToHost, s));
   GS_TRY(hipEventRecord(hs->ev, s));
   // Phase 2 needs only nnz-sized memory, so it is queued before the host
-  // waits for the total: a stable sort of the slots by depth, then the
-  // entry offsets of the slots in depth order.
+  // waits for the total: a stable sort of the slots by depth.
   bool in_b = false;
-  hipError_t e = launch_sort_passes(ws.dkeys_a, ws.dvals_a, ws.dkeys_b, ws.dvals_b, uint64_t(nnz),
-                                    0, 32, sc, &in_b, s);
+  const hipError_t e = launch_sort_passes(ws.dkeys_a, ws.dvals_a, ws.dkeys_b, ws.dvals_b,
+                                          uint64_t(nnz), 0, 32, sc, &in_b, s);
   const uint32_t* order = in_b ? ws.dvals_b : ws.dvals_a;
-  if (e == hipSuccess)
-    e = launch_scan_u32(ws.cnt, order, uint64_t(nnz), nullptr, ws.offs, ws.total2, ws.scan_lb,
-                        ws.ticket, ws.err, s);
   // wait even after an error: the copy into the staging words must land
   const hipError_t e2 = hipEventSynchronize(hs->ev);
   if (e != hipSuccess || e2 != hipSuccess) return GS_E_HIP;
@@ -332,14 +327,14 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   if (I == 0) {
     GS_TRY(launch_fill_u32(tile_offsets, 0u, 2 * (n_tiles + 1), s));
   } else {
-    // Phase 3: emit (tile id, slot) in depth order.
+    // Phase 3: offsets and (tile id, slot) entries in depth order.
     const int tbits = bits_for(n_tiles);
     const int passes = sort_passes(tbits);
     // the final pass must land its values in flatten_ids
     uint32_t* v_first = (passes & 1) ? ws.tvals : flatten_ids;
     uint32_t* v_second = (passes & 1) ? flatten_ids : ws.tvals;
-    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.offs, ws.cam_off, C, W, H, I,
-                             ws.tkeys_a, v_first, s));
+    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.cam_off, C, W, H, I, ws.tkeys_a,
+                             v_first, ws.scan_lb, ws.ticket, ws.err, s));
     // Phase 4: stable sort of the entries by tile id.
     GS_TRY(launch_sort_passes(ws.tkeys_a, v_first, ws.tkeys_b, v_second, I, 0, tbits, sc, &in_b,
                               s));

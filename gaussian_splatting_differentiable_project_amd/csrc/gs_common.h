@@ -32,6 +32,8 @@ constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kSortThreads = 256;
 constexpr int kSortChunks = 1024;  // count/scatter blocks per pass: 4 per CU, all resident
+constexpr int kSortGroup = 32;                        // chunks per group total
+constexpr int kSortGroups = kSortChunks / kSortGroup;
 
 // Scan geometry (decoupled look-back): 256 lanes x 16 values.
 constexpr int kScanThreads = 256;
@@ -133,6 +135,54 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
     if (l >= o) v += t;
   }
   return v;
+}
+
+// Exclusive prefix of everything before block `blk` for a single-counter
+// decoupled look-back chain (lb[block]), computed by one whole wave: each
+// step loads the 64 nearest unresolved predecessors at once, so a walk
+// over d predecessors costs about d/64 round trips instead of d. Every
+// lane of the wave must call it; all get the result. Spins are bounded
+// (on timeout *err is set and 0 is returned).
+__device__ __forceinline__ uint64_t lookback_prefix_wave(const uint64_t* lb, int64_t blk,
+                                                         uint32_t tag, int* err) {
+  const int lane = __lane_id();
+  uint64_t acc = 0;
+  int64_t p = blk - 1;  // nearest predecessor not yet summed
+  uint32_t spins = 0;
+  while (p >= 0) {
+    const int64_t q = p - lane;
+    const uint64_t w = q >= 0 ? lb_load(lb + q) : (kLbPrefix | (uint64_t(tag & 63u) << 56));
+    const bool ready = lb_tag(w) == tag && lb_status(w) != 0;
+    const bool pref = ready && lb_status(w) == kLbPrefix;
+    const uint64_t not_ready = __ballot(!ready);
+    const uint64_t prefixes = __ballot(pref);
+    // lanes up to and including the nearest inclusive prefix
+    const int first_pref = prefixes ? __builtin_ctzll(prefixes) : 64;
+    const uint64_t upto = first_pref >= 63 ? ~0ull : ((2ull << first_pref) - 1);
+    if (not_ready & upto) {
+      // sum the ready run before the first gap, then wait on the gap
+      const int gap = __builtin_ctzll(not_ready);
+      const uint64_t take = gap == 0 ? 0ull : (~0ull >> (64 - gap));
+      uint64_t v = ((take >> lane) & 1ull) ? (w & kLbValueMask) : 0ull;
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+      acc += v;
+      p -= gap;
+      if (gap == 0) {
+        if (++spins > kSpinLimit) {
+          if (lane == 0) atomicOr(err, 1);
+          return 0;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      continue;
+    }
+    uint64_t v = ((upto >> lane) & 1ull) ? (w & kLbValueMask) : 0ull;
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    acc += v;
+    if (prefixes) break;
+    p -= 64;
+  }
+  return acc;
 }
 
 }  // namespace gs

@@ -63,29 +63,35 @@ hipError_t launch_fill_u32(void* p, uint32_t v, uint64_t n_words, hipStream_t s)
 
 // Stable LSD radix sort, one 8-bit digit per pass, of uint32 keys with
 // uint32 values, over the bit range [bit0, bit0 + bits). The scratch has
-// a fixed size (sort_scratch_bytes) whatever n is, needs no clearing, and
-// serves one sort at a time on a stream.
+// fixed sizes whatever n is. The group totals must be zero before the
+// first pass of the first sort that uses a scratch; each pass clears the
+// buffer the next one fills, so consecutive sorts on one stream can share
+// it (parity tracks which buffer is live).
 struct SortScratch {
-  uint64_t* total;  // [256] keys per digit
-  uint64_t* base;   // [kSortChunks][256] start of each chunk's run per digit (before the digit base)
-  uint32_t* cnt;    // [kSortChunks][256] per-chunk digit counts
+  uint32_t* cnt;   // [kSortChunks][256] per-chunk digit counts (sort_counts_bytes)
+  uint64_t* grp;   // [2][kSortGroups][256] group totals (sort_groups_bytes), zeroed
+  int parity = 0;
 };
 int sort_passes(int bits);
-uint64_t sort_scratch_bytes();
-SortScratch sort_scratch(void* base);
+uint64_t sort_counts_bytes();
+uint64_t sort_groups_bytes();
 // Runs all passes; the result ends in (keys_a, vals_a) when the pass count
 // is even, else in (keys_b, vals_b), which *in_b reports.
 hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys_b,
                               uint32_t* vals_b, uint64_t n, int bit0, int bits,
-                              const SortScratch& sc, bool* in_b, hipStream_t s);
+                              SortScratch& sc, bool* in_b, hipStream_t s);
 
 // Intersection stages (gs_intersect.hip).
 hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* aabb16, int W,
-                             int H, uint32_t* dkeys, uint32_t* dvals, uint32_t* cnt,
-                             uint64_t* total, hipStream_t s);
+                             int H, uint32_t* dkeys, uint32_t* dvals, uint64_t* total,
+                             hipStream_t s);
+// Offsets (single-pass scan with look-back) and entries of the slots in
+// depth order. lb[isect_emit_lookback_words(nnz)] and *ticket must be zero.
 hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
-                             const uint64_t* offs, const int64_t* cam_off, int C, int W, int H,
-                             uint64_t cap, uint32_t* tkeys, uint32_t* tvals, hipStream_t s);
+                             const int64_t* cam_off, int C, int W, int H, uint64_t cap,
+                             uint32_t* tkeys, uint32_t* tvals, uint64_t* lb, uint32_t* ticket,
+                             int* err, hipStream_t s);
+uint64_t isect_emit_lookback_words(uint64_t nnz);
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
                               hipStream_t s);
 hipError_t launch_tile_order_keys(const int64_t* toff, uint64_t n_tiles, uint32_t* keys,

@@ -44,13 +44,12 @@ __device__ __forceinline__ uint32_t rect_count(const TileRect& r) {
   return wx * wy;
 }
 
-// Per slot: depth key bits and identity value for the depth sort, tile
-// count, and the exact 64-bit total (one atomic per work-group).
+// Per slot: depth key bits and identity value for the depth sort, and
+// the exact 64-bit total of tile counts (one atomic per work-group).
 __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* __restrict__ screen,
                                                    const uint2* __restrict__ aabb16, uint32_t W,
                                                    uint32_t H, uint32_t* __restrict__ dkeys,
-                                                   uint32_t* __restrict__ dvals,
-                                                   uint32_t* __restrict__ cnt, uint64_t* total) {
+                                                   uint32_t* __restrict__ dvals, uint64_t* total) {
   __shared__ uint64_t s_w[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   uint64_t n = 0;
@@ -59,9 +58,7 @@ __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* _
   for (uint64_t i = uint64_t(blockIdx.x) * 256 + tid; i < nnz; i += stride) {
     dkeys[i] = __float_as_uint(screen[i * kRow + 6]);
     dvals[i] = uint32_t(i);
-    const uint32_t k = rect_count(rect_of(aabb16[i], W, H));
-    cnt[i] = k;
-    n += k;
+    n += rect_count(rect_of(aabb16[i], W, H));
   }
   const uint64_t incl = wave_incl_scan_u64(n);
   if (lane == 63) s_w[wave] = incl;
@@ -72,34 +69,114 @@ __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* _
   }
 }
 
-// Intersections of the slots in depth order: position i of the depth sort
-// holds slot order[i], whose entries start at offs[i]. Writes are clamped
-// to `cap` entries.
+// Intersections of the slots in depth order, with their offsets found on
+// the way. Block b takes positions [b*512, (b+1)*512) of the depth order
+// (position i holds slot order[i]); it counts their tiles, scans the
+// counts, gets the number of entries of all earlier positions from a
+// single-word decoupled look-back, and then writes its entries with
+// consecutive lanes on consecutive entries: lane e finds its slot by a
+// binary search over the block's offsets in LDS. Writes are clamped to
+// `cap` entries. The look-back words and the ticket must start at zero.
+constexpr int kEmitItems = 2;
+constexpr int kEmitSlots = 256 * kEmitItems;
+
 __global__ __launch_bounds__(256) void k_isect_emit(
     uint64_t nnz, const uint32_t* __restrict__ order, const uint2* __restrict__ aabb16,
-    const uint64_t* __restrict__ offs, const int64_t* __restrict__ cam_off, int C, uint32_t W,
-    uint32_t H, uint32_t tiles_x, uint32_t T, uint64_t cap, uint32_t* __restrict__ tkeys,
-    uint32_t* __restrict__ tvals) {
-  const uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= nnz) return;
-  const uint32_t s = order[i];
-  // camera of slot s: cameras own consecutive slot ranges
-  int lo = 0, hi = C - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (int64_t(s) >= cam_off[mid]) lo = mid; else hi = mid - 1;
-  }
-  const uint32_t tbase = uint32_t(lo) * T;
-  const TileRect r = rect_of(aabb16[s], W, H);
-  uint64_t o = offs[i];
-  for (uint32_t ty = r.ty0; ty < r.ty1; ++ty)
-    for (uint32_t tx = r.tx0; tx < r.tx1; ++tx) {
-      if (o < cap) {
-        tkeys[o] = tbase + ty * tiles_x + tx;
-        tvals[o] = s;
+    const int64_t* __restrict__ cam_off, int C, uint32_t W, uint32_t H, uint32_t tiles_x,
+    uint32_t T, uint64_t cap, uint32_t* __restrict__ tkeys, uint32_t* __restrict__ tvals,
+    uint64_t* lb, uint32_t* ticket, int* err) {
+  __shared__ uint32_t s_blk;
+  __shared__ uint64_t s_w[4];
+  __shared__ uint64_t s_prefix;
+  __shared__ uint64_t s_off[kEmitSlots + 1];  // block-local exclusive entry offsets
+  __shared__ uint32_t s_slot[kEmitSlots];
+  __shared__ uint32_t s_base[kEmitSlots];     // camera tile base + first tile of the rect
+  __shared__ uint32_t s_wx[kEmitSlots];       // rect width in tiles
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid == 0) s_blk = atomicAdd(ticket, 1u);
+  __syncthreads();
+  const uint64_t blk = s_blk;
+  const uint64_t base = blk * kEmitSlots;
+  // slot data, read with consecutive lanes on consecutive positions
+#pragma unroll
+  for (int j = 0; j < kEmitItems; ++j) {
+    const int li = j * 256 + tid;
+    const uint64_t i = base + li;
+    uint32_t k = 0, slot = 0, b0 = 0, wx = 0;
+    if (i < nnz) {
+      slot = order[i];
+      // camera of the slot: cameras own consecutive slot ranges
+      int lo = 0, hi = C - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (int64_t(slot) >= cam_off[mid]) lo = mid; else hi = mid - 1;
       }
-      ++o;
+      const TileRect r = rect_of(aabb16[slot], W, H);
+      k = rect_count(r);
+      wx = r.tx1 > r.tx0 ? r.tx1 - r.tx0 : 1u;
+      b0 = uint32_t(lo) * T + r.ty0 * tiles_x + r.tx0;
     }
+    s_slot[li] = slot;
+    s_base[li] = b0;
+    s_wx[li] = wx;
+    s_off[li] = k;  // counts for now
+  }
+  __syncthreads();
+  // exclusive scan of the 1024 counts: four consecutive ones per lane
+  uint64_t c[kEmitItems], sum = 0;
+#pragma unroll
+  for (int j = 0; j < kEmitItems; ++j) {
+    c[j] = s_off[tid * kEmitItems + j];
+    sum += c[j];
+  }
+  const uint64_t incl = wave_incl_scan_u64(sum);
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  uint64_t woff = 0, btot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    woff += (w < wave) ? s_w[w] : 0ull;
+    btot += s_w[w];
+  }
+  uint64_t run = woff + incl - sum;
+#pragma unroll
+  for (int j = 0; j < kEmitItems; ++j) {
+    s_off[tid * kEmitItems + j] = run;
+    run += c[j];
+  }
+  if (wave == 0) {
+    uint64_t prefix = 0;
+    if (blk == 0) {
+      if (lane == 0) lb_store(lb, lb_word(kLbPrefix, 1, btot));
+    } else {
+      if (lane == 0) lb_store(lb + blk, lb_word(kLbAgg, 1, btot));
+      prefix = lookback_prefix_wave(lb, int64_t(blk), 1, err);
+      if (lane == 0) lb_store(lb + blk, lb_word(kLbPrefix, 1, prefix + btot));
+    }
+    if (lane == 0) {
+      s_off[kEmitSlots] = btot;
+      s_prefix = prefix;
+    }
+  }
+  __syncthreads();
+  const uint64_t prefix = s_prefix;
+  for (uint64_t e = tid; e < btot; e += 256) {
+    // last position whose offset is <= e (a position with no entries has
+    // the same offset as the next one, so the search lands on the owner)
+    int lo = 0, hi = kEmitSlots - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    const uint64_t o = prefix + e;
+    if (o < cap) {
+      const uint32_t k = uint32_t(e - s_off[lo]);
+      const uint32_t wx = s_wx[lo];
+      const uint32_t dy = k / wx, dx = k - dy * wx;
+      tkeys[o] = s_base[lo] + dy * tiles_x + dx;
+      tvals[o] = s_slot[lo];
+    }
+  }
 }
 
 // tile_offsets[t] = first sorted position whose tile id is >= t.
@@ -155,31 +232,35 @@ inline uint32_t grid_stride_blocks(uint64_t n) {
 }  // namespace
 
 hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* aabb16, int W,
-                             int H, uint32_t* dkeys, uint32_t* dvals, uint32_t* cnt,
-                             uint64_t* total, hipStream_t s) {
+                             int H, uint32_t* dkeys, uint32_t* dvals, uint64_t* total,
+                             hipStream_t s) {
   if (nnz == 0) return hipSuccess;
   uint32_t blocks = grid_for(nnz);
   if (blocks > 1024) blocks = 1024;
   ProfScope prof("k_isect_prep", s);
   hipLaunchKernelGGL(k_isect_prep, dim3(blocks), dim3(256), 0, s, nnz, screen,
                      reinterpret_cast<const uint2*>(aabb16), uint32_t(W), uint32_t(H), dkeys,
-                     dvals, cnt, total);
+                     dvals, total);
   return hipGetLastError();
 }
 
 hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
-                             const uint64_t* offs, const int64_t* cam_off, int C, int W, int H,
-                             uint64_t cap, uint32_t* tkeys, uint32_t* tvals, hipStream_t s) {
+                             const int64_t* cam_off, int C, int W, int H, uint64_t cap,
+                             uint32_t* tkeys, uint32_t* tvals, uint64_t* lb, uint32_t* ticket,
+                             int* err, hipStream_t s) {
   if (nnz == 0) return hipSuccess;
-  if (!fits_dispatch(grid_for(nnz), 256)) return hipErrorInvalidConfiguration;
+  const uint64_t blocks = (nnz + kEmitSlots - 1) / kEmitSlots;
+  if (!fits_dispatch(blocks, 256)) return hipErrorInvalidConfiguration;
   const uint32_t tiles_x = uint32_t((W + kTile - 1) / kTile);
   const uint32_t T = tiles_x * uint32_t((H + kTile - 1) / kTile);
   ProfScope prof("k_isect_emit", s);
-  hipLaunchKernelGGL(k_isect_emit, dim3(grid_for(nnz)), dim3(256), 0, s, nnz, order,
-                     reinterpret_cast<const uint2*>(aabb16), offs, cam_off, C, uint32_t(W),
-                     uint32_t(H), tiles_x, T, cap, tkeys, tvals);
+  hipLaunchKernelGGL(k_isect_emit, dim3(uint32_t(blocks)), dim3(256), 0, s, nnz, order,
+                     reinterpret_cast<const uint2*>(aabb16), cam_off, C, uint32_t(W),
+                     uint32_t(H), tiles_x, T, cap, tkeys, tvals, lb, ticket, err);
   return hipGetLastError();
 }
+
+uint64_t isect_emit_lookback_words(uint64_t nnz) { return (nnz + kEmitSlots - 1) / kEmitSlots + 1; }
 
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
                               hipStream_t s) {

@@ -16,9 +16,11 @@
 // cross-die coherent path, and on this chip that traffic and its latency
 // cost about half of every pass. Each pass is reduce-then-scan instead:
 // the keys are split into at most 1024 contiguous chunks (one resident
-// block each), a counting kernel writes per-chunk digit counts, a tiny
-// kernel turns them into each chunk's start per digit, and the scatter
-// kernel walks its chunk tile by tile with running per-digit cursors.
+// block each); a counting kernel writes per-chunk digit counts and adds
+// them into totals per group of 32 chunks; the scatter kernel derives its
+// chunk's start per digit from at most 32 group totals and 31 chunk counts
+// (no separate scan launch) and walks its chunk tile by tile with running
+// per-digit cursors.
 // Inside a tile, ranks come from eight ballots (lanes with equal digits),
 // per-wave counters live in LDS, and the tile is reordered in LDS so each
 // digit run is written contiguously. Stability: tiles are taken in order
@@ -68,17 +70,19 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint32_t* __restric
     woff += (w < wave) ? s_wave[w] : 0ull;
     btot += s_wave[w];
   }
-  if (tid == 0) {
+  if (wave == 0) {
     uint64_t prefix = 0;
     if (blk == 0) {
-      lb_store(lb, lb_word(kLbPrefix, 1, btot));
+      if (lane == 0) lb_store(lb, lb_word(kLbPrefix, 1, btot));
     } else {
-      lb_store(lb + blk, lb_word(kLbAgg, 1, btot));
-      prefix = lookback_prefix(lb, int64_t(blk), 1, 1, err);
-      lb_store(lb + blk, lb_word(kLbPrefix, 1, prefix + btot));
+      if (lane == 0) lb_store(lb + blk, lb_word(kLbAgg, 1, btot));
+      prefix = lookback_prefix_wave(lb, int64_t(blk), 1, err);
+      if (lane == 0) lb_store(lb + blk, lb_word(kLbPrefix, 1, prefix + btot));
     }
-    s_prefix = prefix;
-    if ((blk + 1) * kScanTile >= n) *total = prefix + btot;
+    if (lane == 0) {
+      s_prefix = prefix;
+      if ((blk + 1) * kScanTile >= n) *total = prefix + btot;
+    }
   }
   __syncthreads();
   uint64_t run = s_prefix + woff + incl - tsum;
@@ -131,7 +135,8 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s_
 template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void k_radix_count(const uint32_t* __restrict__ keys, uint64_t n,
                                                     int shift, uint64_t ct,
-                                                    uint32_t* __restrict__ cnt) {
+                                                    uint32_t* __restrict__ cnt,
+                                                    uint64_t* __restrict__ grp) {
   constexpr uint64_t TILE = uint64_t(kSortThreads) * ITEMS;
   __shared__ uint32_t s_h[4][256];
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -155,33 +160,18 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_count(const uint32_t* __
     }
   }
   __syncthreads();
-  cnt[uint64_t(blockIdx.x) * 256 + tid] = s_h[0][tid] + s_h[1][tid] + s_h[2][tid] + s_h[3][tid];
-}
-
-// One block per digit: exclusive prefix over chunks, and the digit total.
-__global__ __launch_bounds__(kSortThreads) void k_radix_scan(const uint32_t* __restrict__ cnt, uint32_t P,
-                                                   uint64_t* __restrict__ base_rel,
-                                                   uint64_t* __restrict__ total) {
-  __shared__ uint64_t s_w[4];
-  const int tid = threadIdx.x, d = blockIdx.x;
-  const uint32_t per = (P + kSortThreads - 1) / kSortThreads;
-  const uint32_t r0 = tid * per, r1 = min(P, r0 + per);
-  uint64_t sum = 0;
-  for (uint32_t r = r0; r < r1; ++r) sum += cnt[uint64_t(r) * 256 + d];
-  uint64_t tot;
-  uint64_t run = block_excl_scan_u64(sum, s_w, &tot);
-  for (uint32_t r = r0; r < r1; ++r) {
-    base_rel[uint64_t(r) * 256 + d] = run;
-    run += cnt[uint64_t(r) * 256 + d];
-  }
-  if (tid == 0) total[d] = tot;
+  const uint32_t c = s_h[0][tid] + s_h[1][tid] + s_h[2][tid] + s_h[3][tid];
+  cnt[uint64_t(blockIdx.x) * 256 + tid] = c;
+  if (c) atomicAdd(reinterpret_cast<unsigned long long*>(grp + (blockIdx.x / kSortGroup) * 256 + tid),
+                   (unsigned long long)c);
 }
 
 template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint64_t n, int shift,
-    uint64_t ct, const uint64_t* __restrict__ base_rel, const uint64_t* __restrict__ total) {
+    uint64_t ct, const uint32_t* __restrict__ cnt, const uint64_t* __restrict__ grp,
+    uint64_t* __restrict__ grp_next) {
   constexpr int TILE = kSortThreads * ITEMS;
   __shared__ int64_t s_gstart[256];
   __shared__ uint32_t s_whist[4][256];
@@ -191,12 +181,34 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
   __shared__ uint32_t s_keys[TILE];
   __shared__ uint32_t s_vals[TILE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // Start of this chunk's run of digit tid: the keys of all smaller
+  // digits, plus this digit's keys in earlier chunk groups (group totals)
+  // and in earlier chunks of this group.
+  // Every load is issued unconditionally (clamped row, result selected)
+  // so that all of them are in flight together.
+  const uint32_t g = blockIdx.x / kSortGroup;
+  const uint32_t G = (gridDim.x + kSortGroup - 1) / kSortGroup;
+  uint64_t tot_d = 0, before = 0;
+#pragma unroll
+  for (uint32_t i = 0; i < uint32_t(kSortGroups); ++i) {
+    const uint64_t v = grp[(i < G ? i : G - 1) * 256 + tid];
+    tot_d += i < G ? v : 0ull;
+    before += i < g ? v : 0ull;
+  }
+  const uint32_t q0 = g * kSortGroup;
+#pragma unroll
+  for (uint32_t i = 0; i + 1 < uint32_t(kSortGroup); ++i) {
+    const uint32_t q = q0 + i;
+    const uint32_t v = cnt[uint64_t(q < blockIdx.x ? q : blockIdx.x) * 256 + tid];
+    before += q < blockIdx.x ? v : 0u;
+  }
   uint64_t run;  // next output position of digit tid
   {
     uint64_t tot;
-    const uint64_t db = block_excl_scan_u64(total[tid], s_w64, &tot);
-    run = db + base_rel[uint64_t(blockIdx.x) * 256 + tid];
+    run = block_excl_scan_u64(tot_d, s_w64, &tot) + before;
   }
+  // the next pass's group totals start from zero
+  for (uint32_t r = blockIdx.x; r < uint32_t(kSortGroups); r += gridDim.x) grp_next[r * 256 + tid] = 0;
   const uint64_t lt = lanemask_lt();
   const uint64_t e0 = uint64_t(blockIdx.x) * ct * TILE;
   uint64_t e1 = e0 + ct * uint64_t(TILE);
@@ -337,42 +349,31 @@ SortPlan sort_plan(uint64_t n) {
 
 template <int ITEMS>
 void launch_pass(const SortPlan& pl, const uint32_t* ki, const uint32_t* vi, uint32_t* ko,
-                 uint32_t* vo, uint64_t n, int shift, const SortScratch& sc, hipStream_t s) {
+                 uint32_t* vo, uint64_t n, int shift, SortScratch& sc, hipStream_t s) {
+  uint64_t* grp = sc.grp + sc.parity * (kSortGroups * kRadix);
+  uint64_t* grp_next = sc.grp + (sc.parity ^ 1) * (kSortGroups * kRadix);
   {
     ProfScope prof("k_radix_count", s);
     hipLaunchKernelGGL(k_radix_count<ITEMS>, dim3(pl.P), dim3(kSortThreads), 0, s, ki, n, shift,
-                       pl.ct, sc.cnt);
-  }
-  {
-    ProfScope prof("k_radix_scan", s);
-    hipLaunchKernelGGL(k_radix_scan, dim3(kRadix), dim3(kSortThreads), 0, s, sc.cnt, pl.P,
-                       sc.base, sc.total);
+                       pl.ct, sc.cnt, grp);
   }
   {
     ProfScope prof("k_radix_scatter", s);
     hipLaunchKernelGGL(k_radix_scatter<ITEMS>, dim3(pl.P), dim3(kSortThreads), 0, s, ki, vi, ko,
-                       vo, n, shift, pl.ct, sc.base, sc.total);
+                       vo, n, shift, pl.ct, sc.cnt, grp, grp_next);
   }
+  sc.parity ^= 1;
 }
 
 }  // namespace
 
-uint64_t sort_scratch_bytes() {
-  return uint64_t(kSortChunks) * kRadix * (sizeof(uint32_t) + sizeof(uint64_t)) +
-         kRadix * sizeof(uint64_t);
-}
+uint64_t sort_counts_bytes() { return uint64_t(kSortChunks) * kRadix * sizeof(uint32_t); }
 
-SortScratch sort_scratch(void* base) {
-  SortScratch sc;
-  sc.total = static_cast<uint64_t*>(base);
-  sc.base = sc.total + kRadix;
-  sc.cnt = reinterpret_cast<uint32_t*>(sc.base + uint64_t(kSortChunks) * kRadix);
-  return sc;
-}
+uint64_t sort_groups_bytes() { return 2ull * kSortGroups * kRadix * sizeof(uint64_t); }
 
 hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys_b,
                               uint32_t* vals_b, uint64_t n, int bit0, int bits,
-                              const SortScratch& sc, bool* in_b, hipStream_t s) {
+                              SortScratch& sc, bool* in_b, hipStream_t s) {
   const int passes = sort_passes(bits);
   *in_b = (passes & 1) != 0;
   if (n == 0) return hipSuccess;
