@@ -13,8 +13,9 @@ Splatting trainer:
   n_isects), the per-element buffer cost table, "Bitmask compaction",
   "16-bit packed AABB" and "The 4 GiB rule and the 2^31 limit".
 * [BWD] "How Spirula Studio's backward pass sends image gradients back to
-  every Gaussian" -- sections 4 (rasterize backward) and 5 (projection
-  backward).
+  every Gaussian" -- sections 2-3 (the per-pixel output gradients of the
+  colour, depth and transmittance images; the background hook), 4
+  (rasterize backward) and 5 (projection backward).
 * [PROFILE] "Performance profiling guide: reading every step with
   SS_PROFILE=1" (kernel names only).
 * [GSPLAT] a deployment blog about a CUDA splatting library (C API over
@@ -40,12 +41,12 @@ float32, exactly as the rasterizer must.
 from .sh import sh_basis, sh_basis_grad, num_sh
 from .project import project, project_camera, quat_to_rotmat
 from .intersect import intersect, tile_rects_from_aabb16
-from .raster import rasterize_fwd, rasterize_bwd
+from .raster import rasterize_fwd, rasterize_bwd, background_grad
 from .project_bwd import project_bwd
 from .pipeline import render, loss_and_grads
 
 __all__ = [
     "sh_basis", "sh_basis_grad", "num_sh", "project", "project_camera",
     "quat_to_rotmat", "intersect", "tile_rects_from_aabb16", "rasterize_fwd",
-    "rasterize_bwd", "project_bwd", "render", "loss_and_grads",
+    "rasterize_bwd", "background_grad", "project_bwd", "render", "loss_and_grads",
 ]

@@ -15,13 +15,25 @@ Readings for the per-pixel rule (the pages give none), for pixel centre
   skip the entry if sigma < 0; alpha = min(0.99, o exp(-sigma));
   skip if alpha < 1/255; T' = T (1 - alpha); if T' < 1e-4 stop *without*
   compositing this entry; else C += rgb alpha T, T = T', last = index.
-Output: premultiplied colour (no background), final T, and ``last`` as the
-local index within the tile's range (-1 when nothing was composited).
+Output: premultiplied colour, final T, and ``last`` as the local index
+within the tile's range (-1 when nothing was composited).
 
-Backward, for L = <v_rgb, C> + <v_T, T_final> and composited entry i at a
-pixel, with T_i the transmittance before i and S_i = sum_{j>i} c_j a_j T_j:
-  dL/drgb_i  = a_i T_i v_rgb
-  dL/da_i    = v_rgb . (c_i T_i - S_i / (1 - a_i)) - v_T T_final / (1 - a_i)
+Depth channel and background ([BWD] section 2: the per-pixel output
+gradients are v_render_rgb, v_render_depth and v_render_Ts; section 3:
+the background blend's backward hook adds its transmittance gradient into
+v_render_Ts). Readings: the rendered depth is composited like a colour
+channel whose value is the entry's depth z (D = sum z alpha T, not
+normalised); the background is one RGB colour per camera added as
+C_out = C + T_final bg, absent (zero) when not given.
+
+Backward, for L = <v_rgb, C_out> + <v_T, T_final> + <v_depth, D> and
+composited entry i at a pixel, with T_i the transmittance before i,
+S_i = sum_{j>i} c_j a_j T_j and S^D_i = sum_{j>i} z_j a_j T_j:
+  dL/drgb_i  = a_i T_i v_rgb,  dL/dz_i = a_i T_i v_depth
+  dL/da_i    = v_rgb . (c_i T_i - S_i / (1 - a_i))
+               + v_depth (z_i T_i - S^D_i / (1 - a_i))
+               - (v_T + v_rgb . bg) T_final / (1 - a_i)
+  dL/dbg     = sum over the camera's pixels of v_rgb T_final
   dL/do      = dL/da e^-sigma,  dL/dsigma = -dL/da a  (both 0 when the 0.99
                clamp is active), and sigma's partials in (u, v, a, b, c).
 The discrete decisions (skips, the stop, the clamp) are not differentiated.
@@ -30,7 +42,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["rasterize_fwd", "rasterize_bwd", "ALPHA_MIN", "ALPHA_MAX", "T_STOP"]
+__all__ = ["rasterize_fwd", "rasterize_bwd", "background_grad", "ALPHA_MIN", "ALPHA_MAX",
+           "T_STOP"]
 
 TILE = 16
 ALPHA_MIN = 1.0 / 255.0
@@ -50,7 +63,7 @@ def _walk_tile(rows: np.ndarray, px: np.ndarray, py: np.ndarray, record: bool):
     """Composite one tile's entries over its pixels, entry by entry."""
     P, n = px.size, rows.shape[0]
     T = np.ones(P)
-    C = np.zeros((P, 3))
+    C = np.zeros((P, 4))   # rgb and depth
     last = np.full(P, -1, np.int64)
     evals = np.zeros(P, np.int64)
     active = np.ones(P, bool)
@@ -63,7 +76,7 @@ def _walk_tile(rows: np.ndarray, px: np.ndarray, py: np.ndarray, record: bool):
         if not active.any():
             break
         u, v, a, b, c, o = rows[j, :6]
-        rgb = rows[j, 7:10]
+        rgbz = rows[j, [7, 8, 9, 6]]
         dx = u - px
         dy = v - py
         sigma = 0.5 * (a * dx * dx + c * dy * dy) + b * dx * dy
@@ -84,7 +97,7 @@ def _walk_tile(rows: np.ndarray, px: np.ndarray, py: np.ndarray, record: bool):
             rec["clamp"][:, j] = raw_alpha > ALPHA_MAX
             rec["dx"][:, j] = dx
             rec["dy"][:, j] = dy
-        C[ok] += rgb[None, :] * (alpha[ok] * T[ok])[:, None]
+        C[ok] += rgbz[None, :] * (alpha[ok] * T[ok])[:, None]
         T = np.where(ok, Tn, T)
         last[ok] = j
     return C, T, last, evals, rec
@@ -94,37 +107,49 @@ def _tile_list(tile_offsets, flatten_ids, t):
     return np.asarray(flatten_ids[int(tile_offsets[t]):int(tile_offsets[t + 1])], np.int64)
 
 
-def rasterize_fwd(screen, flatten_ids, tile_offsets, C: int, W: int, H: int, tiles=None):
-    """(out_rgb[C,H,W,3], out_T[C,H,W], last_ids[C,H,W], evals[C,H,W]).
+def rasterize_fwd(screen, flatten_ids, tile_offsets, C: int, W: int, H: int, tiles=None,
+                  background=None, depth: bool = False):
+    """(out_rgb[C,H,W,3], out_T[C,H,W], last_ids[C,H,W], evals[C,H,W]),
+    plus out_depth[C,H,W] last when ``depth`` is set.
 
     ``tiles``: optional iterable of global tile ids (c * T + local) to
     evaluate; other pixels are left NaN (last_ids -2, evals -1).
+    ``background``: optional [C, 3] colour blended in as C + T_final bg.
     """
     tiles_x, tiles_y = (W + TILE - 1) // TILE, (H + TILE - 1) // TILE
     T_per = tiles_x * tiles_y
     out_rgb = np.full((C, H, W, 3), np.nan)
     out_T = np.full((C, H, W), np.nan)
+    out_depth = np.full((C, H, W), np.nan)
     last_ids = np.full((C, H, W), -2, np.int64)
     evals = np.full((C, H, W), -1, np.int64)
     screen = np.asarray(screen, np.float64)
+    bg = None if background is None else np.asarray(background, np.float64).reshape(C, 3)
     for t in (range(C * T_per) if tiles is None else tiles):
         c, tl = divmod(int(t), T_per)
         ii, jj = _tile_pixels(tl, tiles_x, W, H)
         ids = _tile_list(tile_offsets, flatten_ids, t)
         Cc, Tt, last, ev, _ = _walk_tile(screen[ids], jj + 0.5, ii + 0.5, record=False)
-        out_rgb[c, ii, jj] = Cc
+        rgb = Cc[:, :3] if bg is None else Cc[:, :3] + Tt[:, None] * bg[c][None, :]
+        out_rgb[c, ii, jj] = rgb
+        out_depth[c, ii, jj] = Cc[:, 3]
         out_T[c, ii, jj] = Tt
         last_ids[c, ii, jj] = last
         evals[c, ii, jj] = ev
+    if depth:
+        return out_rgb, out_T, last_ids, evals, out_depth
     return out_rgb, out_T, last_ids, evals
 
 
 def rasterize_bwd(screen, flatten_ids, tile_offsets, C: int, W: int, H: int,
-                  v_rgb, v_T=None, tiles=None):
-    """dL/d(screen rows) [nnz, 10] for L = <v_rgb, out_rgb> + <v_T, out_T>.
+                  v_rgb, v_T=None, tiles=None, v_depth=None, background=None):
+    """dL/d(screen rows) [nnz, 10] for L = <v_rgb, out_rgb> + <v_T, out_T>
+    + <v_depth, out_depth>.
 
-    The depth column of the result stays 0 (the colour image does not
-    depend on it). ``tiles`` restricts the sum to those global tile ids.
+    The depth column of the result is 0 when ``v_depth`` is None (the
+    colour image does not depend on it). ``background`` is the forward's
+    [C, 3] colour (None = no blend). ``tiles`` restricts the sum to those
+    global tile ids.
     """
     tiles_x, tiles_y = (W + TILE - 1) // TILE, (H + TILE - 1) // TILE
     T_per = tiles_x * tiles_y
@@ -132,6 +157,11 @@ def rasterize_bwd(screen, flatten_ids, tile_offsets, C: int, W: int, H: int,
     v_screen = np.zeros_like(screen)
     v_rgb = np.asarray(v_rgb, np.float64)
     v_T = np.zeros(v_rgb.shape[:3]) if v_T is None else np.asarray(v_T, np.float64)
+    v_D = np.zeros(v_rgb.shape[:3]) if v_depth is None else np.asarray(v_depth, np.float64)
+    if background is not None:
+        # the background hook: T_final also feeds C_out through T bg
+        bg = np.asarray(background, np.float64).reshape(C, 3)
+        v_T = v_T + np.einsum("chwk,ck->chw", v_rgb, bg)
     for t in (range(C * T_per) if tiles is None else tiles):
         c, tl = divmod(int(t), T_per)
         ii, jj = _tile_pixels(tl, tiles_x, W, H)
@@ -152,14 +182,16 @@ def rasterize_bwd(screen, flatten_ids, tile_offsets, C: int, W: int, H: int,
         ex = rec["ex"][:, :n_used]
         clamp = rec["clamp"][:, :n_used]
         dx, dy = rec["dx"][:, :n_used], rec["dy"][:, :n_used]
-        gr = v_rgb[c, ii, jj]            # [P, 3]
+        # the depth is a fourth channel with value z and upstream v_depth
+        gr = np.concatenate([v_rgb[c, ii, jj], v_D[c, ii, jj][:, None]], 1)   # [P, 4]
         gT = v_T[c, ii, jj]              # [P]
+        chan = rows[:, [7, 8, 9, 6]]                       # [n, 4]
         w = np.where(comp, alpha * Tb, 0.0)               # [P, n]
-        contrib = w[:, :, None] * rows[None, :, 7:10]     # [P, n, 3]
+        contrib = w[:, :, None] * chan[None]               # [P, n, 4]
         suffix = np.cumsum(contrib[:, ::-1], axis=1)[:, ::-1]
         S = suffix - contrib                               # sum over j > i
         one_m = 1.0 - alpha
-        v_alpha = (np.einsum("pc,pnc->pn", gr, rows[None, :, 7:10] * Tb[:, :, None] - S / one_m[:, :, None])
+        v_alpha = (np.einsum("pc,pnc->pn", gr, chan[None] * Tb[:, :, None] - S / one_m[:, :, None])
                    - gT[:, None] * Tfin[:, None] / one_m)
         v_alpha = np.where(comp, v_alpha, 0.0)
         free = comp & ~clamp
@@ -173,9 +205,16 @@ def rasterize_bwd(screen, flatten_ids, tile_offsets, C: int, W: int, H: int,
         g[:, 3] = (v_sigma * dx * dy).sum(0)
         g[:, 4] = (v_sigma * 0.5 * dy * dy).sum(0)
         g[:, 5] = v_o.sum(0)
-        g[:, 7:10] = np.einsum("pn,pc->nc", w, gr)
+        g[:, 7:10] = np.einsum("pn,pc->nc", w, gr[:, :3])
+        g[:, 6] = np.einsum("pn,p->n", w, gr[:, 3])
         np.add.at(v_screen, ids, g)
     return v_screen
+
+
+def background_grad(out_T, v_rgb):
+    """dL/dbg [C, 3] of the blend C + T_final bg: sum over each camera's
+    pixels of v_rgb T_final."""
+    return np.einsum("chwk,chw->ck", np.asarray(v_rgb, np.float64), np.asarray(out_T, np.float64))
 
 
 def decision_signature(screen, flatten_ids, tile_offsets, C: int, W: int, H: int) -> bytes:
