@@ -67,9 +67,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gs_intersect.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i64, c_vp, c_vp, P_i64, c_vp, c_u64,
                                  c_vp, c_i64, c_vp, c_vp, c_vp, P_i64, P_u64]
     lib.gs_rasterize_fwd.restype = ctypes.c_int
-    lib.gs_rasterize_fwd.argtypes = [c_vp, c_i32, c_i32, c_i32] + [c_vp] * 7
+    lib.gs_rasterize_fwd.argtypes = [c_vp, c_i32, c_i32, c_i32] + [c_vp] * 9
     lib.gs_rasterize_bwd.restype = ctypes.c_int
-    lib.gs_rasterize_bwd.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i64] + [c_vp] * 9
+    lib.gs_rasterize_bwd.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i64] + [c_vp] * 12
     lib.gs_project_bwd.restype = ctypes.c_int
     lib.gs_project_bwd.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
         [c_vp] * 3 + [c_vp] * 5 + [c_i32]
@@ -164,19 +164,19 @@ def gs_intersect(C, W, H, nnz, screen, aabb16, cam_offsets, workspace, workspace
     return st, n_is.value, need.value
 
 
-def gs_rasterize_fwd(C, W, H, screen, flatten_ids, tile_offsets, tile_order, out_rgb, out_T,
-                     last_ids, stream=None):
+def gs_rasterize_fwd(C, W, H, screen, flatten_ids, tile_offsets, tile_order, background, out_rgb,
+                     out_T, out_depth, last_ids, stream=None):
     return load().gs_rasterize_fwd(_stream(stream), C, W, H, _ptr(screen), _ptr(flatten_ids),
-                                   _ptr(tile_offsets), _ptr(tile_order), _ptr(out_rgb),
-                                   _ptr(out_T), _ptr(last_ids))
+                                   _ptr(tile_offsets), _ptr(tile_order), _ptr(background),
+                                   _ptr(out_rgb), _ptr(out_T), _ptr(out_depth), _ptr(last_ids))
 
 
-def gs_rasterize_bwd(C, W, H, nnz, screen, flatten_ids, tile_offsets, tile_order, out_T,
-                     last_ids, v_rgb, v_T, v_screen, stream=None):
+def gs_rasterize_bwd(C, W, H, nnz, screen, flatten_ids, tile_offsets, tile_order, background,
+                     out_T, last_ids, v_rgb, v_T, v_depth, v_screen, v_background, stream=None):
     return load().gs_rasterize_bwd(_stream(stream), C, W, H, nnz, _ptr(screen),
                                    _ptr(flatten_ids), _ptr(tile_offsets), _ptr(tile_order),
-                                   _ptr(out_T), _ptr(last_ids), _ptr(v_rgb), _ptr(v_T),
-                                   _ptr(v_screen))
+                                   _ptr(background), _ptr(out_T), _ptr(last_ids), _ptr(v_rgb),
+                                   _ptr(v_T), _ptr(v_depth), _ptr(v_screen), _ptr(v_background))
 
 
 def gs_project_bwd(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, sh,
@@ -318,23 +318,31 @@ class Rasterizer:
                                keys[:n_is] if keys is not None else None, order)
         raise GsError(GS_E_CAPACITY, "gs_intersect")
 
-    def rasterize_fwd(self, s: Scene, p: Projected, it: Intersected):
+    def rasterize_fwd(self, s: Scene, p: Projected, it: Intersected, background=None,
+                      depth: bool = False):
+        """(rgb, T, last), plus the depth image last when ``depth``;
+        ``background``: optional [C, 3] device tensor."""
         dev = self.device
         rgb = torch.empty(s.C, s.H, s.W, 3, device=dev)
         T = torch.empty(s.C, s.H, s.W, device=dev)
         last = torch.empty(s.C, s.H, s.W, dtype=torch.int32, device=dev)
+        D = torch.empty(s.C, s.H, s.W, device=dev) if depth else None
         self._check(gs_rasterize_fwd(s.C, s.W, s.H, p.screen, it.flatten_ids, it.tile_offsets,
-                                     it.tile_order, rgb, T, last), "gs_rasterize_fwd")
-        return rgb, T, last
+                                     it.tile_order, background, rgb, T, D, last),
+                    "gs_rasterize_fwd")
+        return (rgb, T, last, D) if depth else (rgb, T, last)
 
-    def rasterize_bwd(self, s: Scene, p: Projected, it: Intersected, out_T, last, v_rgb, v_T=None):
+    def rasterize_bwd(self, s: Scene, p: Projected, it: Intersected, out_T, last, v_rgb, v_T=None,
+                      v_depth=None, background=None, v_background=None):
+        """v_screen [nnz, 10]; ``v_background`` (optional [C, 3] device
+        tensor) receives dL/dbackground."""
         dev = self.device
         self._vscreen = _grow(self._vscreen, max(p.nnz * ROW, 1), torch.float32, dev, self.slack)
         v = self._vscreen[: p.nnz * ROW].view(p.nnz, ROW) if p.nnz else \
             torch.empty(0, ROW, device=dev)
         self._check(gs_rasterize_bwd(s.C, s.W, s.H, p.nnz, p.screen, it.flatten_ids,
-                                     it.tile_offsets, it.tile_order, out_T, last, v_rgb, v_T, v),
-                    "gs_rasterize_bwd")
+                                     it.tile_offsets, it.tile_order, background, out_T, last, v_rgb,
+                                     v_T, v_depth, v, v_background), "gs_rasterize_bwd")
         return v
 
     def project_bwd(self, s: Scene, p: Projected, v_screen, grads=None, accumulate=False):
@@ -353,12 +361,22 @@ class Rasterizer:
                                    grads["v_sh"], 1 if accumulate else 0), "gs_project_bwd")
         return grads
 
-    def step(self, s: Scene, v_rgb, v_T=None):
+    def step(self, s: Scene, v_rgb, v_T=None, v_depth=None, background=None):
         """One whole pass: project, intersect, raster forward and backward,
-        projection backward. Returns everything the passes produced."""
+        projection backward. Returns everything the passes produced. With
+        ``v_depth`` the depth image is rendered and back-propagated; with
+        ``background`` ([C, 3]) it is blended in and its gradient returned."""
         p = self.project(s)
         it = self.intersect(s, p)
-        rgb, T, last = self.rasterize_fwd(s, p, it)
-        v_screen = self.rasterize_bwd(s, p, it, T, last, v_rgb, v_T)
+        depth = v_depth is not None
+        out = self.rasterize_fwd(s, p, it, background, depth=depth)
+        rgb, T, last = out[:3]
+        v_bg = torch.empty(s.C, 3, device=self.device) if background is not None else None
+        v_screen = self.rasterize_bwd(s, p, it, T, last, v_rgb, v_T, v_depth, background, v_bg)
         grads = self.project_bwd(s, p, v_screen)
-        return dict(proj=p, isect=it, rgb=rgb, T=T, last=last, v_screen=v_screen, grads=grads)
+        res = dict(proj=p, isect=it, rgb=rgb, T=T, last=last, v_screen=v_screen, grads=grads)
+        if depth:
+            res["depth"] = out[3]
+        if v_bg is not None:
+            res["v_background"] = v_bg
+        return res

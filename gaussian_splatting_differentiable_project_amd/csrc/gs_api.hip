@@ -355,27 +355,31 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
 
 int gs_rasterize_fwd(void* stream, int32_t C, int32_t W, int32_t H, const float* screen,
                      const uint32_t* flatten_ids, const int64_t* tile_offsets,
-                     const uint32_t* tile_order, float* out_rgb, float* out_T,
-                     int32_t* last_ids) {
+                     const uint32_t* tile_order, const float* background, float* out_rgb,
+                     float* out_T, float* out_depth, int32_t* last_ids) {
   if (!valid_image(C, W, H) || !tile_offsets || !out_rgb || !out_T || !last_ids)
     return GS_E_INVALID;
   if (!aligned(screen, 8)) return GS_E_INVALID;
   return hip_status(launch_raster_fwd(C, W, H, screen, flatten_ids, tile_offsets, tile_order,
-                                      out_rgb, out_T, last_ids, static_cast<hipStream_t>(stream)));
+                                      background, out_rgb, out_T, out_depth, last_ids,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int gs_rasterize_bwd(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz,
                      const float* screen, const uint32_t* flatten_ids, const int64_t* tile_offsets,
-                     const uint32_t* tile_order, const float* out_T, const int32_t* last_ids,
-                     const float* v_rgb, const float* v_T, float* v_screen) {
+                     const uint32_t* tile_order, const float* background, const float* out_T,
+                     const int32_t* last_ids, const float* v_rgb, const float* v_T,
+                     const float* v_depth, float* v_screen, float* v_background) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!valid_image(C, W, H) || nnz < 0 || !tile_offsets || !out_T || !last_ids || !v_rgb)
     return GS_E_INVALID;
   if (nnz > 0 && !v_screen) return GS_E_INVALID;
   if (!aligned(screen, 8)) return GS_E_INVALID;
   GS_TRY(launch_fill_u32(v_screen, 0u, uint64_t(nnz) * kRow, s));
-  return hip_status(launch_raster_bwd(C, W, H, screen, flatten_ids, tile_offsets, tile_order, out_T,
-                                      last_ids, v_rgb, v_T, v_screen, s));
+  if (v_background) GS_TRY(launch_fill_u32(v_background, 0u, 3ull * uint64_t(C), s));
+  return hip_status(launch_raster_bwd(C, W, H, screen, flatten_ids, tile_offsets, tile_order,
+                                      background, out_T, last_ids, v_rgb, v_T, v_depth, v_screen,
+                                      v_background, s));
 }
 
 int gs_project_bwd(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t sh_degree,

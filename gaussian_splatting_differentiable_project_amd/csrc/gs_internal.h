@@ -101,12 +101,14 @@ hipError_t launch_compose_keys(const uint32_t* tkeys, const uint32_t* ids, const
 
 // Rasterization (gs_raster.hip).
 hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uint32_t* ids,
-                             const int64_t* toff, const uint32_t* order, float* out_rgb,
-                             float* out_T, int32_t* last_ids, hipStream_t s);
+                             const int64_t* toff, const uint32_t* order, const float* background,
+                             float* out_rgb, float* out_T, float* out_depth, int32_t* last_ids,
+                             hipStream_t s);
 hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uint32_t* ids,
-                             const int64_t* toff, const uint32_t* order, const float* out_T,
-                             const int32_t* last_ids, const float* v_rgb, const float* v_T,
-                             float* v_screen, hipStream_t s);
+                             const int64_t* toff, const uint32_t* order, const float* background,
+                             const float* out_T, const int32_t* last_ids, const float* v_rgb,
+                             const float* v_T, const float* v_depth, float* v_screen,
+                             float* v_background, hipStream_t s);
 
 // First slot of every camera from the group scan (gs_project.hip).
 hipError_t launch_cam_offsets(const uint32_t* wg_scan, int64_t groups_per_cam, int C,

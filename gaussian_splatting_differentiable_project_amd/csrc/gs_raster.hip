@@ -8,6 +8,12 @@
 // into fp32 screen-space gradients with atomics. The pages give no
 // per-pixel formula; the rule is the textbook one fixed in gs.h.
 //
+// Optional outputs ([BWD] sections 2-3: the per-pixel gradients of the
+// colour, depth and transmittance images, and the background hook that
+// adds into the transmittance gradient): a depth image composited like a
+// colour channel whose value is the entry's depth, D = sum z alpha T, and
+// a per-camera background colour blended as C + T_final bg.
+//
 // gfx950 mapping: one work-group per 16x16 tile; PPT pixels per lane, so
 // a 256-pixel tile is 256/PPT lanes. Screen rows of a batch of the tile's
 // list are staged in LDS (gathered through the flattened ids) and read
@@ -35,6 +41,7 @@ struct Staged {
   float4 a;  // u, v, a', c'
   float4 b;  // b, log2(o), r, g
   float2 c;  // blue, 1/o
+  float z;   // depth (used only with a depth image)
 };
 
 __device__ __forceinline__ Staged stage_row(const float* __restrict__ screen, uint32_t s) {
@@ -44,6 +51,7 @@ __device__ __forceinline__ Staged stage_row(const float* __restrict__ screen, ui
   e.a = make_float4(r0.x, r0.y, 0.5f * r1.x, 0.5f * r2.x);
   e.b = make_float4(r1.y, __builtin_amdgcn_logf(r2.y), r3.y, r4.x);
   e.c = make_float2(r4.y, __builtin_amdgcn_rcpf(r2.y));
+  e.z = r3.x;
   return e;
 }
 
@@ -138,17 +146,18 @@ __device__ __forceinline__ int compact_slot(bool keep, int* s_wcnt, int* pos) {
   }
 }
 
-template <int PPT>
+template <int PPT, bool DEPTH>
 __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
     const float* __restrict__ screen, const uint32_t* __restrict__ ids,
     const int64_t* __restrict__ toff, const uint32_t* __restrict__ order, int W, int H,
-    int tiles_x, int T, float* __restrict__ out_rgb, float* __restrict__ out_T,
-    int32_t* __restrict__ last_ids) {
+    int tiles_x, int T, const float* __restrict__ background, float* __restrict__ out_rgb,
+    float* __restrict__ out_T, float* __restrict__ out_depth, int32_t* __restrict__ last_ids) {
   constexpr int NT = kTilePix / PPT;
   constexpr int B = NT;
   __shared__ float4 s_a[B];
   __shared__ float4 s_b[B];
   __shared__ float s_c[B];
+  __shared__ float s_z[DEPTH ? B : 1];
   __shared__ int s_lid[B];
   __shared__ uint32_t s_reach[B];
   __shared__ int s_wcnt[NT / kWave];
@@ -159,7 +168,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
   const int ty = tl / tiles_x, tx = tl - ty * tiles_x;
   const int64_t start = toff[t], end = toff[t + 1];
 
-  float px[PPT], py[PPT], Tr[PPT], cr[PPT], cg[PPT], cb[PPT];
+  float px[PPT], py[PPT], Tr[PPT], cr[PPT], cg[PPT], cb[PPT], cd[PPT];
   int last[PPT];
   bool live[PPT];
   bool inside[PPT];
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
     px[k] = float(X) + 0.5f;
     py[k] = float(Yp) + 0.5f;
     Tr[k] = 1.f;
-    cr[k] = cg[k] = cb[k] = 0.f;
+    cr[k] = cg[k] = cb[k] = cd[k] = 0.f;
     last[k] = -1;
   }
 
@@ -196,6 +205,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
       s_a[pos] = e.a;
       s_b[pos] = e.b;
       s_c[pos] = e.c.x;
+      if (DEPTH) s_z[pos] = e.z;
       s_lid[pos] = int(b0 - start) + tid;
       s_reach[pos] = reach;
     }
@@ -204,6 +214,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
       const uint32_t rm = s_reach[j];
       const float4 A = s_a[j], Bv = s_b[j];
       const float cblue = s_c[j];
+      const float zj = DEPTH ? s_z[j] : 0.f;
       const int lid = s_lid[j];
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
@@ -219,21 +230,29 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
           cr[k] = fmaf(Bv.z, w, cr[k]);
           cg[k] = fmaf(Bv.w, w, cg[k]);
           cb[k] = fmaf(cblue, w, cb[k]);
+          if (DEPTH) cd[k] = fmaf(zj, w, cd[k]);
           Tr[k] = Tn;
           last[k] = lid;
         }
       }
     }
   }
+  float bg0 = 0.f, bg1 = 0.f, bg2 = 0.f;
+  if (background) {
+    bg0 = background[3 * c + 0];
+    bg1 = background[3 * c + 1];
+    bg2 = background[3 * c + 2];
+  }
 #pragma unroll
   for (int k = 0; k < PPT; ++k) {
     if (!inside[k]) continue;
     const int p = tid + k * NT;
     const int64_t pix = (int64_t(c) * H + ty * kTile + (p >> 4)) * W + tx * kTile + (p & 15);
-    out_rgb[3 * pix + 0] = cr[k];
-    out_rgb[3 * pix + 1] = cg[k];
-    out_rgb[3 * pix + 2] = cb[k];
+    out_rgb[3 * pix + 0] = fmaf(Tr[k], bg0, cr[k]);
+    out_rgb[3 * pix + 1] = fmaf(Tr[k], bg1, cg[k]);
+    out_rgb[3 * pix + 2] = fmaf(Tr[k], bg2, cb[k]);
     out_T[pix] = Tr[k];
+    if (DEPTH) out_depth[pix] = cd[k];
     last_ids[pix] = last[k];
   }
 }
@@ -249,15 +268,18 @@ constexpr int kDppRowHalfMirror = 0x141;  // lane reads 7 - l within its half-ro
 constexpr int kDppXor2 = 0x4E;            // quad_perm [2,3,0,1]
 constexpr int kDppXor1 = 0xB1;            // quad_perm [1,0,3,2]
 
-// Sum nine per-lane values over the wave and add the totals to
-// dst[field] with one atomic instruction. Transposed reduction: at each
-// step a lane pairs with a partner differing in one lane bit and keeps the
-// sums of half of the remaining values (9 -> 5 -> 3 -> 2 -> 1), so a lane
-// ends with one value summed over its 16-lane row; two exchanges across
-// rows finish the sum. Lanes 0..15 then hold: lane -> value index
-// 0,1,2,-,3,4,-,-,5,6,7,-,8,-,-,- (value index -> screen field
-// 0,1,2,3,4,5,7,8,9). Must be called with all 64 lanes active.
-__device__ __forceinline__ void wave_reduce9_atomic(const float (&v)[9], float* dst) {
+// Sum nine (or, with the depth term, ten) per-lane values over the wave
+// and add the totals to dst[field] with one atomic instruction. Transposed
+// reduction: at each step a lane pairs with a partner differing in one
+// lane bit and keeps the sums of half of the remaining values
+// (9|10 -> 5 -> 3 -> 2 -> 1), so a lane ends with one value summed over
+// its 16-lane row; two exchanges across rows finish the sum. Lanes 0..15
+// then hold: lane -> value index 0,1,2,-,3,4,-,-,5,6,7,-,8,9,-,- (value
+// index -> screen field 0,1,2,3,4,5,7,8,9, then 6). Must be called with
+// all 64 lanes active.
+template <int NV>
+__device__ __forceinline__ void wave_reduce_atomic(const float (&v)[NV], float* dst) {
+  static_assert(NV == 9 || NV == 10, "nine or ten fields");
   // Every DPP read is evaluated by all lanes before any select: a DPP
   // inside a conditional would read lanes that are switched off.
   const int lane = __lane_id();
@@ -271,7 +293,8 @@ __device__ __forceinline__ void wave_reduce9_atomic(const float (&v)[9], float* 
   }
   {
     const float lo_s = v[4] + dpp<kDppRowMirror>(v[4]);
-    w1[4] = hi ? 0.f : lo_s;
+    const float hi_s = NV == 10 ? v[NV - 1] + dpp<kDppRowMirror>(v[NV - 1]) : 0.f;
+    w1[4] = hi ? hi_s : lo_s;
   }
   hi = (lane & 4) != 0;
   float w2[3];
@@ -297,22 +320,26 @@ __device__ __forceinline__ void wave_reduce9_atomic(const float (&v)[9], float* 
   float w4 = hi ? s41 : s40;
   w4 += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, w4), 0x401F));
   w4 += __shfl_xor(w4, 32, kWave);
-  constexpr uint64_t kFieldPlus1 = 0xa098600540321ull;  // 4 bits per lane 0..15
+  constexpr uint64_t kFieldPlus1 =
+      NV == 10 ? 0x7a098600540321ull : 0xa098600540321ull;  // 4 bits per lane 0..15
   const int f = lane < 16 ? int((kFieldPlus1 >> (4 * lane)) & 15u) - 1 : -1;
   if (f >= 0) atomicAdd(dst + f, w4);
 }
 
-template <int PPT>
+template <int PPT, bool DEPTH>
 __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
     const float* __restrict__ screen, const uint32_t* __restrict__ ids,
     const int64_t* __restrict__ toff, const uint32_t* __restrict__ order, int W, int H,
-    int tiles_x, int T, const float* __restrict__ out_T, const int32_t* __restrict__ last_ids,
-    const float* __restrict__ v_rgb, const float* __restrict__ v_T, float* __restrict__ v_screen) {
+    int tiles_x, int T, const float* __restrict__ background, const float* __restrict__ out_T,
+    const int32_t* __restrict__ last_ids, const float* __restrict__ v_rgb,
+    const float* __restrict__ v_T, const float* __restrict__ v_depth,
+    float* __restrict__ v_screen, float* __restrict__ v_background) {
   constexpr int NT = kTilePix / PPT;
   constexpr int B = NT;
   __shared__ float4 s_a[B];
   __shared__ float4 s_b[B];
   __shared__ float2 s_c[B];
+  __shared__ float s_z[DEPTH ? B : 1];
   __shared__ uint32_t s_id[B];
   __shared__ int s_lid[B];
   __shared__ int s_wcnt[NT / kWave];
@@ -326,11 +353,19 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
   if (tid == 0) s_max = -1;
 
   // Per pixel: current transmittance (walking back to front), the running
-  // dot product P = g . sum_{later} colour alpha T, the upstream colour
-  // gradient g and the T gradient term g_T T_final.
-  float px[PPT], py[PPT], Tc[PPT], Pd[PPT], g0[PPT], g1[PPT], g2[PPT], gTT[PPT];
+  // dot product P = g . sum_{later} colour alpha T (depth included as a
+  // fourth channel), the upstream colour and depth gradients g, gD, and
+  // the T gradient term (g_T + g . bg) T_final (the background hook).
+  float px[PPT], py[PPT], Tc[PPT], Pd[PPT], g0[PPT], g1[PPT], g2[PPT], gD[PPT], gTT[PPT];
   int last[PPT];
   int my_max = -1;
+  float bg0 = 0.f, bg1 = 0.f, bg2 = 0.f;
+  if (background) {
+    bg0 = background[3 * c + 0];
+    bg1 = background[3 * c + 1];
+    bg2 = background[3 * c + 2];
+  }
+  float vb0 = 0.f, vb1 = 0.f, vb2 = 0.f;  // this lane's share of dL/dbg
 #pragma unroll
   for (int k = 0; k < PPT; ++k) {
     const int p = tid + k * NT;
@@ -346,13 +381,29 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
       g0[k] = v_rgb[3 * pix + 0];
       g1[k] = v_rgb[3 * pix + 1];
       g2[k] = v_rgb[3 * pix + 2];
-      gTT[k] = (v_T ? v_T[pix] : 0.f) * Tc[k];
+      gD[k] = DEPTH ? v_depth[pix] : 0.f;
+      const float gT = (v_T ? v_T[pix] : 0.f) + fmaf(g2[k], bg2, fmaf(g1[k], bg1, g0[k] * bg0));
+      gTT[k] = gT * Tc[k];
+      vb0 = fmaf(g0[k], Tc[k], vb0);
+      vb1 = fmaf(g1[k], Tc[k], vb1);
+      vb2 = fmaf(g2[k], Tc[k], vb2);
     } else {
       Tc[k] = 1.f;
       last[k] = -1;
-      g0[k] = g1[k] = g2[k] = gTT[k] = 0.f;
+      g0[k] = g1[k] = g2[k] = gD[k] = gTT[k] = 0.f;
     }
     my_max = max(my_max, last[k]);
+  }
+  if (v_background) {
+    // dL/dbg = sum over the camera's pixels of v_rgb T_final
+    vb0 = wave_sum(vb0);
+    vb1 = wave_sum(vb1);
+    vb2 = wave_sum(vb2);
+    if ((tid & (kWave - 1)) == 0) {
+      atomicAdd(v_background + 3 * c + 0, vb0);
+      atomicAdd(v_background + 3 * c + 1, vb1);
+      atomicAdd(v_background + 3 * c + 2, vb2);
+    }
   }
   __syncthreads();
   if (my_max >= 0) atomicMax(&s_max, my_max);
@@ -381,6 +432,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
       s_a[pos] = e.a;
       s_b[pos] = e.b;
       s_c[pos] = e.c;
+      if (DEPTH) s_z[pos] = e.z;
       s_id[pos] = sid;
       s_lid[pos] = int(b_start - start) + tid;
     }
@@ -388,11 +440,13 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
     for (int j = nb - 1; j >= 0; --j) {
       const float4 A = s_a[j], Bv = s_b[j];
       const float2 Cv = s_c[j];
+      const float zj = DEPTH ? s_z[j] : 0.f;
       const int lid = s_lid[j];
       // per-lane sums over its pixels: first moments and second moments of
-      // (dx, dy) weighted by dL/dsigma, sum of dL/dalpha raw, colour grads
+      // (dx, dy) weighted by dL/dsigma, sum of dL/dalpha raw, colour and
+      // depth grads
       float mx = 0.f, my = 0.f, mxx = 0.f, mxy = 0.f, myy = 0.f, mo = 0.f;
-      float gr = 0.f, gg = 0.f, gbl = 0.f;
+      float gr = 0.f, gg = 0.f, gbl = 0.f, gz = 0.f;
       bool any = false;
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
@@ -405,7 +459,9 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
           gr = fmaf(w, g0[k], gr);
           gg = fmaf(w, g1[k], gg);
           gbl = fmaf(w, g2[k], gbl);
-          const float gc = fmaf(g2[k], Cv.x, fmaf(g1[k], Bv.w, g0[k] * Bv.z));
+          if (DEPTH) gz = fmaf(w, gD[k], gz);
+          float gc = fmaf(g2[k], Cv.x, fmaf(g1[k], Bv.w, g0[k] * Bv.z));
+          if (DEPTH) gc = fmaf(gD[k], zj, gc);
           const float va = fmaf(Ti, gc, -(Pd[k] + gTT[k]) * om);
           Pd[k] = fmaf(w, gc, Pd[k]);
           Tc[k] = Ti;
@@ -424,9 +480,16 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
         // dsigma/du = a dx + b dy, dsigma/dv = b dx + c dy, dsigma/da = dx^2/2,
         // dsigma/db = dx dy, dsigma/dc = dy^2/2, dalpha/do = exp(-sigma)
         const float a2 = A.z + A.z, c2 = A.w + A.w;
-        const float vals[9] = {fmaf(a2, mx, Bv.x * my), fmaf(Bv.x, mx, c2 * my), 0.5f * mxx, mxy,
-                               0.5f * myy, mo * Cv.y, gr, gg, gbl};
-        wave_reduce9_atomic(vals, v_screen + int64_t(s_id[j]) * kRow);
+        float* dst = v_screen + int64_t(s_id[j]) * kRow;
+        if (DEPTH) {
+          const float vals[10] = {fmaf(a2, mx, Bv.x * my), fmaf(Bv.x, mx, c2 * my), 0.5f * mxx,
+                                  mxy, 0.5f * myy, mo * Cv.y, gr, gg, gbl, gz};
+          wave_reduce_atomic<10>(vals, dst);
+        } else {
+          const float vals[9] = {fmaf(a2, mx, Bv.x * my), fmaf(Bv.x, mx, c2 * my), 0.5f * mxx,
+                                 mxy, 0.5f * myy, mo * Cv.y, gr, gg, gbl};
+          wave_reduce_atomic<9>(vals, dst);
+        }
       }
     }
   }
@@ -448,8 +511,9 @@ constexpr int kFwdPPT = 1;
 constexpr int kBwdPPT = 4;
 
 hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uint32_t* ids,
-                             const int64_t* toff, const uint32_t* order, float* out_rgb,
-                             float* out_T, int32_t* last_ids, hipStream_t s) {
+                             const int64_t* toff, const uint32_t* order, const float* background,
+                             float* out_rgb, float* out_T, float* out_depth, int32_t* last_ids,
+                             hipStream_t s) {
   static const int ppt = ppt_from_env("GS_RASTER_PPT_FWD", kFwdPPT);
   const int tiles_x = (W + kTile - 1) / kTile, tiles_y = (H + kTile - 1) / kTile;
   const int T = tiles_x * tiles_y;
@@ -457,19 +521,24 @@ hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uin
   if (blocks == 0) return hipSuccess;
   if (!fits_dispatch(uint64_t(blocks), kTilePix)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)};
-#define GS_FWD(P)                                                                            \
-  hipLaunchKernelGGL(k_raster_fwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, order, \
-                     W, H, tiles_x, T, out_rgb, out_T, last_ids)
+#define GS_FWD(P, D)                                                                           \
+  hipLaunchKernelGGL((k_raster_fwd<P, D>), grid, dim3(kTilePix / P), 0, s, screen, ids, toff,  \
+                     order, W, H, tiles_x, T, background, out_rgb, out_T, out_depth, last_ids)
   ProfScope prof("k_raster_fwd", s);
-  if (ppt == 4) GS_FWD(4); else if (ppt == 2) GS_FWD(2); else GS_FWD(1);
+  if (out_depth) {
+    if (ppt == 4) GS_FWD(4, true); else if (ppt == 2) GS_FWD(2, true); else GS_FWD(1, true);
+  } else {
+    if (ppt == 4) GS_FWD(4, false); else if (ppt == 2) GS_FWD(2, false); else GS_FWD(1, false);
+  }
 #undef GS_FWD
   return hipGetLastError();
 }
 
 hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uint32_t* ids,
-                             const int64_t* toff, const uint32_t* order, const float* out_T,
-                             const int32_t* last_ids, const float* v_rgb, const float* v_T,
-                             float* v_screen, hipStream_t s) {
+                             const int64_t* toff, const uint32_t* order, const float* background,
+                             const float* out_T, const int32_t* last_ids, const float* v_rgb,
+                             const float* v_T, const float* v_depth, float* v_screen,
+                             float* v_background, hipStream_t s) {
   static const int ppt = ppt_from_env("GS_RASTER_PPT_BWD", kBwdPPT);
   const int tiles_x = (W + kTile - 1) / kTile, tiles_y = (H + kTile - 1) / kTile;
   const int T = tiles_x * tiles_y;
@@ -477,11 +546,16 @@ hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uin
   if (blocks == 0) return hipSuccess;
   if (!fits_dispatch(uint64_t(blocks), kTilePix)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)};
-#define GS_BWD(P)                                                                             \
-  hipLaunchKernelGGL(k_raster_bwd<P>, grid, dim3(kTilePix / P), 0, s, screen, ids, toff, order, \
-                     W, H, tiles_x, T, out_T, last_ids, v_rgb, v_T, v_screen)
+#define GS_BWD(P, D)                                                                           \
+  hipLaunchKernelGGL((k_raster_bwd<P, D>), grid, dim3(kTilePix / P), 0, s, screen, ids, toff,  \
+                     order, W, H, tiles_x, T, background, out_T, last_ids, v_rgb, v_T, v_depth, \
+                     v_screen, v_background)
   ProfScope prof("k_raster_bwd", s);
-  if (ppt == 4) GS_BWD(4); else if (ppt == 2) GS_BWD(2); else GS_BWD(1);
+  if (v_depth) {
+    if (ppt == 4) GS_BWD(4, true); else if (ppt == 2) GS_BWD(2, true); else GS_BWD(1, true);
+  } else {
+    if (ppt == 4) GS_BWD(4, false); else if (ppt == 2) GS_BWD(2, false); else GS_BWD(1, false);
+  }
 #undef GS_BWD
   return hipGetLastError();
 }

@@ -183,37 +183,51 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz,
  * that entry; otherwise rgb += colour*alpha*T and T *= 1-alpha.
  * tile_order (nullable) is the order in which tiles are launched (from
  * gs_intersect; null = tile id order); it changes no result.
+ * background (nullable) is one RGB colour per camera, background[C][3],
+ * blended in as rgb + T_final * background[c] (null = no blend).
  * Outputs (all C x H x W, row-major): out_rgb[C][H][W][3] (premultiplied,
- * no background), out_T[C][H][W] final transmittance, last_ids[C][H][W]
- * local index (within the tile's list) of the last composited entry, -1 if
- * none. Errors: GS_E_INVALID.
+ * plus the background term), out_T[C][H][W] final transmittance,
+ * out_depth[C][H][W] (nullable) the depth composited like a colour
+ * channel, sum of z*alpha*T with z the row's depth (not normalised),
+ * last_ids[C][H][W] local index (within the tile's list) of the last
+ * composited entry, -1 if none. [BWD] sections 2-3 name the depth image
+ * among the rendered outputs and the background blend among the image
+ * corrections. Errors: GS_E_INVALID.
  * ------------------------------------------------------------------- */
 int gs_rasterize_fwd(void* stream, int32_t C, int32_t W, int32_t H,
                      const float* screen, const uint32_t* flatten_ids,
                      const int64_t* tile_offsets, const uint32_t* tile_order,
-                     float* out_rgb, float* out_T, int32_t* last_ids);
+                     const float* background, float* out_rgb, float* out_T,
+                     float* out_depth, int32_t* last_ids);
 
 /* ---------------------------------------------------------------------
  * gs_rasterize_bwd -- gradient of L = <v_rgb, out_rgb> + <v_T, out_T>
- * with respect to every screen row. [BWD] section 4
+ * + <v_depth, out_depth> with respect to every screen row. [BWD] section 4
  * (rasterize_to_pixels_3dgs_bwd: the pixel gradient is split over the
  * Gaussians on that pixel in proportion to their alpha contribution, in
- * blend order, and summed with atomics into the fp32 screen gradients).
+ * blend order, and summed with atomics into the fp32 screen gradients)
+ * and sections 2-3 (the depth image's gradient v_render_depth; the
+ * background hook adds its transmittance gradient into v_render_Ts).
  *
  * Walks each pixel's entries back to front from last_ids, recovering the
  * transmittance before entry i as T_{i+1} / (1 - alpha_i). Writes
  * v_screen[nnz][10] fp32 (zeroed by this call first; the depth column is
- * 0). v_T may be null (taken as zero). Entries whose alpha hit the 0.99
- * clamp get no opacity or position/conic gradient. tile_order as for
+ * the depth image's gradient, 0 when v_depth is null). v_T and v_depth may
+ * be null (taken as zero). background: the forward's (nullable); with it,
+ * v_T is taken as v_T + v_rgb . background[c]. v_background[C][3]
+ * (nullable) receives dL/dbackground = sum over each camera's pixels of
+ * v_rgb * out_T (overwritten). Entries whose alpha hit the 0.99 clamp get
+ * no opacity or position/conic gradient. tile_order as for
  * gs_rasterize_fwd. Summation order is not fixed (float atomics), so
  * results vary in the last bits run to run.
  * ------------------------------------------------------------------- */
 int gs_rasterize_bwd(void* stream, int32_t C, int32_t W, int32_t H,
                      int64_t nnz, const float* screen,
                      const uint32_t* flatten_ids, const int64_t* tile_offsets,
-                     const uint32_t* tile_order, const float* out_T,
-                     const int32_t* last_ids, const float* v_rgb,
-                     const float* v_T, float* v_screen);
+                     const uint32_t* tile_order, const float* background,
+                     const float* out_T, const int32_t* last_ids,
+                     const float* v_rgb, const float* v_T, const float* v_depth,
+                     float* v_screen, float* v_background);
 
 /* ---------------------------------------------------------------------
  * gs_project_bwd -- screen-row gradients to parameter gradients.
@@ -225,7 +239,8 @@ int gs_rasterize_bwd(void* stream, int32_t C, int32_t W, int32_t H,
  * v_screen[slot] (slot from wg_scan and the mask, as gs_project assigned
  * it) and applies the exact chain rule of the projection: means (camera
  * transform, the Jacobian's dependence on the camera-space point and the
- * SH view direction), raw quaternions (through normalisation), log-scales,
+ * SH view direction, and the row's depth z, whose gradient is the depth
+ * column of v_screen), raw quaternions (through normalisation), log-scales,
  * opacity logits and SH coefficients (zero where the colour clamp at 0 is
  * active). Nothing flows through the radius, box or visibility test.
  * Outputs v_means[N][3], v_quats[N][4], v_log_scales[N][3],

@@ -248,7 +248,7 @@ def raster_tiles(o: OracleScene, tiles, sc, with_bwd=False):
             last[c, ii, jj] = -1
             continue
         Cc, Tt, ll, _, rec = oraster._walk_tile(rows[ids], jj + 0.5, ii + 0.5, record=True)
-        rgb[c, ii, jj] = Cc
+        rgb[c, ii, jj] = Cc[:, :3]
         Tm[c, ii, jj] = Tt
         last[c, ii, jj] = ll
         a = rec["alpha"]

@@ -79,7 +79,8 @@ def test_invalid_arguments_need_no_gpu(lib):
     st = lib.gs_project(None, 10, 1, 10, 10, 4, *([None] * 7), None, None, None, None, None, 0,
                         None, 0, ctypes.byref(nnz), cam)
     assert st == gsd.GS_E_INVALID
-    assert lib.gs_rasterize_fwd(None, 0, 10, 10, None, None, None, None, None, None, None) == \
+    assert lib.gs_rasterize_fwd(None, 0, 10, 10, None, None, None, None, None, None, None, None,
+                                None) == \
         gsd.GS_E_INVALID
     n_is = ctypes.c_int64(0)
     need = ctypes.c_uint64(0)

@@ -144,7 +144,7 @@ def test_raster_fwd_stage(lib, name, ordered):
     last = torch.empty(C, H, W, dtype=torch.int32, device="cuda")
     order = P.to_dev(launch_order(isect.tile_offsets)) if ordered else None
     st = gsd.gs_rasterize_fwd(C, W, H, P.to_dev(rows32), P.to_dev(P.u32_as_i32(isect.flatten_ids)),
-                              P.to_dev(isect.tile_offsets), order, rgb, T, last)
+                              P.to_dev(isect.tile_offsets), order, None, rgb, T, None, last)
     torch.cuda.synchronize()
     assert st == 0
     frag = P.fragile_pixels(rows32, isect.flatten_ids, isect.tile_offsets, C, W, H)
@@ -177,10 +177,10 @@ def test_raster_bwd_stage(lib, name, ordered):
     T = torch.empty(C, H, W, device="cuda")
     last = torch.empty(C, H, W, dtype=torch.int32, device="cuda")
     order = P.to_dev(launch_order(isect.tile_offsets)) if ordered else None
-    assert gsd.gs_rasterize_fwd(C, W, H, d_rows, d_ids, d_toff, order, rgb, T, last) == 0
+    assert gsd.gs_rasterize_fwd(C, W, H, d_rows, d_ids, d_toff, order, None, rgb, T, None, last) == 0
     v_screen = torch.empty(proj.nnz, 10, device="cuda")
-    st = gsd.gs_rasterize_bwd(C, W, H, proj.nnz, d_rows, d_ids, d_toff, order, T, last,
-                              P.to_dev(sc["v_rgb"]), P.to_dev(sc["v_T"]), v_screen)
+    st = gsd.gs_rasterize_bwd(C, W, H, proj.nnz, d_rows, d_ids, d_toff, order, None, T, last,
+                              P.to_dev(sc["v_rgb"]), P.to_dev(sc["v_T"]), None, v_screen, None)
     torch.cuda.synchronize()
     assert st == 0
     vg = v_screen.cpu().numpy()
