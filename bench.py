@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
+    ap.add_argument("--mode", choices=("train", "render"), default="train",
+                    help="train: the whole fwd+bwd step (the headline metric); render: "
+                         "projection, intersection and forward only, in frames/s")
     return ap.parse_args()
 
 
@@ -111,7 +114,7 @@ def raster_work(last_ids, W, H):
     return walked, comp
 
 
-def cpu_baseline(sc, spec, seconds, max_isect_sample=20_000_000):
+def cpu_baseline(sc, spec, seconds, max_isect_sample=20_000_000, render_only=False):
     """The fp64 oracle on a bounded sample of the same scene, single-threaded:
     projection on the whole scene; intersection/sort on the whole scene, or
     on a seeded subset of pairs scaled to all entries when the scene has
@@ -175,27 +178,29 @@ def cpu_baseline(sc, spec, seconds, max_isect_sample=20_000_000):
                 toff[int(t) + 1:] = lst.size
             t0 = time.perf_counter()
             oracle.rasterize_fwd(proj.screen, ids, toff, C, W, H, tiles=[int(t)])
-            oracle.rasterize_bwd(proj.screen, ids, toff, C, W, H, sc["v_rgb"], sc["v_T"],
-                                 tiles=[int(t)])
+            if not render_only:
+                oracle.rasterize_bwd(proj.screen, ids, toff, C, W, H, sc["v_rgb"], sc["v_T"],
+                                     tiles=[int(t)])
             t_raster += time.perf_counter() - t0
             done += 1
             if t_raster > seconds:
                 break
         t_raster = t_raster * n_tiles / done
         # projection backward on a seeded sample of visible pairs, scaled
-        n_pb = min(proj.nnz, 100_000)
+        n_pb = 0 if render_only else min(proj.nnz, 100_000)
         pick = np.sort(rng.choice(proj.nnz, n_pb, replace=False)) if n_pb else np.zeros(0, int)
         sub = Projection(**{**proj.__dict__, "cam": proj.cam[pick],
                              "gauss": proj.gauss[pick]})
         t0 = time.perf_counter()
         oracle.project_bwd(sc, sub, np.zeros((n_pb, 10)))
-        t_pbwd = (time.perf_counter() - t0) * proj.nnz / max(n_pb, 1)
+        t_pbwd = (time.perf_counter() - t0) * proj.nnz / max(n_pb, 1) if n_pb else 0.0
     est = t_proj + t_isect + t_raster + t_pbwd
-    return dict(value=1.0 / est, unit="steps/s", cores=1, kind="oracle",
+    return dict(value=1.0 / est, unit="frames/s" if render_only else "steps/s", cores=1,
+                kind="oracle",
                 sample=(f"fp64 NumPy oracle, one thread: projection on the whole scene "
                         f"({t_proj:.1f} s); intersect + stable sort {isect_note} ({t_isect:.1f} s); "
                         f"projection backward on {n_pb} of {proj.nnz} seeded random visible pairs "
-                        f"scaled to all ({t_pbwd:.1f} s); raster fwd+bwd on {done} of {n_tiles} "
+                        f"scaled to all ({t_pbwd:.1f} s); raster {'fwd' if render_only else 'fwd+bwd'} on {done} of {n_tiles} "
                         f"seeded random tiles scaled to all tiles ({t_raster:.0f} s); "
                         f"est. {est:.0f} s/step"))
 
@@ -232,7 +237,9 @@ def main():
     v_T = torch.from_numpy(sc["v_T"]).cuda()
     r = gsd.Rasterizer("cuda")
     stream = torch.cuda.current_stream()
-    stages = ["project", "intersect", "raster_fwd", "raster_bwd", "project_bwd"]
+    render = a.mode == "render"
+    stages = ["project", "intersect", "raster_fwd"] + ([] if render else ["raster_bwd",
+                                                                          "project_bwd"])
 
     def step(ev=None):
         def mark(i):
@@ -245,10 +252,11 @@ def main():
         mark(2)
         rgb, T, last = r.rasterize_fwd(s, p, it)
         mark(3)
-        vs = r.rasterize_bwd(s, p, it, T, last, v_rgb, v_T)
-        mark(4)
-        r.project_bwd(s, p, vs)
-        mark(5)
+        if not render:
+            vs = r.rasterize_bwd(s, p, it, T, last, v_rgb, v_T)
+            mark(4)
+            r.project_bwd(s, p, vs)
+            mark(5)
         return p, it, last
 
     for _ in range(a.warmup):
@@ -259,7 +267,8 @@ def main():
     n_bd = 3
     gsd.profile_reset()
     gsd.profile_enable(None)
-    bd_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_bd)]
+    bd_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+             for _ in range(n_bd)]
     for k in range(n_bd):
         step(bd_ev[k])
     torch.cuda.synchronize()
@@ -321,9 +330,10 @@ def main():
             roof["traffic"] = ent["hbm_bytes_per_launch"]
 
     out = {
-        "metric": "fwd+bwd rasterizer steps/s and M visible pairs/s at 1 MI355X; % HBM peak",
+        "metric": ("render frames/s (projection, intersection, forward) at 1 MI355X" if render else
+                   "fwd+bwd rasterizer steps/s and M visible pairs/s at 1 MI355X; % HBM peak"),
         "value": steps_s,
-        "unit": "steps/s",
+        "unit": "frames/s" if render else "steps/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
@@ -333,7 +343,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": spec.name, "N": spec.n, "sh_degree": spec.sh_degree,
+        "config": {"workload": spec.name + ("-render" if render else ""), "N": spec.n,
+                   "sh_degree": spec.sh_degree,
                    "cameras": spec.n_cams, "width": spec.width, "height": spec.height,
                    "focal": spec.focal, "seed": spec.seed},
         "m_visible_pairs_per_s": nnz * steps_s / 1e6,
@@ -361,8 +372,10 @@ def main():
     if sort_ms > 0:
         hb["sort (all radix kernels)"] = sort_bytes / (sort_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     out["hbm_frac_by_kernel"] = hb
+    if render:
+        out["ms_per_frame"] = out.pop("ms_per_step")
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(sc, spec, a.cpu_sample_seconds)
+        out["cpu_baseline"] = cpu_baseline(sc, spec, a.cpu_sample_seconds, render_only=render)
     print(json.dumps(out))
 
 
