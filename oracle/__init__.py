@@ -15,7 +15,8 @@ Splatting trainer:
 * [BWD] "How Spirula Studio's backward pass sends image gradients back to
   every Gaussian" -- sections 2-3 (the per-pixel output gradients of the
   colour, depth and transmittance images; the background hook), 4
-  (rasterize backward) and 5 (projection backward).
+  (rasterize backward), 5 (projection backward) and 6 (the fused
+  projection backward + Adam).
 * [PROFILE] "Performance profiling guide: reading every step with
   SS_PROFILE=1" (kernel names only).
 * [GSPLAT] a deployment blog about a CUDA splatting library (C API over
@@ -44,9 +45,11 @@ from .intersect import intersect, tile_rects_from_aabb16
 from .raster import rasterize_fwd, rasterize_bwd, background_grad
 from .project_bwd import project_bwd
 from .pipeline import render, loss_and_grads
+from .adam import adam_step, LR_KEYS
 
 __all__ = [
     "sh_basis", "sh_basis_grad", "num_sh", "project", "project_camera",
     "quat_to_rotmat", "intersect", "tile_rects_from_aabb16", "rasterize_fwd",
     "rasterize_bwd", "background_grad", "project_bwd", "render", "loss_and_grads",
+    "adam_step", "LR_KEYS",
 ]
