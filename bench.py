@@ -40,7 +40,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 KERNELS = ["k_project_mask", "k_scan", "k_cam_offsets", "k_project_compact", "k_fill_u32",
            "k_isect_prep", "k_radix_count", "k_radix_scatter", "k_isect_emit",
-           "k_tile_ranges", "k_tile_order_keys", "k_raster_fwd", "k_raster_bwd", "k_project_bwd"]
+           "k_tile_ranges", "k_tile_order_keys", "k_raster_fwd", "k_raster_bwd", "k_project_bwd",
+           "k_project_bwd_adam"]
 KERNEL_SOURCE = {"k_raster_fwd": "gs_raster.hip", "k_raster_bwd": "gs_raster.hip",
                  "k_project_mask": "gs_project.hip", "k_project_compact": "gs_project.hip",
                  "k_project_bwd": "gs_project_bwd.hip", "k_radix_scatter": "gs_sort.hip",
@@ -64,6 +65,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
+    ap.add_argument("--adam", action="store_true",
+                    help="train mode: fold the projection backward into one Adam step "
+                         "(gs_project_bwd_adam) instead of writing gradients")
     ap.add_argument("--mode", choices=("train", "render"), default="train",
                     help="train: the whole fwd+bwd step (the headline metric); render: "
                          "projection, intersection and forward only, in frames/s")
@@ -91,6 +95,8 @@ def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes):
         return pairs / 8 + 4 * pairs / 128 + (44 + 12 * K) * V + 48 * nnz
     if kernel == "k_project_bwd":    # params + SH read and grads written per Gaussian
         return (44 + 12 * K) * (V + N) + 40 * nnz + pairs / 8 + 4 * pairs / 128
+    if kernel == "k_project_bwd_adam":  # params, first and second moments read and written
+        return 6 * (44 + 12 * K) * N + 40 * nnz + pairs / 8 + 4 * pairs / 128
     if kernel == "k_radix_scatter":  # mean over the step's passes: 8 B read + 8 B written per key
         tiles = C * ((spec.width + 15) // 16) * ((spec.height + 15) // 16)
         return 16 * (4 * nnz + tile_passes * n_isects + 2 * tiles) / (4 + tile_passes + 2)
@@ -238,6 +244,7 @@ def main():
     r = gsd.Rasterizer("cuda")
     stream = torch.cuda.current_stream()
     render = a.mode == "render"
+    adam = gsd.AdamState.zeros_like(s) if (a.adam and not render) else None
     stages = ["project", "intersect", "raster_fwd"] + ([] if render else ["raster_bwd",
                                                                           "project_bwd"])
 
@@ -255,7 +262,10 @@ def main():
         if not render:
             vs = r.rasterize_bwd(s, p, it, T, last, v_rgb, v_T)
             mark(4)
-            r.project_bwd(s, p, vs)
+            if adam is not None:
+                r.project_bwd_adam(s, p, vs, adam)
+            else:
+                r.project_bwd(s, p, vs)
             mark(5)
         return p, it, last
 
@@ -343,7 +353,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": spec.name + ("-render" if render else ""), "N": spec.n,
+        "config": {"workload": spec.name + ("-render" if render else "-adam" if adam else ""),
+                   "N": spec.n,
                    "sh_degree": spec.sh_degree,
                    "cameras": spec.n_cams, "width": spec.width, "height": spec.height,
                    "focal": spec.focal, "seed": spec.seed},

@@ -25,7 +25,8 @@ ROW = 10
 
 EXPORTS = ("gs_status_str", "gs_version", "gs_pad_n", "gs_project_workspace_bytes",
            "gs_intersect_workspace_bytes", "gs_project", "gs_intersect", "gs_rasterize_fwd",
-           "gs_rasterize_bwd", "gs_project_bwd", "gs_profile_enable", "gs_profile_disable",
+           "gs_rasterize_bwd", "gs_project_bwd", "gs_project_bwd_adam", "gs_profile_enable",
+           "gs_profile_disable",
            "gs_profile_reset", "gs_profile_query")
 
 _lib = None
@@ -70,6 +71,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gs_rasterize_fwd.argtypes = [c_vp, c_i32, c_i32, c_i32] + [c_vp] * 9
     lib.gs_rasterize_bwd.restype = ctypes.c_int
     lib.gs_rasterize_bwd.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i64] + [c_vp] * 12
+    lib.gs_project_bwd_adam.restype = ctypes.c_int
+    lib.gs_project_bwd_adam.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
+        [c_vp] * 3 + [ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), ctypes.POINTER(ctypes.c_float),
+                      ctypes.c_float, ctypes.c_float, ctypes.c_float, c_i32]
     lib.gs_project_bwd.restype = ctypes.c_int
     lib.gs_project_bwd.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
         [c_vp] * 3 + [c_vp] * 5 + [c_i32]
@@ -190,6 +195,22 @@ def gs_project_bwd(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logi
                                  int(accumulate))
 
 
+def gs_project_bwd_adam(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, sh,
+                        viewmats, Ks, mask, wg_scan, v_screen, adam_m, adam_v, lr, beta1, beta2,
+                        eps, step, stream=None):
+    """adam_m / adam_v: five device tensors each (means, quats, log_scales,
+    opacity_logits, sh); lr: six floats (means, quats, log_scales,
+    opacity_logits, SH coefficient 0, higher SH)."""
+    m = (c_vp * 5)(*[_ptr(t) for t in adam_m])
+    v = (c_vp * 5)(*[_ptr(t) for t in adam_v])
+    lrs = (ctypes.c_float * 6)(*[float(x) for x in lr])
+    return load().gs_project_bwd_adam(_stream(stream), N, C, W, H, sh_degree, _ptr(means),
+                                      _ptr(quats), _ptr(log_scales), _ptr(opacity_logits),
+                                      _ptr(sh), _ptr(viewmats), _ptr(Ks), _ptr(mask),
+                                      _ptr(wg_scan), _ptr(v_screen), m, v, lrs, beta1, beta2,
+                                      eps, step)
+
+
 # ---------------------------------------------------------------------------
 # Buffer-managing front end.
 
@@ -214,6 +235,26 @@ class Scene:
         f = lambda k: torch.from_numpy(sc[k]).to(device=device, dtype=torch.float32).contiguous()
         return Scene(sc["N"], sc["C"], sc["W"], sc["H"], sc["sh_degree"], f("means"), f("quats"),
                      f("log_scales"), f("opacity_logits"), f("sh"), f("viewmats"), f("Ks"))
+
+
+@dataclass
+class AdamState:
+    """Adam moments for the five parameter tensors of a Scene, learning
+    rates of the six groups (means, quats, log_scales, opacity_logits, SH
+    DC, higher SH) and the step count."""
+    m: list
+    v: list
+    lr: tuple
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-15
+    step: int = 0
+
+    @staticmethod
+    def zeros_like(s: "Scene", lr=(1.6e-4, 1e-3, 5e-3, 5e-2, 2.5e-3, 1.25e-4), **kw) -> "AdamState":
+        ps = (s.means, s.quats, s.log_scales, s.opacity_logits, s.sh)
+        return AdamState([torch.zeros_like(t) for t in ps], [torch.zeros_like(t) for t in ps],
+                         tuple(lr), **kw)
 
 
 @dataclass
@@ -360,6 +401,17 @@ class Rasterizer:
                                    grads["v_log_scales"], grads["v_opacity_logits"],
                                    grads["v_sh"], 1 if accumulate else 0), "gs_project_bwd")
         return grads
+
+    def project_bwd_adam(self, s: Scene, p: Projected, v_screen, adam: "AdamState"):
+        """The projection backward fused with one Adam step: updates the
+        scene's parameters and ``adam``'s moments in place; writes no
+        gradient."""
+        adam.step += 1
+        self._check(gs_project_bwd_adam(s.N, s.C, s.W, s.H, s.sh_degree, s.means, s.quats,
+                                        s.log_scales, s.opacity_logits, s.sh, s.viewmats, s.Ks,
+                                        p.mask, p.wg_scan, v_screen, adam.m, adam.v, adam.lr,
+                                        adam.beta1, adam.beta2, adam.eps, adam.step),
+                    "gs_project_bwd_adam")
 
     def step(self, s: Scene, v_rgb, v_T=None, v_depth=None, background=None):
         """One whole pass: project, intersect, raster forward and backward,

@@ -7,6 +7,7 @@
 // queues any kernel whose size depends on them, and returns the required
 // size instead of writing past an allocation. Kernels queued before the
 // check (the compaction) clamp their writes to the capacity themselves.
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 
@@ -180,6 +181,20 @@ int check_device_error(const int* err, hipStream_t s) {
 
 bool valid_image(int32_t C, int32_t W, int32_t H) {
   return C >= 1 && W >= 1 && H >= 1 && W <= 65535 && H <= 65535;
+}
+
+ProjectArgs project_args(int64_t N, int32_t C, int32_t W, int32_t H, int32_t deg,
+                         const float* means, const float* quats, const float* log_scales,
+                         const float* opacity_logits, const float* sh, const float* viewmats,
+                         const float* Ks) {
+  ProjectArgs a{};
+  a.N = N, a.N_pad = gs_pad_n(N), a.C = C, a.W = W, a.H = H, a.deg = deg;
+  a.means = means, a.quats = quats, a.log_scales = log_scales, a.opacity_logits = opacity_logits;
+  a.sh = sh, a.viewmats = viewmats, a.Ks = Ks;
+  a.norm = sh_norm_table();
+  a.qsx = float(kQ16) / float(W);
+  a.qsy = float(kQ16) / float(H);
+  return a;
 }
 
 }  // namespace
@@ -394,15 +409,48 @@ int gs_project_bwd(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int
       !wg_scan || !v_means || !v_quats || !v_log_scales || !v_opacity_logits || !v_sh)
     return GS_E_INVALID;
   if (!aligned(quats, 16) || !aligned(v_quats, 16) || !aligned(v_screen, 8)) return GS_E_INVALID;
-  ProjectArgs a{};
-  a.N = N, a.N_pad = gs_pad_n(N), a.C = C, a.W = W, a.H = H, a.deg = sh_degree;
-  a.means = means, a.quats = quats, a.log_scales = log_scales, a.opacity_logits = opacity_logits;
-  a.sh = sh, a.viewmats = viewmats, a.Ks = Ks;
-  a.norm = sh_norm_table();
-  a.qsx = float(kQ16) / float(W);
-  a.qsy = float(kQ16) / float(H);
+  const ProjectArgs a = project_args(N, C, W, H, sh_degree, means, quats, log_scales,
+                                     opacity_logits, sh, viewmats, Ks);
   return hip_status(launch_project_bwd(a, mask, wg_scan, v_screen, v_means, v_quats, v_log_scales,
-                                       v_opacity_logits, v_sh, accumulate,
+                                       v_opacity_logits, v_sh, accumulate, nullptr,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int gs_project_bwd_adam(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
+                        int32_t sh_degree, float* means, float* quats, float* log_scales,
+                        float* opacity_logits, float* sh, const float* viewmats, const float* Ks,
+                        const uint64_t* mask, const uint32_t* wg_scan, const float* v_screen,
+                        float* const* adam_m, float* const* adam_v, const float* lr, float beta1,
+                        float beta2, float eps, int32_t step) {
+  if (N < 0 || !valid_image(C, W, H) || sh_degree < 0 || sh_degree > 3) return GS_E_INVALID;
+  if (!adam_m || !adam_v || !lr || step < 1 || !(beta1 >= 0.f && beta1 < 1.f) ||
+      !(beta2 >= 0.f && beta2 < 1.f) || !(eps > 0.f))
+    return GS_E_INVALID;
+  if (N == 0) return GS_OK;
+  if (!means || !quats || !log_scales || !opacity_logits || !sh || !viewmats || !Ks || !mask ||
+      !wg_scan)
+    return GS_E_INVALID;
+  for (int i = 0; i < 5; ++i)
+    if (!adam_m[i] || !adam_v[i]) return GS_E_INVALID;
+  if (!aligned(quats, 16) || !aligned(v_screen, 8)) return GS_E_INVALID;
+  const ProjectArgs a = project_args(N, C, W, H, sh_degree, means, quats, log_scales,
+                                     opacity_logits, sh, viewmats, Ks);
+  AdamArgs ad{};
+  float* const params[5] = {means, quats, log_scales, opacity_logits, sh};
+  for (int i = 0; i < 5; ++i) {
+    ad.p[i] = params[i];
+    ad.m[i] = adam_m[i];
+    ad.v[i] = adam_v[i];
+  }
+  for (int i = 0; i < 6; ++i) ad.lr[i] = lr[i];
+  ad.beta1 = beta1;
+  ad.beta2 = beta2;
+  ad.eps = eps;
+  // bias corrections in double, then rounded once
+  ad.inv_bc1 = float(1.0 / (1.0 - std::pow(double(beta1), double(step))));
+  ad.inv_bc2 = float(1.0 / (1.0 - std::pow(double(beta2), double(step))));
+  return hip_status(launch_project_bwd(a, mask, wg_scan, v_screen, nullptr, nullptr, nullptr,
+                                       nullptr, nullptr, 0, &ad,
                                        static_cast<hipStream_t>(stream)));
 }
 

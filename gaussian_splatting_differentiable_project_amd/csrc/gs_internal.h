@@ -47,10 +47,25 @@ hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, uint32_t* w
 hipError_t launch_project_compact(const ProjectArgs& a, const uint64_t* mask,
                                   const uint32_t* wg_scan, float* screen, uint32_t* aabb16,
                                   hipStream_t s);
+// Adam state for the fused projection backward: parameter, first and
+// second moment pointers for means, quats, log_scales, opacity_logits, sh
+// (updated in place), learning rates of the six groups (means, quats,
+// log_scales, opacity_logits, SH coefficient 0, higher SH), betas, eps and
+// the inverse bias corrections 1 / (1 - beta^t).
+struct AdamArgs {
+  float* p[5];
+  float* m[5];
+  float* v[5];
+  float lr[6];
+  float beta1, beta2, eps, inv_bc1, inv_bc2;
+};
+
+// adam == nullptr: write (or add) the gradients; else fold them into one
+// Adam step and write no gradient (the v_* pointers are then unused).
 hipError_t launch_project_bwd(const ProjectArgs& a, const uint64_t* mask,
                               const uint32_t* wg_scan, const float* v_screen, float* v_means,
                               float* v_quats, float* v_log_scales, float* v_opacity_logits,
-                              float* v_sh, int accumulate, hipStream_t s);
+                              float* v_sh, int accumulate, const AdamArgs* adam, hipStream_t s);
 
 // Exclusive scan of n uint32 values (optionally gathered through idx) into
 // uint32 or uint64 outputs; the total is written to *total (device).

@@ -6,6 +6,10 @@
 // all in fp32. [BWD] section 6: only the first sub-batch zeroes the
 // accumulators (our `accumulate` flag).
 //
+// [BWD] section 6 (fused projection backward + optimizer): the fused
+// variant folds each Gaussian's gradient straight into an Adam step of its
+// parameters and moments, so no gradient buffer is written.
+//
 // gfx950 mapping: the same Gaussian-major, 128-lane geometry as the
 // projection passes. A lane owns one Gaussian, walks the cameras whose
 // mask bit is set, recovers the pair's slot from the scan and the mask
@@ -18,12 +22,43 @@ namespace gs {
 
 namespace {
 
-template <int DEG>
+// One Adam step of n consecutive parameter elements (bias corrections
+// precomputed). The three arrays never overlap, and the restrict-qualified
+// parameters say so: every load is issued before the first store, instead
+// of one load-update-store round trip per element. Elements below
+// n_first take lr_first, the others lr_rest.
+template <int n>
+__device__ __forceinline__ void adam_run(float* __restrict__ p, float* __restrict__ m,
+                                         float* __restrict__ v, const float* g, int n_first,
+                                         float lr_first, float lr_rest, const AdamArgs& ad) {
+  float pp[n], mm[n], vv[n];
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    pp[i] = p[i];
+    mm[i] = m[i];
+    vv[i] = v[i];
+  }
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    mm[i] = fmaf(ad.beta1, mm[i], (1.f - ad.beta1) * g[i]);
+    vv[i] = fmaf(ad.beta2, vv[i], (1.f - ad.beta2) * g[i] * g[i]);
+    const float lr = i < n_first ? lr_first : lr_rest;
+    pp[i] -= lr * (mm[i] * ad.inv_bc1) / (sqrtf(vv[i] * ad.inv_bc2) + ad.eps);
+  }
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    p[i] = pp[i];
+    m[i] = mm[i];
+    v[i] = vv[i];
+  }
+}
+
+template <int DEG, bool ADAM>
 __global__ __launch_bounds__(kMaskGroup) void k_project_bwd(
     ProjectArgs a, const uint64_t* __restrict__ mask, const uint32_t* __restrict__ wg_scan,
     const float* __restrict__ v_screen, float* __restrict__ v_means, float* __restrict__ v_quats,
     float* __restrict__ v_log_scales, float* __restrict__ v_opacity_logits,
-    float* __restrict__ v_sh, int accumulate) {
+    float* __restrict__ v_sh, int accumulate, AdamArgs ad) {
   constexpr int K = (DEG + 1) * (DEG + 1);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t g = int64_t(blockIdx.x) * kMaskGroup + tid;
@@ -189,7 +224,25 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_bwd(
     gq[3] = (vz - z * dot) * iqn;
   }
 
-  if (accumulate) {
+  if (ADAM) {
+    // every element steps, a zero gradient included (as Adam would on
+    // gradient buffers); each lane touches only its own Gaussian, so the
+    // in-place parameter update cannot race with another lane's reads
+    adam_run<3>(ad.p[0] + 3 * g, ad.m[0] + 3 * g, ad.v[0] + 3 * g, gmu, 3, ad.lr[0], ad.lr[0], ad);
+    adam_run<4>(ad.p[1] + 4 * g, ad.m[1] + 4 * g, ad.v[1] + 4 * g, gq, 4, ad.lr[1], ad.lr[1], ad);
+    adam_run<3>(ad.p[2] + 3 * g, ad.m[2] + 3 * g, ad.v[2] + 3 * g, gls, 3, ad.lr[2], ad.lr[2], ad);
+    adam_run<1>(ad.p[3] + g, ad.m[3] + g, ad.v[3] + g, &glogit, 1, ad.lr[3], ad.lr[3], ad);
+    // SH in runs of at most 12 values that divide the 3K values exactly
+    // (3, 12, 9, 12 for degrees 0-3), to bound the registers held at once;
+    // coefficient 0 (the first 3 values) is DC
+    constexpr int kRun = (K * 3) % 12 == 0 ? 12 : ((K * 3) % 9 == 0 ? 9 : K * 3);
+    static_assert((K * 3) % kRun == 0, "runs must tile the SH values");
+    const int64_t e0 = g * (K * 3);
+#pragma unroll
+    for (int r = 0; r < K * 3; r += kRun)
+      adam_run<kRun>(ad.p[4] + e0 + r, ad.m[4] + e0 + r, ad.v[4] + e0 + r, gsh + r, r == 0 ? 3 : 0,
+                     ad.lr[4], ad.lr[5], ad);
+  } else if (accumulate) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       v_means[3 * g + j] += gmu[j];
@@ -220,20 +273,30 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_bwd(
 hipError_t launch_project_bwd(const ProjectArgs& a, const uint64_t* mask,
                               const uint32_t* wg_scan, const float* v_screen, float* v_means,
                               float* v_quats, float* v_log_scales, float* v_opacity_logits,
-                              float* v_sh, int accumulate, hipStream_t s) {
+                              float* v_sh, int accumulate, const AdamArgs* adam, hipStream_t s) {
   const int64_t blocks = a.N_pad / kMaskGroup;
   if (blocks == 0) return hipSuccess;
   if (!fits_dispatch(uint64_t(blocks), kMaskGroup)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)}, block{uint32_t(kMaskGroup)};
-#define GS_LAUNCH_PB(D)                                                                      \
-  hipLaunchKernelGGL(k_project_bwd<D>, grid, block, 0, s, a, mask, wg_scan, v_screen, v_means, \
-                     v_quats, v_log_scales, v_opacity_logits, v_sh, accumulate)
-  ProfScope prof("k_project_bwd", s);
-  switch (a.deg) {
-    case 0: GS_LAUNCH_PB(0); break;
-    case 1: GS_LAUNCH_PB(1); break;
-    case 2: GS_LAUNCH_PB(2); break;
-    default: GS_LAUNCH_PB(3); break;
+  const AdamArgs ad = adam ? *adam : AdamArgs{};
+#define GS_LAUNCH_PB(D, A)                                                                    \
+  hipLaunchKernelGGL((k_project_bwd<D, A>), grid, block, 0, s, a, mask, wg_scan, v_screen,      \
+                     v_means, v_quats, v_log_scales, v_opacity_logits, v_sh, accumulate, ad)
+  ProfScope prof(adam ? "k_project_bwd_adam" : "k_project_bwd", s);
+  if (adam) {
+    switch (a.deg) {
+      case 0: GS_LAUNCH_PB(0, true); break;
+      case 1: GS_LAUNCH_PB(1, true); break;
+      case 2: GS_LAUNCH_PB(2, true); break;
+      default: GS_LAUNCH_PB(3, true); break;
+    }
+  } else {
+    switch (a.deg) {
+      case 0: GS_LAUNCH_PB(0, false); break;
+      case 1: GS_LAUNCH_PB(1, false); break;
+      case 2: GS_LAUNCH_PB(2, false); break;
+      default: GS_LAUNCH_PB(3, false); break;
+    }
   }
 #undef GS_LAUNCH_PB
   return hipGetLastError();

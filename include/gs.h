@@ -257,6 +257,36 @@ int gs_project_bwd(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
                    int32_t accumulate);
 
 /* ---------------------------------------------------------------------
+ * gs_project_bwd_adam -- projection backward fused with one Adam step.
+ * [BWD] section 6 (the fused projection backward + optimizer: the
+ * world-space gradients are folded straight into the Adam optimizer and
+ * no fp32 gradient buffer is allocated).
+ *
+ * Computes exactly the gradients gs_project_bwd would write (same inputs,
+ * accumulate = 0) and, instead of writing them, applies one bias-corrected
+ * Adam step to every element of every Gaussian, a zero gradient included:
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2;
+ *   p -= lr * (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps).
+ * means, quats, log_scales, opacity_logits and sh are read for the
+ * backward and then updated in place. adam_m[5] and adam_v[5] (host
+ * arrays of device pointers, in the order means, quats, log_scales,
+ * opacity_logits, sh, each shaped like its parameter) are the moments,
+ * updated in place. lr[6] (host): learning rates of means, quats,
+ * log_scales, opacity_logits, SH coefficient 0 (DC colour) and the higher
+ * SH coefficients. step >= 1 is the step number after this update.
+ * Each Gaussian is touched by one lane only. Errors: GS_E_INVALID (also
+ * for beta outside [0, 1), eps <= 0 or step < 1).
+ * ------------------------------------------------------------------- */
+int gs_project_bwd_adam(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
+                        int32_t sh_degree, float* means, float* quats,
+                        float* log_scales, float* opacity_logits, float* sh,
+                        const float* viewmats, const float* Ks,
+                        const uint64_t* mask, const uint32_t* wg_scan,
+                        const float* v_screen, float* const* adam_m,
+                        float* const* adam_v, const float* lr, float beta1,
+                        float beta2, float eps, int32_t step);
+
+/* ---------------------------------------------------------------------
  * Per-kernel timing (opt-in; a HIP event pair around each launch of a
  * kernel whose name contains `filter`, on the stream it runs on).
  * [PROF] sections 3-4 describe the trainer's own per-kernel GPU timing

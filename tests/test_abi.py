@@ -36,7 +36,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == {"gs_status_str", "gs_version", "gs_pad_n", "gs_project_workspace_bytes",
                           "gs_intersect_workspace_bytes", "gs_project", "gs_intersect",
                           "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd",
-                          "gs_profile_enable", "gs_profile_disable", "gs_profile_reset",
+                          "gs_project_bwd_adam", "gs_profile_enable", "gs_profile_disable",
+                          "gs_profile_reset",
                           "gs_profile_query"}
     for n in names:
         assert hasattr(lib, n), n
@@ -107,3 +108,16 @@ def test_buffer_formulas_reproduce_pages_numbers():
     assert abs(old_mib - g["mask_compaction"]["old_mib"]) < 0.01
     # screen rows and box codes: 40 and 8 bytes per visible pair
     assert gsd.load and _lib.ROW * 4 == 40
+
+
+def test_fused_adam_argument_checks(lib):
+    """Invalid optimizer settings are refused before any GPU work."""
+    m = (ctypes.c_void_p * 5)()
+    lr = (ctypes.c_float * 6)(*([1e-3] * 6))
+    base = [None, 10, 1, 16, 16, 0] + [None] * 10
+    assert lib.gs_project_bwd_adam(*base, m, m, lr, 0.9, 0.999, 1e-8, 0) == gsd.GS_E_INVALID  # step
+    assert lib.gs_project_bwd_adam(*base, m, m, lr, 1.0, 0.999, 1e-8, 1) == gsd.GS_E_INVALID  # beta1
+    assert lib.gs_project_bwd_adam(*base, m, m, lr, 0.9, 0.999, 0.0, 1) == gsd.GS_E_INVALID   # eps
+    assert lib.gs_project_bwd_adam(*base, None, m, lr, 0.9, 0.999, 1e-8, 1) == gsd.GS_E_INVALID
+    # null moments for N = 10 Gaussians
+    assert lib.gs_project_bwd_adam(*base, m, m, lr, 0.9, 0.999, 1e-8, 1) == gsd.GS_E_INVALID
