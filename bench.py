@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--adam", action="store_true",
                     help="train mode: fold the projection backward into one Adam step "
                          "(gs_project_bwd_adam) instead of writing gradients")
+    ap.add_argument("--arena", action="store_true",
+                    help="train mode: carve every per-step buffer from one phase arena "
+                         "(GS_POOL_ALIAS=0 turns the aliasing off)")
     ap.add_argument("--mode", choices=("train", "render"), default="train",
                     help="train: the whole fwd+bwd step (the headline metric); render: "
                          "projection, intersection and forward only, in frames/s")
@@ -245,6 +248,7 @@ def main():
     stream = torch.cuda.current_stream()
     render = a.mode == "render"
     adam = gsd.AdamState.zeros_like(s) if (a.adam and not render) else None
+    arena = gsd.PhaseArena() if (a.arena and not render) else None
     stages = ["project", "intersect", "raster_fwd"] + ([] if render else ["raster_bwd",
                                                                           "project_bwd"])
 
@@ -252,6 +256,12 @@ def main():
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
+        if arena is not None:   # one call: the stage split is not recorded
+            mark(0)
+            out = r.step_arena(s, v_rgb, v_T, arena)
+            for i in range(1, len(stages) + 1):
+                mark(i)
+            return out["proj"], out["isect"], out["last"]
         mark(0)
         p = r.project(s)
         mark(1)
@@ -296,11 +306,13 @@ def main():
     # timed region: events only around the dominant kernel, on its stream
     gsd.profile_enable(dom)
     torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
     t0 = time.perf_counter()
     for _ in range(a.steps):
         p, it, last = step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    peak_mib = torch.cuda.max_memory_allocated() / 2**20
     gsd.profile_disable()
     n_dom, dom_ms_total = gsd.profile_query(dom)
     gsd.profile_reset()
@@ -353,7 +365,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": spec.name + ("-render" if render else "-adam" if adam else ""),
+        "config": {"workload": spec.name + ("-render" if render else "-adam" if adam else
+                                           "-arena" if arena else ""),
                    "N": spec.n,
                    "sh_degree": spec.sh_degree,
                    "cameras": spec.n_cams, "width": spec.width, "height": spec.height,
@@ -366,7 +379,10 @@ def main():
         "kernel_ms_per_step": kernel_ms,
         "dominant_launches_per_step": launches_per_step,
         "roofline": roof,
+        "peak_device_MiB": peak_mib,
     }
+    if arena is not None:
+        out["arena"] = {"alias": arena.alias, "MiB": arena.buf.numel() / 2**20}
     hb = {}
     for kn, ms in kernel_ms.items():
         byt = hbm_bytes(kn, spec, nnz, n_is, V, tile_passes)

@@ -9,6 +9,7 @@ pointers; ``Rasterizer`` adds growth-only buffer management on top
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 
@@ -22,11 +23,14 @@ GS_OK, GS_E_INVALID, GS_E_CAPACITY, GS_E_WORKSPACE, GS_E_OVERFLOW, GS_E_HIP, GS_
 MASK_GROUP = 128
 TILE = 16
 ROW = 10
+ARENA_SLOTS = ("mask", "wg_count", "wg_scan", "project_ws", "screen", "aabb16", "isect_ws",
+               "flatten_ids", "tile_offsets", "tile_order", "out_rgb", "out_T", "last_ids",
+               "v_screen")
 
 EXPORTS = ("gs_status_str", "gs_version", "gs_pad_n", "gs_project_workspace_bytes",
            "gs_intersect_workspace_bytes", "gs_project", "gs_intersect", "gs_rasterize_fwd",
-           "gs_rasterize_bwd", "gs_project_bwd", "gs_project_bwd_adam", "gs_profile_enable",
-           "gs_profile_disable",
+           "gs_rasterize_bwd", "gs_project_bwd", "gs_project_bwd_adam", "gs_arena_plan",
+           "gs_profile_enable", "gs_profile_disable",
            "gs_profile_reset", "gs_profile_query")
 
 _lib = None
@@ -75,6 +79,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gs_project_bwd_adam.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
         [c_vp] * 3 + [ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), ctypes.POINTER(ctypes.c_float),
                       ctypes.c_float, ctypes.c_float, ctypes.c_float, c_i32]
+    lib.gs_arena_plan.restype = ctypes.c_int
+    lib.gs_arena_plan.argtypes = [c_i64, c_i32, c_i32, c_i32, c_i64, c_i64, c_i32, P_u64, P_u64,
+                                  P_u64]
     lib.gs_project_bwd.restype = ctypes.c_int
     lib.gs_project_bwd.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
         [c_vp] * 3 + [c_vp] * 5 + [c_i32]
@@ -195,6 +202,17 @@ def gs_project_bwd(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logi
                                  int(accumulate))
 
 
+def gs_arena_plan(N, C, W, H, nnz, n_isects, alias=True):
+    """(status, {slot: (offset, bytes)}, arena_bytes)."""
+    n = len(ARENA_SLOTS)
+    off = (ctypes.c_uint64 * n)()
+    sz = (ctypes.c_uint64 * n)()
+    tot = ctypes.c_uint64(0)
+    st = load().gs_arena_plan(N, C, W, H, nnz, n_isects, 1 if alias else 0, off, sz,
+                              ctypes.byref(tot))
+    return st, {k: (off[i], sz[i]) for i, k in enumerate(ARENA_SLOTS)}, tot.value
+
+
 def gs_project_bwd_adam(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, sh,
                         viewmats, Ks, mask, wg_scan, v_screen, adam_m, adam_v, lr, beta1, beta2,
                         eps, step, stream=None):
@@ -284,6 +302,49 @@ def _grow(buf, numel, dtype, device, slack=1.0):
     return buf
 
 
+class PhaseArena:
+    """One growth-only device allocation carved per step by gs_arena_plan
+    ([VRAM] "Phase Arena"): buffers whose phases never overlap share bytes.
+    GS_POOL_ALIAS=0 in the environment turns the sharing off (same layout as
+    separate buffers), an A/B switch and an escape hatch."""
+
+    def __init__(self, device="cuda", alias=None, slack: float = 1.1):
+        self.device = torch.device(device)
+        if alias is None:
+            alias = os.environ.get("GS_POOL_ALIAS", "1") not in ("0", "")
+        self.alias = bool(alias)
+        self.slack = slack
+        self.buf = None
+        self.cap_nnz = 0
+        self.cap_isects = 0
+        self.slots = {}
+
+    def plan(self, s: "Scene", nnz: int, n_isects: int) -> bool:
+        """Lay out capacities >= (nnz, n_isects); grows (and returns True) when
+        the planned arena is larger than the current allocation."""
+        if nnz > self.cap_nnz:
+            self.cap_nnz = int(nnz * self.slack) + 1
+        if n_isects > self.cap_isects:
+            self.cap_isects = int(n_isects * self.slack) + 1
+        st, self.slots, total = gs_arena_plan(s.N, s.C, s.W, s.H, self.cap_nnz, self.cap_isects,
+                                              self.alias)
+        if st != GS_OK:
+            raise GsError(st, "gs_arena_plan")
+        if self.buf is None or self.buf.numel() < total:
+            self.buf = torch.empty(max(total, 1), dtype=torch.uint8, device=self.device)
+            return True
+        return False
+
+    def view(self, slot: str, dtype, shape=None):
+        off, size = self.slots[slot]
+        t = self.buf[off:off + size].view(dtype) if size else torch.empty(0, dtype=dtype,
+                                                                          device=self.device)
+        return t if shape is None else t[: math.prod(shape)].view(*shape)
+
+    def bytes(self, slot: str) -> int:
+        return int(self.slots[slot][1])
+
+
 class Rasterizer:
     """Runs the five library calls with growth-only device buffers."""
 
@@ -293,6 +354,7 @@ class Rasterizer:
         self.slack = slack
         self._screen = self._aabb = self._pws = self._iws = self._ids = self._vscreen = None
         self._keys = None
+        self._arena = None
 
     def _check(self, st, where):
         if st != GS_OK:
@@ -412,6 +474,61 @@ class Rasterizer:
                                         p.mask, p.wg_scan, v_screen, adam.m, adam.v, adam.lr,
                                         adam.beta1, adam.beta2, adam.eps, adam.step),
                     "gs_project_bwd_adam")
+
+    def step_arena(self, s: Scene, v_rgb, v_T=None, arena: PhaseArena = None):
+        """The whole step with every per-step buffer carved from one phase
+        arena. The returned images, ids and screen-row gradients are views
+        into the arena, valid until the next step; gradients are allocated
+        as usual."""
+        A = arena if arena is not None else self._arena
+        if A is None:
+            A = self._arena = PhaseArena(self.device)
+        dev = self.device
+        Np = pad_n(s.N)
+        tx, ty = tiles(s.W, s.H)
+        n_tiles = s.C * tx * ty
+        nnz_need, is_need = A.cap_nnz, A.cap_isects
+        for _ in range(4):
+            A.plan(s, nnz_need, is_need)
+            mask = A.view("mask", torch.int64, (max(s.C * Np // 64, 1),))
+            wgc = A.view("wg_count", torch.int32, (max(s.C * Np // MASK_GROUP, 1),))
+            wgs = A.view("wg_scan", torch.int32, (max(s.C * Np // MASK_GROUP, 1),))
+            screen = A.view("screen", torch.float32)
+            aabb = A.view("aabb16", torch.int32)
+            st, nnz, cam = gs_project(s.N, s.C, s.W, s.H, s.sh_degree, s.means, s.quats,
+                                      s.log_scales, s.opacity_logits, s.sh, s.viewmats, s.Ks,
+                                      mask, wgc, wgs, screen, aabb, A.cap_nnz,
+                                      A.view("project_ws", torch.uint8), A.bytes("project_ws"))
+            if st == GS_E_CAPACITY:
+                nnz_need = nnz
+                continue
+            self._check(st, "gs_project")
+            screen = screen[: nnz * ROW].view(nnz, ROW)
+            aabb = aabb[: nnz * 2].view(nnz, 2)
+            ids = A.view("flatten_ids", torch.int32)
+            toff = A.view("tile_offsets", torch.int64, (n_tiles + 1,))
+            order = A.view("tile_order", torch.int32, (n_tiles,))
+            st, n_is, need = gs_intersect(s.C, s.W, s.H, nnz, screen, aabb, cam,
+                                          A.view("isect_ws", torch.uint8), A.bytes("isect_ws"),
+                                          ids, A.cap_isects, toff, None, order)
+            if st in (GS_E_CAPACITY, GS_E_WORKSPACE):
+                is_need = max(n_is, is_need)
+                continue
+            self._check(st, "gs_intersect")
+            ids = ids[:n_is]
+            rgb = A.view("out_rgb", torch.float32, (s.C, s.H, s.W, 3))
+            T = A.view("out_T", torch.float32, (s.C, s.H, s.W))
+            last = A.view("last_ids", torch.int32, (s.C, s.H, s.W))
+            self._check(gs_rasterize_fwd(s.C, s.W, s.H, screen, ids, toff, order, None, rgb, T,
+                                         None, last), "gs_rasterize_fwd")
+            vs = A.view("v_screen", torch.float32)[: nnz * ROW].view(nnz, ROW)
+            self._check(gs_rasterize_bwd(s.C, s.W, s.H, nnz, screen, ids, toff, order, None, T,
+                                         last, v_rgb, v_T, None, vs, None), "gs_rasterize_bwd")
+            p = Projected(nnz, cam, mask, wgc, wgs, screen, aabb)
+            grads = self.project_bwd(s, p, vs)
+            it = Intersected(n_is, ids, toff, None, order)
+            return dict(proj=p, isect=it, rgb=rgb, T=T, last=last, v_screen=vs, grads=grads)
+        raise GsError(GS_E_CAPACITY, "step_arena")
 
     def step(self, s: Scene, v_rgb, v_T=None, v_depth=None, background=None):
         """One whole pass: project, intersect, raster forward and backward,

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgs.so")
 
 SOURCES = ["gs_api.hip", "gs_project.hip", "gs_project_bwd.hip", "gs_sort.hip",
-           "gs_intersect.hip", "gs_raster.hip", "gs_profile.hip"]
+           "gs_intersect.hip", "gs_raster.hip", "gs_profile.hip", "gs_arena.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",

@@ -287,6 +287,47 @@ int gs_project_bwd_adam(void* stream, int64_t N, int32_t C, int32_t W, int32_t H
                         float beta2, float eps, int32_t step);
 
 /* ---------------------------------------------------------------------
+ * gs_arena_plan -- one allocation for every buffer of a step, with the
+ * buffers whose lives never overlap sharing bytes ([VRAM] "Phase Arena":
+ * the intersection sort buffers live only inside the intersection phase
+ * and the screen-row gradients only from the rasterize backward on, so
+ * they can share one allocation; the arena then costs its largest phase,
+ * not the sum; SS_POOL_ALIAS=0 there turns the sharing off).
+ *
+ * Host arithmetic only. For a step with N Gaussians, C cameras of W x H,
+ * capacities nnz (visible pairs) and n_isects (intersections), writes for
+ * each slot below (host arrays of GS_ARENA_SLOTS) its byte offset in the
+ * arena (256-byte aligned) and its size, and (host) *arena_bytes. Phases:
+ * 0 gs_project, 1 gs_intersect, 2 gs_rasterize_fwd, 3 gs_rasterize_bwd,
+ * 4 gs_project_bwd; a slot's bytes are valid from its first to its last
+ * phase, and another slot may reuse them outside that range:
+ *   MASK 0-4, WG_COUNT 0, WG_SCAN 0-4, PROJECT_WS 0, SCREEN 0-3,
+ *   AABB16 0-1, ISECT_WS 1, FLATTEN_IDS 1-3, TILE_OFFSETS 1-3,
+ *   TILE_ORDER 1-3, OUT_RGB 2-4, OUT_T 2-4, LAST_IDS 2-3, V_SCREEN 3-4.
+ * alias = 0 gives every slot bytes of its own. Calls on one stream keep
+ * the phases apart; parameters, gradients and optimizer state are not in
+ * the arena. Errors: GS_E_INVALID.
+ * ------------------------------------------------------------------- */
+#define GS_ARENA_SLOTS 14
+#define GS_SLOT_MASK 0
+#define GS_SLOT_WG_COUNT 1
+#define GS_SLOT_WG_SCAN 2
+#define GS_SLOT_PROJECT_WS 3
+#define GS_SLOT_SCREEN 4
+#define GS_SLOT_AABB16 5
+#define GS_SLOT_ISECT_WS 6
+#define GS_SLOT_FLATTEN_IDS 7
+#define GS_SLOT_TILE_OFFSETS 8
+#define GS_SLOT_TILE_ORDER 9
+#define GS_SLOT_OUT_RGB 10
+#define GS_SLOT_OUT_T 11
+#define GS_SLOT_LAST_IDS 12
+#define GS_SLOT_V_SCREEN 13
+int gs_arena_plan(int64_t N, int32_t C, int32_t W, int32_t H, int64_t nnz,
+                  int64_t n_isects, int32_t alias, uint64_t* offsets,
+                  uint64_t* sizes, uint64_t* arena_bytes);
+
+/* ---------------------------------------------------------------------
  * Per-kernel timing (opt-in; a HIP event pair around each launch of a
  * kernel whose name contains `filter`, on the stream it runs on).
  * [PROF] sections 3-4 describe the trainer's own per-kernel GPU timing

@@ -36,7 +36,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == {"gs_status_str", "gs_version", "gs_pad_n", "gs_project_workspace_bytes",
                           "gs_intersect_workspace_bytes", "gs_project", "gs_intersect",
                           "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd",
-                          "gs_project_bwd_adam", "gs_profile_enable", "gs_profile_disable",
+                          "gs_project_bwd_adam", "gs_arena_plan", "gs_profile_enable",
+                          "gs_profile_disable",
                           "gs_profile_reset",
                           "gs_profile_query"}
     for n in names:
@@ -121,3 +122,47 @@ def test_fused_adam_argument_checks(lib):
     assert lib.gs_project_bwd_adam(*base, None, m, lr, 0.9, 0.999, 1e-8, 1) == gsd.GS_E_INVALID
     # null moments for N = 10 Gaussians
     assert lib.gs_project_bwd_adam(*base, m, m, lr, 0.9, 0.999, 1e-8, 1) == gsd.GS_E_INVALID
+
+
+PHASES = {"mask": (0, 4), "wg_count": (0, 0), "wg_scan": (0, 4), "project_ws": (0, 0),
+          "screen": (0, 3), "aabb16": (0, 1), "isect_ws": (1, 1), "flatten_ids": (1, 3),
+          "tile_offsets": (1, 3), "tile_order": (1, 3), "out_rgb": (2, 4), "out_T": (2, 4),
+          "last_ids": (2, 3), "v_screen": (3, 4)}
+
+
+@pytest.mark.parametrize("shape", [(1_000_000, 1, 1920, 1080, 971_385, 6_284_871),
+                                   (15_000_000, 5, 1297, 840, 14_840_666, 78_674_028),
+                                   (4096, 1, 128, 128, 4096, 10_358), (1, 1, 1, 1, 0, 0)])
+def test_arena_plan_properties(lib, shape):
+    """Phase arena ([VRAM] "Phase Arena"): every slot lies inside the arena;
+    with aliasing, slots alive in a common phase never share a byte; the
+    aliased arena is never larger than the plain one, whose size is the sum;
+    the pages' pair (intersection sort buffers, screen-row gradients) shares."""
+    N, C, W, H, nnz, I = shape
+    st0, plain, tot0 = gsd.gs_arena_plan(N, C, W, H, nnz, I, alias=False)
+    st1, al, tot1 = gsd.gs_arena_plan(N, C, W, H, nnz, I, alias=True)
+    assert st0 == st1 == gsd.GS_OK
+    up = lambda b: (b + 255) // 256 * 256
+    assert tot0 == sum(up(b) for _, b in plain.values())
+    assert tot1 <= tot0
+    for plan, tot in ((plain, tot0), (al, tot1)):
+        for k, (o, b) in plan.items():
+            assert o % 256 == 0 and o + b <= tot, k
+    for a in al:
+        for b in al:
+            if a >= b:
+                continue
+            (fa, la), (fb, lb) = PHASES[a], PHASES[b]
+            if la < fb or lb < fa:
+                continue
+            (oa, sa), (ob, sb) = al[a], al[b]
+            assert oa + sa <= ob or ob + sb <= oa, (a, b)
+    # sizes follow the documented formulas
+    Np = (N + 127) // 128 * 128
+    assert plain["mask"][1] == C * Np // 8 and plain["v_screen"][1] == 40 * nnz
+    assert plain["isect_ws"][1] == lib.gs_intersect_workspace_bytes(C, W, H, nnz, I)
+    if nnz > 1000:
+        o_i, s_i = al["isect_ws"]
+        o_v, s_v = al["v_screen"]
+        assert o_i < o_v + s_v and o_v < o_i + s_i   # they share bytes
+    assert lib.gs_arena_plan(-1, 1, 1, 1, 0, 0, 1, None, None, None) == gsd.GS_E_INVALID
