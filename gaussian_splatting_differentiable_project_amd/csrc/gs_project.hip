@@ -29,27 +29,67 @@ __device__ __forceinline__ void zero_local(GaussLocal<T>& G) {
   for (int i = 0; i < 9; ++i) G.Rq[i] = G.M[i] = (i % 4 == 0) ? T(1) : T(0);
 }
 
+// Visibility of one pair: the depth test on the fp32 key depth (exact by
+// definition) and the four margins of the clamped box, u + r > 0,
+// u - r < W, v + r > 0, v - r < H. They are first evaluated in fp32; a
+// margin within a generous bound of zero (1e-3 relative to the terms
+// involved, far above the fp32 rounding of this chain, including the
+// cancellation inside the radius) leaves the pair "unsure", and only then
+// is it evaluated again in fp64 as the compaction pass evaluates it.
+__device__ __forceinline__ bool visible_fp32(const PairFwd<float>& P, float cx, float cy,
+                                             float W, float H, bool* unsure) {
+  *unsure = false;
+  if (!(P.z32 > kNear)) return false;
+  const float tx = 1e-3f * (1.f + fabsf(P.u) + fabsf(P.u - cx) + P.r);
+  const float ty = 1e-3f * (1.f + fabsf(P.v) + fabsf(P.v - cy) + P.r);
+  const float m0 = P.u + P.r, m1 = W - (P.u - P.r), m2 = P.v + P.r, m3 = H - (P.v - P.r);
+  if (!(fabsf(m0) < 3e38f && fabsf(m1) < 3e38f && fabsf(m2) < 3e38f && fabsf(m3) < 3e38f &&
+        tx < 3e38f && ty < 3e38f)) {
+    *unsure = true;
+    return false;
+  }
+  if (m0 < -tx || m1 < -tx || m2 < -ty || m3 < -ty) return false;
+  if (m0 > tx && m1 > tx && m2 > ty && m3 > ty) return true;
+  *unsure = true;
+  return false;
+}
+
 __global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint64_t* mask,
                                                              uint32_t* wg_count) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t g = int64_t(blockIdx.x) * kMaskGroup + tid;
   const bool valid = g < a.N;
-  // The projection is evaluated in fp64 (full rate on gfx950; this pass
-  // is bound by memory, not arithmetic) and only its results are rounded,
-  // so visibility is decided as the exact arithmetic decides it except at
-  // ties.
-  GaussLocal<double> G;
+  // The decision is the fp64 projection's (the compaction pass computes
+  // the rows in fp64 and the two must agree); fp32 settles every pair not
+  // close to an edge of the decision, and fp64 runs only for the others.
+  GaussLocal<float> Gf;
   if (valid)
-    gauss_local(a.means, a.quats, a.log_scales, g, G);
+    gauss_local(a.means, a.quats, a.log_scales, g, Gf);
   else
-    zero_local(G);
+    zero_local(Gf);
+  GaussLocal<double> G;
+  bool have_g64 = false;
   __shared__ uint32_t pc[2][2];
-  const double Wf = double(a.W), Hf = double(a.H);
+  const float Wf = float(a.W), Hf = float(a.H);
   for (int c = 0; c < a.C; ++c) {
     const Camera k = load_camera(a.viewmats, a.Ks, c);
-    PairFwd<double> P;
-    pair_fwd(k, G, Wf, Hf, P);
-    const uint64_t word = __ballot(valid && P.visible);
+    PairFwd<float> Pf;
+    pair_fwd(k, Gf, Wf, Hf, Pf);
+    bool unsure;
+    bool vis = visible_fp32(Pf, float(k.cx), float(k.cy), Wf, Hf, &unsure);
+    unsure = unsure && valid;
+    if (__ballot(unsure)) {
+      if (unsure) {
+        if (!have_g64) {
+          gauss_local(a.means, a.quats, a.log_scales, g, G);
+          have_g64 = true;
+        }
+        PairFwd<double> P;
+        pair_fwd(k, G, double(a.W), double(a.H), P);
+        vis = P.visible;
+      }
+    }
+    const uint64_t word = __ballot(valid && vis);
     const int64_t p0 = int64_t(c) * a.N_pad + int64_t(blockIdx.x) * kMaskGroup;
     if (lane == 0) {
       mask[p0 / 64 + wave] = word;
