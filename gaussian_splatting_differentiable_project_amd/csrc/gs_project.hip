@@ -100,77 +100,170 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint
   }
 }
 
+// One visible pair: its fp32 screen row and 16-bit box at slot `slot`.
+// fp64 arithmetic, rounded once into the fp32 row (see the mask pass).
+// G carries the Gaussian's position and M = Rq diag(s), the only parts
+// the pair's projection reads.
 template <int DEG>
-__global__ __launch_bounds__(kMaskGroup) void k_project_compact(ProjectArgs a,
-                                                                const uint64_t* __restrict__ mask,
-                                                                const uint32_t* __restrict__ wg_scan,
-                                                                float* __restrict__ screen,
-                                                                uint32_t* __restrict__ aabb16) {
+__device__ __forceinline__ void compact_pair(const ProjectArgs& a, const GaussLocal<double>& G,
+                                             float opac, const float* shg, int c, int64_t slot,
+                                             float* __restrict__ screen,
+                                             uint32_t* __restrict__ aabb16) {
   constexpr int K = (DEG + 1) * (DEG + 1);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t g = int64_t(blockIdx.x) * kMaskGroup + tid;
+  const Camera k = load_camera(a.viewmats, a.Ks, c);
+  PairFwd<double> P;
+  pair_fwd(k, G, double(a.W), double(a.H), P);
+  // colour toward the camera centre
+  double dx = double(G.mu[0]) - k.cc[0], dy = double(G.mu[1]) - k.cc[1],
+         dz = double(G.mu[2]) - k.cc[2];
+  const double inv = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
+  dx *= inv, dy *= inv, dz *= inv;
+  double Y[K];
+  sh_basis<DEG>(a.norm, dx, dy, dz, Y);
+  float rgb[3];
+#pragma unroll
+  for (int ch = 0; ch < 3; ++ch) {
+    double acc = 0.5;
+#pragma unroll
+    for (int kk = 0; kk < K; ++kk) acc = fma(Y[kk], double(shg[3 * kk + ch]), acc);
+    rgb[ch] = float(fmax(acc, 0.0));
+  }
+  float2* row = reinterpret_cast<float2*>(screen + slot * kRow);
+  row[0] = make_float2(float(P.u), float(P.v));
+  row[1] = make_float2(float(P.ca), float(P.cb));
+  row[2] = make_float2(float(P.cc), opac);
+  row[3] = make_float2(P.z32, rgb[0]);
+  row[4] = make_float2(rgb[1], rgb[2]);
+  // 16-bit box: min edges round down, max edges round up, on the grid
+  // of 65535 steps over [0, extent]; the edge is taken in fp32 and scaled
+  // in fp32 (a float deciding an integer code: one fixed precision).
+  const float fx0 = fminf(fmaxf(floorf(float(P.x0) * a.qsx), 0.f), 65535.f);
+  const float fy0 = fminf(fmaxf(floorf(float(P.y0) * a.qsy), 0.f), 65535.f);
+  const float fx1 = fminf(fmaxf(ceilf(float(P.x1) * a.qsx), 0.f), 65535.f);
+  const float fy1 = fminf(fmaxf(ceilf(float(P.y1) * a.qsy), 0.f), 65535.f);
+  uint2 box;
+  box.x = uint32_t(fx0) | (uint32_t(fy0) << 16);
+  box.y = uint32_t(fx1) | (uint32_t(fy1) << 16);
+  reinterpret_cast<uint2*>(aabb16)[slot] = box;
+}
+
+// Compaction, one wave per 64 Gaussians (half a mask group), in one of
+// two ways chosen per wave:
+//  - dense (the wave's visible pairs are at least half of 64 per camera):
+//    each lane walks the cameras for its own Gaussian, the camera uniform
+//    across the wave, its SH coefficients read once into registers;
+//  - sparse (many cameras, each seeing a small part of the scene): such a
+//    walk would run every camera's fp64 projection with only the visible
+//    lanes active -- about one in five in a five-camera scene -- so the
+//    wave instead gathers its visible pairs camera by camera into an LDS
+//    queue, in slot order, and computes them 64 at a time, one pair per
+//    lane; the camera-independent part of each Gaussian is computed once
+//    by its own lane and shared through LDS.
+// A pair past the caller's capacity is counted by the scan, not written.
+template <int DEG>
+__global__ __launch_bounds__(kWave) void k_project_compact(ProjectArgs a,
+                                                           const uint64_t* __restrict__ mask,
+                                                           const uint32_t* __restrict__ wg_scan,
+                                                           float* __restrict__ screen,
+                                                           uint32_t* __restrict__ aabb16) {
+  constexpr int K = (DEG + 1) * (DEG + 1);
+  __shared__ uint32_t s_cl[2 * kWave];  // camera << 6 | lane of the Gaussian
+  __shared__ int64_t s_slot[2 * kWave];
+  __shared__ double s_M[9][kWave];
+  __shared__ float s_mu[3][kWave];
+  __shared__ float s_op[kWave];
+  const int lane = threadIdx.x;
+  const int half = int(blockIdx.x & 1);
+  const int64_t grp = int64_t(blockIdx.x >> 1);
+  const int64_t gw = int64_t(blockIdx.x) * kWave;  // this wave's first Gaussian
   const uint64_t lt = lanemask_lt();
-  // Which cameras see this Gaussian (mask words are wave-uniform loads).
+  // Which cameras see this lane's Gaussian (mask words are wave-uniform
+  // loads; the bits of padding lanes are clear).
   bool any = false;
+  int npairs = 0;  // the wave's visible pairs (wave-uniform)
   for (int c = 0; c < a.C; ++c) {
-    const int64_t p0 = int64_t(c) * a.N_pad + int64_t(blockIdx.x) * kMaskGroup;
-    const uint64_t mine = mask[p0 / 64 + wave];
+    const uint64_t mine = mask[(int64_t(c) * a.N_pad + grp * kMaskGroup) / 64 + half];
     any |= ((mine >> lane) & 1ull) != 0;
+    npairs += __popcll(mine);
   }
-  if (!any) return;
-  // fp64 arithmetic, rounded once into the fp32 row (see the mask pass)
+  if (npairs == 0) return;
   GaussLocal<double> G;
-  gauss_local(a.means, a.quats, a.log_scales, g, G);
-  const float opac = float(1.0 / (1.0 + exp(-double(a.opacity_logits[g]))));
-  float shc[K * 3];
-  const float* shg = a.sh + g * (K * 3);
-#pragma unroll
-  for (int i = 0; i < K * 3; ++i) shc[i] = shg[i];
-  const double Wf = double(a.W), Hf = double(a.H);
-  for (int c = 0; c < a.C; ++c) {
-    const int64_t p0 = int64_t(c) * a.N_pad + int64_t(blockIdx.x) * kMaskGroup;
-    const uint64_t w0 = mask[p0 / 64], w1 = mask[p0 / 64 + 1];
-    const uint64_t mine = wave ? w1 : w0;
-    if (!((mine >> lane) & 1ull)) continue;
-    const int64_t slot = int64_t(wg_scan[p0 / kMaskGroup]) + (wave ? __popcll(w0) : 0) +
-                         __popcll(mine & lt);
-    if (slot >= a.cap) continue;  // past the caller's capacity: counted, not written
-    const Camera k = load_camera(a.viewmats, a.Ks, c);
-    PairFwd<double> P;
-    pair_fwd(k, G, Wf, Hf, P);
-    // colour toward the camera centre
-    double dx = double(G.mu[0]) - k.cc[0], dy = double(G.mu[1]) - k.cc[1],
-           dz = double(G.mu[2]) - k.cc[2];
-    const double inv = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
-    dx *= inv, dy *= inv, dz *= inv;
-    double Y[K];
-    sh_basis<DEG>(a.norm, dx, dy, dz, Y);
-    float rgb[3];
-#pragma unroll
-    for (int ch = 0; ch < 3; ++ch) {
-      double acc = 0.5;
-#pragma unroll
-      for (int kk = 0; kk < K; ++kk) acc = fma(Y[kk], double(shc[3 * kk + ch]), acc);
-      rgb[ch] = float(fmax(acc, 0.0));
-    }
-    float2* row = reinterpret_cast<float2*>(screen + slot * kRow);
-    row[0] = make_float2(float(P.u), float(P.v));
-    row[1] = make_float2(float(P.ca), float(P.cb));
-    row[2] = make_float2(float(P.cc), opac);
-    row[3] = make_float2(P.z32, rgb[0]);
-    row[4] = make_float2(rgb[1], rgb[2]);
-    // 16-bit box: min edges round down, max edges round up, on the grid
-    // of 65535 steps over [0, extent]; the edge is taken in fp32 and scaled
-    // in fp32 (a float deciding an integer code: one fixed precision).
-    const float fx0 = fminf(fmaxf(floorf(float(P.x0) * a.qsx), 0.f), 65535.f);
-    const float fy0 = fminf(fmaxf(floorf(float(P.y0) * a.qsy), 0.f), 65535.f);
-    const float fx1 = fminf(fmaxf(ceilf(float(P.x1) * a.qsx), 0.f), 65535.f);
-    const float fy1 = fminf(fmaxf(ceilf(float(P.y1) * a.qsy), 0.f), 65535.f);
-    uint2 box;
-    box.x = uint32_t(fx0) | (uint32_t(fy0) << 16);
-    box.y = uint32_t(fx1) | (uint32_t(fy1) << 16);
-    reinterpret_cast<uint2*>(aabb16)[slot] = box;
+  float opac = 0.f;
+  if (any) {
+    gauss_local(a.means, a.quats, a.log_scales, gw + lane, G);
+    opac = float(1.0 / (1.0 + exp(-double(a.opacity_logits[gw + lane]))));
   }
+  if (2 * npairs >= a.C * kWave) {
+    if (!any) return;
+    float shc[K * 3];
+    const float* shg = a.sh + (gw + lane) * (K * 3);
+#pragma unroll
+    for (int i = 0; i < K * 3; ++i) shc[i] = shg[i];
+    for (int c = 0; c < a.C; ++c) {
+      const int64_t p0 = int64_t(c) * a.N_pad + grp * kMaskGroup;
+      const uint64_t w0 = mask[p0 / 64], w1 = mask[p0 / 64 + 1];
+      const uint64_t mine = half ? w1 : w0;
+      if (!((mine >> lane) & 1ull)) continue;
+      const int64_t slot = int64_t(wg_scan[p0 / kMaskGroup]) + (half ? __popcll(w0) : 0) +
+                           __popcll(mine & lt);
+      if (slot < a.cap) compact_pair<DEG>(a, G, opac, shc, c, slot, screen, aabb16);
+    }
+    return;
+  }
+  if (any) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) s_M[i][lane] = G.M[i];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) s_mu[i][lane] = G.mu[i];
+    s_op[lane] = opac;
+  }
+  auto run = [&](uint32_t cl, int64_t slot) {
+    if (slot >= a.cap) return;
+    const int src = int(cl & 63u);
+    GaussLocal<double> Gs;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) Gs.M[i] = s_M[i][src];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) Gs.mu[i] = s_mu[i][src];
+    compact_pair<DEG>(a, Gs, s_op[src], a.sh + (gw + src) * (K * 3), int(cl >> 6), slot, screen,
+                      aabb16);
+  };
+  int qn = 0;  // queued pairs (wave-uniform)
+  for (int c = 0; c < a.C; ++c) {
+    const int64_t p0 = int64_t(c) * a.N_pad + grp * kMaskGroup;
+    const uint64_t w0 = mask[p0 / 64], w1 = mask[p0 / 64 + 1];
+    const uint64_t mine = half ? w1 : w0;
+    if (mine == 0) continue;
+    const int64_t base = int64_t(wg_scan[p0 / kMaskGroup]) + (half ? __popcll(w0) : 0);
+    if ((mine >> lane) & 1ull) {
+      const int r = __popcll(mine & lt);
+      s_cl[qn + r] = (uint32_t(c) << 6) | uint32_t(lane);
+      s_slot[qn + r] = base + r;
+    }
+    qn += __popcll(mine);
+    if (qn >= kWave) {
+      __syncthreads();
+      const uint32_t cl = s_cl[lane];
+      const int64_t slot = s_slot[lane];
+      // move the entries past the first 64 to the front
+      const bool mv = lane < qn - kWave;
+      uint32_t t_cl = 0;
+      int64_t t_slot = 0;
+      if (mv) {
+        t_cl = s_cl[kWave + lane];
+        t_slot = s_slot[kWave + lane];
+      }
+      __syncthreads();
+      if (mv) {
+        s_cl[lane] = t_cl;
+        s_slot[lane] = t_slot;
+      }
+      qn -= kWave;
+      run(cl, slot);
+    }
+  }
+  __syncthreads();
+  if (lane < qn) run(s_cl[lane], s_slot[lane]);
 }
 
 __global__ void k_cam_offsets(const uint32_t* __restrict__ wg_scan, int64_t groups_per_cam, int C,
@@ -227,10 +320,10 @@ hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, uint32_t* w
 hipError_t launch_project_compact(const ProjectArgs& a, const uint64_t* mask,
                                   const uint32_t* wg_scan, float* screen, uint32_t* aabb16,
                                   hipStream_t s) {
-  const int64_t blocks = a.N_pad / kMaskGroup;
+  const int64_t blocks = a.N_pad / kWave;  // one wave per half mask group
   if (blocks == 0) return hipSuccess;
-  if (!fits_dispatch(uint64_t(blocks), kMaskGroup)) return hipErrorInvalidConfiguration;
-  const dim3 grid{uint32_t(blocks)}, block{uint32_t(kMaskGroup)};
+  if (!fits_dispatch(uint64_t(blocks), kWave)) return hipErrorInvalidConfiguration;
+  const dim3 grid{uint32_t(blocks)}, block{uint32_t(kWave)};
   ProfScope prof("k_project_compact", s);
   switch (a.deg) {
     case 0: hipLaunchKernelGGL(k_project_compact<0>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;

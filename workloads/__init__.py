@@ -90,6 +90,10 @@ SMALL = {
                            -2.8, 0.4, 5.0, seed=2003),
     "sh2-dense": SceneSpec("sh2-12k-64x48", 12_000, 2, 1, 64, 48, 60.0, 1.5,
                            -2.5, 0.4, 5.0, seed=2004),
+    # six narrow cameras, each seeing a few percent of the Gaussians: most
+    # (camera, Gaussian) pairs are invisible
+    "sparse-6cam": SceneSpec("sh2-9001-6cam-80x60-narrow", 9001, 2, 6, 80, 60, 320.0,
+                             2.0, -3.0, 0.5, 5.0, seed=2005),
 }
 
 
