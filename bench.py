@@ -39,13 +39,13 @@ CSRC = os.path.join(ROOT, "gaussian_splatting_differentiable_project_amd", "csrc
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 KERNELS = ["k_project_mask", "k_scan", "k_cam_offsets", "k_project_compact", "k_fill_u32",
-           "k_isect_prep", "k_radix_count", "k_radix_scatter", "k_isect_emit",
+           "k_isect_prep", "k_radix_count", "k_radix_scatter", "k_emit_count", "k_emit_write",
            "k_tile_ranges", "k_tile_order_keys", "k_raster_fwd", "k_raster_bwd", "k_project_bwd",
            "k_project_bwd_adam"]
 KERNEL_SOURCE = {"k_raster_fwd": "gs_raster.hip", "k_raster_bwd": "gs_raster.hip",
                  "k_project_mask": "gs_project.hip", "k_project_compact": "gs_project.hip",
                  "k_project_bwd": "gs_project_bwd.hip", "k_radix_scatter": "gs_sort.hip",
-                 "k_isect_emit": "gs_intersect.hip"}
+                 "k_emit_write": "gs_intersect.hip"}
 
 # Flops of one (pixel, entry) evaluation in the raster kernels: the alpha
 # test every evaluation needs (dx, dy, three products, the quadratic form,
@@ -87,6 +87,16 @@ def source_sha(kernel: str) -> str | None:
     return h.hexdigest()[:16]
 
 
+def tile_sort_digits(spec):
+    """(bits of the emit's fused first digit, radix passes after it) of the
+    sort by tile id, as the library chooses them."""
+    n_tiles = spec.n_cams * ((spec.width + 15) // 16) * ((spec.height + 15) // 16)
+    bits = max(0, int(n_tiles - 1).bit_length())
+    b1 = 8
+    rest = max(0, bits - b1)
+    return b1, (rest + 7) // 8
+
+
 def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes):
     """Algorithmic HBM bytes of one launch of an HBM-bound kernel."""
     N, C, K = spec.n, spec.n_cams, spec.K
@@ -103,8 +113,8 @@ def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes):
     if kernel == "k_radix_scatter":  # mean over the step's passes: 8 B read + 8 B written per key
         tiles = C * ((spec.width + 15) // 16) * ((spec.height + 15) // 16)
         return 16 * (4 * nnz + tile_passes * n_isects + 2 * tiles) / (4 + tile_passes + 2)
-    if kernel == "k_isect_emit":     # order, box, offset per pair; 8 B per entry
-        return 16 * nnz + 8 * n_isects
+    if kernel == "k_emit_write":     # order + box per pair; 8 B per entry
+        return 12 * nnz + 8 * n_isects
     return None
 
 
@@ -326,8 +336,7 @@ def main():
     Np = gsd.pad_n(spec.n)
     V = int(vis[: spec.n_cams * Np].reshape(spec.n_cams, Np).any(0).sum())
     tx, ty = gsd.tiles(spec.width, spec.height)
-    tile_bits = max(1, int(np.ceil(np.log2(max(spec.n_cams * tx * ty, 2)))))
-    tile_passes = (tile_bits + 7) // 8
+    _, tile_passes = tile_sort_digits(spec)
     walked, comp = raster_work(last, spec.width, spec.height)
 
     if dom in ("k_raster_bwd", "k_raster_fwd"):

@@ -82,14 +82,17 @@ ProjectWs carve_project(void* base, int64_t n_groups, int32_t C) {
 struct IsectWs {
   uint64_t* total;      // n_isects (prep)
   int* err;
-  uint32_t* ticket;     // emit blocks
-  uint64_t* scan_lb;    // emit look-back
+  uint32_t* ticket;     // scan of the emit count matrix
+  uint64_t* scan_lb;    // its look-back words
   uint64_t* sort_grp;   // radix sort group totals
   uint64_t zero_words;  // u32 words to clear, from the start
   int64_t* cam_off;     // [C+1]
   uint32_t *dkeys_a, *dkeys_b, *dvals_a, *dvals_b;
   uint32_t *ord_keys_a, *ord_keys_b, *ord_vals_b;  // launch-order sort of the tiles
   uint32_t* sort_cnt;   // radix sort chunk counts (fixed size)
+  uint32_t* emit_cnt;   // [digit][emit block] entry counts
+  uint64_t* emit_off;   // their exclusive scan: first output position of each run
+  uint64_t* emit_total;
   uint64_t phase1_bytes;  // enough to count (I still unknown)
   uint32_t *tkeys_a, *tkeys_b, *tvals;
   uint64_t bytes;
@@ -99,10 +102,11 @@ IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects, uint64
   Carver cv{static_cast<char*>(base)};
   IsectWs w{};
   const uint64_t n = uint64_t(nnz);
+  const uint64_t mat = emit_matrix_len(n);
   w.total = cv.take<uint64_t>(1);
   w.err = cv.take<int>(1);
   w.ticket = cv.take<uint32_t>(1);
-  w.scan_lb = cv.take<uint64_t>(isect_emit_lookback_words(n));
+  w.scan_lb = cv.take<uint64_t>((mat + kScanTile - 1) / kScanTile + 1);
   w.sort_grp = cv.take<uint64_t>(sort_groups_bytes() / sizeof(uint64_t));
   w.zero_words = cv.off / 4;
   w.cam_off = cv.take<int64_t>(uint64_t(C) + 1);
@@ -114,6 +118,9 @@ IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects, uint64
   w.ord_keys_b = cv.take<uint32_t>(n_tiles);
   w.ord_vals_b = cv.take<uint32_t>(n_tiles);
   w.sort_cnt = cv.take<uint32_t>(sort_counts_bytes() / sizeof(uint32_t));
+  w.emit_cnt = cv.take<uint32_t>(mat);
+  w.emit_off = cv.take<uint64_t>(mat);
+  w.emit_total = cv.take<uint64_t>(1);
   w.phase1_bytes = cv.off;
   const uint64_t I = n_isects > 0 ? uint64_t(n_isects) : 0;
   w.tkeys_a = cv.take<uint32_t>(I);
@@ -342,17 +349,23 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   if (I == 0) {
     GS_TRY(launch_fill_u32(tile_offsets, 0u, 2 * (n_tiles + 1), s));
   } else {
-    // Phase 3: offsets and (tile id, slot) entries in depth order.
+    // Phase 3: (tile id, slot) entries in depth order, written already
+    // partitioned by the low digit of the tile id (the first sort pass).
     const int tbits = bits_for(n_tiles);
-    const int passes = sort_passes(tbits);
+    const int b1 = emit_digit_bits();
+    const int rest = tbits > b1 ? tbits - b1 : 0;
+    const int passes = rest ? sort_passes(rest) : 0;
     // the final pass must land its values in flatten_ids
     uint32_t* v_first = (passes & 1) ? ws.tvals : flatten_ids;
     uint32_t* v_second = (passes & 1) ? flatten_ids : ws.tvals;
-    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.cam_off, C, W, H, I, ws.tkeys_a,
-                             v_first, ws.scan_lb, ws.ticket, ws.err, s));
-    // Phase 4: stable sort of the entries by tile id.
-    GS_TRY(launch_sort_passes(ws.tkeys_a, v_first, ws.tkeys_b, v_second, I, 0, tbits, sc, &in_b,
-                              s));
+    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.cam_off, C, W, H, I, I,
+                             ws.emit_cnt, ws.emit_off, ws.emit_total, ws.scan_lb, ws.ticket,
+                             ws.err, ws.tkeys_a, v_first, s));
+    // Phase 4: the remaining digits of the stable sort by tile id.
+    in_b = false;
+    if (passes)
+      GS_TRY(launch_sort_passes(ws.tkeys_a, v_first, ws.tkeys_b, v_second, I, b1, rest, sc,
+                                &in_b, s));
     const uint32_t* tkeys = in_b ? ws.tkeys_b : ws.tkeys_a;
     // Phase 5: per-tile ranges (and the composed 64-bit keys on request).
     GS_TRY(launch_tile_ranges(tkeys, I, n_tiles, tile_offsets, s));

@@ -185,4 +185,40 @@ __device__ __forceinline__ uint64_t lookback_prefix_wave(const uint64_t* lb, int
   return acc;
 }
 
+// Exclusive prefix over the 256 lanes of a 4-wave block; *total gets the
+// block sum. s_w holds one word per wave. Every lane must call it; it
+// synchronizes the block once.
+__device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* s_w /*[4]*/,
+                                                        uint64_t* total) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t incl = wave_incl_scan_u64(v);
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  uint64_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint64_t t = s_w[w];
+    off += (w < wave) ? t : 0ull;
+    tot += t;
+  }
+  *total = tot;
+  return off + incl - v;
+}
+
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s_w, uint32_t* total) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint32_t incl = wave_incl_scan_u32(v);
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t t = s_w[w];
+    off += (w < wave) ? t : 0u;
+    tot += t;
+  }
+  *total = tot;
+  return off + incl - v;
+}
+
 }  // namespace gs

@@ -100,13 +100,19 @@ hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys
 hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* aabb16, int W,
                              int H, uint32_t* dkeys, uint32_t* dvals, uint64_t* total,
                              hipStream_t s);
-// Offsets (single-pass scan with look-back) and entries of the slots in
-// depth order. lb[isect_emit_lookback_words(nnz)] and *ticket must be zero.
+// Entries of the slots in depth order, written already stably
+// partitioned by the low emit_digit_bits() bits of their tile id (the
+// first pass of the LSD sort by tile id). Scratch: a count matrix
+// mat[emit_matrix_len(nnz)] (uint32), its scan mat_off (uint64) and total,
+// and the scan's look-back words (ceil(emit_matrix_len / kScanTile)) and
+// ticket, which must be zero. Writes are clamped to `cap` entries.
+int emit_digit_bits();
+uint64_t emit_matrix_len(uint64_t nnz);
 hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
-                             const int64_t* cam_off, int C, int W, int H, uint64_t cap,
-                             uint32_t* tkeys, uint32_t* tvals, uint64_t* lb, uint32_t* ticket,
-                             int* err, hipStream_t s);
-uint64_t isect_emit_lookback_words(uint64_t nnz);
+                             const int64_t* cam_off, int C, int W, int H, uint64_t n_isects,
+                             uint64_t cap, uint32_t* mat, uint64_t* mat_off, uint64_t* mat_total,
+                             uint64_t* lb, uint32_t* ticket, int* err, uint32_t* tkeys,
+                             uint32_t* tvals, hipStream_t s);
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
                               hipStream_t s);
 hipError_t launch_tile_order_keys(const int64_t* toff, uint64_t n_tiles, uint32_t* keys,

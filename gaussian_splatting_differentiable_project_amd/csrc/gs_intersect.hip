@@ -69,113 +69,305 @@ __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* _
   }
 }
 
-// Intersections of the slots in depth order, with their offsets found on
-// the way. Block b takes positions [b*512, (b+1)*512) of the depth order
-// (position i holds slot order[i]); it counts their tiles, scans the
-// counts, gets the number of entries of all earlier positions from a
-// single-word decoupled look-back, and then writes its entries with
-// consecutive lanes on consecutive entries: lane e finds its slot by a
-// binary search over the block's offsets in LDS. Writes are clamped to
-// `cap` entries. The look-back words and the ticket must start at zero.
-constexpr int kEmitItems = 2;
-constexpr int kEmitSlots = 256 * kEmitItems;
+// Emission of the intersections, fused with the first digit pass of the
+// stable LSD sort by tile id. Block b owns a contiguous range of
+// depth-order positions (position i holds slot order[i]), walked in
+// sub-batches of 512. A pass of an LSD radix sort over the emitted
+// sequence would place the entries of digit d (the low 8 bits of the tile
+// id) after every entry of a smaller digit, and among equal digits in
+// emission order. That placement is computed here without ever writing
+// the unsorted sequence:
+//   k_emit_count  counts, per block, its entries of every digit (from the
+//                 tile rectangles alone: each rectangle row is a run of
+//                 consecutive tile ids, i.e. a cyclic run of digits);
+//   a scan of the [digit][block] count matrix in that order gives each
+//                 block the first output position of each of its digit runs;
+//   k_emit_write  enumerates the block's entries in emission order, ranks
+//                 them within their digit stably, and writes each digit run
+//                 of a round contiguously.
+// Each slot meets a tile at most once, so the entries of one tile are in
+// depth order (then slot order) exactly as the stable sort of
+// (tile << 32) | depth keys leaves them.
+constexpr int kEmitBits = 8;
+constexpr uint32_t kEmitRadix = 1u << kEmitBits;
+constexpr int kEmitSlots = 512;      // positions per sub-batch
+constexpr uint64_t kEmitBlocks = 2048;  // target block count (8 per CU)
 
-__global__ __launch_bounds__(256) void k_isect_emit(
-    uint64_t nnz, const uint32_t* __restrict__ order, const uint2* __restrict__ aabb16,
-    const int64_t* __restrict__ cam_off, int C, uint32_t W, uint32_t H, uint32_t tiles_x,
-    uint32_t T, uint64_t cap, uint32_t* __restrict__ tkeys, uint32_t* __restrict__ tvals,
-    uint64_t* lb, uint32_t* ticket, int* err) {
-  __shared__ uint32_t s_blk;
-  __shared__ uint64_t s_w[4];
-  __shared__ uint64_t s_prefix;
-  __shared__ uint64_t s_off[kEmitSlots + 1];  // block-local exclusive entry offsets
-  __shared__ uint32_t s_slot[kEmitSlots];
-  __shared__ uint32_t s_base[kEmitSlots];     // camera tile base + first tile of the rect
-  __shared__ uint32_t s_wx[kEmitSlots];       // rect width in tiles
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (tid == 0) s_blk = atomicAdd(ticket, 1u);
+struct EmitGeom {
+  uint32_t W, H, tiles_x, T;
+  int C;
+  uint64_t nnz, per_blk;  // positions per block (a multiple of kEmitSlots)
+};
+
+// Depth-order position i: its slot, the global id of the first tile of
+// its rectangle (camera tile base included) and the rectangle's size.
+__device__ __forceinline__ void emit_slot(uint64_t i, const uint32_t* __restrict__ order,
+                                          const uint2* __restrict__ aabb16,
+                                          const int64_t* __restrict__ cam_off,
+                                          const EmitGeom& g, uint32_t& slot, uint32_t& b0,
+                                          uint32_t& wx, uint32_t& wy) {
+  slot = order[i];
+  // camera of the slot: cameras own consecutive slot ranges
+  int lo = 0, hi = g.C - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (int64_t(slot) >= cam_off[mid]) lo = mid; else hi = mid - 1;
+  }
+  const TileRect r = rect_of(aabb16[slot], g.W, g.H);
+  wx = r.tx1 > r.tx0 ? r.tx1 - r.tx0 : 0u;
+  wy = r.ty1 > r.ty0 ? r.ty1 - r.ty0 : 0u;
+  b0 = uint32_t(lo) * g.T + r.ty0 * g.tiles_x + r.tx0;
+}
+
+// mat[d * nblk + b] = entries of block b whose tile id has low digit d.
+// A rectangle row of wx tiles starting at tile id s covers every digit
+// floor(wx / 256) times plus the cyclic run [s, s + wx mod 256); the runs
+// are added to a difference array in LDS and summed once.
+__global__ __launch_bounds__(256) void k_emit_count(const uint32_t* __restrict__ order,
+                                                   const uint2* __restrict__ aabb16,
+                                                   const int64_t* __restrict__ cam_off,
+                                                   EmitGeom g, uint64_t nblk,
+                                                   uint32_t* __restrict__ mat) {
+  constexpr uint32_t R = kEmitRadix, M = R - 1;
+  __shared__ uint32_t s_diff[R];
+  __shared__ uint32_t s_full;
+  __shared__ uint32_t s_w[4];
+  const int tid = threadIdx.x;
+  s_diff[tid] = 0;
+  if (tid == 0) s_full = 0;
   __syncthreads();
-  const uint64_t blk = s_blk;
-  const uint64_t base = blk * kEmitSlots;
-  // slot data, read with consecutive lanes on consecutive positions
-#pragma unroll
-  for (int j = 0; j < kEmitItems; ++j) {
-    const int li = j * 256 + tid;
-    const uint64_t i = base + li;
-    uint32_t k = 0, slot = 0, b0 = 0, wx = 0;
-    if (i < nnz) {
-      slot = order[i];
-      // camera of the slot: cameras own consecutive slot ranges
-      int lo = 0, hi = C - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (int64_t(slot) >= cam_off[mid]) lo = mid; else hi = mid - 1;
+  uint32_t full = 0;
+  const uint64_t i0 = uint64_t(blockIdx.x) * g.per_blk;
+  const uint64_t i1 = i0 + g.per_blk < g.nnz ? i0 + g.per_blk : g.nnz;
+  for (uint64_t i = i0 + tid; i < i1; i += 256) {
+    uint32_t slot, b0, wx, wy;
+    emit_slot(i, order, aabb16, cam_off, g, slot, b0, wx, wy);
+    if (wx == 0 || wy == 0) continue;
+    full += (wx >> kEmitBits) * wy;
+    const uint32_t rem = wx & M;
+    if (rem == 0) continue;
+    for (uint32_t dy = 0; dy < wy; ++dy) {
+      const uint32_t s = (b0 + dy * g.tiles_x) & M;
+      const uint32_t e = s + rem;
+      atomicAdd(&s_diff[s], 1u);
+      if (e < R) {
+        atomicAdd(&s_diff[e], 0xFFFFFFFFu);
+      } else {  // the run wraps: [s, R) and [0, e - R)
+        atomicAdd(&s_diff[0], 1u);
+        atomicAdd(&s_diff[e - R], 0xFFFFFFFFu);
       }
-      const TileRect r = rect_of(aabb16[slot], W, H);
-      k = rect_count(r);
-      wx = r.tx1 > r.tx0 ? r.tx1 - r.tx0 : 1u;
-      b0 = uint32_t(lo) * T + r.ty0 * tiles_x + r.tx0;
     }
-    s_slot[li] = slot;
-    s_base[li] = b0;
-    s_wx[li] = wx;
-    s_off[li] = k;  // counts for now
   }
+  if (full) atomicAdd(&s_full, full);
   __syncthreads();
-  // exclusive scan of the 1024 counts: four consecutive ones per lane
-  uint64_t c[kEmitItems], sum = 0;
+  // counts = inclusive prefix of the differences (modulo 2^32, exact for
+  // the true counts) plus the whole-round part
+  const uint32_t v = s_diff[tid];
+  uint32_t tot;
+  const uint32_t run = block_excl_scan_u32(v, s_w, &tot) + v + s_full;
+  mat[uint64_t(tid) * nblk + blockIdx.x] = run;
+}
+
+// Inclusive running maximum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_max_u32(uint32_t v) {
+  const int l = __lane_id();
 #pragma unroll
-  for (int j = 0; j < kEmitItems; ++j) {
-    c[j] = s_off[tid * kEmitItems + j];
-    sum += c[j];
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t t = __shfl_up(v, o, kWave);
+    if (l >= o) v = t > v ? t : v;
   }
-  const uint64_t incl = wave_incl_scan_u64(sum);
-  if (lane == 63) s_w[wave] = incl;
-  __syncthreads();
-  uint64_t woff = 0, btot = 0;
+  return v;
+}
+
+// mat_off: exclusive scan of mat in [digit][block] order. Writes are
+// clamped to `cap` entries.
+// Each sub-batch's entries are walked in rounds of 256 * ITEMS, in
+// emission order. The position owning each entry of a round comes from
+// an owner map in LDS: every position whose first entry falls in the
+// round marks that entry, and a running maximum over the round (started
+// from the previous round's last owner) fills the rest. Ranks within a
+// digit come from 8 ballots per wave and per-wave digit counters; each
+// digit run of the round is then gathered in LDS and written contiguously.
+template <int ITEMS>
+__global__ __launch_bounds__(256) void k_emit_write(
+    const uint32_t* __restrict__ order, const uint2* __restrict__ aabb16,
+    const int64_t* __restrict__ cam_off, EmitGeom g, uint64_t nblk,
+    const uint64_t* __restrict__ mat_off, uint64_t cap, uint32_t* __restrict__ keys_out,
+    uint32_t* __restrict__ vals_out) {
+  constexpr uint32_t M = kEmitRadix - 1;
+  constexpr int TILE = 256 * ITEMS;
+  constexpr int OWN = TILE / 256;  // owner-map entries per thread
+  static_assert(64 * ITEMS < 65536, "per-wave digit counters are 16-bit");
+  __shared__ uint64_t s_off[kEmitSlots + 1];  // sub-batch exclusive entry offsets
+  __shared__ uint32_t s_slot[kEmitSlots];
+  __shared__ uint32_t s_base[kEmitSlots];     // global id of the rectangle's first tile
+  __shared__ uint32_t s_wx[kEmitSlots];       // rectangle width in tiles
+  __shared__ int64_t s_gstart[kEmitRadix];    // output position of digit run d, minus its LDS start
+  __shared__ uint16_t s_whist[4][kEmitRadix]; // per-wave digit counts, then LDS starts
+  __shared__ uint16_t s_own[TILE];            // owning position of each entry of the round
+  __shared__ uint64_t s_w64[4];
+  __shared__ uint32_t s_w32[4];
+  __shared__ uint32_t s_keys[TILE];
+  __shared__ uint32_t s_vals[TILE];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t blk = blockIdx.x;
+  // first output position of this block's run of digit tid
+  uint64_t run = mat_off[uint64_t(tid) * nblk + blk];
+  const uint64_t lt = lanemask_lt();
+  const uint64_t i0 = blk * g.per_blk;
+  const uint64_t i1 = i0 + g.per_blk < g.nnz ? i0 + g.per_blk : g.nnz;
+  for (uint64_t sb = i0; sb < i1; sb += kEmitSlots) {
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    woff += (w < wave) ? s_w[w] : 0ull;
-    btot += s_w[w];
-  }
-  uint64_t run = woff + incl - sum;
+    for (int j = 0; j < kEmitSlots / 256; ++j) {
+      const int li = j * 256 + tid;
+      const uint64_t i = sb + li;
+      uint32_t slot = 0, b0 = 0, wx = 1, wy = 0;
+      if (i < i1) emit_slot(i, order, aabb16, cam_off, g, slot, b0, wx, wy);
+      s_slot[li] = slot;
+      s_base[li] = b0;
+      s_wx[li] = wx ? wx : 1u;
+      s_off[li] = uint64_t(wx) * wy;  // counts for now
+    }
+    __syncthreads();
+    constexpr int PT = kEmitSlots / 256;
+    uint64_t c[PT], sum = 0;
 #pragma unroll
-  for (int j = 0; j < kEmitItems; ++j) {
-    s_off[tid * kEmitItems + j] = run;
-    run += c[j];
-  }
-  if (wave == 0) {
-    uint64_t prefix = 0;
-    if (blk == 0) {
-      if (lane == 0) lb_store(lb, lb_word(kLbPrefix, 1, btot));
-    } else {
-      if (lane == 0) lb_store(lb + blk, lb_word(kLbAgg, 1, btot));
-      prefix = lookback_prefix_wave(lb, int64_t(blk), 1, err);
-      if (lane == 0) lb_store(lb + blk, lb_word(kLbPrefix, 1, prefix + btot));
+    for (int j = 0; j < PT; ++j) {
+      c[j] = s_off[tid * PT + j];
+      sum += c[j];
     }
-    if (lane == 0) {
-      s_off[kEmitSlots] = btot;
-      s_prefix = prefix;
+    uint64_t btot;
+    uint64_t o = block_excl_scan_u64(sum, s_w64, &btot);
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      s_off[tid * PT + j] = o;
+      o += c[j];
     }
-  }
-  __syncthreads();
-  const uint64_t prefix = s_prefix;
-  for (uint64_t e = tid; e < btot; e += 256) {
-    // last position whose offset is <= e (a position with no entries has
-    // the same offset as the next one, so the search lands on the owner)
-    int lo = 0, hi = kEmitSlots - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= e) lo = mid; else hi = mid - 1;
+    if (tid == 0) s_off[kEmitSlots] = btot;
+    uint32_t carry = 0;  // owner of the last entry of the previous round
+    for (uint64_t rb = 0; rb < btot; rb += TILE) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) s_whist[w][tid] = 0;
+#pragma unroll
+      for (int q = 0; q < OWN; ++q) s_own[q * 256 + tid] = 0;
+      __syncthreads();
+      // positions whose first entry lies in this round mark it
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const int pos = j * 256 + tid;
+        const uint64_t first = s_off[pos];
+        if (s_off[pos + 1] > first && first >= rb && first - rb < uint64_t(TILE))
+          s_own[first - rb] = uint16_t(pos);
+      }
+      __syncthreads();
+      {  // running maximum over the round, OWN consecutive entries per thread
+        uint32_t m = 0;
+        uint32_t loc[OWN];
+#pragma unroll
+        for (int q = 0; q < OWN; ++q) {
+          const uint32_t x = s_own[tid * OWN + q];
+          m = x > m ? x : m;
+          loc[q] = m;
+        }
+        const uint32_t incl = wave_incl_max_u32(m);
+        if (lane == 63) s_w32[wave] = incl;
+        __syncthreads();
+        uint32_t before = carry;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x = s_w32[w];
+          before = (w < wave && x > before) ? x : before;
+        }
+        const uint32_t prev = __shfl_up(incl, 1, kWave);
+        if (lane > 0 && prev > before) before = prev;
+#pragma unroll
+        for (int q = 0; q < OWN; ++q)
+          s_own[tid * OWN + q] = uint16_t(loc[q] > before ? loc[q] : before);
+      }
+      __syncthreads();
+      carry = s_own[TILE - 1];
+      uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int le = wave * (ITEMS * kWave) + i * kWave + lane;
+        const uint64_t e = rb + uint64_t(le);
+        const bool valid = e < btot;
+        uint32_t t = 0, v = 0;
+        if (valid) {
+          const uint32_t own = s_own[le];
+          const uint32_t k = uint32_t(e - s_off[own]);
+          const uint32_t w = s_wx[own];
+          // k < 2^24 and w <= 4096: the fp32 quotient is within a step or
+          // two of floor(k / w); the corrections make it exact
+          uint32_t dy = uint32_t(float(k) * __builtin_amdgcn_rcpf(float(w)));
+          while (dy * w > k) --dy;
+          while ((dy + 1) * w <= k) ++dy;
+          t = s_base[own] + dy * g.tiles_x + (k - dy * w);
+          v = s_slot[own];
+        }
+        key[i] = t;
+        val[i] = v;
+        // rank among the wave's earlier entries with the same digit
+        const uint32_t d = t & M;
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < kEmitBits; ++b) {
+          const bool bit = (d >> b) & 1u;
+          const uint64_t bb = __ballot(bit);
+          peers &= bit ? bb : ~bb;
+        }
+        const uint32_t before = s_whist[wave][d];
+        const uint32_t r = uint32_t(__popcll(peers & lt));
+        if (valid && r == 0) s_whist[wave][d] = uint16_t(before + uint32_t(__popcll(peers)));
+        rank[i] = before + r;
+      }
+      __syncthreads();
+      // digit tid: its LDS start plus the earlier waves' counts, and the
+      // output position of its run
+      uint32_t cw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) cw[w] = s_whist[w][tid];
+      const uint32_t cnt = cw[0] + cw[1] + cw[2] + cw[3];
+      uint32_t ttot;
+      const uint32_t ls = block_excl_scan_u32(cnt, s_w32, &ttot);
+      {
+        uint32_t x = ls;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          s_whist[w][tid] = uint16_t(x);
+          x += cw[w];
+        }
+      }
+      s_gstart[tid] = int64_t(run) - int64_t(ls);
+      run += cnt;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const uint64_t e = rb + uint64_t(wave) * (ITEMS * kWave) + i * kWave + lane;
+        if (e < btot) {
+          const uint32_t pos = uint32_t(s_whist[wave][key[i] & M]) + rank[i];
+          s_keys[pos] = key[i];
+          s_vals[pos] = val[i];
+        }
+      }
+      __syncthreads();
+      const uint32_t n_here =
+          uint32_t((btot - rb) < uint64_t(TILE) ? (btot - rb) : uint64_t(TILE));
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        const uint32_t li = uint32_t(j * 256 + tid);
+        if (li < n_here) {
+          const uint32_t k = s_keys[li];
+          const uint64_t gpos = uint64_t(s_gstart[k & M] + int64_t(li));
+          if (gpos < cap) {
+            keys_out[gpos] = k;
+            vals_out[gpos] = s_vals[li];
+          }
+        }
+      }
+      __syncthreads();
     }
-    const uint64_t o = prefix + e;
-    if (o < cap) {
-      const uint32_t k = uint32_t(e - s_off[lo]);
-      const uint32_t wx = s_wx[lo];
-      const uint32_t dy = k / wx, dx = k - dy * wx;
-      tkeys[o] = s_base[lo] + dy * tiles_x + dx;
-      tvals[o] = s_slot[lo];
-    }
+    __syncthreads();  // the next sub-batch overwrites the slot data
   }
 }
 
@@ -244,23 +436,60 @@ hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
-                             const int64_t* cam_off, int C, int W, int H, uint64_t cap,
-                             uint32_t* tkeys, uint32_t* tvals, uint64_t* lb, uint32_t* ticket,
-                             int* err, hipStream_t s) {
-  if (nnz == 0) return hipSuccess;
-  const uint64_t blocks = (nnz + kEmitSlots - 1) / kEmitSlots;
-  if (!fits_dispatch(blocks, 256)) return hipErrorInvalidConfiguration;
-  const uint32_t tiles_x = uint32_t((W + kTile - 1) / kTile);
-  const uint32_t T = tiles_x * uint32_t((H + kTile - 1) / kTile);
-  ProfScope prof("k_isect_emit", s);
-  hipLaunchKernelGGL(k_isect_emit, dim3(uint32_t(blocks)), dim3(256), 0, s, nnz, order,
-                     reinterpret_cast<const uint2*>(aabb16), cam_off, C, uint32_t(W),
-                     uint32_t(H), tiles_x, T, cap, tkeys, tvals, lb, ticket, err);
-  return hipGetLastError();
+int emit_digit_bits() { return kEmitBits; }
+
+namespace {
+
+// Positions per emit block: whole sub-batches, about kEmitBlocks blocks.
+uint64_t emit_per_block(uint64_t nnz) {
+  const uint64_t subs = (nnz + kEmitSlots - 1) / kEmitSlots;
+  return ((subs + kEmitBlocks - 1) / kEmitBlocks) * kEmitSlots;
 }
 
-uint64_t isect_emit_lookback_words(uint64_t nnz) { return (nnz + kEmitSlots - 1) / kEmitSlots + 1; }
+uint64_t emit_blocks(uint64_t nnz) {
+  return nnz ? (nnz + emit_per_block(nnz) - 1) / emit_per_block(nnz) : 0;
+}
+
+}  // namespace
+
+uint64_t emit_matrix_len(uint64_t nnz) { return emit_blocks(nnz) * kEmitRadix; }
+
+hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
+                             const int64_t* cam_off, int C, int W, int H, uint64_t n_isects,
+                             uint64_t cap, uint32_t* mat, uint64_t* mat_off, uint64_t* mat_total,
+                             uint64_t* lb, uint32_t* ticket, int* err, uint32_t* tkeys,
+                             uint32_t* tvals, hipStream_t s) {
+  if (nnz == 0) return hipSuccess;
+  EmitGeom g;
+  g.W = uint32_t(W);
+  g.H = uint32_t(H);
+  g.tiles_x = uint32_t((W + kTile - 1) / kTile);
+  g.T = g.tiles_x * uint32_t((H + kTile - 1) / kTile);
+  g.C = C;
+  g.nnz = nnz;
+  g.per_blk = emit_per_block(nnz);
+  const uint64_t nblk = emit_blocks(nnz);
+  const uint2* box = reinterpret_cast<const uint2*>(aabb16);
+  {
+    ProfScope prof("k_emit_count", s);
+    hipLaunchKernelGGL(k_emit_count, dim3(uint32_t(nblk)), dim3(256), 0, s, order, box, cam_off,
+                       g, nblk, mat);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_scan_u32(mat, nullptr, nblk * kEmitRadix, nullptr, mat_off, mat_total, lb, ticket,
+                      err, s);
+  if (e != hipSuccess) return e;
+  // longer rounds when a sub-batch holds many entries
+  ProfScope prof("k_emit_write", s);
+  if (n_isects >= 8 * nnz)
+    hipLaunchKernelGGL(k_emit_write<16>, dim3(uint32_t(nblk)), dim3(256), 0, s, order, box,
+                       cam_off, g, nblk, mat_off, cap, tkeys, tvals);
+  else
+    hipLaunchKernelGGL(k_emit_write<8>, dim3(uint32_t(nblk)), dim3(256), 0, s, order, box,
+                       cam_off, g, nblk, mat_off, cap, tkeys, tvals);
+  return hipGetLastError();
+}
 
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
                               hipStream_t s) {

@@ -99,42 +99,9 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint32_t* __restric
   }
 }
 
-__device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* s_w /*[4]*/,
-                                                        uint64_t* total) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint64_t incl = wave_incl_scan_u64(v);
-  if (lane == 63) s_w[wave] = incl;
-  __syncthreads();
-  uint64_t off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint64_t t = s_w[w];
-    off += (w < wave) ? t : 0ull;
-    tot += t;
-  }
-  *total = tot;
-  return off + incl - v;
-}
-
-__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s_w, uint32_t* total) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t incl = wave_incl_scan_u32(v);
-  if (lane == 63) s_w[wave] = incl;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t t = s_w[w];
-    off += (w < wave) ? t : 0u;
-    tot += t;
-  }
-  *total = tot;
-  return off + incl - v;
-}
-
 template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void k_radix_count(const uint32_t* __restrict__ keys, uint64_t n,
-                                                    int shift, uint64_t ct,
+                                                    int shift, uint32_t dmask, uint64_t ct,
                                                     uint32_t* __restrict__ cnt,
                                                     uint64_t* __restrict__ grp) {
   constexpr uint64_t TILE = uint64_t(kSortThreads) * ITEMS;
@@ -156,7 +123,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_count(const uint32_t* __
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       const uint64_t e = b + uint64_t(i) * kSortThreads + tid;
-      if (e < e1) atomicAdd(&s_h[wave][(k[i] >> shift) & 255u], 1u);
+      if (e < e1) atomicAdd(&s_h[wave][(k[i] >> shift) & dmask], 1u);
     }
   }
   __syncthreads();
@@ -170,7 +137,7 @@ template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint64_t n, int shift,
-    uint64_t ct, const uint32_t* __restrict__ cnt, const uint64_t* __restrict__ grp,
+    uint32_t dmask, uint64_t ct, const uint32_t* __restrict__ cnt, const uint64_t* __restrict__ grp,
     uint64_t* __restrict__ grp_next) {
   constexpr int TILE = kSortThreads * ITEMS;
   __shared__ int64_t s_gstart[256];
@@ -229,7 +196,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
     for (int i = 0; i < ITEMS; ++i) {
       const uint64_t e = base + uint64_t(wave) * (ITEMS * kWave) + i * kWave + lane;
       const bool valid = e < e1;
-      const uint32_t d = (key[i] >> shift) & 255u;
+      const uint32_t d = (key[i] >> shift) & dmask;
       uint64_t peers = __ballot(valid);
 #pragma unroll
       for (int b = 0; b < kRadixBits; ++b) {
@@ -260,7 +227,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
     for (int i = 0; i < ITEMS; ++i) {
       const uint64_t e = base + uint64_t(wave) * (ITEMS * kWave) + i * kWave + lane;
       if (e < e1) {
-        const uint32_t d = (key[i] >> shift) & 255u;
+        const uint32_t d = (key[i] >> shift) & dmask;
         const uint32_t pos = s_lstart[d] + s_whist[wave][d] + rank[i];
         s_keys[pos] = key[i];
         s_vals[pos] = val[i];
@@ -281,7 +248,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
       const uint32_t li = uint32_t(j * kSortThreads + tid);
       if (li < cnt_blk) {
         const uint32_t k = s_keys[li];
-        const uint32_t d = (k >> shift) & 255u;
+        const uint32_t d = (k >> shift) & dmask;
         const uint64_t g = uint64_t(s_gstart[d] + int64_t(li));
         keys_out[g] = k;
         vals_out[g] = s_vals[li];
@@ -351,18 +318,19 @@ SortPlan sort_plan(uint64_t n) {
 
 template <int ITEMS>
 void launch_pass(const SortPlan& pl, const uint32_t* ki, const uint32_t* vi, uint32_t* ko,
-                 uint32_t* vo, uint64_t n, int shift, SortScratch& sc, hipStream_t s) {
+                 uint32_t* vo, uint64_t n, int shift, uint32_t dmask, SortScratch& sc,
+                 hipStream_t s) {
   uint64_t* grp = sc.grp + sc.parity * (kSortGroups * kRadix);
   uint64_t* grp_next = sc.grp + (sc.parity ^ 1) * (kSortGroups * kRadix);
   {
     ProfScope prof("k_radix_count", s);
     hipLaunchKernelGGL(k_radix_count<ITEMS>, dim3(pl.P), dim3(kSortThreads), 0, s, ki, n, shift,
-                       pl.ct, sc.cnt, grp);
+                       dmask, pl.ct, sc.cnt, grp);
   }
   {
     ProfScope prof("k_radix_scatter", s);
     hipLaunchKernelGGL(k_radix_scatter<ITEMS>, dim3(pl.P), dim3(kSortThreads), 0, s, ki, vi, ko,
-                       vo, n, shift, pl.ct, sc.cnt, grp, grp_next);
+                       vo, n, shift, dmask, pl.ct, sc.cnt, grp, grp_next);
   }
   sc.parity ^= 1;
 }
@@ -381,14 +349,18 @@ hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys
   if (n == 0) return hipSuccess;
   const SortPlan pl = sort_plan(n);
   uint32_t *ki = keys_a, *vi = vals_a, *ko = keys_b, *vo = vals_b;
+  // the bits are split evenly over the passes: fewer digit values per
+  // pass make longer runs of equal digits, so the scattered writes coalesce
+  const int width = bits <= 0 ? 1 : (bits + passes - 1) / passes;
   for (int p = 0; p < passes; ++p) {
-    const int shift = bit0 + kRadixBits * p;
+    const int shift = bit0 + width * p;
+    const uint32_t dmask = (1u << width) - 1u;
     if (pl.items == 4)
-      launch_pass<4>(pl, ki, vi, ko, vo, n, shift, sc, s);
+      launch_pass<4>(pl, ki, vi, ko, vo, n, shift, dmask, sc, s);
     else if (pl.items == 8)
-      launch_pass<8>(pl, ki, vi, ko, vo, n, shift, sc, s);
+      launch_pass<8>(pl, ki, vi, ko, vo, n, shift, dmask, sc, s);
     else
-      launch_pass<16>(pl, ki, vi, ko, vo, n, shift, sc, s);
+      launch_pass<16>(pl, ki, vi, ko, vo, n, shift, dmask, sc, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint32_t* t = ki;

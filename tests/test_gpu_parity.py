@@ -98,7 +98,33 @@ def test_intersect_sort_bit_exact(lib, name):
     """Stage-isolated: the oracle's own fp32 rows and box codes go in, so
     counts, keys, order and tile ranges must match bit for bit."""
     sc, _, ref = reference(name)
-    proj, isect = ref["proj"], ref["isect"]
+    check_intersect(sc, ref["proj"], ref["isect"])
+
+
+# Scenes with many tiles (over 2^16 tile ids), so that the sort by tile id
+# takes its wider first digit and, past 2^18 tiles, more than one further
+# pass. Only projection and intersection are compared.
+WIDE = {
+    "wide-2cam-4096px": workloads.SceneSpec("sh0-3000-2cam-4096px", 3000, 0, 2, 4096, 4096,
+                                            3547.0, 2.0, -3.5, 0.5, 5.0, seed=2101),
+    "wide-5cam-4096x4000": workloads.SceneSpec("sh0-2000-5cam-4096x4000", 2000, 0, 5, 4096,
+                                               4000, 3547.0, 2.0, -3.5, 0.5, 5.0, seed=2102),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE))
+def test_intersect_sort_many_tiles(lib, name):
+    sc = workloads.make_scene(WIDE[name])
+    proj = oracle.project(sc)
+    proj.screen = proj.screen.astype(np.float32).astype(np.float64)
+    isect = oracle.intersect(proj, sc["W"], sc["H"])
+    n_tiles = isect.tile_offsets.size - 1
+    print(f"{name}: tiles={n_tiles} nnz={proj.nnz} n_isects={isect.n_isects}")
+    assert n_tiles > (1 << 16)
+    check_intersect(sc, proj, isect)
+
+
+def check_intersect(sc, proj, isect):
     screen = P.to_dev(proj.screen.astype(np.float32))
     aabb = P.to_dev(P.u32_as_i32(proj.aabb16))
     cam = [0] + [int(np.searchsorted(proj.cam, c)) for c in range(1, sc["C"])] + [proj.nnz]
