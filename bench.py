@@ -92,7 +92,8 @@ def tile_sort_digits(spec):
     sort by tile id, as the library chooses them."""
     n_tiles = spec.n_cams * ((spec.width + 15) // 16) * ((spec.height + 15) // 16)
     bits = max(0, int(n_tiles - 1).bit_length())
-    b1 = 8
+    total = 1 if bits <= 8 else (bits + 7) // 8
+    b1 = max(1, (bits + total - 1) // total)
     rest = max(0, bits - b1)
     return b1, (rest + 7) // 8
 

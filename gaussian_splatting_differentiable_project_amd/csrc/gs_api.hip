@@ -91,6 +91,7 @@ struct IsectWs {
   uint32_t *ord_keys_a, *ord_keys_b, *ord_vals_b;  // launch-order sort of the tiles
   uint32_t* sort_cnt;   // radix sort chunk counts (fixed size)
   uint32_t* emit_cnt;   // [digit][emit block] entry counts
+  uint32_t* emit_rec;   // [nnz][2] rectangle of each depth-order position
   uint64_t* emit_off;   // their exclusive scan: first output position of each run
   uint64_t* emit_total;
   uint64_t phase1_bytes;  // enough to count (I still unknown)
@@ -119,6 +120,7 @@ IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects, uint64
   w.ord_vals_b = cv.take<uint32_t>(n_tiles);
   w.sort_cnt = cv.take<uint32_t>(sort_counts_bytes() / sizeof(uint32_t));
   w.emit_cnt = cv.take<uint32_t>(mat);
+  w.emit_rec = cv.take<uint32_t>(2 * n);
   w.emit_off = cv.take<uint64_t>(mat);
   w.emit_total = cv.take<uint64_t>(1);
   w.phase1_bytes = cv.off;
@@ -352,14 +354,15 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
     // Phase 3: (tile id, slot) entries in depth order, written already
     // partitioned by the low digit of the tile id (the first sort pass).
     const int tbits = bits_for(n_tiles);
-    const int b1 = emit_digit_bits();
+    const int b1 = emit_digit_bits(tbits);
     const int rest = tbits > b1 ? tbits - b1 : 0;
     const int passes = rest ? sort_passes(rest) : 0;
     // the final pass must land its values in flatten_ids
     uint32_t* v_first = (passes & 1) ? ws.tvals : flatten_ids;
     uint32_t* v_second = (passes & 1) ? flatten_ids : ws.tvals;
-    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.cam_off, C, W, H, I, I,
-                             ws.emit_cnt, ws.emit_off, ws.emit_total, ws.scan_lb, ws.ticket,
+    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.cam_off, C, W, H, b1, I, I,
+                             ws.emit_cnt, ws.emit_rec, ws.emit_off, ws.emit_total, ws.scan_lb,
+                             ws.ticket,
                              ws.err, ws.tkeys_a, v_first, s));
     // Phase 4: the remaining digits of the stable sort by tile id.
     in_b = false;

@@ -101,16 +101,18 @@ hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* 
                              int H, uint32_t* dkeys, uint32_t* dvals, uint64_t* total,
                              hipStream_t s);
 // Entries of the slots in depth order, written already stably
-// partitioned by the low emit_digit_bits() bits of their tile id (the
-// first pass of the LSD sort by tile id). Scratch: a count matrix
-// mat[emit_matrix_len(nnz)] (uint32), its scan mat_off (uint64) and total,
+// partitioned by the low `bits` = emit_digit_bits(tile_bits) bits of their
+// tile id (the first pass of the LSD sort by tile id). Scratch: a count matrix
+// mat[emit_matrix_len(nnz)] (uint32), per-position rectangle records
+// rec[2 * nnz] (uint32), the matrix scan mat_off (uint64) and its total,
 // and the scan's look-back words (ceil(emit_matrix_len / kScanTile)) and
 // ticket, which must be zero. Writes are clamped to `cap` entries.
-int emit_digit_bits();
+int emit_digit_bits(int tile_bits);
 uint64_t emit_matrix_len(uint64_t nnz);
 hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
-                             const int64_t* cam_off, int C, int W, int H, uint64_t n_isects,
-                             uint64_t cap, uint32_t* mat, uint64_t* mat_off, uint64_t* mat_total,
+                             const int64_t* cam_off, int C, int W, int H, int bits,
+                             uint64_t n_isects, uint64_t cap, uint32_t* mat, uint32_t* rec,
+                             uint64_t* mat_off, uint64_t* mat_total,
                              uint64_t* lb, uint32_t* ticket, int* err, uint32_t* tkeys,
                              uint32_t* tvals, hipStream_t s);
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,

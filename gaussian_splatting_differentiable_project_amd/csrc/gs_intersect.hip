@@ -73,10 +73,10 @@ __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* _
 // stable LSD sort by tile id. Block b owns a contiguous range of
 // depth-order positions (position i holds slot order[i]), walked in
 // sub-batches of 512. A pass of an LSD radix sort over the emitted
-// sequence would place the entries of digit d (the low 8 bits of the tile
-// id) after every entry of a smaller digit, and among equal digits in
-// emission order. That placement is computed here without ever writing
-// the unsorted sequence:
+// sequence would place the entries of digit d after every entry of a
+// smaller digit, and among equal digits in emission order. The digit is the low `bits` (at most 8) bits of the
+// tile id. That placement is computed here without ever writing the
+// unsorted sequence:
 //   k_emit_count  counts, per block, its entries of every digit (from the
 //                 tile rectangles alone: each rectangle row is a run of
 //                 consecutive tile ids, i.e. a cyclic run of digits);
@@ -96,6 +96,7 @@ constexpr uint64_t kEmitBlocks = 2048;  // target block count (8 per CU)
 struct EmitGeom {
   uint32_t W, H, tiles_x, T;
   int C;
+  uint32_t bits;          // digit width, 1..kEmitBits
   uint64_t nnz, per_blk;  // positions per block (a multiple of kEmitSlots)
 };
 
@@ -119,17 +120,21 @@ __device__ __forceinline__ void emit_slot(uint64_t i, const uint32_t* __restrict
   b0 = uint32_t(lo) * g.T + r.ty0 * g.tiles_x + r.tx0;
 }
 
-// mat[d * nblk + b] = entries of block b whose tile id has low digit d.
-// A rectangle row of wx tiles starting at tile id s covers every digit
-// floor(wx / 256) times plus the cyclic run [s, s + wx mod 256); the runs
-// are added to a difference array in LDS and summed once.
+// mat[d * nblk + b] = entries of block b whose tile id has low digit d
+// (rows d >= 2^bits are zero); rec[i] = (first tile id, wx | wy << 16) of
+// position i, so the write kernel reads its rectangles without the
+// dependent gathers. A rectangle row of wx tiles starting at
+// tile id s covers every digit floor(wx / R) times plus the cyclic run
+// [s, s + wx mod R), R = 2^bits; the runs are added to a difference array
+// in LDS and summed once.
 __global__ __launch_bounds__(256) void k_emit_count(const uint32_t* __restrict__ order,
                                                    const uint2* __restrict__ aabb16,
                                                    const int64_t* __restrict__ cam_off,
                                                    EmitGeom g, uint64_t nblk,
-                                                   uint32_t* __restrict__ mat) {
-  constexpr uint32_t R = kEmitRadix, M = R - 1;
-  __shared__ uint32_t s_diff[R];
+                                                   uint32_t* __restrict__ mat,
+                                                   uint2* __restrict__ rec) {
+  const uint32_t R = 1u << g.bits, M = R - 1;
+  __shared__ uint32_t s_diff[kEmitRadix];
   __shared__ uint32_t s_full;
   __shared__ uint32_t s_w[4];
   const int tid = threadIdx.x;
@@ -142,8 +147,9 @@ __global__ __launch_bounds__(256) void k_emit_count(const uint32_t* __restrict__
   for (uint64_t i = i0 + tid; i < i1; i += 256) {
     uint32_t slot, b0, wx, wy;
     emit_slot(i, order, aabb16, cam_off, g, slot, b0, wx, wy);
+    rec[i] = make_uint2(b0, wx | (wy << 16));  // both at most 4096
     if (wx == 0 || wy == 0) continue;
-    full += (wx >> kEmitBits) * wy;
+    full += (wx >> g.bits) * wy;
     const uint32_t rem = wx & M;
     if (rem == 0) continue;
     for (uint32_t dy = 0; dy < wy; ++dy) {
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(256) void k_emit_count(const uint32_t* __restrict__
   const uint32_t v = s_diff[tid];
   uint32_t tot;
   const uint32_t run = block_excl_scan_u32(v, s_w, &tot) + v + s_full;
-  mat[uint64_t(tid) * nblk + blockIdx.x] = run;
+  mat[uint64_t(tid) * nblk + blockIdx.x] = uint32_t(tid) < R ? run : 0u;
 }
 
 // Inclusive running maximum over the 64 lanes.
@@ -186,15 +192,14 @@ __device__ __forceinline__ uint32_t wave_incl_max_u32(uint32_t v) {
 // an owner map in LDS: every position whose first entry falls in the
 // round marks that entry, and a running maximum over the round (started
 // from the previous round's last owner) fills the rest. Ranks within a
-// digit come from 8 ballots per wave and per-wave digit counters; each
+// digit come from one ballot per digit bit and per-wave digit counters; each
 // digit run of the round is then gathered in LDS and written contiguously.
 template <int ITEMS>
 __global__ __launch_bounds__(256) void k_emit_write(
-    const uint32_t* __restrict__ order, const uint2* __restrict__ aabb16,
-    const int64_t* __restrict__ cam_off, EmitGeom g, uint64_t nblk,
+    const uint32_t* __restrict__ order, const uint2* __restrict__ rec, EmitGeom g, uint64_t nblk,
     const uint64_t* __restrict__ mat_off, uint64_t cap, uint32_t* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out) {
-  constexpr uint32_t M = kEmitRadix - 1;
+  const uint32_t M = (1u << g.bits) - 1;
   constexpr int TILE = 256 * ITEMS;
   constexpr int OWN = TILE / 256;  // owner-map entries per thread
   static_assert(64 * ITEMS < 65536, "per-wave digit counters are 16-bit");
@@ -216,20 +221,32 @@ __global__ __launch_bounds__(256) void k_emit_write(
   const uint64_t lt = lanemask_lt();
   const uint64_t i0 = blk * g.per_blk;
   const uint64_t i1 = i0 + g.per_blk < g.nnz ? i0 + g.per_blk : g.nnz;
+  // slot data of a sub-batch, two positions per thread; the next
+  // sub-batch's is loaded while this one is written
+  constexpr int PT = kEmitSlots / 256;
+  uint2 nrec[PT];
+  uint32_t nslot[PT];
+  auto fetch = [&](uint64_t sb) {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const uint64_t i = sb + j * 256 + tid;
+      nrec[j] = i < i1 ? rec[i] : make_uint2(0u, 1u);  // width 1, height 0: no entries
+      nslot[j] = i < i1 ? order[i] : 0u;
+    }
+  };
+  fetch(i0);
   for (uint64_t sb = i0; sb < i1; sb += kEmitSlots) {
 #pragma unroll
-    for (int j = 0; j < kEmitSlots / 256; ++j) {
+    for (int j = 0; j < PT; ++j) {
       const int li = j * 256 + tid;
-      const uint64_t i = sb + li;
-      uint32_t slot = 0, b0 = 0, wx = 1, wy = 0;
-      if (i < i1) emit_slot(i, order, aabb16, cam_off, g, slot, b0, wx, wy);
-      s_slot[li] = slot;
-      s_base[li] = b0;
+      const uint32_t wx = nrec[j].y & 0xFFFFu, wy = nrec[j].y >> 16;
+      s_slot[li] = nslot[j];
+      s_base[li] = nrec[j].x;
       s_wx[li] = wx ? wx : 1u;
       s_off[li] = uint64_t(wx) * wy;  // counts for now
     }
+    if (sb + kEmitSlots < i1) fetch(sb + kEmitSlots);
     __syncthreads();
-    constexpr int PT = kEmitSlots / 256;
     uint64_t c[PT], sum = 0;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
@@ -287,27 +304,29 @@ __global__ __launch_bounds__(256) void k_emit_write(
       __syncthreads();
       carry = s_own[TILE - 1];
       uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
+      const uint32_t n_here =
+          uint32_t((btot - rb) < uint64_t(TILE) ? (btot - rb) : uint64_t(TILE));
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        const int le = wave * (ITEMS * kWave) + i * kWave + lane;
-        const uint64_t e = rb + uint64_t(le);
-        const bool valid = e < btot;
-        uint32_t t = 0, v = 0;
-        if (valid) {
-          const uint32_t own = s_own[le];
-          const uint32_t k = uint32_t(e - s_off[own]);
-          const uint32_t w = s_wx[own];
-          // k < 2^24 and w <= 4096: the fp32 quotient is within a step or
-          // two of floor(k / w); the corrections make it exact
-          uint32_t dy = uint32_t(float(k) * __builtin_amdgcn_rcpf(float(w)));
-          while (dy * w > k) --dy;
-          while ((dy + 1) * w <= k) ++dy;
-          t = s_base[own] + dy * g.tiles_x + (k - dy * w);
-          v = s_slot[own];
-        }
+        const uint32_t le = uint32_t(wave * (ITEMS * kWave) + i * kWave + lane);
+        const bool valid = le < n_here;
+        // straight-line for every lane (an entry past the round's end reads
+        // owner 0's data and is dropped), so the items' loads overlap
+        const uint32_t own = s_own[le];
+        const uint32_t k = uint32_t(rb + le - s_off[own]);
+        const uint32_t w = s_wx[own];
+        // k < 2^24 and w <= 4096: the fp32 quotient is within one of
+        // floor(k / w); two corrections each way make it exact
+        uint32_t dy = uint32_t(float(k) * __builtin_amdgcn_rcpf(float(w)));
+        dy = dy * w > k ? dy - 1 : dy;
+        dy = dy * w > k ? dy - 1 : dy;
+        dy = (dy + 1) * w <= k ? dy + 1 : dy;
+        dy = (dy + 1) * w <= k ? dy + 1 : dy;
+        const uint32_t t = valid ? s_base[own] + dy * g.tiles_x + (k - dy * w) : 0u;
         key[i] = t;
-        val[i] = v;
-        // rank among the wave's earlier entries with the same digit
+        val[i] = s_slot[own];
+        // rank among the wave's earlier entries with the same digit (digits
+        // are below 2^bits, so the ballots of higher bits agree everywhere)
         const uint32_t d = t & M;
         uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -343,16 +362,14 @@ __global__ __launch_bounds__(256) void k_emit_write(
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        const uint64_t e = rb + uint64_t(wave) * (ITEMS * kWave) + i * kWave + lane;
-        if (e < btot) {
+        const uint32_t le = uint32_t(wave * (ITEMS * kWave) + i * kWave + lane);
+        if (le < n_here) {
           const uint32_t pos = uint32_t(s_whist[wave][key[i] & M]) + rank[i];
           s_keys[pos] = key[i];
           s_vals[pos] = val[i];
         }
       }
       __syncthreads();
-      const uint32_t n_here =
-          uint32_t((btot - rb) < uint64_t(TILE) ? (btot - rb) : uint64_t(TILE));
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
         const uint32_t li = uint32_t(j * 256 + tid);
@@ -372,20 +389,46 @@ __global__ __launch_bounds__(256) void k_emit_write(
 }
 
 // tile_offsets[t] = first sorted position whose tile id is >= t.
-// Grid-stride over the n + 1 boundaries: a dispatch's work-item count is
-// a 32-bit quantity, and n_isects can exceed 2^32.
+// Each lane takes four consecutive boundaries with one 16-byte load; the
+// key before its first one comes from the lane below (or, for lane 0, one
+// more load). Grid-stride over the n + 1 boundaries: a dispatch's
+// work-item count is a 32-bit quantity, and n_isects can exceed 2^32.
 __global__ __launch_bounds__(256) void k_tile_ranges(const uint32_t* __restrict__ tkeys,
                                                     uint64_t n, uint64_t n_tiles,
                                                     int64_t* __restrict__ toff) {
+  const uint64_t groups = (n + 4) / 4;  // boundaries 0..n, four per lane
   const uint64_t stride = uint64_t(gridDim.x) * 256;
-  for (uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x; i <= n; i += stride) {
-    // ids are < n_tiles by construction; the clamps only keep the writes
-    // inside toff[0..n_tiles] whatever the keys hold
-    uint64_t cur = i < n ? tkeys[i] : n_tiles;
-    cur = cur < n_tiles ? cur : n_tiles;
-    int64_t prev = i > 0 ? int64_t(tkeys[i - 1]) : -1;
-    prev = prev < int64_t(n_tiles) ? prev : int64_t(n_tiles);
-    for (int64_t t = prev + 1; t <= int64_t(cur); ++t) toff[t] = int64_t(i);
+  const int lane = threadIdx.x & 63;
+  // ids are < n_tiles by construction; the clamps only keep the writes
+  // inside toff[0..n_tiles] whatever the keys hold
+  const uint32_t cap = n_tiles < 0xFFFFFFFFull ? uint32_t(n_tiles) : 0xFFFFFFFFu;
+  for (uint64_t q = uint64_t(blockIdx.x) * 256 + threadIdx.x; q < groups; q += stride) {
+    const uint64_t i0 = q * 4;
+    uint32_t k[4];
+    if (i0 + 3 < n) {
+      const uint4 v = *reinterpret_cast<const uint4*>(tkeys + i0);
+      k[0] = v.x, k[1] = v.y, k[2] = v.z, k[3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k[j] = i0 + j < n ? tkeys[i0 + j] : cap;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[j] = k[j] < cap ? k[j] : cap;
+    // lanes leave the loop from the top, so the lane below is still in it
+    const uint32_t below = __shfl_up(k[3], 1, kWave);
+    int64_t prev = -1;
+    if (i0 > 0) {
+      const uint32_t p = lane == 0 ? tkeys[i0 - 1] : below;
+      prev = int64_t(p < cap ? p : cap);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t i = i0 + j;
+      if (i > n) break;
+      const int64_t cur = i < n ? int64_t(k[j]) : int64_t(cap);
+      for (int64_t t = prev + 1; t <= cur; ++t) toff[t] = int64_t(i);
+      prev = cur;
+    }
   }
 }
 
@@ -436,7 +479,15 @@ hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* 
   return hipGetLastError();
 }
 
-int emit_digit_bits() { return kEmitBits; }
+// The digit widths of the whole sort by tile id are balanced: P passes
+// in all (P = ceil(bits / 8), at least one, the emit's included), the
+// emit's digit ceil(bits / P) wide. Narrower digits make longer runs of
+// equal digits, so the scattered writes coalesce better.
+int emit_digit_bits(int tile_bits) {
+  const int passes = tile_bits <= kEmitBits ? 1 : (tile_bits + kEmitBits - 1) / kEmitBits;
+  const int b = (tile_bits + passes - 1) / passes;
+  return b < 1 ? 1 : b;
+}
 
 namespace {
 
@@ -455,8 +506,9 @@ uint64_t emit_blocks(uint64_t nnz) {
 uint64_t emit_matrix_len(uint64_t nnz) { return emit_blocks(nnz) * kEmitRadix; }
 
 hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
-                             const int64_t* cam_off, int C, int W, int H, uint64_t n_isects,
-                             uint64_t cap, uint32_t* mat, uint64_t* mat_off, uint64_t* mat_total,
+                             const int64_t* cam_off, int C, int W, int H, int bits,
+                             uint64_t n_isects, uint64_t cap, uint32_t* mat, uint32_t* rec,
+                             uint64_t* mat_off, uint64_t* mat_total,
                              uint64_t* lb, uint32_t* ticket, int* err, uint32_t* tkeys,
                              uint32_t* tvals, hipStream_t s) {
   if (nnz == 0) return hipSuccess;
@@ -466,6 +518,7 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
   g.tiles_x = uint32_t((W + kTile - 1) / kTile);
   g.T = g.tiles_x * uint32_t((H + kTile - 1) / kTile);
   g.C = C;
+  g.bits = uint32_t(bits < 1 ? 1 : bits > kEmitBits ? kEmitBits : bits);
   g.nnz = nnz;
   g.per_blk = emit_per_block(nnz);
   const uint64_t nblk = emit_blocks(nnz);
@@ -473,29 +526,30 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
   {
     ProfScope prof("k_emit_count", s);
     hipLaunchKernelGGL(k_emit_count, dim3(uint32_t(nblk)), dim3(256), 0, s, order, box, cam_off,
-                       g, nblk, mat);
+                       g, nblk, mat, reinterpret_cast<uint2*>(rec));
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_scan_u32(mat, nullptr, nblk * kEmitRadix, nullptr, mat_off, mat_total, lb, ticket,
                       err, s);
   if (e != hipSuccess) return e;
-  // longer rounds when a sub-batch holds many entries
+  // longer rounds (fewer, longer runs per digit) when a sub-batch holds
+  // many entries; shorter ones keep more blocks resident otherwise
   ProfScope prof("k_emit_write", s);
-  if (n_isects >= 8 * nnz)
-    hipLaunchKernelGGL(k_emit_write<16>, dim3(uint32_t(nblk)), dim3(256), 0, s, order, box,
-                       cam_off, g, nblk, mat_off, cap, tkeys, tvals);
+  if (n_isects >= 32 * nnz)
+    hipLaunchKernelGGL(k_emit_write<16>, dim3(uint32_t(nblk)), dim3(256), 0, s, order,
+                       reinterpret_cast<const uint2*>(rec), g, nblk, mat_off, cap, tkeys, tvals);
   else
-    hipLaunchKernelGGL(k_emit_write<8>, dim3(uint32_t(nblk)), dim3(256), 0, s, order, box,
-                       cam_off, g, nblk, mat_off, cap, tkeys, tvals);
+    hipLaunchKernelGGL(k_emit_write<8>, dim3(uint32_t(nblk)), dim3(256), 0, s, order,
+                       reinterpret_cast<const uint2*>(rec), g, nblk, mat_off, cap, tkeys, tvals);
   return hipGetLastError();
 }
 
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
                               hipStream_t s) {
   ProfScope prof("k_tile_ranges", s);
-  hipLaunchKernelGGL(k_tile_ranges, dim3(grid_stride_blocks(n + 1)), dim3(256), 0, s, tkeys, n, n_tiles,
-                     toff);
+  hipLaunchKernelGGL(k_tile_ranges, dim3(grid_stride_blocks((n + 4) / 4)), dim3(256), 0, s, tkeys, n,
+                     n_tiles, toff);
   return hipGetLastError();
 }
 
