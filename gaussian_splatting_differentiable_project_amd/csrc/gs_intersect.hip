@@ -187,13 +187,17 @@ __device__ __forceinline__ uint32_t wave_incl_max_u32(uint32_t v) {
 
 // mat_off: exclusive scan of mat in [digit][block] order. Writes are
 // clamped to `cap` entries.
-// Each sub-batch's entries are walked in rounds of 256 * ITEMS, in
-// emission order. The position owning each entry of a round comes from
-// an owner map in LDS: every position whose first entry falls in the
-// round marks that entry, and a running maximum over the round (started
-// from the previous round's last owner) fills the rest. Ranks within a
-// digit come from one ballot per digit bit and per-wave digit counters; each
-// digit run of the round is then gathered in LDS and written contiguously.
+// The block's entries are walked in emission order in rounds of up to
+// 256 * ITEMS. Slot data lives in a window of two sub-batch halves: a
+// sub-batch is loaded into the half whose previous occupant has no entry
+// left at or after the round's start, so rounds run across sub-batch
+// boundaries and are full unless the window runs dry. The position owning
+// each entry of a round comes from an owner map in LDS: every position
+// whose first entry falls in the round marks that entry with its block-
+// relative index, and a running maximum over the round (started from the
+// previous round's last owner) fills the rest. Ranks within a digit come
+// from one ballot per digit bit and per-wave digit counters; each digit
+// run of the round is then gathered in LDS and written contiguously.
 template <int ITEMS>
 __global__ __launch_bounds__(256) void k_emit_write(
     const uint32_t* __restrict__ order, const uint2* __restrict__ rec, EmitGeom g, uint64_t nblk,
@@ -201,15 +205,18 @@ __global__ __launch_bounds__(256) void k_emit_write(
     uint32_t* __restrict__ vals_out) {
   const uint32_t M = (1u << g.bits) - 1;
   constexpr int TILE = 256 * ITEMS;
-  constexpr int OWN = TILE / 256;  // owner-map entries per thread
+  constexpr int OWN = TILE / 256;        // owner-map entries per thread
+  constexpr int WIN = 2 * kEmitSlots;    // window of two halves
+  constexpr int PT = kEmitSlots / 256;   // positions per thread in a half
   static_assert(64 * ITEMS < 65536, "per-wave digit counters are 16-bit");
-  __shared__ uint64_t s_off[kEmitSlots + 1];  // sub-batch exclusive entry offsets
-  __shared__ uint32_t s_slot[kEmitSlots];
-  __shared__ uint32_t s_base[kEmitSlots];     // global id of the rectangle's first tile
-  __shared__ uint32_t s_wx[kEmitSlots];       // rectangle width in tiles
+  __shared__ uint64_t s_off[WIN];             // block entry offset of each position's first entry
+  __shared__ uint64_t s_end[2];               // block entry offset where each half's sub-batch ends
+  __shared__ uint32_t s_slot[WIN];
+  __shared__ uint32_t s_base[WIN];            // global id of the rectangle's first tile
+  __shared__ uint32_t s_wx[WIN];              // rectangle width in tiles
   __shared__ int64_t s_gstart[kEmitRadix];    // output position of digit run d, minus its LDS start
   __shared__ uint16_t s_whist[4][kEmitRadix]; // per-wave digit counts, then LDS starts
-  __shared__ uint16_t s_own[TILE];            // owning position of each entry of the round
+  __shared__ uint32_t s_own[TILE];            // block-relative position owning each entry
   __shared__ uint64_t s_w64[4];
   __shared__ uint32_t s_w32[4];
   __shared__ uint32_t s_keys[TILE];
@@ -221,170 +228,194 @@ __global__ __launch_bounds__(256) void k_emit_write(
   const uint64_t lt = lanemask_lt();
   const uint64_t i0 = blk * g.per_blk;
   const uint64_t i1 = i0 + g.per_blk < g.nnz ? i0 + g.per_blk : g.nnz;
-  // slot data of a sub-batch, two positions per thread; the next
-  // sub-batch's is loaded while this one is written
-  constexpr int PT = kEmitSlots / 256;
+  const uint64_t n_sb = (i1 - i0 + kEmitSlots - 1) / kEmitSlots;
+  // slot data of the next sub-batch, two positions per thread, loaded
+  // ahead of its use
   uint2 nrec[PT];
   uint32_t nslot[PT];
   auto fetch = [&](uint64_t sb) {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const uint64_t i = sb + j * 256 + tid;
+      const uint64_t i = i0 + sb * kEmitSlots + j * 256 + tid;
       nrec[j] = i < i1 ? rec[i] : make_uint2(0u, 1u);  // width 1, height 0: no entries
       nslot[j] = i < i1 ? order[i] : 0u;
     }
   };
-  fetch(i0);
-  for (uint64_t sb = i0; sb < i1; sb += kEmitSlots) {
+  uint64_t loaded = 0;  // sub-batches loaded so far (uniform)
+  uint64_t e_end = 0;   // block entry offset after the last loaded one (uniform)
+  // Loads sub-batch `loaded` into half (loaded & 1). The caller has
+  // synchronized, so no lane still reads that half.
+  auto load = [&]() {
+    const int h = int(loaded & 1) * kEmitSlots;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const int li = j * 256 + tid;
+      const int li = h + j * 256 + tid;
       const uint32_t wx = nrec[j].y & 0xFFFFu, wy = nrec[j].y >> 16;
       s_slot[li] = nslot[j];
       s_base[li] = nrec[j].x;
       s_wx[li] = wx ? wx : 1u;
       s_off[li] = uint64_t(wx) * wy;  // counts for now
     }
-    if (sb + kEmitSlots < i1) fetch(sb + kEmitSlots);
+    if (loaded + 1 < n_sb) fetch(loaded + 1);
     __syncthreads();
     uint64_t c[PT], sum = 0;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      c[j] = s_off[tid * PT + j];
+      c[j] = s_off[h + tid * PT + j];
       sum += c[j];
     }
     uint64_t btot;
-    uint64_t o = block_excl_scan_u64(sum, s_w64, &btot);
+    uint64_t o = e_end + block_excl_scan_u64(sum, s_w64, &btot);
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      s_off[tid * PT + j] = o;
+      s_off[h + tid * PT + j] = o;
       o += c[j];
     }
-    if (tid == 0) s_off[kEmitSlots] = btot;
-    uint32_t carry = 0;  // owner of the last entry of the previous round
-    for (uint64_t rb = 0; rb < btot; rb += TILE) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) s_whist[w][tid] = 0;
-#pragma unroll
-      for (int q = 0; q < OWN; ++q) s_own[q * 256 + tid] = 0;
-      __syncthreads();
-      // positions whose first entry lies in this round mark it
-#pragma unroll
-      for (int j = 0; j < PT; ++j) {
-        const int pos = j * 256 + tid;
-        const uint64_t first = s_off[pos];
-        if (s_off[pos + 1] > first && first >= rb && first - rb < uint64_t(TILE))
-          s_own[first - rb] = uint16_t(pos);
-      }
-      __syncthreads();
-      {  // running maximum over the round, OWN consecutive entries per thread
-        uint32_t m = 0;
-        uint32_t loc[OWN];
-#pragma unroll
-        for (int q = 0; q < OWN; ++q) {
-          const uint32_t x = s_own[tid * OWN + q];
-          m = x > m ? x : m;
-          loc[q] = m;
-        }
-        const uint32_t incl = wave_incl_max_u32(m);
-        if (lane == 63) s_w32[wave] = incl;
+    e_end += btot;
+    if (tid == 0) s_end[loaded & 1] = e_end;
+    ++loaded;
+  };
+  fetch(0);
+  uint64_t rb = 0;
+  uint32_t carry = 0;  // owner of the last entry of the previous round
+  while (true) {
+    // fill the window while the round is not covered and the half to
+    // refill holds no entry at or after rb
+    while (loaded < n_sb && e_end < rb + TILE) {
+      if (loaded >= 2) {
         __syncthreads();
-        uint32_t before = carry;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t x = s_w32[w];
-          before = (w < wave && x > before) ? x : before;
-        }
-        const uint32_t prev = __shfl_up(incl, 1, kWave);
-        if (lane > 0 && prev > before) before = prev;
-#pragma unroll
-        for (int q = 0; q < OWN; ++q)
-          s_own[tid * OWN + q] = uint16_t(loc[q] > before ? loc[q] : before);
+        if (s_end[loaded & 1] > rb) break;
       }
       __syncthreads();
-      carry = s_own[TILE - 1];
-      uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
-      const uint32_t n_here =
-          uint32_t((btot - rb) < uint64_t(TILE) ? (btot - rb) : uint64_t(TILE));
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        const uint32_t le = uint32_t(wave * (ITEMS * kWave) + i * kWave + lane);
-        const bool valid = le < n_here;
-        // straight-line for every lane (an entry past the round's end reads
-        // owner 0's data and is dropped), so the items' loads overlap
-        const uint32_t own = s_own[le];
-        const uint32_t k = uint32_t(rb + le - s_off[own]);
-        const uint32_t w = s_wx[own];
-        // k < 2^24 and w <= 4096: the fp32 quotient is within one of
-        // floor(k / w); two corrections each way make it exact
-        uint32_t dy = uint32_t(float(k) * __builtin_amdgcn_rcpf(float(w)));
-        dy = dy * w > k ? dy - 1 : dy;
-        dy = dy * w > k ? dy - 1 : dy;
-        dy = (dy + 1) * w <= k ? dy + 1 : dy;
-        dy = (dy + 1) * w <= k ? dy + 1 : dy;
-        const uint32_t t = valid ? s_base[own] + dy * g.tiles_x + (k - dy * w) : 0u;
-        key[i] = t;
-        val[i] = s_slot[own];
-        // rank among the wave's earlier entries with the same digit (digits
-        // are below 2^bits, so the ballots of higher bits agree everywhere)
-        const uint32_t d = t & M;
-        uint64_t peers = __ballot(valid);
-#pragma unroll
-        for (int b = 0; b < kEmitBits; ++b) {
-          const bool bit = (d >> b) & 1u;
-          const uint64_t bb = __ballot(bit);
-          peers &= bit ? bb : ~bb;
-        }
-        const uint32_t before = s_whist[wave][d];
-        const uint32_t r = uint32_t(__popcll(peers & lt));
-        if (valid && r == 0) s_whist[wave][d] = uint16_t(before + uint32_t(__popcll(peers)));
-        rank[i] = before + r;
-      }
-      __syncthreads();
-      // digit tid: its LDS start plus the earlier waves' counts, and the
-      // output position of its run
-      uint32_t cw[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) cw[w] = s_whist[w][tid];
-      const uint32_t cnt = cw[0] + cw[1] + cw[2] + cw[3];
-      uint32_t ttot;
-      const uint32_t ls = block_excl_scan_u32(cnt, s_w32, &ttot);
-      {
-        uint32_t x = ls;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          s_whist[w][tid] = uint16_t(x);
-          x += cw[w];
-        }
-      }
-      s_gstart[tid] = int64_t(run) - int64_t(ls);
-      run += cnt;
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        const uint32_t le = uint32_t(wave * (ITEMS * kWave) + i * kWave + lane);
-        if (le < n_here) {
-          const uint32_t pos = uint32_t(s_whist[wave][key[i] & M]) + rank[i];
-          s_keys[pos] = key[i];
-          s_vals[pos] = val[i];
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < ITEMS; ++j) {
-        const uint32_t li = uint32_t(j * 256 + tid);
-        if (li < n_here) {
-          const uint32_t k = s_keys[li];
-          const uint64_t gpos = uint64_t(s_gstart[k & M] + int64_t(li));
-          if (gpos < cap) {
-            keys_out[gpos] = k;
-            vals_out[gpos] = s_vals[li];
-          }
-        }
-      }
-      __syncthreads();
+      load();
     }
-    __syncthreads();  // the next sub-batch overwrites the slot data
+    __syncthreads();
+    if (rb >= e_end) break;  // nothing loaded is left, and nothing more to load
+    const uint32_t n_here = uint32_t(e_end - rb < uint64_t(TILE) ? e_end - rb : uint64_t(TILE));
+    // block-relative index of the sub-batch in each half
+    const uint64_t sb_new = loaded - 1, sb_old = loaded >= 2 ? loaded - 2 : loaded - 1;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s_whist[w][tid] = 0;
+#pragma unroll
+    for (int q = 0; q < OWN; ++q) s_own[q * 256 + tid] = 0;
+    __syncthreads();
+    // positions whose first entry lies in this round mark it
+#pragma unroll
+    for (int j = 0; j < WIN / 256; ++j) {
+      const int wpos = j * 256 + tid;
+      const int h = wpos / kEmitSlots, li = wpos % kEmitSlots;
+      // a half is live once a sub-batch has been loaded into it
+      const bool live = loaded >= 2 || uint64_t(h) == (sb_new & 1);
+      const uint64_t first = s_off[wpos];
+      const uint64_t end = li + 1 < kEmitSlots ? s_off[wpos + 1] : s_end[h];
+      const uint64_t sb = (sb_new & 1) == uint64_t(h) ? sb_new : sb_old;
+      if (live && end > first && first >= rb && first - rb < uint64_t(n_here))
+        s_own[first - rb] = uint32_t(sb * kEmitSlots + li);
+    }
+    __syncthreads();
+    {  // running maximum over the round, OWN consecutive entries per thread
+      uint32_t m = 0;
+      uint32_t loc[OWN];
+#pragma unroll
+      for (int q = 0; q < OWN; ++q) {
+        const uint32_t x = s_own[tid * OWN + q];
+        m = x > m ? x : m;
+        loc[q] = m;
+      }
+      const uint32_t incl = wave_incl_max_u32(m);
+      if (lane == 63) s_w32[wave] = incl;
+      __syncthreads();
+      uint32_t before = carry;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = s_w32[w];
+        before = (w < wave && x > before) ? x : before;
+      }
+      const uint32_t prev = __shfl_up(incl, 1, kWave);
+      if (lane > 0 && prev > before) before = prev;
+#pragma unroll
+      for (int q = 0; q < OWN; ++q) s_own[tid * OWN + q] = loc[q] > before ? loc[q] : before;
+    }
+    __syncthreads();
+    carry = s_own[n_here - 1];
+    uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const uint32_t le = uint32_t(wave * (ITEMS * kWave) + i * kWave + lane);
+      const bool valid = le < n_here;
+      // straight-line for every lane (an entry past the round's end reads
+      // some loaded position's data and is dropped), so the loads overlap
+      const uint32_t own = s_own[le] % WIN;  // window slot of the owner
+      const uint32_t k = uint32_t(rb + le - s_off[own]);
+      const uint32_t w = s_wx[own];
+      // k < 2^24 and w <= 4096: the fp32 quotient is within one of
+      // floor(k / w); two corrections each way make it exact
+      uint32_t dy = uint32_t(float(k) * __builtin_amdgcn_rcpf(float(w)));
+      dy = dy * w > k ? dy - 1 : dy;
+      dy = dy * w > k ? dy - 1 : dy;
+      dy = (dy + 1) * w <= k ? dy + 1 : dy;
+      dy = (dy + 1) * w <= k ? dy + 1 : dy;
+      const uint32_t t = valid ? s_base[own] + dy * g.tiles_x + (k - dy * w) : 0u;
+      key[i] = t;
+      val[i] = s_slot[own];
+      // rank among the wave's earlier entries with the same digit (digits
+      // are below 2^bits, so the ballots of higher bits agree everywhere)
+      const uint32_t d = t & M;
+      uint64_t peers = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < kEmitBits; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bb = __ballot(bit);
+        peers &= bit ? bb : ~bb;
+      }
+      const uint32_t before = s_whist[wave][d];
+      const uint32_t r = uint32_t(__popcll(peers & lt));
+      if (valid && r == 0) s_whist[wave][d] = uint16_t(before + uint32_t(__popcll(peers)));
+      rank[i] = before + r;
+    }
+    __syncthreads();
+    // digit tid: its LDS start plus the earlier waves' counts, and the
+    // output position of its run
+    uint32_t cw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) cw[w] = s_whist[w][tid];
+    const uint32_t cnt = cw[0] + cw[1] + cw[2] + cw[3];
+    uint32_t ttot;
+    const uint32_t ls = block_excl_scan_u32(cnt, s_w32, &ttot);
+    {
+      uint32_t x = ls;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        s_whist[w][tid] = uint16_t(x);
+        x += cw[w];
+      }
+    }
+    s_gstart[tid] = int64_t(run) - int64_t(ls);
+    run += cnt;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const uint32_t le = uint32_t(wave * (ITEMS * kWave) + i * kWave + lane);
+      if (le < n_here) {
+        const uint32_t pos = uint32_t(s_whist[wave][key[i] & M]) + rank[i];
+        s_keys[pos] = key[i];
+        s_vals[pos] = val[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const uint32_t li = uint32_t(j * 256 + tid);
+      if (li < n_here) {
+        const uint32_t k = s_keys[li];
+        const uint64_t gpos = uint64_t(s_gstart[k & M] + int64_t(li));
+        if (gpos < cap) {
+          keys_out[gpos] = k;
+          vals_out[gpos] = s_vals[li];
+        }
+      }
+    }
+    rb += n_here;
   }
 }
 
@@ -533,10 +564,11 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
   e = launch_scan_u32(mat, nullptr, nblk * kEmitRadix, nullptr, mat_off, mat_total, lb, ticket,
                       err, s);
   if (e != hipSuccess) return e;
-  // longer rounds (fewer, longer runs per digit) when a sub-batch holds
-  // many entries; shorter ones keep more blocks resident otherwise
+  // 4096-entry rounds (longer runs per digit: each is written in fewer,
+  // fuller memory granules) once a block holds at least two of them;
+  // 2048-entry rounds keep more blocks resident otherwise
   ProfScope prof("k_emit_write", s);
-  if (n_isects >= 32 * nnz)
+  if (n_isects >= 8192 * nblk)
     hipLaunchKernelGGL(k_emit_write<16>, dim3(uint32_t(nblk)), dim3(256), 0, s, order,
                        reinterpret_cast<const uint2*>(rec), g, nblk, mat_off, cap, tkeys, tvals);
   else
