@@ -98,7 +98,7 @@ def tile_sort_digits(spec):
     return b1, (rest + 7) // 8
 
 
-def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes):
+def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes, depth_passes=4):
     """Algorithmic HBM bytes of one launch of an HBM-bound kernel."""
     N, C, K = spec.n, spec.n_cams, spec.K
     Np = ((N + 127) // 128) * 128
@@ -113,7 +113,8 @@ def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes):
         return 6 * (44 + 12 * K) * N + 40 * nnz + pairs / 8 + 4 * pairs / 128
     if kernel == "k_radix_scatter":  # mean over the step's passes: 8 B read + 8 B written per key
         tiles = C * ((spec.width + 15) // 16) * ((spec.height + 15) // 16)
-        return 16 * (4 * nnz + tile_passes * n_isects + 2 * tiles) / (4 + tile_passes + 2)
+        return (16 * (depth_passes * nnz + tile_passes * n_isects + 2 * tiles)
+                / (depth_passes + tile_passes + 2))
     if kernel == "k_emit_write":     # order + box per pair; 8 B per entry
         return 12 * nnz + 8 * n_isects
     return None
@@ -338,6 +339,11 @@ def main():
     V = int(vis[: spec.n_cams * Np].reshape(spec.n_cams, Np).any(0).sum())
     tx, ty = gsd.tiles(spec.width, spec.height)
     _, tile_passes = tile_sort_digits(spec)
+    # the depth sort runs its top 8-bit pass only when the keys differ there
+    depth_passes = 3
+    if nnz:
+        kb = p.screen[:nnz, 6].contiguous().view(torch.int32).to(torch.int64)
+        depth_passes += int(((int(kb.min()) ^ int(kb.max())) >> 24) != 0)
     walked, comp = raster_work(last, spec.width, spec.height)
 
     if dom in ("k_raster_bwd", "k_raster_fwd"):
@@ -349,7 +355,7 @@ def main():
                 "flops_per_launch": work, "evaluations_walked": walked,
                 "composited_upper_bound": comp, "launch_ms": dom_ms}
     else:
-        byt = hbm_bytes(dom, spec, nnz, n_is, V, tile_passes)
+        byt = hbm_bytes(dom, spec, nnz, n_is, V, tile_passes, depth_passes)
         achieved = byt / (dom_ms * 1e-3) / 1e9 if byt else None
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
@@ -395,17 +401,17 @@ def main():
         out["arena"] = {"alias": arena.alias, "MiB": arena.buf.numel() / 2**20}
     hb = {}
     for kn, ms in kernel_ms.items():
-        byt = hbm_bytes(kn, spec, nnz, n_is, V, tile_passes)
+        byt = hbm_bytes(kn, spec, nnz, n_is, V, tile_passes, depth_passes)
         if byt:
             if kn == "k_radix_scatter":   # per-launch mean; ms is the step's sum
-                byt *= 4 + tile_passes + 2
+                byt *= depth_passes + tile_passes + 2
             hb[kn] = byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     # the whole sort (depth passes over the pairs, tile passes over the
     # entries, launch-order passes over the tiles; each pass reads and
     # writes a 4 B key and a 4 B value per element) against the time of all
     # its kernels: counting and scatter
     sort_ms = sum(kernel_ms.get(k, 0.0) for k in ("k_radix_count", "k_radix_scatter"))
-    sort_bytes = 16 * (4 * nnz + tile_passes * n_is + 2 * spec.n_cams * tx * ty)
+    sort_bytes = 16 * (depth_passes * nnz + tile_passes * n_is + 2 * spec.n_cams * tx * ty)
     if sort_ms > 0:
         hb["sort (all radix kernels)"] = sort_bytes / (sort_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     out["hbm_frac_by_kernel"] = hb

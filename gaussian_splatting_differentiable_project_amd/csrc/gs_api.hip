@@ -80,7 +80,7 @@ ProjectWs carve_project(void* base, int64_t n_groups, int32_t C) {
 // every array the first phase needs (sized by nnz and the tile count),
 // then the entry arrays sized by n_isects.
 struct IsectWs {
-  uint64_t* total;      // n_isects (prep)
+  uint64_t* total;      // [1 + kPrepBlocks]: n_isects, then per-block depth key ranges (prep)
   int* err;
   uint32_t* ticket;     // scan of the emit count matrix
   uint64_t* scan_lb;    // its look-back words
@@ -104,7 +104,7 @@ IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects, uint64
   IsectWs w{};
   const uint64_t n = uint64_t(nnz);
   const uint64_t mat = emit_matrix_len(n);
-  w.total = cv.take<uint64_t>(1);
+  w.total = cv.take<uint64_t>(1 + kPrepBlocks);
   w.err = cv.take<int>(1);
   w.ticket = cv.take<uint32_t>(1);
   w.scan_lb = cv.take<uint64_t>((mat + kScanTile - 1) / kScanTile + 1);
@@ -320,7 +320,7 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   sc.cnt = ws.sort_cnt;
   sc.grp = ws.sort_grp;
   HostStage* hs = nullptr;
-  GS_TRY(host_stage(1, &hs));
+  GS_TRY(host_stage(1 + kPrepBlocks, &hs));
 
   // Phase 1: depth keys, per-slot tile counts and their exact 64-bit total.
   GS_TRY(launch_fill_u32(workspace, 0u, ws.zero_words, s));
@@ -328,17 +328,36 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
                         hipMemcpyHostToDevice, s));
   GS_TRY(launch_isect_prep(uint64_t(nnz), screen, aabb16, W, H, ws.dkeys_a, ws.dvals_a, ws.total,
                            s));
-  GS_TRY(hipMemcpyAsync(hs->buf, ws.total, sizeof(uint64_t), hipMemcpyDeviceToHost, s));
+  GS_TRY(hipMemcpyAsync(hs->buf, ws.total, (1 + kPrepBlocks) * sizeof(uint64_t),
+                        hipMemcpyDeviceToHost, s));
   GS_TRY(hipEventRecord(hs->ev, s));
   // Phase 2 needs only nnz-sized memory, so it is queued before the host
-  // waits for the total: a stable sort of the slots by depth.
+  // waits for the total: a stable sort of the slots by depth, low 24 bits
+  // first (three passes, ending in the b buffers).
   bool in_b = false;
   const hipError_t e = launch_sort_passes(ws.dkeys_a, ws.dvals_a, ws.dkeys_b, ws.dvals_b,
-                                          uint64_t(nnz), 0, 32, sc, &in_b, s);
-  const uint32_t* order = in_b ? ws.dvals_b : ws.dvals_a;
+                                          uint64_t(nnz), 0, 24, sc, &in_b, s);
   // wait even after an error: the copy into the staging words must land
   const hipError_t e2 = hipEventSynchronize(hs->ev);
   if (e != hipSuccess || e2 != hipSuccess) return GS_E_HIP;
+  // The top 8 bits need a pass only when the keys differ there: every key
+  // lies between the smallest and the largest, so when those two agree
+  // above bit 24, all keys do (positive depths order like their bits).
+  uint32_t kmax = 0, knmin = 0;
+  for (uint32_t b = 0; b < kPrepBlocks; ++b) {
+    const uint64_t w = uint64_t(hs->buf[1 + b]);
+    const uint32_t m = uint32_t(w >> 32), nm = uint32_t(w);
+    kmax = m > kmax ? m : kmax;
+    knmin = nm > knmin ? nm : knmin;
+  }
+  const uint32_t kmin = ~knmin;
+  if (nnz > 0 && ((kmin ^ kmax) >> 24) != 0) {
+    bool in_b2 = false;
+    GS_TRY(launch_sort_passes(ws.dkeys_b, ws.dvals_b, ws.dkeys_a, ws.dvals_a, uint64_t(nnz), 24,
+                              8, sc, &in_b2, s));
+    in_b = !in_b2;  // one pass: from b back into a
+  }
+  const uint32_t* order = in_b ? ws.dvals_b : ws.dvals_a;
   const uint64_t I = uint64_t(hs->buf[0]);
   *n_isects_out = int64_t(I);
   if (I >= (uint64_t(1) << 62)) return GS_E_OVERFLOW;

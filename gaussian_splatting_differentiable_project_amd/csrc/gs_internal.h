@@ -97,6 +97,10 @@ hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys
                               SortScratch& sc, bool* in_b, hipStream_t s);
 
 // Intersection stages (gs_intersect.hip).
+// total[1 + kPrepBlocks] (zeroed): total[0] = intersection count; for
+// each block b, total[1 + b] = (largest depth key << 32) | complement of
+// its smallest depth key.
+constexpr uint32_t kPrepBlocks = 1024;
 hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* aabb16, int W,
                              int H, uint32_t* dkeys, uint32_t* dvals, uint64_t* total,
                              hipStream_t s);

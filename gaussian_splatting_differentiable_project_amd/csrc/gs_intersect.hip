@@ -44,28 +44,60 @@ __device__ __forceinline__ uint32_t rect_count(const TileRect& r) {
   return wx * wy;
 }
 
+// Inclusive running maximum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_max_u32(uint32_t v) {
+  const int l = __lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t t = __shfl_up(v, o, kWave);
+    if (l >= o) v = t > v ? t : v;
+  }
+  return v;
+}
+
 // Per slot: depth key bits and identity value for the depth sort, and
 // the exact 64-bit total of tile counts (one atomic per work-group).
+// total[1 + b] receives block b's largest key (high word) and the
+// complement of its smallest key (low word): the host reduces them and
+// skips the depth passes over digits that every key shares. Words of
+// blocks that are not launched stay zero, which neither maximum notices.
 __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* __restrict__ screen,
                                                    const uint2* __restrict__ aabb16, uint32_t W,
                                                    uint32_t H, uint32_t* __restrict__ dkeys,
                                                    uint32_t* __restrict__ dvals, uint64_t* total) {
   __shared__ uint64_t s_w[4];
+  __shared__ uint32_t s_max[4], s_nmin[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   uint64_t n = 0;
+  uint32_t kmax = 0, knmin = 0;
   // grid-stride, so few blocks contend for the one 64-bit total
   const uint64_t stride = uint64_t(gridDim.x) * 256;
   for (uint64_t i = uint64_t(blockIdx.x) * 256 + tid; i < nnz; i += stride) {
-    dkeys[i] = __float_as_uint(screen[i * kRow + 6]);
+    const uint32_t k = __float_as_uint(screen[i * kRow + 6]);
+    dkeys[i] = k;
     dvals[i] = uint32_t(i);
+    kmax = k > kmax ? k : kmax;
+    knmin = ~k > knmin ? ~k : knmin;
     n += rect_count(rect_of(aabb16[i], W, H));
   }
   const uint64_t incl = wave_incl_scan_u64(n);
-  if (lane == 63) s_w[wave] = incl;
+  const uint32_t wmax = wave_incl_max_u32(kmax), wnmin = wave_incl_max_u32(knmin);
+  if (lane == 63) {
+    s_w[wave] = incl;
+    s_max[wave] = wmax;
+    s_nmin[wave] = wnmin;
+  }
   __syncthreads();
   if (tid == 0) {
     const uint64_t b = s_w[0] + s_w[1] + s_w[2] + s_w[3];
     if (b) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)b);
+    uint32_t m = 0, nm = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      m = s_max[w] > m ? s_max[w] : m;
+      nm = s_nmin[w] > nm ? s_nmin[w] : nm;
+    }
+    total[1 + blockIdx.x] = (uint64_t(m) << 32) | nm;
   }
 }
 
@@ -172,17 +204,6 @@ __global__ __launch_bounds__(256) void k_emit_count(const uint32_t* __restrict__
   uint32_t tot;
   const uint32_t run = block_excl_scan_u32(v, s_w, &tot) + v + s_full;
   mat[uint64_t(tid) * nblk + blockIdx.x] = uint32_t(tid) < R ? run : 0u;
-}
-
-// Inclusive running maximum over the 64 lanes.
-__device__ __forceinline__ uint32_t wave_incl_max_u32(uint32_t v) {
-  const int l = __lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o, kWave);
-    if (l >= o) v = t > v ? t : v;
-  }
-  return v;
 }
 
 // mat_off: exclusive scan of mat in [digit][block] order. Writes are
@@ -502,7 +523,7 @@ hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* 
                              hipStream_t s) {
   if (nnz == 0) return hipSuccess;
   uint32_t blocks = grid_for(nnz);
-  if (blocks > 1024) blocks = 1024;
+  if (blocks > kPrepBlocks) blocks = kPrepBlocks;
   ProfScope prof("k_isect_prep", s);
   hipLaunchKernelGGL(k_isect_prep, dim3(blocks), dim3(256), 0, s, nnz, screen,
                      reinterpret_cast<const uint2*>(aabb16), uint32_t(W), uint32_t(H), dkeys,

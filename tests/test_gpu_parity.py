@@ -124,6 +124,24 @@ def test_intersect_sort_many_tiles(lib, name):
     check_intersect(sc, proj, isect)
 
 
+# Depths from about 2 to 10 (across 8.0, where the fp32 exponent and the
+# key's top byte change), so the depth sort needs its fourth pass; the
+# other small scenes keep every depth within [2, 8) and skip it.
+DEEP = workloads.SceneSpec("sh1-3000-2cam-200x150-deep", 3000, 1, 2, 200, 150, 180.0, 4.0,
+                           -3.0, 0.5, 6.0, seed=2103)
+
+
+def test_intersect_sort_wide_depth_range(lib):
+    sc = workloads.make_scene(DEEP)
+    proj = oracle.project(sc)
+    proj.screen = proj.screen.astype(np.float32).astype(np.float64)
+    isect = oracle.intersect(proj, sc["W"], sc["H"])
+    bits = proj.screen[:, 6].astype(np.float32).view(np.uint32)
+    print(f"depth keys {bits.min():#x}..{bits.max():#x} nnz={proj.nnz} n_isects={isect.n_isects}")
+    assert (int(bits.min()) ^ int(bits.max())) >> 24 != 0
+    check_intersect(sc, proj, isect)
+
+
 def check_intersect(sc, proj, isect):
     screen = P.to_dev(proj.screen.astype(np.float32))
     aabb = P.to_dev(P.u32_as_i32(proj.aabb16))
