@@ -156,14 +156,14 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
   const uint32_t g = blockIdx.x / kSortGroup;
   const uint32_t G = (gridDim.x + kSortGroup - 1) / kSortGroup;
   uint64_t tot_d = 0, before = 0;
-#pragma unroll
+#pragma unroll 8
   for (uint32_t i = 0; i < uint32_t(kSortGroups); ++i) {
     const uint64_t v = grp[(i < G ? i : G - 1) * 256 + tid];
     tot_d += i < G ? v : 0ull;
     before += i < g ? v : 0ull;
   }
   const uint32_t q0 = g * kSortGroup;
-#pragma unroll
+#pragma unroll 8
   for (uint32_t i = 0; i + 1 < uint32_t(kSortGroup); ++i) {
     const uint32_t q = q0 + i;
     const uint32_t v = cnt[uint64_t(q < blockIdx.x ? q : blockIdx.x) * 256 + tid];
@@ -180,12 +180,19 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
   const uint64_t e0 = uint64_t(blockIdx.x) * ct * TILE;
   uint64_t e1 = e0 + ct * uint64_t(TILE);
   if (e1 > n) e1 = n;
+  // Each lane reads items i * 64 past its own first key of a tile: one
+  // base pointer per lane, the item offsets are immediates.
+  const uint64_t lane0 = uint64_t(wave) * (ITEMS * kWave) + lane;
   uint32_t key[ITEMS], val[ITEMS];
+  {
+    const uint32_t* kp = keys_in + e0 + lane0;
+    const uint32_t* vp = vals_in + e0 + lane0;
+    const int64_t left = int64_t(e1) - int64_t(e0 + lane0);  // keys from this lane's first on
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const uint64_t e = e0 + uint64_t(wave) * (ITEMS * kWave) + i * kWave + lane;
-    key[i] = e < e1 ? keys_in[e] : 0u;
-    val[i] = e < e1 ? vals_in[e] : 0u;
+    for (int i = 0; i < ITEMS; ++i) {
+      key[i] = i * kWave < left ? kp[i * kWave] : 0u;
+      val[i] = i * kWave < left ? vp[i * kWave] : 0u;
+    }
   }
   for (uint64_t base = e0; base < e1; base += TILE) {
 #pragma unroll
@@ -235,12 +242,16 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
     }
     __syncthreads();
     // the next tile's loads overlap this tile's scatter
-    const uint64_t nb = base + TILE;
+    {
+      const uint64_t nb = base + TILE;
+      const uint32_t* kp = keys_in + nb + lane0;
+      const uint32_t* vp = vals_in + nb + lane0;
+      const int64_t left = int64_t(e1) - int64_t(nb + lane0);
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const uint64_t e = nb + uint64_t(wave) * (ITEMS * kWave) + i * kWave + lane;
-      key[i] = e < e1 ? keys_in[e] : 0u;
-      val[i] = e < e1 ? vals_in[e] : 0u;
+      for (int i = 0; i < ITEMS; ++i) {
+        key[i] = i * kWave < left ? kp[i * kWave] : 0u;
+        val[i] = i * kWave < left ? vp[i * kWave] : 0u;
+      }
     }
     const uint64_t cnt_blk = (e1 - base) < uint64_t(TILE) ? (e1 - base) : uint64_t(TILE);
 #pragma unroll
