@@ -32,16 +32,19 @@ __device__ __forceinline__ void zero_local(GaussLocal<T>& G) {
 // Visibility of one pair: the depth test on the fp32 key depth (exact by
 // definition) and the four margins of the clamped box, u + r > 0,
 // u - r < W, v + r > 0, v - r < H. They are first evaluated in fp32; a
-// margin within a generous bound of zero (1e-3 relative to the terms
-// involved, far above the fp32 rounding of this chain, including the
-// cancellation inside the radius) leaves the pair "unsure", and only then
-// is it evaluated again in fp64 as the compaction pass evaluates it.
+// margin within a bound of zero leaves the pair "unsure", and only then is
+// it evaluated again in fp64 as the compaction pass evaluates it. The
+// bound has two parts: 4e-5 of the coordinate scale (1 + |u| + |u - cx|),
+// against a measured fp32 error of the centre below 1.2e-6 of it, and
+// 6e-4 of r, against the radius' worst case: sqrt(m^2 - det) cancels for
+// nearly isotropic covariances, leaving a relative error of about
+// 2^-12 in lambda_max and 1.7e-4 in r.
 __device__ __forceinline__ bool visible_fp32(const PairFwd<float>& P, float cx, float cy,
                                              float W, float H, bool* unsure) {
   *unsure = false;
   if (!(P.z32 > kNear)) return false;
-  const float tx = 1e-3f * (1.f + fabsf(P.u) + fabsf(P.u - cx) + P.r);
-  const float ty = 1e-3f * (1.f + fabsf(P.v) + fabsf(P.v - cy) + P.r);
+  const float tx = 4e-5f * (1.f + fabsf(P.u) + fabsf(P.u - cx)) + 6e-4f * P.r;
+  const float ty = 4e-5f * (1.f + fabsf(P.v) + fabsf(P.v - cy)) + 6e-4f * P.r;
   const float m0 = P.u + P.r, m1 = W - (P.u - P.r), m2 = P.v + P.r, m3 = H - (P.v - P.r);
   if (!(fabsf(m0) < 3e38f && fabsf(m1) < 3e38f && fabsf(m2) < 3e38f && fabsf(m3) < 3e38f &&
         tx < 3e38f && ty < 3e38f)) {
