@@ -555,7 +555,13 @@ uint64_t emit_blocks(uint64_t nnz) {
 
 }  // namespace
 
-uint64_t emit_matrix_len(uint64_t nnz) { return emit_blocks(nnz) * kEmitRadix; }
+// Sized by min(sub-batches, kEmitBlocks), which bounds emit_blocks and,
+// unlike it, never decreases as nnz grows, so a workspace sized for a
+// capacity also fits every smaller count.
+uint64_t emit_matrix_len(uint64_t nnz) {
+  const uint64_t subs = (nnz + kEmitSlots - 1) / kEmitSlots;
+  return (subs < kEmitBlocks ? subs : kEmitBlocks) * kEmitRadix;
+}
 
 hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
                              const int64_t* cam_off, int C, int W, int H, int bits,

@@ -8,6 +8,7 @@ import json
 import os
 import re
 
+import numpy as np
 import pytest
 
 import gaussian_splatting_differentiable_project_amd as gsd
@@ -67,6 +68,20 @@ def test_workspace_sizes_monotone(lib):
     assert f(1, 7680, 7680, 13_000_000, 5_000_000_000) > 3 * 4 * 5_000_000_000
     assert lib.gs_project_workspace_bytes(15_000_000, 5) > 0
     assert lib.gs_intersect_workspace_bytes(0, 10, 10, 1, 1) == 0  # C < 1
+
+
+def test_intersect_workspace_never_shrinks_as_nnz_grows(lib):
+    """A workspace sized for a capacity (the growth-only buffers, the phase
+    arena) must fit every smaller pair count: the size may not dip where the
+    emit's block layout changes (every 2048 sub-batches of 512 pairs)."""
+    f = lib.gs_intersect_workspace_bytes
+    edges = [512 * 2048 * k + d for k in (1, 2, 3) for d in (-513, -1, 0, 1, 511, 512, 513)]
+    rng = np.random.default_rng(7)
+    pts = sorted(set(edges + [int(x) for x in rng.integers(1, 40_000_000, 200)] + [971_385, 1_068_524]))
+    for C, W, H in ((1, 1920, 1080), (5, 1297, 840)):
+        sizes = [f(C, W, H, n, 1_000_000) for n in pts]
+        bad = [(pts[i], pts[i + 1]) for i in range(len(pts) - 1) if sizes[i + 1] < sizes[i]]
+        assert not bad, bad[:5]
 
 
 def test_invalid_arguments_need_no_gpu(lib):
