@@ -124,6 +124,23 @@ def test_intersect_sort_many_tiles(lib, name):
     check_intersect(sc, proj, isect)
 
 
+# About 2.1M visible pairs: past 2048 sub-batches of 512, so each emit
+# block walks three sub-batches and its rounds cross sub-batch boundaries
+# (the smaller scenes give every block a single sub-batch).
+MULTI = workloads.SceneSpec("sh0-2.2M-1080p", 2_200_000, 0, 1, 1920, 1080, 1100.0, 2.0, -4.5, 0.5,
+                            5.0, seed=2105)
+
+
+def test_intersect_sort_multi_subbatch(lib):
+    sc = workloads.make_scene(MULTI)
+    proj = oracle.project(sc)
+    proj.screen = proj.screen.astype(np.float32).astype(np.float64)
+    isect = oracle.intersect(proj, sc["W"], sc["H"])
+    print(f"nnz={proj.nnz} n_isects={isect.n_isects}")
+    assert proj.nnz > 2048 * 512 * 2
+    check_intersect(sc, proj, isect)
+
+
 # Depths from about 2 to 10 (across 8.0, where the fp32 exponent and the
 # key's top byte change), so the depth sort needs its fourth pass; the
 # other small scenes keep every depth within [2, 8) and skip it.
