@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
 
 // Pixels per lane of the forward and backward tiles (1, 2 or 4, i.e. 4, 2
 // or 1 wave per tile). GS_RASTER_PPT_FWD / GS_RASTER_PPT_BWD override the
-// defaults for launch-shape sweeps.
+// defaults for launch-shape sweeps (0 = the default).
 int ppt_from_env(const char* name, int dflt) {
   const char* v = std::getenv(name);
   if (!v) return dflt;
@@ -507,18 +507,24 @@ int ppt_from_env(const char* name, int dflt) {
   return (p == 1 || p == 2 || p == 4) ? p : dflt;
 }
 
-constexpr int kFwdPPT = 1;
+// Forward: four waves per tile while tiles are few, two (two pixels per
+// lane, half the staging and barrier work per pixel) from kFwdManyTiles
+// tiles on. Measured: 5-camera 1600x1064 (33,500 tiles) 1.11 -> 0.92 ms,
+// 15M 5-camera (21,730) 0.72 -> 0.58 ms, 7680x7680 (230,400) 4.10 ->
+// 3.49 ms; 1920x1080 (8,160) even; 128x128 (64) 0.14 -> 0.20 ms.
+constexpr int64_t kFwdManyTiles = 16384;
 constexpr int kBwdPPT = 4;
 
 hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uint32_t* ids,
                              const int64_t* toff, const uint32_t* order, const float* background,
                              float* out_rgb, float* out_T, float* out_depth, int32_t* last_ids,
                              hipStream_t s) {
-  static const int ppt = ppt_from_env("GS_RASTER_PPT_FWD", kFwdPPT);
+  static const int ppt_env = ppt_from_env("GS_RASTER_PPT_FWD", 0);
   const int tiles_x = (W + kTile - 1) / kTile, tiles_y = (H + kTile - 1) / kTile;
   const int T = tiles_x * tiles_y;
   const int64_t blocks = int64_t(C) * T;
   if (blocks == 0) return hipSuccess;
+  const int ppt = ppt_env ? ppt_env : (blocks >= kFwdManyTiles ? 2 : 1);
   if (!fits_dispatch(uint64_t(blocks), kTilePix)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)};
 #define GS_FWD(P, D)                                                                           \

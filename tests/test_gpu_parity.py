@@ -219,6 +219,40 @@ def test_raster_fwd_stage(lib, name, ordered):
     np.testing.assert_array_equal(lg[ok], last_o[ok])
 
 
+# 32,768 tiles: past the tile count from which the forward runs two pixels
+# per lane (two waves per tile) instead of one.
+MANY_TILES = workloads.SceneSpec("sh0-4000-2cam-2048px", 4000, 0, 2, 2048, 2048, 1773.0, 2.0,
+                                 -3.5, 0.5, 5.0, seed=2106)
+
+
+def test_raster_fwd_stage_many_tiles(lib):
+    sc = workloads.make_scene(MANY_TILES)
+    proj = oracle.project(sc)
+    rows32 = proj.screen.astype(np.float32)
+    proj.screen = rows32.astype(np.float64)
+    isect = oracle.intersect(proj, sc["W"], sc["H"])
+    C, W, H = sc["C"], sc["W"], sc["H"]
+    assert isect.tile_offsets.size - 1 >= 16384
+    rgb_o, T_o, last_o, _ = oracle.rasterize_fwd(proj.screen, isect.flatten_ids,
+                                                 isect.tile_offsets, C, W, H)
+    rgb = torch.empty(C, H, W, 3, device="cuda")
+    T = torch.empty(C, H, W, device="cuda")
+    last = torch.empty(C, H, W, dtype=torch.int32, device="cuda")
+    order = P.to_dev(launch_order(isect.tile_offsets))
+    st = gsd.gs_rasterize_fwd(C, W, H, P.to_dev(rows32), P.to_dev(P.u32_as_i32(isect.flatten_ids)),
+                              P.to_dev(isect.tile_offsets), order, None, rgb, T, None, last)
+    torch.cuda.synchronize()
+    assert st == 0
+    frag = P.fragile_pixels(rows32, isect.flatten_ids, isect.tile_offsets, C, W, H)
+    ok = ~frag
+    e_rgb = np.abs(rgb.cpu().numpy() - rgb_o)[ok].max()
+    e_T = np.abs(T.cpu().numpy() - T_o)[ok].max()
+    lg = last.cpu().numpy()
+    print(f"fragile px={int(frag.sum())}/{frag.size} rgb err={e_rgb:.2e} T err={e_T:.2e}")
+    assert e_rgb <= P.IMG_TOL and e_T <= P.IMG_TOL
+    np.testing.assert_array_equal(lg[ok], last_o[ok])
+
+
 @pytest.mark.parametrize("ordered", [False, True], ids=["id-order", "heavy-first"])
 @pytest.mark.parametrize("name", SCENES)
 def test_raster_bwd_stage(lib, name, ordered):
