@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* _
 constexpr int kEmitBits = 8;
 constexpr uint32_t kEmitRadix = 1u << kEmitBits;
 constexpr int kEmitSlots = 512;      // positions per sub-batch
-constexpr uint64_t kEmitBlocks = 2048;  // target block count (8 per CU)
+constexpr uint64_t kEmitBlocks = 8192;  // target block count (32 per CU; measured against 2048 and 16384)
 
 struct EmitGeom {
   uint32_t W, H, tiles_x, T;

@@ -124,10 +124,11 @@ def test_intersect_sort_many_tiles(lib, name):
     check_intersect(sc, proj, isect)
 
 
-# About 2.1M visible pairs: past 2048 sub-batches of 512, so each emit
-# block walks three sub-batches and its rounds cross sub-batch boundaries
-# (the smaller scenes give every block a single sub-batch).
-MULTI = workloads.SceneSpec("sh0-2.2M-1080p", 2_200_000, 0, 1, 1920, 1080, 1100.0, 2.0, -4.5, 0.5,
+# About 9.2M visible pairs: past 8192 emit blocks of one 512-pair
+# sub-batch, so each emit block walks three sub-batches and its rounds
+# cross sub-batch boundaries (the smaller scenes give every block a single
+# sub-batch). About 60M entries; the oracle needs about 30 s and 8 GB.
+MULTI = workloads.SceneSpec("sh0-9.5M-1080p", 9_500_000, 0, 1, 1920, 1080, 1100.0, 2.0, -4.5, 0.5,
                             5.0, seed=2105)
 
 
@@ -137,7 +138,7 @@ def test_intersect_sort_multi_subbatch(lib):
     proj.screen = proj.screen.astype(np.float32).astype(np.float64)
     isect = oracle.intersect(proj, sc["W"], sc["H"])
     print(f"nnz={proj.nnz} n_isects={isect.n_isects}")
-    assert proj.nnz > 2048 * 512 * 2
+    assert proj.nnz > 8192 * 512 * 2
     check_intersect(sc, proj, isect)
 
 
