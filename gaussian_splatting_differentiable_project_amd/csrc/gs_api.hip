@@ -379,7 +379,7 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
     // the final pass must land its values in flatten_ids
     uint32_t* v_first = (passes & 1) ? ws.tvals : flatten_ids;
     uint32_t* v_second = (passes & 1) ? flatten_ids : ws.tvals;
-    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.cam_off, C, W, H, b1, I, I,
+    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.cam_off, C, W, H, b1, I,
                              ws.emit_cnt, ws.emit_rec, ws.emit_off, ws.emit_total, ws.scan_lb,
                              ws.ticket,
                              ws.err, ws.tkeys_a, v_first, s));

@@ -115,7 +115,7 @@ int emit_digit_bits(int tile_bits);
 uint64_t emit_matrix_len(uint64_t nnz);
 hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
                              const int64_t* cam_off, int C, int W, int H, int bits,
-                             uint64_t n_isects, uint64_t cap, uint32_t* mat, uint32_t* rec,
+                             uint64_t cap, uint32_t* mat, uint32_t* rec,
                              uint64_t* mat_off, uint64_t* mat_total,
                              uint64_t* lb, uint32_t* ticket, int* err, uint32_t* tkeys,
                              uint32_t* tvals, hipStream_t s);
