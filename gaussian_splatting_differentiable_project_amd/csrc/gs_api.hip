@@ -274,8 +274,10 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t
   HostStage* hs = nullptr;
   GS_TRY(host_stage(uint64_t(C) + 1, &hs));
   GS_TRY(launch_fill_u32(workspace, 0u, ws.bytes / 4, s));
-  GS_TRY(launch_project_mask(a, mask, wg_count, s));
-  GS_TRY(launch_scan_u32(wg_count, nullptr, uint64_t(n_groups), wg_scan, nullptr, ws.total,
+  GS_TRY(launch_project_mask(a, mask, s));
+  // the group counts are the popcounts of the mask words; the scan takes
+  // them from the words and writes them out on the way
+  GS_TRY(launch_scan_u32(nullptr, mask, wg_count, uint64_t(n_groups), wg_scan, nullptr, ws.total,
                          ws.lookback, ws.ticket, ws.err, s));
   GS_TRY(launch_cam_offsets(wg_scan, Np / kMaskGroup, C, ws.total, ws.cam_off, s));
   GS_TRY(hipMemcpyAsync(hs->buf, ws.cam_off, sizeof(int64_t) * (C + 1), hipMemcpyDeviceToHost, s));

@@ -42,8 +42,7 @@ struct ProjectArgs {
 
 ShNorm sh_norm_table();
 
-hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, uint32_t* wg_count,
-                               hipStream_t s);
+hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, hipStream_t s);
 hipError_t launch_project_compact(const ProjectArgs& a, const uint64_t* mask,
                                   const uint32_t* wg_scan, float* screen, uint32_t* aabb16,
                                   hipStream_t s);
@@ -67,12 +66,14 @@ hipError_t launch_project_bwd(const ProjectArgs& a, const uint64_t* mask,
                               float* v_quats, float* v_log_scales, float* v_opacity_logits,
                               float* v_sh, int accumulate, const AdamArgs* adam, hipStream_t s);
 
-// Exclusive scan of n uint32 values (optionally gathered through idx) into
-// uint32 or uint64 outputs; the total is written to *total (device).
-// Scratch: lookback[ceil(n / kScanTile)] + one ticket; both must be zero.
-hipError_t launch_scan_u32(const uint32_t* in, const uint32_t* idx, uint64_t n, uint32_t* out32,
-                           uint64_t* out64, uint64_t* total, uint64_t* lookback,
-                           uint32_t* ticket, int* err, hipStream_t s);
+// Exclusive scan of n uint32 values into uint32 or uint64 outputs; the
+// total is written to *total (device). With `mask` non-null the values are
+// the popcounts of mask word pairs (2e, 2e + 1), also written to counts[e],
+// and `in` is unused. Scratch: lookback[ceil(n / kScanTile)] + one ticket;
+// both must be zero.
+hipError_t launch_scan_u32(const uint32_t* in, const uint64_t* mask, uint32_t* counts,
+                           uint64_t n, uint32_t* out32, uint64_t* out64, uint64_t* total,
+                           uint64_t* lookback, uint32_t* ticket, int* err, hipStream_t s);
 
 hipError_t launch_fill_u32(void* p, uint32_t v, uint64_t n_words, hipStream_t s);
 

@@ -588,7 +588,8 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_scan_u32(mat, nullptr, nblk * kEmitRadix, nullptr, mat_off, mat_total, lb, ticket,
+  e = launch_scan_u32(mat, nullptr, nullptr, nblk * kEmitRadix, nullptr, mat_off, mat_total, lb,
+                      ticket,
                       err, s);
   if (e != hipSuccess) return e;
   // 2048-entry rounds: four blocks per CU stay resident (4096-entry rounds

@@ -57,8 +57,7 @@ __device__ __forceinline__ bool visible_fp32(const PairFwd<float>& P, float cx, 
   return false;
 }
 
-__global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint64_t* mask,
-                                                             uint32_t* wg_count) {
+__global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint64_t* mask) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t g = int64_t(blockIdx.x) * kMaskGroup + tid;
   const bool valid = g < a.N;
@@ -72,10 +71,12 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint
     zero_local(Gf);
   GaussLocal<double> G;
   bool have_g64 = false;
-  __shared__ uint32_t pc[2][2];
   const float Wf = float(a.W), Hf = float(a.H);
+  Camera kn = load_camera(a.viewmats, a.Ks, 0);
   for (int c = 0; c < a.C; ++c) {
-    const Camera k = load_camera(a.viewmats, a.Ks, c);
+    const Camera k = kn;
+    // the next camera's parameters load while this one is projected
+    if (c + 1 < a.C) kn = load_camera(a.viewmats, a.Ks, c + 1);
     PairFwd<float> Pf;
     pair_fwd(k, Gf, Wf, Hf, Pf);
     bool unsure;
@@ -94,12 +95,7 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint
     }
     const uint64_t word = __ballot(valid && vis);
     const int64_t p0 = int64_t(c) * a.N_pad + int64_t(blockIdx.x) * kMaskGroup;
-    if (lane == 0) {
-      mask[p0 / 64 + wave] = word;
-      pc[c & 1][wave] = uint32_t(__popcll(word));
-    }
-    __syncthreads();
-    if (tid == 0) wg_count[p0 / kMaskGroup] = pc[c & 1][0] + pc[c & 1][1];
+    if (lane == 0) mask[p0 / 64 + wave] = word;
   }
 }
 
@@ -309,14 +305,12 @@ ShNorm sh_norm_table() {
   return t;
 }
 
-hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, uint32_t* wg_count,
-                               hipStream_t s) {
+hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, hipStream_t s) {
   const int64_t blocks = a.N_pad / kMaskGroup;
   if (blocks == 0) return hipSuccess;
   if (!fits_dispatch(uint64_t(blocks), kMaskGroup)) return hipErrorInvalidConfiguration;
   ProfScope prof("k_project_mask", s);
-  hipLaunchKernelGGL(k_project_mask, dim3(uint32_t(blocks)), dim3(kMaskGroup), 0, s, a, mask,
-                     wg_count);
+  hipLaunchKernelGGL(k_project_mask, dim3(uint32_t(blocks)), dim3(kMaskGroup), 0, s, a, mask);
   return hipGetLastError();
 }
 

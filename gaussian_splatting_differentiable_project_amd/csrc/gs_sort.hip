@@ -36,9 +36,12 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t v, uint64_t n) {
   for (uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
 }
 
-template <bool GATHER, bool OUT64>
+// FROM_MASK: element e is the popcount of mask words 2e and 2e + 1 (one
+// 128-pair group of the visibility bitmask), also written to counts[e].
+template <bool FROM_MASK, bool OUT64>
 __global__ __launch_bounds__(kScanThreads) void k_scan(const uint32_t* __restrict__ in,
-                                                       const uint32_t* __restrict__ idx, uint64_t n,
+                                                       const uint64_t* __restrict__ mask,
+                                                       uint32_t* __restrict__ counts, uint64_t n,
                                                        uint32_t* __restrict__ out32,
                                                        uint64_t* __restrict__ out64,
                                                        uint64_t* total, uint64_t* lb,
@@ -57,7 +60,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint32_t* __restric
   for (int i = 0; i < kScanItems; ++i) {
     const uint64_t e = base + i;
     uint32_t x = 0;
-    if (e < n) x = GATHER ? in[idx[e]] : in[e];
+    if (e < n) {
+      if (FROM_MASK) {
+        x = uint32_t(__popcll(mask[2 * e]) + __popcll(mask[2 * e + 1]));
+        counts[e] = x;
+      } else {
+        x = in[e];
+      }
+    }
     v[i] = x;
     tsum += x;
   }
@@ -281,24 +291,24 @@ hipError_t launch_fill_u32(void* p, uint32_t v, uint64_t n_words, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_scan_u32(const uint32_t* in, const uint32_t* idx, uint64_t n, uint32_t* out32,
-                           uint64_t* out64, uint64_t* total, uint64_t* lookback,
-                           uint32_t* ticket, int* err, hipStream_t s) {
+hipError_t launch_scan_u32(const uint32_t* in, const uint64_t* mask, uint32_t* counts,
+                           uint64_t n, uint32_t* out32, uint64_t* out64, uint64_t* total,
+                           uint64_t* lookback, uint32_t* ticket, int* err, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const uint64_t blocks = (n + kScanTile - 1) / kScanTile;
   if (!fits_dispatch(blocks, kScanThreads)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)}, block{uint32_t(kScanThreads)};
   ProfScope prof("k_scan", s);
-  if (idx) {
+  if (mask) {
     if (out64)
-      hipLaunchKernelGGL((k_scan<true, true>), grid, block, 0, s, in, idx, n, out32, out64, total, lookback, ticket, err);
+      hipLaunchKernelGGL((k_scan<true, true>), grid, block, 0, s, in, mask, counts, n, out32, out64, total, lookback, ticket, err);
     else
-      hipLaunchKernelGGL((k_scan<true, false>), grid, block, 0, s, in, idx, n, out32, out64, total, lookback, ticket, err);
+      hipLaunchKernelGGL((k_scan<true, false>), grid, block, 0, s, in, mask, counts, n, out32, out64, total, lookback, ticket, err);
   } else {
     if (out64)
-      hipLaunchKernelGGL((k_scan<false, true>), grid, block, 0, s, in, idx, n, out32, out64, total, lookback, ticket, err);
+      hipLaunchKernelGGL((k_scan<false, true>), grid, block, 0, s, in, mask, counts, n, out32, out64, total, lookback, ticket, err);
     else
-      hipLaunchKernelGGL((k_scan<false, false>), grid, block, 0, s, in, idx, n, out32, out64, total, lookback, ticket, err);
+      hipLaunchKernelGGL((k_scan<false, false>), grid, block, 0, s, in, mask, counts, n, out32, out64, total, lookback, ticket, err);
   }
   return hipGetLastError();
 }
