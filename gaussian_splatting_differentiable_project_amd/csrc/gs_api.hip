@@ -396,11 +396,16 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
     if (sorted_keys) GS_TRY(launch_compose_keys(tkeys, flatten_ids, screen, I, sorted_keys, s));
   }
   // Phase 6: launch order for the raster calls, longest tiles first (a
-  // stable sort of 16-bit inverted counts: two passes end in tile_order).
+  // stable sort of 16-bit inverted counts): ranks of unique keys for small
+  // tile counts, else two radix passes that end in tile_order.
   if (tile_order) {
-    GS_TRY(launch_tile_order_keys(tile_offsets, n_tiles, ws.ord_keys_a, tile_order, s));
-    GS_TRY(launch_sort_passes(ws.ord_keys_a, tile_order, ws.ord_keys_b, ws.ord_vals_b, n_tiles, 0,
-                              16, sc, &in_b, s));
+    if (tile_order_small(n_tiles)) {
+      GS_TRY(launch_tile_order_small(tile_offsets, n_tiles, tile_order, s));
+    } else {
+      GS_TRY(launch_tile_order_keys(tile_offsets, n_tiles, ws.ord_keys_a, tile_order, s));
+      GS_TRY(launch_sort_passes(ws.ord_keys_a, tile_order, ws.ord_keys_b, ws.ord_vals_b, n_tiles,
+                                0, 16, sc, &in_b, s));
+    }
   }
   return check_device_error(ws.err, s);
 }

@@ -122,6 +122,10 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
                              uint32_t* tvals, hipStream_t s);
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
                               hipStream_t s);
+// Heavy-first launch order in one kernel for small tile counts.
+bool tile_order_small(uint64_t n_tiles);
+hipError_t launch_tile_order_small(const int64_t* toff, uint64_t n_tiles, uint32_t* order,
+                                   hipStream_t s);
 hipError_t launch_tile_order_keys(const int64_t* toff, uint64_t n_tiles, uint32_t* keys,
                                   uint32_t* vals, hipStream_t s);
 hipError_t launch_compose_keys(const uint32_t* tkeys, const uint32_t* ids, const float* screen,

@@ -509,6 +509,73 @@ __global__ __launch_bounds__(256) void k_tile_order_keys(const int64_t* __restri
   }
 }
 
+// The launch order for at most kOrderSmall tiles without a radix sort. The
+// key (0xFFFF - saturated count) << 16 | tile id is unique per tile, so the
+// position of tile i in the stable heavy-first order is the number of keys
+// below its own. A block ranks 64 tiles (one per lane); its sixteen waves
+// split the other keys, built in LDS a chunk at a time from the offsets
+// (all of a thread's loads issued before the first is used) and read back
+// as 16-byte broadcasts.
+constexpr uint32_t kOrderSmall = 16384;
+constexpr uint32_t kOrderChunk = 4096;
+constexpr uint32_t kOrderThreads = 1024;
+constexpr uint32_t kOrderLoads = (kOrderChunk + kOrderThreads) / kOrderThreads;  // covers len + 1
+
+__device__ __forceinline__ uint32_t order_key(int64_t n, uint32_t t) {
+  return ((0xFFFFu - uint32_t(n < 0xFFFF ? n : 0xFFFF)) << 16) | t;
+}
+
+__global__ __launch_bounds__(kOrderThreads) void k_tile_order_rank(
+    const int64_t* __restrict__ toff, uint32_t n_tiles, uint32_t* __restrict__ order) {
+  __shared__ int64_t s_off[kOrderChunk + 1];
+  __shared__ uint4 s_k[kOrderChunk / 4];
+  __shared__ uint32_t s_part[kOrderThreads / 64][64];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr uint32_t kWaves = kOrderThreads / 64;
+  const uint32_t i = blockIdx.x * 64 + lane;
+  const uint32_t ic = min(i, n_tiles - 1);
+  const int64_t o0 = toff[ic], o1 = toff[ic + 1];
+  // ids stay below 2^15, so a real key is never 0xFFFFFFFF: padding ranks
+  // after every tile and a lane past the end writes nothing
+  const uint32_t v = i < n_tiles ? order_key(o1 - o0, i) : 0xFFFFFFFFu;
+  uint32_t cnt = 0;
+  uint32_t* s_flat = reinterpret_cast<uint32_t*>(s_k);
+  for (uint32_t c0 = 0; c0 < n_tiles; c0 += kOrderChunk) {
+    const uint32_t len = min(kOrderChunk, n_tiles - c0);
+    int64_t r[kOrderLoads];
+#pragma unroll
+    for (uint32_t q = 0; q < kOrderLoads; ++q)
+      r[q] = toff[min(c0 + tid + q * kOrderThreads, n_tiles)];  // toff has n_tiles + 1 values
+#pragma unroll
+    for (uint32_t q = 0; q < kOrderLoads; ++q) {
+      const uint32_t t = tid + q * kOrderThreads;
+      if (t <= len) s_off[t] = r[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t q = 0; q < kOrderChunk / kOrderThreads; ++q) {
+      const uint32_t t = tid + q * kOrderThreads;
+      s_flat[t] = t < len ? order_key(s_off[t + 1] - s_off[t], c0 + t) : 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    const uint32_t groups = (len + 3) >> 2;
+#pragma unroll 4
+    for (uint32_t g = wave; g < groups; g += kWaves) {
+      const uint4 k = s_k[g];
+      cnt += uint32_t(k.x < v) + uint32_t(k.y < v) + uint32_t(k.z < v) + uint32_t(k.w < v);
+    }
+    __syncthreads();
+  }
+  s_part[wave][lane] = cnt;
+  __syncthreads();
+  if (wave == 0 && i < n_tiles) {
+    uint32_t rank = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kWaves; ++w) rank += s_part[w][lane];
+    order[rank] = i;
+  }
+}
+
 inline uint32_t grid_for(uint64_t n) { return uint32_t((n + 255) / 256); }
 // Blocks for a grid-stride loop over n elements.
 inline uint32_t grid_stride_blocks(uint64_t n) {
@@ -607,6 +674,17 @@ hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tile
   ProfScope prof("k_tile_ranges", s);
   hipLaunchKernelGGL(k_tile_ranges, dim3(grid_stride_blocks((n + 4) / 4)), dim3(256), 0, s, tkeys, n,
                      n_tiles, toff);
+  return hipGetLastError();
+}
+
+bool tile_order_small(uint64_t n_tiles) { return n_tiles > 0 && n_tiles <= kOrderSmall; }
+
+hipError_t launch_tile_order_small(const int64_t* toff, uint64_t n_tiles, uint32_t* order,
+                                   hipStream_t s) {
+  if (!tile_order_small(n_tiles)) return hipErrorInvalidValue;
+  ProfScope prof("k_tile_order_rank", s);
+  hipLaunchKernelGGL(k_tile_order_rank, dim3(uint32_t((n_tiles + 63) / 64)), dim3(kOrderThreads), 0, s, toff,
+                     uint32_t(n_tiles), order);
   return hipGetLastError();
 }
 

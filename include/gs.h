@@ -341,7 +341,8 @@ int gs_arena_plan(int64_t N, int32_t C, int32_t W, int32_t H, int64_t nnz,
  *   count and summed duration in milliseconds (host out-params).
  * Kernel names: k_project_mask, k_scan, k_cam_offsets, k_project_compact,
  * k_fill_u32, k_isect_prep, k_radix_count, k_radix_scatter, k_emit_count,
- * k_emit_write, k_tile_ranges, k_tile_order_keys, k_compose_keys,
+ * k_emit_write, k_tile_ranges, k_tile_order_keys, k_tile_order_rank,
+ * k_compose_keys,
  * k_raster_fwd, k_raster_bwd, k_project_bwd, k_project_bwd_adam.
  * Recording adds host overhead per launch
  * and is not meant to stay on in production.

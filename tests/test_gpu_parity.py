@@ -160,6 +160,34 @@ def test_intersect_sort_wide_depth_range(lib):
     check_intersect(sc, proj, isect)
 
 
+# Tile counts around the limits of the rank-based launch order (one chunk of
+# 4,096 keys, several chunks, exactly 16,384 tiles) and just past it, where
+# the order comes from two radix passes instead. Most tiles are empty, so
+# ties (kept in increasing tile id) dominate.
+ORDER_SIZES = {
+    "tiles-4096": workloads.SceneSpec("sh0-3000-1024px", 3000, 0, 1, 1024, 1024, 887.0, 2.0,
+                                      -3.5, 0.5, 5.0, seed=2107),
+    "tiles-4160": workloads.SceneSpec("sh0-3000-1024x1040", 3000, 0, 1, 1024, 1040, 887.0, 2.0,
+                                      -3.5, 0.5, 5.0, seed=2108),
+    "tiles-16384": workloads.SceneSpec("sh0-3000-2048px", 3000, 0, 1, 2048, 2048, 1773.0, 2.0,
+                                       -3.5, 0.5, 5.0, seed=2109),
+    "tiles-16512": workloads.SceneSpec("sh0-3000-2064x2048", 3000, 0, 1, 2064, 2048, 1773.0,
+                                       2.0, -3.5, 0.5, 5.0, seed=2110),
+}
+
+
+@pytest.mark.parametrize("name", list(ORDER_SIZES))
+def test_intersect_launch_order_sizes(lib, name):
+    sc = workloads.make_scene(ORDER_SIZES[name])
+    proj = oracle.project(sc)
+    proj.screen = proj.screen.astype(np.float32).astype(np.float64)
+    isect = oracle.intersect(proj, sc["W"], sc["H"])
+    n_tiles = isect.tile_offsets.size - 1
+    assert n_tiles == int(name.split("-")[1])
+    print(f"{name}: nnz={proj.nnz} n_isects={isect.n_isects}")
+    check_intersect(sc, proj, isect)
+
+
 def check_intersect(sc, proj, isect):
     screen = P.to_dev(proj.screen.astype(np.float32))
     aabb = P.to_dev(P.u32_as_i32(proj.aabb16))
