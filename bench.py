@@ -98,6 +98,13 @@ def tile_sort_digits(spec):
     return b1, (rest + 7) // 8
 
 
+def order_passes(spec):
+    """Radix passes of the heavy-first launch order, as the library chooses
+    them: none up to 16,384 tiles (one rank kernel), else two 8-bit passes."""
+    n_tiles = spec.n_cams * ((spec.width + 15) // 16) * ((spec.height + 15) // 16)
+    return 0 if 0 < n_tiles <= 16384 else 2
+
+
 def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes, depth_passes=4):
     """Algorithmic HBM bytes of one launch of an HBM-bound kernel."""
     N, C, K = spec.n, spec.n_cams, spec.K
@@ -113,8 +120,9 @@ def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes, depth_passes=4):
         return 6 * (44 + 12 * K) * N + 40 * nnz + pairs / 8 + 4 * pairs / 128
     if kernel == "k_radix_scatter":  # mean over the step's passes: 8 B read + 8 B written per key
         tiles = C * ((spec.width + 15) // 16) * ((spec.height + 15) // 16)
-        return (16 * (depth_passes * nnz + tile_passes * n_isects + 2 * tiles)
-                / (depth_passes + tile_passes + 2))
+        op = order_passes(spec)
+        return (16 * (depth_passes * nnz + tile_passes * n_isects + op * tiles)
+                / (depth_passes + tile_passes + op))
     if kernel == "k_emit_write":     # order + box per pair; 8 B per entry
         return 12 * nnz + 8 * n_isects
     return None
@@ -404,14 +412,15 @@ def main():
         byt = hbm_bytes(kn, spec, nnz, n_is, V, tile_passes, depth_passes)
         if byt:
             if kn == "k_radix_scatter":   # per-launch mean; ms is the step's sum
-                byt *= depth_passes + tile_passes + 2
+                byt *= depth_passes + tile_passes + order_passes(spec)
             hb[kn] = byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     # the whole sort (depth passes over the pairs, tile passes over the
-    # entries, launch-order passes over the tiles; each pass reads and
+    # entries, launch-order passes over the tiles if any; each pass reads and
     # writes a 4 B key and a 4 B value per element) against the time of all
     # its kernels: counting and scatter
     sort_ms = sum(kernel_ms.get(k, 0.0) for k in ("k_radix_count", "k_radix_scatter"))
-    sort_bytes = 16 * (depth_passes * nnz + tile_passes * n_is + 2 * spec.n_cams * tx * ty)
+    sort_bytes = 16 * (depth_passes * nnz + tile_passes * n_is
+                       + order_passes(spec) * spec.n_cams * tx * ty)
     if sort_ms > 0:
         hb["sort (all radix kernels)"] = sort_bytes / (sort_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     out["hbm_frac_by_kernel"] = hb
