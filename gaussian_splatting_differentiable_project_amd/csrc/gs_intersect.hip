@@ -218,8 +218,9 @@ __global__ __launch_bounds__(256) void k_emit_count(const uint32_t* __restrict__
 // relative index, and a running maximum over the round (started from the
 // previous round's last owner) fills the rest. Ranks within a digit come
 // from one ballot per digit bit and per-wave digit counters; each digit
-// run of the round is then gathered in LDS and written contiguously.
-template <int ITEMS>
+// run of the round is then gathered in LDS and written contiguously. DB is
+// the number of those ballots: the digit width rounded up to 6, 7 or 8.
+template <int ITEMS, int DB>
 __global__ __launch_bounds__(256) void k_emit_write(
     const uint32_t* __restrict__ order, const uint2* __restrict__ rec, EmitGeom g, uint64_t nblk,
     const uint64_t* __restrict__ mat_off, uint64_t cap, uint32_t* __restrict__ keys_out,
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(256) void k_emit_write(
       const uint32_t d = t & M;
       uint64_t peers = __ballot(valid);
 #pragma unroll
-      for (int b = 0; b < kEmitBits; ++b) {
+      for (int b = 0; b < DB; ++b) {
         const bool bit = (d >> b) & 1u;
         const uint64_t bb = __ballot(bit);
         peers &= bit ? bb : ~bb;
@@ -664,8 +665,16 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
   // 13M-sh3-7680px 24.9 -> 21.4 ms, 15M 5-camera 0.59 -> 0.55 ms, 3M
   // 5-camera 0.73 -> 0.77 ms.
   ProfScope prof("k_emit_write", s);
-  hipLaunchKernelGGL(k_emit_write<8>, dim3(uint32_t(nblk)), dim3(256), 0, s, order,
-                     reinterpret_cast<const uint2*>(rec), g, nblk, mat_off, cap, tkeys, tvals);
+#define GS_EMIT(DB)                                                                          \
+  hipLaunchKernelGGL((k_emit_write<8, DB>), dim3(uint32_t(nblk)), dim3(256), 0, s, order,    \
+                     reinterpret_cast<const uint2*>(rec), g, nblk, mat_off, cap, tkeys, tvals)
+  if (g.bits <= 6)
+    GS_EMIT(6);
+  else if (g.bits == 7)
+    GS_EMIT(7);
+  else
+    GS_EMIT(8);
+#undef GS_EMIT
   return hipGetLastError();
 }
 

@@ -143,7 +143,9 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_count(const uint32_t* __
                    (unsigned long long)c);
 }
 
-template <int ITEMS>
+// DB: ballots per key, the digit's width rounded up to 6, 7 or 8 (bits of
+// the digit above its width are zero, so ballots on them add nothing).
+template <int ITEMS, int DB>
 __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint64_t n, int shift,
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
       const uint32_t d = (key[i] >> shift) & dmask;
       uint64_t peers = __ballot(valid);
 #pragma unroll
-      for (int b = 0; b < kRadixBits; ++b) {
+      for (int b = 0; b < DB; ++b) {
         const bool bit = (d >> b) & 1u;
         const uint64_t bb = __ballot(bit);
         peers &= bit ? bb : ~bb;
@@ -350,8 +352,17 @@ void launch_pass(const SortPlan& pl, const uint32_t* ki, const uint32_t* vi, uin
   }
   {
     ProfScope prof("k_radix_scatter", s);
-    hipLaunchKernelGGL(k_radix_scatter<ITEMS>, dim3(pl.P), dim3(kSortThreads), 0, s, ki, vi, ko,
-                       vo, n, shift, dmask, pl.ct, sc.cnt, grp, grp_next);
+    const int width = 32 - __builtin_clz(dmask | 1u);
+#define GS_SCATTER(DB)                                                                            \
+  hipLaunchKernelGGL((k_radix_scatter<ITEMS, DB>), dim3(pl.P), dim3(kSortThreads), 0, s, ki, vi, \
+                     ko, vo, n, shift, dmask, pl.ct, sc.cnt, grp, grp_next)
+    if (width <= 6)
+      GS_SCATTER(6);
+    else if (width == 7)
+      GS_SCATTER(7);
+    else
+      GS_SCATTER(8);
+#undef GS_SCATTER
   }
   sc.parity ^= 1;
 }
