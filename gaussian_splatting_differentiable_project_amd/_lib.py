@@ -27,11 +27,12 @@ ARENA_SLOTS = ("mask", "wg_count", "wg_scan", "project_ws", "screen", "aabb16", 
                "flatten_ids", "tile_offsets", "tile_order", "out_rgb", "out_T", "last_ids",
                "v_screen")
 
-EXPORTS = ("gs_status_str", "gs_version", "gs_pad_n", "gs_project_workspace_bytes",
+EXPORTS = ("gs_status_str", "gs_version", "gs_readback_status", "gs_tile_offsets_check",
+           "gs_pad_n", "gs_project_workspace_bytes",
            "gs_intersect_workspace_bytes", "gs_project", "gs_intersect", "gs_rasterize_fwd",
            "gs_rasterize_bwd", "gs_project_bwd", "gs_project_bwd_adam", "gs_arena_plan",
            "gs_profile_enable", "gs_profile_disable",
-           "gs_profile_reset", "gs_profile_query")
+           "gs_profile_reset", "gs_profile_query", "gs_valu_probe")
 
 _lib = None
 
@@ -59,6 +60,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gs_status_str.restype = ctypes.c_char_p
     lib.gs_status_str.argtypes = [ctypes.c_int]
     lib.gs_version.restype = ctypes.c_int
+    lib.gs_readback_status.restype = ctypes.c_int
+    lib.gs_readback_status.argtypes = [c_i32, c_i64, c_i64, c_i64]
+    lib.gs_tile_offsets_check.restype = ctypes.c_int
+    lib.gs_tile_offsets_check.argtypes = [P_i64, c_u64]
     lib.gs_pad_n.restype = c_i64
     lib.gs_pad_n.argtypes = [c_i64]
     lib.gs_project_workspace_bytes.restype = c_u64
@@ -91,6 +96,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gs_profile_reset.restype = ctypes.c_int
     lib.gs_profile_query.restype = ctypes.c_int
     lib.gs_profile_query.argtypes = [ctypes.c_char_p, P_i64, ctypes.POINTER(ctypes.c_double)]
+    lib.gs_valu_probe.restype = ctypes.c_int
+    lib.gs_valu_probe.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp]
     if path is None:
         _lib = lib
     return lib
@@ -116,6 +123,15 @@ def profile_query(kernel: str) -> tuple[int, float]:
     if st != GS_OK:
         raise GsError(st, "gs_profile_query")
     return n.value, ms.value
+
+
+def valu_probe(kind: int, blocks: int, iters: int, out, stream=None) -> None:
+    """Launch the fp32 VALU throughput probe (kind 0 FMA, 1 exp) on the
+    stream; ``out`` is a device float tensor of blocks * 256 elements."""
+    assert out.numel() >= blocks * 256
+    st = load().gs_valu_probe(_stream(stream), kind, blocks, iters, _ptr(out))
+    if st != GS_OK:
+        raise GsError(st, "gs_valu_probe")
 
 
 def status_str(status: int) -> str:
@@ -280,10 +296,10 @@ class Projected:
     nnz: int
     cam_offsets: list
     mask: torch.Tensor
-    wg_count: torch.Tensor
+    wg_count: torch.Tensor | None  # None once its bytes may be reused (step_arena)
     wg_scan: torch.Tensor
     screen: torch.Tensor   # [nnz, 10] view
-    aabb16: torch.Tensor   # [nnz, 2] view
+    aabb16: torch.Tensor | None   # [nnz, 2] view; None as wg_count
 
 
 @dataclass
@@ -477,9 +493,11 @@ class Rasterizer:
 
     def step_arena(self, s: Scene, v_rgb, v_T=None, arena: PhaseArena = None):
         """The whole step with every per-step buffer carved from one phase
-        arena. The returned images, ids and screen-row gradients are views
-        into the arena, valid until the next step; gradients are allocated
-        as usual."""
+        arena. The returned images, ids, rows and screen-row gradients are
+        views into the arena, valid until the next step; gradients are
+        allocated as usual. The group counts and the 16-bit boxes live only
+        through the projection and intersection phases, after which later
+        phases may reuse their bytes: they are returned as None."""
         A = arena if arena is not None else self._arena
         if A is None:
             A = self._arena = PhaseArena(self.device)
@@ -524,7 +542,7 @@ class Rasterizer:
             vs = A.view("v_screen", torch.float32)[: nnz * ROW].view(nnz, ROW)
             self._check(gs_rasterize_bwd(s.C, s.W, s.H, nnz, screen, ids, toff, order, None, T,
                                          last, v_rgb, v_T, None, vs, None), "gs_rasterize_bwd")
-            p = Projected(nnz, cam, mask, wgc, wgs, screen, aabb)
+            p = Projected(nnz, cam, mask, None, wgs, screen, None)
             grads = self.project_bwd(s, p, vs)
             it = Intersected(n_is, ids, toff, None, order)
             return dict(proj=p, isect=it, rgb=rgb, T=T, last=last, v_screen=vs, grads=grads)

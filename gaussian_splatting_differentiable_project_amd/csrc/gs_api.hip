@@ -21,14 +21,6 @@ constexpr uint64_t kAlign = 256;
 
 inline uint64_t align_up(uint64_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
-bool check_env() {
-  static const bool on = [] {
-    const char* v = std::getenv("GS_CHECK");
-    return v && v[0] && v[0] != '0';
-  }();
-  return on;
-}
-
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int64_t tiles_x_of(int W) { return (W + kTile - 1) / kTile; }
@@ -180,14 +172,6 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_E_HIP; }
     if (e_ != hipSuccess) return GS_E_HIP;      \
   } while (0)
 
-int check_device_error(const int* err, hipStream_t s) {
-  if (!check_env()) return GS_OK;
-  int h = 0;
-  GS_TRY(hipMemcpyAsync(&h, err, sizeof(int), hipMemcpyDeviceToHost, s));
-  GS_TRY(hipStreamSynchronize(s));
-  return h ? GS_E_DEVICE : GS_OK;
-}
-
 bool valid_image(int32_t C, int32_t W, int32_t H) {
   return C >= 1 && W >= 1 && H >= 1 && W <= 65535 && H <= 65535;
 }
@@ -223,7 +207,27 @@ const char* gs_status_str(int status) {
   }
 }
 
-int gs_version(void) { return 100; }
+int gs_version(void) { return 200; }
+
+int gs_readback_status(int32_t device_flag, int64_t count, int64_t count_limit,
+                       int64_t capacity) {
+  if (device_flag != 0) return GS_E_DEVICE;  // the count itself is then unreliable
+  if (count < 0 || count >= count_limit) return GS_E_OVERFLOW;
+  if (count > capacity) return GS_E_CAPACITY;
+  return GS_OK;
+}
+
+int gs_tile_offsets_check(const int64_t* tile_offsets, uint64_t n_tiles) {
+  if (!tile_offsets) return GS_E_INVALID;
+  if (tile_offsets[0] != 0) return GS_E_INVALID;
+  int overflow = 0;
+  for (uint64_t t = 0; t < n_tiles; ++t) {
+    const int64_t a = tile_offsets[t], b = tile_offsets[t + 1];
+    if (b < a) return GS_E_INVALID;
+    if (b - a >= (int64_t(1) << 31)) overflow = 1;
+  }
+  return overflow ? GS_E_OVERFLOW : GS_OK;
+}
 
 int64_t gs_pad_n(int64_t N) { return N <= 0 ? 0 : ((N + kMaskGroup - 1) / kMaskGroup) * kMaskGroup; }
 
@@ -272,7 +276,8 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t
   a.cap = screen_capacity;
 
   HostStage* hs = nullptr;
-  GS_TRY(host_stage(uint64_t(C) + 1, &hs));
+  GS_TRY(host_stage(uint64_t(C) + 2, &hs));
+  hs->buf[C + 1] = 0;  // receives the 4-byte error flag in its low half
   GS_TRY(launch_fill_u32(workspace, 0u, ws.bytes / 4, s));
   GS_TRY(launch_project_mask(a, mask, s));
   // the group counts are the popcounts of the mask words; the scan takes
@@ -281,6 +286,9 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t
                          ws.lookback, ws.ticket, ws.err, s));
   GS_TRY(launch_cam_offsets(wg_scan, Np / kMaskGroup, C, ws.total, ws.cam_off, s));
   GS_TRY(hipMemcpyAsync(hs->buf, ws.cam_off, sizeof(int64_t) * (C + 1), hipMemcpyDeviceToHost, s));
+  // the scan's bounded look-back raises this flag if a wait timed out;
+  // the slots and nnz are then wrong, so it is checked before them
+  GS_TRY(hipMemcpyAsync(hs->buf + C + 1, ws.err, sizeof(int), hipMemcpyDeviceToHost, s));
   GS_TRY(hipEventRecord(hs->ev, s));
   // The compaction needs no host decision: slots at or past the capacity
   // are not written, so it is queued before the host reads the count.
@@ -289,11 +297,11 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t
   const hipError_t e2 = hipEventSynchronize(hs->ev);
   if (e != hipSuccess || e2 != hipSuccess) return GS_E_HIP;
   const int64_t nnz = hs->buf[C];
+  int flag = 0;
+  std::memcpy(&flag, hs->buf + C + 1, sizeof(int));
   *nnz_out = nnz;
   if (cam_offsets_out) std::memcpy(cam_offsets_out, hs->buf, sizeof(int64_t) * (C + 1));
-  if (nnz >= (int64_t(1) << 31)) return GS_E_OVERFLOW;
-  if (nnz > screen_capacity) return GS_E_CAPACITY;
-  return check_device_error(ws.err, s);
+  return gs_readback_status(flag, nnz, int64_t(1) << 31, screen_capacity);
 }
 
 int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, const float* screen,
@@ -309,9 +317,17 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   if (!aligned(aabb16, 8) || !aligned(workspace, kAlign)) return GS_E_INVALID;
   *n_isects_out = -1;
   if (nnz >= (int64_t(1) << 31)) return GS_E_OVERFLOW;
-  for (int c = 0; c < C; ++c)
+  int64_t widest = 0;  // most pairs of any one camera
+  for (int c = 0; c < C; ++c) {
     if (cam_offsets[c] < 0 || cam_offsets[c] > cam_offsets[c + 1]) return GS_E_INVALID;
+    widest = cam_offsets[c + 1] - cam_offsets[c] > widest ? cam_offsets[c + 1] - cam_offsets[c]
+                                                          : widest;
+  }
   if (cam_offsets[0] != 0 || cam_offsets[C] != nnz) return GS_E_INVALID;
+  // A pair meets each tile of its camera at most once, so no tile list is
+  // longer than its camera's pair count; the raster calls index a list
+  // with 32-bit local ids (last_ids), which this bound keeps below 2^31.
+  if (widest >= (int64_t(1) << 31)) return GS_E_OVERFLOW;
   const uint64_t n_tiles = uint64_t(C) * uint64_t(tiles_x_of(W) * tiles_y_of(H));
   if (n_tiles >= (uint64_t(1) << 32)) return GS_E_OVERFLOW;
 
@@ -322,7 +338,8 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   sc.cnt = ws.sort_cnt;
   sc.grp = ws.sort_grp;
   HostStage* hs = nullptr;
-  GS_TRY(host_stage(1 + kPrepBlocks, &hs));
+  GS_TRY(host_stage(2 + kPrepBlocks, &hs));
+  hs->buf[1 + kPrepBlocks] = 0;  // receives the emit scan's error flag
 
   // Phase 1: depth keys, per-slot tile counts and their exact 64-bit total.
   GS_TRY(launch_fill_u32(workspace, 0u, ws.zero_words, s));
@@ -361,6 +378,7 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   }
   const uint32_t* order = in_b ? ws.dvals_b : ws.dvals_a;
   const uint64_t I = uint64_t(hs->buf[0]);
+  bool flag_pending = false;
   *n_isects_out = int64_t(I);
   if (I >= (uint64_t(1) << 62)) return GS_E_OVERFLOW;
   ws = carve_isect(workspace, C, nnz, int64_t(I), n_tiles);
@@ -385,6 +403,15 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
                              ws.emit_cnt, ws.emit_rec, ws.emit_off, ws.emit_total, ws.scan_lb,
                              ws.ticket,
                              ws.err, ws.tkeys_a, v_first, s));
+    // The emit's scan of its count matrix waits on predecessors with a
+    // bounded spin and raises ws.err when a wait times out (the emit
+    // offsets are then wrong). The flag is copied here, and the host waits
+    // for that copy only after every later kernel has been queued, so the
+    // device stays busy meanwhile.
+    GS_TRY(hipMemcpyAsync(hs->buf + 1 + kPrepBlocks, ws.err, sizeof(int), hipMemcpyDeviceToHost,
+                          s));
+    GS_TRY(hipEventRecord(hs->ev, s));
+    flag_pending = true;
     // Phase 4: the remaining digits of the stable sort by tile id.
     in_b = false;
     if (passes)
@@ -407,7 +434,11 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
                                 0, 16, sc, &in_b, s));
     }
   }
-  return check_device_error(ws.err, s);
+  if (!flag_pending) return GS_OK;
+  GS_TRY(hipEventSynchronize(hs->ev));
+  int flag = 0;
+  std::memcpy(&flag, hs->buf + 1 + kPrepBlocks, sizeof(int));
+  return flag ? GS_E_DEVICE : GS_OK;
 }
 
 int gs_rasterize_fwd(void* stream, int32_t C, int32_t W, int32_t H, const float* screen,

@@ -102,3 +102,49 @@ int gs_profile_query(const char* kernel, int64_t* launches, double* total_ms) {
 }
 
 }  // extern "C"
+
+// ---- fp32 VALU throughput probe (measurement helper) ----
+// Each lane runs eight independent dependency chains of one instruction
+// kind, so the loop issues back to back and its rate is the issue rate of
+// that instruction: kind 0 a plain fp32 FMA (v_fma_f32), kind 1 the
+// hardware base-2 exponential (v_exp_f32). The chains' sums are written out
+// so nothing is dead.
+namespace gs {
+namespace {
+
+template <int KIND>
+__global__ __launch_bounds__(256) void k_valu_probe(int iters, float seed, float b, float c,
+                                                    float* __restrict__ out) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = seed + 1e-7f * float(threadIdx.x) + 0.01f * float(i);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (KIND == 0)
+        a[i] = fmaf(a[i], b, c);
+      else
+        a[i] = __builtin_amdgcn_exp2f(-a[i]);  // stays in (0.5, 1)
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += a[i];
+  out[int64_t(blockIdx.x) * 256 + threadIdx.x] = s;
+}
+
+}  // namespace
+}  // namespace gs
+
+extern "C" int gs_valu_probe(void* stream, int32_t kind, int32_t blocks, int32_t iters,
+                             float* out) {
+  if (kind < 0 || kind > 1 || blocks < 1 || iters < 1 || !out) return GS_E_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kind == 0)
+    hipLaunchKernelGGL(gs::k_valu_probe<0>, dim3(uint32_t(blocks)), dim3(256), 0, s, iters, 0.5f,
+                       0.9999999f, 1e-7f, out);
+  else
+    hipLaunchKernelGGL(gs::k_valu_probe<1>, dim3(uint32_t(blocks)), dim3(256), 0, s, iters, 0.5f,
+                       0.f, 0.f, out);
+  return hipGetLastError() == hipSuccess ? GS_OK : GS_E_HIP;
+}

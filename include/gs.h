@@ -18,8 +18,8 @@
  *    memory and keeps no device state between calls ([GSPLAT] 2.3: memory
  *    lifetimes belong to the caller).
  *  - `stream` is a hipStream_t passed as void*; all work is enqueued on it.
- *    gs_project and gs_intersect each block the host once, on an event
- *    recorded after the copy of a 64-bit total, for the host-side check of
+ *    gs_project and gs_intersect block the host on an event recorded
+ *    after the copy of a 64-bit total, for the host-side check of
  *    [VRAM] "The 4 GiB rule and the 2^31 limit"; work that does not depend
  *    on that total is queued before the wait, and work sized by it after.
  *    The other calls return without waiting. The stream must belong to
@@ -72,6 +72,34 @@ const char* gs_status_str(int status);
 int gs_version(void);
 
 /* ---------------------------------------------------------------------
+ * Host-side checks (host only, no GPU work).
+ *
+ * gs_readback_status -- the decision gs_project applies to the words it
+ * reads back ([VRAM] "The 4 GiB rule and the 2^31 limit": an exact total is
+ * checked on the host against the storage it must fit before it is
+ * trusted). device_flag is the error word of the call's kernels: a
+ * look-back scan whose bounded wait for a predecessor timed out sets it,
+ * and the total and slots are then wrong. Returns GS_E_DEVICE if
+ * device_flag != 0 (checked first, since the count is then unreliable),
+ * GS_E_OVERFLOW if count < 0 or count >= count_limit, GS_E_CAPACITY if
+ * count > capacity, else GS_OK. gs_intersect maps the same flag of its
+ * emit scan to GS_E_DEVICE.
+ *
+ * gs_tile_offsets_check -- validates (host) tile_offsets[n_tiles + 1]
+ * before it is handed to the raster calls: GS_E_INVALID if
+ * tile_offsets[0] != 0 or a range is negative (null pointer included),
+ * GS_E_OVERFLOW if any tile's list holds 2^31 entries or more (the raster
+ * calls index a tile's list with the 32-bit local ids of last_ids;
+ * [VRAM] "The 4 GiB rule and the 2^31 limit" is about exactly such a
+ * silent wrap), else GS_OK. gs_intersect's output always passes: a pair
+ * meets each tile of its camera at most once, so a list is no longer than
+ * its camera's pair count, which gs_intersect checks below 2^31.
+ * ------------------------------------------------------------------- */
+int gs_readback_status(int32_t device_flag, int64_t count, int64_t count_limit,
+                       int64_t capacity);
+int gs_tile_offsets_check(const int64_t* tile_offsets, uint64_t n_tiles);
+
+/* ---------------------------------------------------------------------
  * Buffer sizes (host only, no GPU work).
  *
  * gs_pad_n: N_pad = ceil(N / 128) * 128.
@@ -114,7 +142,9 @@ uint64_t gs_intersect_workspace_bytes(int32_t C, int32_t W, int32_t H,
  * cam_offsets_out[C+1]: first slot of each camera, cam_offsets_out[C]=nnz.
  * workspace: device scratch of gs_project_workspace_bytes(N, C) bytes.
  * Errors: GS_E_INVALID for N < 0, C < 1, W or H outside [1, 65535],
- * sh_degree outside [0, 3], or a null required pointer.
+ * sh_degree outside [0, 3], or a null required pointer. GS_E_DEVICE when
+ * the scan of the group counts reports a timed-out wait (the host reads
+ * its error word with nnz; see gs_readback_status).
  * GS_E_CAPACITY when nnz > screen_capacity: *nnz_out, cam_offsets_out and
  * mask, wg_count, wg_scan are valid; rows at slots below the capacity may
  * have been written, nothing at or past it (the compaction runs before
@@ -159,7 +189,12 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
  * Errors: GS_E_INVALID as for gs_project or nnz < 0;
  * GS_E_OVERFLOW if nnz >= 2^31; GS_E_CAPACITY if n_isects >
  * isect_capacity (flatten_ids, tile_offsets, sorted_keys and tile_order
- * are then not written); GS_E_WORKSPACE if workspace_bytes is short (the
+ * are then not written); GS_E_OVERFLOW also if one camera holds 2^31
+ * pairs or more (its tiles' lists could then pass the 32-bit local ids of
+ * the raster calls); GS_E_DEVICE if the scan of the emit's per-block
+ * counts reports a timed-out wait (the host reads that flag after queuing
+ * every kernel of the call, so this call waits twice: once for the total,
+ * once for the flag); GS_E_WORKSPACE if workspace_bytes is short (the
  * bytes needed are returned; before the count is known this is the lower
  * bound for counting, after it the full amount). Call again after growing.
  * ------------------------------------------------------------------- */
@@ -348,6 +383,15 @@ int gs_arena_plan(int64_t N, int32_t C, int32_t W, int32_t H, int64_t nnz,
  * and is not meant to stay on in production.
  * ------------------------------------------------------------------- */
 int gs_profile_enable(const char* filter);
+/* gs_valu_probe: a throughput probe of the fp32 vector unit, for sizing the
+ * raster kernels' roofline on the machine at hand (not part of a step).
+ * Launches `blocks` blocks of 256 lanes on `stream`; each lane runs
+ * `iters` rounds of eight independent chains of one instruction: kind 0 a
+ * plain fp32 fused multiply-add, kind 1 the hardware base-2 exponential.
+ * out[blocks * 256] (device) receives each lane's sum. Work per launch:
+ * blocks * 256 * iters * 8 instructions (an FMA counts 2 flops). The
+ * caller times it. Errors: GS_E_INVALID, GS_E_HIP. */
+int gs_valu_probe(void* stream, int32_t kind, int32_t blocks, int32_t iters, float* out);
 int gs_profile_disable(void);
 int gs_profile_reset(void);
 int gs_profile_query(const char* kernel, int64_t* launches, double* total_ms);

@@ -160,3 +160,55 @@ def to_dev(x, dtype=None):
 
 def u32_as_i32(a):
     return np.ascontiguousarray(np.asarray(a, np.uint32)).view(np.int32)
+
+
+def check_step(sc, out, grads_o, ref, label=""):
+    """A whole GPU step (``Rasterizer.step``-shaped dict) against the oracle
+    step (``oracle.loss_and_grads(sc, rows32=True)``): nnz and the mask
+    bit-exact outside fragile pairs; the sorted lists bit-exact as pair
+    ids once fragile pairs' entries are removed; images max-abs 1e-4 and
+    last_ids exact outside fragile pixels; gradients relative L2 1e-3.
+    Returns a report dict."""
+    proj, isect = ref["proj"], ref["isect"]
+    C, W, H = sc["C"], sc["W"], sc["H"]
+    frag = fragile_pairs(sc, proj)
+    p, it = out["proj"], out["isect"]
+    n_pairs = C * proj.N_pad
+    gvis = unpack_mask(p.mask.cpu().numpy(), n_pairs)
+    ovis = np.zeros(n_pairs, bool)
+    ovis[proj.pairs] = True
+    assert not ((gvis != ovis) & ~frag).any(), "mask differs on a non-fragile pair"
+    gp = np.flatnonzero(gvis)
+    ids_g = it.flatten_ids.cpu().numpy().view(np.uint32).astype(np.int64)
+    lists_g = gp[ids_g]
+    lists_o = proj.pairs[isect.flatten_ids.astype(np.int64)]
+    np.testing.assert_array_equal(lists_g[~frag[lists_g]], lists_o[~frag[lists_o]])
+    # tiles whose full lists (fragile pairs kept) differ are left out whole
+    toff_g = it.tile_offsets.cpu().numpy()
+    tiles_touched = np.zeros(isect.tile_offsets.size - 1, bool)
+    for t in range(tiles_touched.size):
+        a = gp[ids_g[toff_g[t]:toff_g[t + 1]]]
+        o0, o1 = isect.tile_offsets[t], isect.tile_offsets[t + 1]
+        b = proj.pairs[isect.flatten_ids[o0:o1].astype(np.int64)]
+        tiles_touched[t] = not np.array_equal(a, b)
+    if not frag.any():
+        np.testing.assert_array_equal(toff_g, isect.tile_offsets)
+    fpx = fragile_pixels(proj.screen, isect.flatten_ids, isect.tile_offsets, C, W, H,
+                         tiles_touched)
+    ok = ~fpx
+    e_rgb = float(np.abs(out["rgb"].cpu().numpy() - ref["rgb"])[ok].max(initial=0))
+    e_T = float(np.abs(out["T"].cpu().numpy() - ref["T"])[ok].max(initial=0))
+    last_bad = int((out["last"].cpu().numpy() != ref["last"])[ok].sum())
+    errs = {k: rel_l2(out["grads"][k].cpu().numpy(), grads_o[k]) for k in grads_o}
+    rep = dict(nnz=p.nnz, n_isects=it.n_isects, oracle_nnz=proj.nnz,
+               oracle_isects=isect.n_isects, fragile_pairs=int(frag.sum()),
+               tiles_differing=int(tiles_touched.sum()), fragile_px=int(fpx.sum()),
+               rgb_err=e_rgb, T_err=e_T, last_ids_diff=last_bad, grads=errs)
+    print(f"{label}: {rep}")
+    assert e_rgb <= IMG_TOL and e_T <= IMG_TOL, rep
+    assert last_bad == 0, rep
+    assert max(errs.values()) <= GRAD_TOL, rep
+    # the exclusions stay small: below 0.5% of pixels, 0.1% of pairs
+    assert fpx.sum() <= 0.005 * fpx.size + 4, rep
+    assert frag.sum() <= 0.001 * proj.nnz + 4, rep
+    return rep

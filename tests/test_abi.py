@@ -34,13 +34,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) == {"gs_status_str", "gs_version", "gs_pad_n", "gs_project_workspace_bytes",
+    assert set(names) == {"gs_status_str", "gs_version", "gs_readback_status",
+                          "gs_tile_offsets_check", "gs_pad_n", "gs_project_workspace_bytes",
                           "gs_intersect_workspace_bytes", "gs_project", "gs_intersect",
                           "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd",
                           "gs_project_bwd_adam", "gs_arena_plan", "gs_profile_enable",
                           "gs_profile_disable",
                           "gs_profile_reset",
-                          "gs_profile_query"}
+                          "gs_profile_query", "gs_valu_probe"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
@@ -106,6 +107,62 @@ def test_invalid_arguments_need_no_gpu(lib):
     st = lib.gs_intersect(None, 1, 16, 16, 1 << 31, 8, 8, cam2, None, 0, None, 0, 8, None, None,
                           ctypes.byref(n_is), ctypes.byref(need))
     assert st == gsd.GS_E_OVERFLOW
+
+
+def test_readback_status_protocol(lib):
+    """The host decision on the words read back after the visibility scan:
+    a raised device flag wins over everything (the count is then garbage),
+    then a count past its storage type, then a short capacity."""
+    f = lib.gs_readback_status
+    lim = 1 << 31
+    assert f(0, 0, lim, 0) == gsd.GS_OK
+    assert f(0, 100, lim, 100) == gsd.GS_OK
+    assert f(0, 101, lim, 100) == gsd.GS_E_CAPACITY
+    assert f(0, lim - 1, lim, lim) == gsd.GS_OK
+    assert f(0, lim, lim, 1 << 40) == gsd.GS_E_OVERFLOW
+    assert f(0, -1, lim, 10) == gsd.GS_E_OVERFLOW
+    # the flag is checked first: a timed-out scan leaves any count behind
+    for count, cap in ((5, 10), (101, 100), (lim, 1 << 40)):
+        assert f(1, count, lim, cap) == gsd.GS_E_DEVICE
+    assert f(-7, 0, lim, 0) == gsd.GS_E_DEVICE
+
+
+def test_tile_offsets_check(lib):
+    """Tile ranges the raster calls can index with 32-bit local ids:
+    ranges of 2^31 entries or more are an overflow ([VRAM] 'The 4 GiB rule
+    and the 2^31 limit'); a decreasing or shifted offset table is invalid."""
+    def check(offs):
+        a = np.ascontiguousarray(np.asarray(offs, np.int64))
+        return lib.gs_tile_offsets_check(a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                         a.size - 1)
+    big = 1 << 31
+    assert check([0]) == gsd.GS_OK                       # no tiles
+    assert check([0, 0, 5, 5, 9]) == gsd.GS_OK
+    assert check([0, big - 1, big - 1 + 3]) == gsd.GS_OK  # 2^31 - 1 still fits
+    assert check([0, 3, 3 + big]) == gsd.GS_E_OVERFLOW   # one list of exactly 2^31
+    assert check([0, 4_000_000_000, 4_000_000_001]) == gsd.GS_E_OVERFLOW
+    assert check([0, 5, 4]) == gsd.GS_E_INVALID           # negative range
+    assert check([1, 5]) == gsd.GS_E_INVALID              # must start at 0
+    assert lib.gs_tile_offsets_check(None, 3) == gsd.GS_E_INVALID
+    # past 2^32 entries in total, every list short: fine (the high-res scene)
+    offs = np.arange(0, 230_401, dtype=np.int64) * 20_700
+    assert offs[-1] > 1 << 32 and check(offs) == gsd.GS_OK
+
+
+def test_intersect_checks_cam_offsets(lib):
+    """gs_intersect validates the host cam_offsets before any GPU work: they
+    bound each tile list (a pair meets a tile of its camera at most once),
+    so they must be a non-decreasing table from 0 to nnz."""
+    n_is = ctypes.c_int64(0)
+    need = ctypes.c_uint64(0)
+    cam = (ctypes.c_int64 * 3)(0, 5, 10)
+    st = lib.gs_intersect(None, 2, 16, 16, 10, 8, 8, cam, None, 0, None, 0, None, None, None,
+                          ctypes.byref(n_is), ctypes.byref(need))
+    assert st == gsd.GS_E_INVALID   # tile_offsets is required
+    bad = (ctypes.c_int64 * 3)(0, 6, 10)
+    st = lib.gs_intersect(None, 2, 16, 16, 11, 8, 8, bad, None, 0, None, 0, 8, None, None,
+                          ctypes.byref(n_is), ctypes.byref(need))
+    assert st == gsd.GS_E_INVALID   # cam_offsets[C] must equal nnz
 
 
 def test_buffer_formulas_reproduce_pages_numbers():

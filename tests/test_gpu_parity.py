@@ -348,26 +348,4 @@ def test_end_to_end(lib, name):
     s = gpu_scene(sc)
     out = r.step(s, P.to_dev(sc["v_rgb"]), P.to_dev(sc["v_T"]))
     torch.cuda.synchronize()
-    proj = ref["proj"]
-    frag = P.fragile_pairs(sc, proj)
-    tiles_touched = np.zeros(ref["isect"].tile_offsets.size - 1, bool)
-    if frag.any():
-        fr_slots = np.flatnonzero(frag[proj.pairs])
-        tx0, ty0, tx1, ty1 = ref["isect"].rects
-        tx_n = ref["isect"].tiles_x
-        for s_ in fr_slots:
-            c = proj.cam[s_]
-            for ty in range(ty0[s_], ty1[s_]):
-                for tx in range(tx0[s_], tx1[s_]):
-                    tiles_touched[c * ref["isect"].T + ty * tx_n + tx] = True
-    fpx = P.fragile_pixels(proj.screen, ref["isect"].flatten_ids, ref["isect"].tile_offsets,
-                           sc["C"], sc["W"], sc["H"], tiles_touched)
-    ok = ~fpx
-    e_rgb = np.abs(out["rgb"].cpu().numpy() - ref["rgb"])[ok].max()
-    e_T = np.abs(out["T"].cpu().numpy() - ref["T"])[ok].max()
-    errs = {k: P.rel_l2(out["grads"][k].cpu().numpy(), grads_o[k]) for k in grads_o}
-    print(f"{name}: nnz={out['proj'].nnz} isects={out['isect'].n_isects} "
-          f"(oracle {proj.nnz}/{ref['isect'].n_isects}) fragile px={int(fpx.sum())} "
-          f"rgb err={e_rgb:.2e} T err={e_T:.2e} grads={errs}")
-    assert e_rgb <= P.IMG_TOL and e_T <= P.IMG_TOL
-    assert max(errs.values()) <= P.GRAD_TOL
+    P.check_step(sc, out, grads_o, ref, name)
