@@ -29,7 +29,8 @@ ARENA_SLOTS = ("mask", "wg_count", "wg_scan", "project_ws", "screen", "aabb16", 
 
 EXPORTS = ("gs_status_str", "gs_version", "gs_readback_status", "gs_tile_offsets_check",
            "gs_pad_n", "gs_project_workspace_bytes",
-           "gs_intersect_workspace_bytes", "gs_project", "gs_intersect", "gs_rasterize_fwd",
+           "gs_intersect_workspace_bytes", "gs_project", "gs_project_noalloc", "gs_intersect",
+           "gs_rasterize_fwd",
            "gs_rasterize_bwd", "gs_project_bwd", "gs_project_bwd_adam", "gs_arena_plan",
            "gs_profile_enable", "gs_profile_disable",
            "gs_profile_reset", "gs_profile_query", "gs_valu_probe")
@@ -73,6 +74,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gs_project.restype = ctypes.c_int
     lib.gs_project.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
         [c_vp] * 3 + [c_vp, c_vp, c_i64, c_vp, c_u64, P_i64, P_i64]
+    lib.gs_project_noalloc.restype = ctypes.c_int
+    lib.gs_project_noalloc.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
+        [c_vp] * 3 + [c_vp, c_vp, c_i64, P_i64, P_i64]
     lib.gs_intersect.restype = ctypes.c_int
     lib.gs_intersect.argtypes = [c_vp, c_i32, c_i32, c_i32, c_i64, c_vp, c_vp, P_i64, c_vp, c_u64,
                                  c_vp, c_i64, c_vp, c_vp, c_vp, P_i64, P_u64]
@@ -174,6 +178,21 @@ def gs_project(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, 
                            _ptr(Ks), _ptr(mask), _ptr(wg_count), _ptr(wg_scan), _ptr(screen),
                            _ptr(aabb16), screen_capacity, _ptr(workspace), workspace_bytes,
                            ctypes.byref(nnz), cam)
+    return st, nnz.value, list(cam)
+
+
+def gs_project_noalloc(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, sh,
+                       viewmats, Ks, mask, wg_count, wg_scan, screen, aabb16, screen_capacity,
+                       stream=None):
+    """gs_project without a workspace (the library's static device scratch).
+    Returns (status, nnz, cam_offsets list)."""
+    nnz = ctypes.c_int64(-1)
+    cam = (ctypes.c_int64 * (C + 1))()
+    st = load().gs_project_noalloc(_stream(stream), N, C, W, H, sh_degree, _ptr(means),
+                                   _ptr(quats), _ptr(log_scales), _ptr(opacity_logits), _ptr(sh),
+                                   _ptr(viewmats), _ptr(Ks), _ptr(mask), _ptr(wg_count),
+                                   _ptr(wg_scan), _ptr(screen), _ptr(aabb16), screen_capacity,
+                                   ctypes.byref(nnz), cam)
     return st, nnz.value, list(cam)
 
 

@@ -10,10 +10,20 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "gs_internal.h"
 
 using namespace gs;
+
+// Device scratch of gs_project_noalloc: the projection workspace (totals,
+// error flag, ticket, camera offsets, look-back words of the group-count
+// scan) lives here instead of in a caller buffer. Every device the library
+// runs on holds its own copy until the process ends. Host code reaches it
+// only through the address hipGetSymbolAddress returns on that device.
+constexpr uint64_t kNoAllocScratchBytes = 64 * 1024;
+constexpr int kNoAllocMaxCams = 256;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -164,6 +174,28 @@ hipError_t host_stage(uint64_t words, HostStage** out) {
   return hipSuccess;
 }
 
+// The device address of `scratch` on the current device, looked up once
+// per device (with that device current) and kept.
+void* g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_E_HIP; }
 
 #define GS_TRY(expr)                            \
@@ -243,6 +275,57 @@ uint64_t gs_intersect_workspace_bytes(int32_t C, int32_t W, int32_t H, int64_t n
   return carve_isect(nullptr, C, nnz, n_isects, n_tiles).bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks and kernel sequence shared by gs_project and
+// gs_project_noalloc, up to (not including) the readback of the totals:
+// the zero fill of the workspace, the visibility pass, the scan of the
+// group counts and the camera offsets, then the compaction. `ws` is the
+// carved workspace; `before_compact` runs after the offsets are queued and
+// before the compaction (gs_project puts its readback there).
+template <typename F>
+int project_queue(hipStream_t s, const ProjectArgs& a, uint64_t* mask, uint32_t* wg_count,
+                  uint32_t* wg_scan, float* screen, uint32_t* aabb16, const ProjectWs& ws,
+                  void* ws_base, F&& before_compact) {
+  const int64_t n_groups = int64_t(a.C) * a.N_pad / kMaskGroup;
+  GS_TRY(launch_fill_u32(ws_base, 0u, ws.bytes / 4, s));
+  GS_TRY(launch_project_mask(a, mask, s));
+  // the group counts are the popcounts of the mask words; the scan takes
+  // them from the words and writes them out on the way
+  GS_TRY(launch_scan_u32(nullptr, mask, wg_count, uint64_t(n_groups), wg_scan, nullptr, ws.total,
+                         ws.lookback, ws.ticket, ws.err, s));
+  GS_TRY(launch_cam_offsets(wg_scan, a.N_pad / kMaskGroup, a.C, ws.total, ws.cam_off, s));
+  GS_TRY(before_compact());
+  // The compaction needs no host decision: slots at or past the capacity
+  // are not written, so it is queued before the host reads the count.
+  GS_TRY(launch_project_compact(a, mask, wg_scan, screen, aabb16, s));
+  return GS_OK;
+}
+
+int project_check(int64_t N, int32_t C, int32_t W, int32_t H, int32_t sh_degree,
+                  const float* means, const float* quats, const float* log_scales,
+                  const float* opacity_logits, const float* sh, const float* viewmats,
+                  const float* Ks, const uint64_t* mask, const uint32_t* wg_count,
+                  const uint32_t* wg_scan, const float* screen, const uint32_t* aabb16,
+                  int64_t screen_capacity, const int64_t* nnz_out) {
+  if (N < 0 || !valid_image(C, W, H) || sh_degree < 0 || sh_degree > 3 || !nnz_out ||
+      screen_capacity < 0)
+    return GS_E_INVALID;
+  if (N > 0 && (!means || !quats || !log_scales || !opacity_logits || !sh || !viewmats || !Ks ||
+                !mask || !wg_count || !wg_scan))
+    return GS_E_INVALID;
+  if (!aligned(quats, 16) || !aligned(screen, 8) || !aligned(aabb16, 8) || !aligned(mask, 8))
+    return GS_E_INVALID;
+  if (screen_capacity > 0 && (!screen || !aabb16)) return GS_E_INVALID;
+  return GS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t sh_degree,
                const float* means, const float* quats, const float* log_scales,
                const float* opacity_logits, const float* sh, const float* viewmats,
@@ -250,57 +333,81 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int32_t
                float* screen, uint32_t* aabb16, int64_t screen_capacity, void* workspace,
                uint64_t workspace_bytes, int64_t* nnz_out, int64_t* cam_offsets_out) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (N < 0 || !valid_image(C, W, H) || sh_degree < 0 || sh_degree > 3 || !nnz_out ||
-      screen_capacity < 0)
-    return GS_E_INVALID;
-  if (N > 0 && (!means || !quats || !log_scales || !opacity_logits || !sh || !viewmats || !Ks ||
-                !mask || !wg_count || !wg_scan || !workspace))
-    return GS_E_INVALID;
-  if (!aligned(quats, 16) || !aligned(screen, 8) || !aligned(aabb16, 8) ||
-      !aligned(workspace, kAlign) || !aligned(mask, 8))
-    return GS_E_INVALID;
-  const int64_t Np = gs_pad_n(N);
-  const int64_t n_groups = int64_t(C) * Np / kMaskGroup;
+  int st = project_check(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, sh,
+                         viewmats, Ks, mask, wg_count, wg_scan, screen, aabb16, screen_capacity,
+                         nnz_out);
+  if (st != GS_OK) return st;
+  if ((N > 0 && !workspace) || !aligned(workspace, kAlign)) return GS_E_INVALID;
+  const ProjectArgs a = [&] {
+    ProjectArgs r = project_args(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits,
+                                 sh, viewmats, Ks);
+    r.cap = screen_capacity;
+    return r;
+  }();
+  const int64_t n_groups = int64_t(C) * a.N_pad / kMaskGroup;
   const ProjectWs ws = carve_project(workspace, n_groups, C);
   if (!workspace || workspace_bytes < ws.bytes) return GS_E_WORKSPACE;
-
-  ProjectArgs a{};
-  a.N = N, a.N_pad = Np, a.C = C, a.W = W, a.H = H, a.deg = sh_degree;
-  a.means = means, a.quats = quats, a.log_scales = log_scales, a.opacity_logits = opacity_logits;
-  a.sh = sh, a.viewmats = viewmats, a.Ks = Ks;
-  a.norm = sh_norm_table();
-  a.qsx = float(kQ16) / float(W);
-  a.qsy = float(kQ16) / float(H);
-
-  if (screen_capacity > 0 && (!screen || !aabb16)) return GS_E_INVALID;
-  a.cap = screen_capacity;
 
   HostStage* hs = nullptr;
   GS_TRY(host_stage(uint64_t(C) + 2, &hs));
   hs->buf[C + 1] = 0;  // receives the 4-byte error flag in its low half
-  GS_TRY(launch_fill_u32(workspace, 0u, ws.bytes / 4, s));
-  GS_TRY(launch_project_mask(a, mask, s));
-  // the group counts are the popcounts of the mask words; the scan takes
-  // them from the words and writes them out on the way
-  GS_TRY(launch_scan_u32(nullptr, mask, wg_count, uint64_t(n_groups), wg_scan, nullptr, ws.total,
-                         ws.lookback, ws.ticket, ws.err, s));
-  GS_TRY(launch_cam_offsets(wg_scan, Np / kMaskGroup, C, ws.total, ws.cam_off, s));
-  GS_TRY(hipMemcpyAsync(hs->buf, ws.cam_off, sizeof(int64_t) * (C + 1), hipMemcpyDeviceToHost, s));
-  // the scan's bounded look-back raises this flag if a wait timed out;
-  // the slots and nnz are then wrong, so it is checked before them
-  GS_TRY(hipMemcpyAsync(hs->buf + C + 1, ws.err, sizeof(int), hipMemcpyDeviceToHost, s));
-  GS_TRY(hipEventRecord(hs->ev, s));
-  // The compaction needs no host decision: slots at or past the capacity
-  // are not written, so it is queued before the host reads the count.
-  const hipError_t e = launch_project_compact(a, mask, wg_scan, screen, aabb16, s);
+  st = project_queue(s, a, mask, wg_count, wg_scan, screen, aabb16, ws, workspace, [&] {
+    hipError_t e = hipMemcpyAsync(hs->buf, ws.cam_off, sizeof(int64_t) * (C + 1),
+                                  hipMemcpyDeviceToHost, s);
+    // the scan's bounded look-back raises this flag if a wait timed out;
+    // the slots and nnz are then wrong, so it is checked before them
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(hs->buf + C + 1, ws.err, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipEventRecord(hs->ev, s);
+    return e;
+  });
   // wait even after an error: the copy into the staging words must land
   const hipError_t e2 = hipEventSynchronize(hs->ev);
-  if (e != hipSuccess || e2 != hipSuccess) return GS_E_HIP;
+  if (st != GS_OK) return st;
+  if (e2 != hipSuccess) return GS_E_HIP;
   const int64_t nnz = hs->buf[C];
   int flag = 0;
   std::memcpy(&flag, hs->buf + C + 1, sizeof(int));
   *nnz_out = nnz;
   if (cam_offsets_out) std::memcpy(cam_offsets_out, hs->buf, sizeof(int64_t) * (C + 1));
+  return gs_readback_status(flag, nnz, int64_t(1) << 31, screen_capacity);
+}
+
+int gs_project_noalloc(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
+                       int32_t sh_degree, const float* means, const float* quats,
+                       const float* log_scales, const float* opacity_logits, const float* sh,
+                       const float* viewmats, const float* Ks, uint64_t* mask,
+                       uint32_t* wg_count, uint32_t* wg_scan, float* screen, uint32_t* aabb16,
+                       int64_t screen_capacity, int64_t* nnz_out, int64_t* cam_offsets_out) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st = project_check(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, sh,
+                         viewmats, Ks, mask, wg_count, wg_scan, screen, aabb16, screen_capacity,
+                         nnz_out);
+  if (st != GS_OK) return st;
+  // sizes past the static scratch (or the host words below) are refused
+  // before any device work
+  const int64_t n_groups = int64_t(C) * gs_pad_n(N) / kMaskGroup;
+  if (C > kNoAllocMaxCams || carve_project(nullptr, n_groups, C).bytes > kNoAllocScratchBytes)
+    return GS_E_WORKSPACE;
+  void* base = nullptr;
+  GS_TRY(scratch_address(&base));
+  const ProjectWs ws = carve_project(base, n_groups, C);
+  ProjectArgs a = project_args(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logits, sh,
+                               viewmats, Ks);
+  a.cap = screen_capacity;
+  st = project_queue(s, a, mask, wg_count, wg_scan, screen, aabb16, ws, base,
+                     [] { return hipSuccess; });
+  if (st != GS_OK) return st;
+  // the totals land in words on this thread's stack: no page-locked
+  // staging, so the host waits for the whole call here
+  int64_t words[kNoAllocMaxCams + 1];
+  int flag = 0;
+  GS_TRY(hipMemcpyAsync(words, ws.cam_off, sizeof(int64_t) * (C + 1), hipMemcpyDeviceToHost, s));
+  GS_TRY(hipMemcpyAsync(&flag, ws.err, sizeof(int), hipMemcpyDeviceToHost, s));
+  GS_TRY(hipStreamSynchronize(s));
+  const int64_t nnz = words[C];
+  *nnz_out = nnz;
+  if (cam_offsets_out) std::memcpy(cam_offsets_out, words, sizeof(int64_t) * (C + 1));
   return gs_readback_status(flag, nnz, int64_t(1) << 31, screen_capacity);
 }
 

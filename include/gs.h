@@ -161,6 +161,32 @@ int gs_project(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
                int64_t* nnz_out, int64_t* cam_offsets_out);
 
 /* ---------------------------------------------------------------------
+ * gs_project_noalloc -- gs_project for callers that cannot allocate
+ * memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.
+ *
+ * Same arguments, results and errors as gs_project, without the workspace:
+ * the projection workspace lives in a fixed 64 KiB device array inside the
+ * library (one per device, held until the process ends), and the totals
+ * are read back into host stack words, so the call allocates nothing
+ * (no device, page-locked or heap memory). Limits: C <= 256 and
+ * gs_project_workspace_bytes(N, C) <= 65536, which holds up to about
+ * 4e9 camera-Gaussian pairs; past them it returns GS_E_WORKSPACE before
+ * any device work. It blocks the host until its kernels finish (the
+ * readback is not overlapped with the compaction as in gs_project). Every
+ * call on one device shares that array: calls that overlap on a device
+ * (two host threads, or two streams) race and must be serialized by the
+ * caller. Each call clears what must start at zero.
+ * ------------------------------------------------------------------- */
+int gs_project_noalloc(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
+                       int32_t sh_degree, const float* means, const float* quats,
+                       const float* log_scales, const float* opacity_logits,
+                       const float* sh, const float* viewmats, const float* Ks,
+                       uint64_t* mask, uint32_t* wg_count, uint32_t* wg_scan,
+                       float* screen, uint32_t* aabb16, int64_t screen_capacity,
+                       int64_t* nnz_out, int64_t* cam_offsets_out);
+
+/* ---------------------------------------------------------------------
  * gs_intersect -- (tile, pair) intersections, sorted per tile by depth.
  * [VRAM] "The 4 GiB rule and the 2^31 limit" (exact 64-bit total checked
  * on the host before anything is sized by it; 64-bit addressing for every

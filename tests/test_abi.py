@@ -36,7 +36,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"gs_status_str", "gs_version", "gs_readback_status",
                           "gs_tile_offsets_check", "gs_pad_n", "gs_project_workspace_bytes",
-                          "gs_intersect_workspace_bytes", "gs_project", "gs_intersect",
+                          "gs_intersect_workspace_bytes", "gs_project", "gs_project_noalloc",
+                          "gs_intersect",
                           "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd",
                           "gs_project_bwd_adam", "gs_arena_plan", "gs_profile_enable",
                           "gs_profile_disable",
