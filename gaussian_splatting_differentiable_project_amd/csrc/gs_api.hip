@@ -588,7 +588,8 @@ int gs_project_bwd(void* stream, int64_t N, int32_t C, int32_t W, int32_t H, int
   if (!means || !quats || !log_scales || !opacity_logits || !sh || !viewmats || !Ks || !mask ||
       !wg_scan || !v_means || !v_quats || !v_log_scales || !v_opacity_logits || !v_sh)
     return GS_E_INVALID;
-  if (!aligned(quats, 16) || !aligned(v_quats, 16) || !aligned(v_screen, 8)) return GS_E_INVALID;
+  if (!aligned(quats, 16) || !aligned(v_quats, 16) || !aligned(v_sh, 16) || !aligned(v_screen, 8))
+    return GS_E_INVALID;
   const ProjectArgs a = project_args(N, C, W, H, sh_degree, means, quats, log_scales,
                                      opacity_logits, sh, viewmats, Ks);
   return hip_status(launch_project_bwd(a, mask, wg_scan, v_screen, v_means, v_quats, v_log_scales,

@@ -96,6 +96,13 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Lane `src`'s value of a 64-bit register (src wave-uniform).
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), src));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), src));
+  return (uint64_t(hi) << 32) | lo;
+}
+
 // Sum of a float over the 64 lanes; every lane gets the total.
 // Row sums (16 lanes) by DPP row rotations, then the four row sums by
 // readlane.

@@ -178,10 +178,13 @@ __global__ __launch_bounds__(kWave) void k_project_compact(ProjectArgs a,
   const uint64_t lt = lanemask_lt();
   // Which cameras see this lane's Gaussian (mask words are wave-uniform
   // loads; the bits of padding lanes are clear).
+  // Cameras are taken 64 at a time: lane j loads camera c0 + j's words.
   bool any = false;
   int npairs = 0;  // the wave's visible pairs (wave-uniform)
+  CamWords cw{};
   for (int c = 0; c < a.C; ++c) {
-    const uint64_t mine = mask[(int64_t(c) * a.N_pad + grp * kMaskGroup) / 64 + half];
+    if ((c & 63) == 0) cw = load_cam_words(mask, wg_scan, a.N_pad, grp, c, a.C);
+    const uint64_t mine = half ? cam_w1(cw, c & 63) : cam_w0(cw, c & 63);
     any |= ((mine >> lane) & 1ull) != 0;
     npairs += __popcll(mine);
   }
@@ -199,11 +202,11 @@ __global__ __launch_bounds__(kWave) void k_project_compact(ProjectArgs a,
 #pragma unroll
     for (int i = 0; i < K * 3; ++i) shc[i] = shg[i];
     for (int c = 0; c < a.C; ++c) {
-      const int64_t p0 = int64_t(c) * a.N_pad + grp * kMaskGroup;
-      const uint64_t w0 = mask[p0 / 64], w1 = mask[p0 / 64 + 1];
+      if ((c & 63) == 0 && c > 0) cw = load_cam_words(mask, wg_scan, a.N_pad, grp, c, a.C);
+      const uint64_t w0 = cam_w0(cw, c & 63), w1 = cam_w1(cw, c & 63);
       const uint64_t mine = half ? w1 : w0;
       if (!((mine >> lane) & 1ull)) continue;
-      const int64_t slot = int64_t(wg_scan[p0 / kMaskGroup]) + (half ? __popcll(w0) : 0) +
+      const int64_t slot = int64_t(cam_base(cw, c & 63)) + (half ? __popcll(w0) : 0) +
                            __popcll(mine & lt);
       if (slot < a.cap) compact_pair<DEG>(a, G, opac, shc, c, slot, screen, aabb16);
     }
@@ -229,11 +232,11 @@ __global__ __launch_bounds__(kWave) void k_project_compact(ProjectArgs a,
   };
   int qn = 0;  // queued pairs (wave-uniform)
   for (int c = 0; c < a.C; ++c) {
-    const int64_t p0 = int64_t(c) * a.N_pad + grp * kMaskGroup;
-    const uint64_t w0 = mask[p0 / 64], w1 = mask[p0 / 64 + 1];
+    if ((c & 63) == 0 && c > 0) cw = load_cam_words(mask, wg_scan, a.N_pad, grp, c, a.C);
+    const uint64_t w0 = cam_w0(cw, c & 63), w1 = cam_w1(cw, c & 63);
     const uint64_t mine = half ? w1 : w0;
     if (mine == 0) continue;
-    const int64_t base = int64_t(wg_scan[p0 / kMaskGroup]) + (half ? __popcll(w0) : 0);
+    const int64_t base = int64_t(cam_base(cw, c & 63)) + (half ? __popcll(w0) : 0);
     if ((mine >> lane) & 1ull) {
       const int r = __popcll(mine & lt);
       s_cl[qn + r] = (uint32_t(c) << 6) | uint32_t(lane);

@@ -66,6 +66,37 @@ __device__ __forceinline__ double t_sqrt(double x) { return sqrt(x); }
 __device__ __forceinline__ float t_exp(float x) { return expf(x); }
 __device__ __forceinline__ double t_exp(double x) { return exp(x); }
 
+// The mask words and group slot base of up to 64 cameras for one 128-pair
+// mask group, loaded at once: lane j holds camera c0 + j's two words (the
+// group's two waves) and the first slot of its group (zeros past C). A
+// camera loop then takes them with readlanes instead of one dependent
+// memory round trip per camera.
+struct CamWords {
+  uint64_t w0, w1;
+  uint32_t base;
+};
+
+__device__ __forceinline__ CamWords load_cam_words(const uint64_t* __restrict__ mask,
+                                                   const uint32_t* __restrict__ wg_scan,
+                                                   int64_t N_pad, int64_t grp, int c0, int C) {
+  CamWords cw{0, 0, 0};
+  const int c = c0 + int(__lane_id());
+  if (c < C) {
+    const int64_t p0 = int64_t(c) * N_pad + grp * kMaskGroup;
+    cw.w0 = mask[p0 / 64];
+    cw.w1 = mask[p0 / 64 + 1];
+    cw.base = wg_scan[p0 / kMaskGroup];
+  }
+  return cw;
+}
+
+// Camera c0 + j's words from a CamWords (j wave-uniform).
+__device__ __forceinline__ uint64_t cam_w0(const CamWords& cw, int j) { return readlane_u64(cw.w0, j); }
+__device__ __forceinline__ uint64_t cam_w1(const CamWords& cw, int j) { return readlane_u64(cw.w1, j); }
+__device__ __forceinline__ uint32_t cam_base(const CamWords& cw, int j) {
+  return uint32_t(__builtin_amdgcn_readlane(int(cw.base), j));
+}
+
 // Rotation matrix of the unit quaternion (w, x, y, z), row-major.
 template <typename T>
 __device__ __forceinline__ void quat_rotmat(T w, T x, T y, T z, T* R) {

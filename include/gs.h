@@ -307,6 +307,7 @@ int gs_rasterize_bwd(void* stream, int32_t C, int32_t W, int32_t H,
  * Outputs v_means[N][3], v_quats[N][4], v_log_scales[N][3],
  * v_opacity_logits[N], v_sh[N][K][3]: overwritten when accumulate == 0
  * (zeros for Gaussians visible nowhere), added to when accumulate != 0.
+ * quats, v_quats and v_sh must be 16-byte aligned (GS_E_INVALID).
  * ------------------------------------------------------------------- */
 int gs_project_bwd(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
                    int32_t sh_degree, const float* means, const float* quats,
