@@ -159,7 +159,7 @@ __device__ __forceinline__ void compact_pair(const ProjectArgs& a, const GaussLo
 //    lane; the camera-independent part of each Gaussian is computed once
 //    by its own lane and shared through LDS.
 // A pair past the caller's capacity is counted by the scan, not written.
-template <int DEG>
+template <int DEG, bool DENSE_ONLY>
 __global__ __launch_bounds__(kWave) void k_project_compact(ProjectArgs a,
                                                            const uint64_t* __restrict__ mask,
                                                            const uint32_t* __restrict__ wg_scan,
@@ -189,6 +189,7 @@ __global__ __launch_bounds__(kWave) void k_project_compact(ProjectArgs a,
     npairs += __popcll(mine);
   }
   if (npairs == 0) return;
+  if (DENSE_ONLY && 2 * npairs < a.C * kWave) return;
   GaussLocal<double> G;
   float opac = 0.f;
   if (any) {
@@ -212,6 +213,7 @@ __global__ __launch_bounds__(kWave) void k_project_compact(ProjectArgs a,
     }
     return;
   }
+  if constexpr (DENSE_ONLY) return;  // sparse waves: k_project_compact_pairs
   if (any) {
 #pragma unroll
     for (int i = 0; i < 9; ++i) s_M[i][lane] = G.M[i];
@@ -266,6 +268,83 @@ __global__ __launch_bounds__(kWave) void k_project_compact(ProjectArgs a,
   }
   __syncthreads();
   if (lane < qn) run(s_cl[lane], s_slot[lane]);
+}
+
+// Compaction of the sparse waves for 2 to kCpMaxCams cameras (the dense
+// ones run in k_project_compact<DEG, true>, launched beside it): the
+// pair-list form of the sparse path above, in a kernel of its own so that
+// it does not carry the dense path's registers (the SH row held across the
+// camera walk): the wave lists its visible pairs in LDS Gaussian by Gaussian, puts
+// each Gaussian's position, M (fp64) and opacity and the cameras in LDS,
+// then computes the listed pairs 64 at a time, one per lane, each reading
+// its Gaussian's SH row from memory.
+constexpr int kCpMaxCams = 32;
+
+template <int DEG>
+__global__ __launch_bounds__(kWave, 4) void k_project_compact_pairs(
+    ProjectArgs a, const uint64_t* __restrict__ mask, const uint32_t* __restrict__ wg_scan,
+    float* __restrict__ screen, uint32_t* __restrict__ aabb16) {
+  constexpr int K = (DEG + 1) * (DEG + 1);
+  __shared__ double s_M[9][kWave];
+  __shared__ float s_mu[3][kWave];
+  __shared__ float s_op[kWave];
+  __shared__ uint32_t s_base[kCpMaxCams];
+  __shared__ uint64_t s_mine[kCpMaxCams];
+  extern __shared__ uint32_t s_who[];  // [64 C] camera << 6 | lane, Gaussian-major
+  const int lane = threadIdx.x;
+  const int C = a.C;
+  const int half = int(blockIdx.x & 1);
+  const int64_t grp = int64_t(blockIdx.x >> 1);
+  const int64_t gw = int64_t(blockIdx.x) * kWave;  // this wave's first Gaussian
+
+  const CamWords cw = load_cam_words(mask, wg_scan, a.N_pad, grp, 0, C);
+  uint32_t vmask = 0;
+  for (int c = 0; c < C; ++c) {
+    const uint64_t w0 = cam_w0(cw, c), w1 = cam_w1(cw, c);
+    const uint64_t mine = half ? w1 : w0;
+    if (lane == 0) {
+      s_mine[c] = mine;
+      s_base[c] = cam_base(cw, c) + (half ? uint32_t(__popcll(w0)) : 0u);
+    }
+    vmask |= uint32_t((mine >> lane) & 1ull) << c;
+  }
+  const int cnt = __popc(vmask);
+  const int off = int(wave_incl_scan_u32(uint32_t(cnt))) - cnt;
+  const int qn = __builtin_amdgcn_readlane(off + cnt, 63);  // wave-uniform
+  // dense waves (at least half of 64 per camera) are k_project_compact's
+  if (qn == 0 || 2 * qn >= C * kWave) return;
+  {
+    uint32_t vm = vmask;
+    for (int j = off; vm; ++j) {
+      const int c = __builtin_ctz(vm);
+      vm &= vm - 1u;
+      s_who[j] = (uint32_t(c) << 6) | uint32_t(lane);
+    }
+  }
+  if (cnt) {
+    GaussLocal<double> G;
+    gauss_local(a.means, a.quats, a.log_scales, gw + lane, G);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) s_M[i][lane] = G.M[i];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) s_mu[i][lane] = G.mu[i];
+    s_op[lane] = float(1.0 / (1.0 + exp(-double(a.opacity_logits[gw + lane]))));
+  }
+  __syncthreads();
+  for (int b = 0; b < qn; b += kWave) {
+    const int e = b + lane;
+    if (e >= qn) break;
+    const uint32_t who = s_who[e];
+    const int c = int(who >> 6), gl = int(who & 63u);
+    const int64_t slot = int64_t(s_base[c]) + __popcll(s_mine[c] & ((1ull << gl) - 1ull));
+    if (slot >= a.cap) continue;
+    GaussLocal<double> Gs;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) Gs.M[i] = s_M[i][gl];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) Gs.mu[i] = s_mu[i][gl];
+    compact_pair<DEG>(a, Gs, s_op[gl], a.sh + (gw + gl) * (K * 3), c, slot, screen, aabb16);
+  }
 }
 
 __global__ void k_cam_offsets(const uint32_t* __restrict__ wg_scan, int64_t groups_per_cam, int C,
@@ -325,12 +404,34 @@ hipError_t launch_project_compact(const ProjectArgs& a, const uint64_t* mask,
   if (!fits_dispatch(uint64_t(blocks), kWave)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)}, block{uint32_t(kWave)};
   ProfScope prof("k_project_compact", s);
-  switch (a.deg) {
-    case 0: hipLaunchKernelGGL(k_project_compact<0>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;
-    case 1: hipLaunchKernelGGL(k_project_compact<1>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;
-    case 2: hipLaunchKernelGGL(k_project_compact<2>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;
-    default: hipLaunchKernelGGL(k_project_compact<3>, grid, block, 0, s, a, mask, wg_scan, screen, aabb16); break;
+  if (a.C >= 2 && a.C <= kCpMaxCams) {
+    const size_t shm = size_t(kWave) * size_t(a.C) * sizeof(uint32_t);
+#define GS_LAUNCH_CP(D)                                                                         \
+  hipLaunchKernelGGL(k_project_compact_pairs<D>, grid, block, shm, s, a, mask, wg_scan, screen, \
+                     aabb16)
+#define GS_LAUNCH_CD(D)                                                                        \
+  hipLaunchKernelGGL((k_project_compact<D, true>), grid, block, 0, s, a, mask, wg_scan, screen, \
+                     aabb16)
+    switch (a.deg) {
+      case 0: GS_LAUNCH_CP(0); GS_LAUNCH_CD(0); break;
+      case 1: GS_LAUNCH_CP(1); GS_LAUNCH_CD(1); break;
+      case 2: GS_LAUNCH_CP(2); GS_LAUNCH_CD(2); break;
+      default: GS_LAUNCH_CP(3); GS_LAUNCH_CD(3); break;
+    }
+#undef GS_LAUNCH_CP
+#undef GS_LAUNCH_CD
+    return hipGetLastError();
   }
+#define GS_LAUNCH_C(D)                                                                          \
+  hipLaunchKernelGGL((k_project_compact<D, false>), grid, block, 0, s, a, mask, wg_scan, screen, \
+                     aabb16)
+  switch (a.deg) {
+    case 0: GS_LAUNCH_C(0); break;
+    case 1: GS_LAUNCH_C(1); break;
+    case 2: GS_LAUNCH_C(2); break;
+    default: GS_LAUNCH_C(3); break;
+  }
+#undef GS_LAUNCH_C
   return hipGetLastError();
 }
 
