@@ -105,11 +105,10 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint
 // the pair's projection reads.
 template <int DEG>
 __device__ __forceinline__ void compact_pair(const ProjectArgs& a, const GaussLocal<double>& G,
-                                             float opac, const float* shg, int c, int64_t slot,
-                                             float* __restrict__ screen,
+                                             float opac, const float* shg, const Camera& k,
+                                             int64_t slot, float* __restrict__ screen,
                                              uint32_t* __restrict__ aabb16) {
   constexpr int K = (DEG + 1) * (DEG + 1);
-  const Camera k = load_camera(a.viewmats, a.Ks, c);
   PairFwd<double> P;
   pair_fwd(k, G, double(a.W), double(a.H), P);
   // colour toward the camera centre
@@ -209,7 +208,8 @@ __global__ __launch_bounds__(kWave) void k_project_compact(ProjectArgs a,
       if (!((mine >> lane) & 1ull)) continue;
       const int64_t slot = int64_t(cam_base(cw, c & 63)) + (half ? __popcll(w0) : 0) +
                            __popcll(mine & lt);
-      if (slot < a.cap) compact_pair<DEG>(a, G, opac, shc, c, slot, screen, aabb16);
+      if (slot < a.cap)
+        compact_pair<DEG>(a, G, opac, shc, load_camera(a.viewmats, a.Ks, c), slot, screen, aabb16);
     }
     return;
   }
@@ -229,8 +229,8 @@ __global__ __launch_bounds__(kWave) void k_project_compact(ProjectArgs a,
     for (int i = 0; i < 9; ++i) Gs.M[i] = s_M[i][src];
 #pragma unroll
     for (int i = 0; i < 3; ++i) Gs.mu[i] = s_mu[i][src];
-    compact_pair<DEG>(a, Gs, s_op[src], a.sh + (gw + src) * (K * 3), int(cl >> 6), slot, screen,
-                      aabb16);
+    compact_pair<DEG>(a, Gs, s_op[src], a.sh + (gw + src) * (K * 3),
+                      load_camera(a.viewmats, a.Ks, int(cl >> 6)), slot, screen, aabb16);
   };
   int qn = 0;  // queued pairs (wave-uniform)
   for (int c = 0; c < a.C; ++c) {
@@ -290,6 +290,7 @@ __global__ __launch_bounds__(kWave, 4) void k_project_compact_pairs(
   __shared__ float s_op[kWave];
   __shared__ uint32_t s_base[kCpMaxCams];
   __shared__ uint64_t s_mine[kCpMaxCams];
+  __shared__ Camera s_cam[kCpMaxCams];
   extern __shared__ uint32_t s_who[];  // [64 C] camera << 6 | lane, Gaussian-major
   const int lane = threadIdx.x;
   const int C = a.C;
@@ -330,6 +331,7 @@ __global__ __launch_bounds__(kWave, 4) void k_project_compact_pairs(
     for (int i = 0; i < 3; ++i) s_mu[i][lane] = G.mu[i];
     s_op[lane] = float(1.0 / (1.0 + exp(-double(a.opacity_logits[gw + lane]))));
   }
+  if (lane < C) s_cam[lane] = load_camera(a.viewmats, a.Ks, lane);
   __syncthreads();
   for (int b = 0; b < qn; b += kWave) {
     const int e = b + lane;
@@ -343,7 +345,8 @@ __global__ __launch_bounds__(kWave, 4) void k_project_compact_pairs(
     for (int i = 0; i < 9; ++i) Gs.M[i] = s_M[i][gl];
 #pragma unroll
     for (int i = 0; i < 3; ++i) Gs.mu[i] = s_mu[i][gl];
-    compact_pair<DEG>(a, Gs, s_op[gl], a.sh + (gw + gl) * (K * 3), c, slot, screen, aabb16);
+    compact_pair<DEG>(a, Gs, s_op[gl], a.sh + (gw + gl) * (K * 3), s_cam[c], slot, screen,
+                      aabb16);
   }
 }
 

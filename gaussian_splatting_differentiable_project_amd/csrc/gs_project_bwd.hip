@@ -268,19 +268,31 @@ __device__ __forceinline__ void finish_gaussian(int64_t g, bool any, const Gauss
 // instead of 64 scattered 16-byte pieces at the row stride. With ADAM the
 // same walk applies one Adam step to the SH parameters and moments
 // (coefficient 0, the first 3 values of a row, is DC). Rows past N are
-// left alone. Every lane of the wave must call it; `stage` holds 32 * 3K
-// floats of this wave's LDS, free on entry and on exit.
+// left alone. Every lane of the wave must call it; `stage` holds
+// 32 * sh_stage_stride<DEG>() floats of this wave's LDS, free on entry and
+// on exit.
+// Row stride of the SH staging (floats): with 3K a multiple of 4, an odd
+// number of 16-byte groups, so rows start 16-byte aligned and eight
+// consecutive rows cover all 32 banks with their 4-word pieces; otherwise
+// odd, so single-word accesses of 32 rows fall in 32 different banks.
+template <int DEG>
+constexpr int sh_stage_stride() {
+  constexpr int R = 3 * (DEG + 1) * (DEG + 1);
+  return R % 4 == 0 ? ((R / 4) % 2 == 1 ? R : R + 4) : (R % 2 == 1 ? R : R + 1);
+}
+
 template <int DEG, bool ADAM>
 __device__ __forceinline__ void store_sh_rows(float* stage, const float* gsh, int64_t g0,
                                               int64_t N, float* __restrict__ v_sh,
                                               int accumulate, const AdamArgs& ad) {
   constexpr int R = 3 * (DEG + 1) * (DEG + 1);
+  constexpr int S = sh_stage_stride<DEG>();
   const int lane = __lane_id();
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {
     const int r0 = h * 32;
     if (lane >= r0 && lane < r0 + 32) {
-      float* dst = stage + (lane - r0) * R;
+      float* dst = stage + (lane - r0) * S;
 #pragma unroll
       for (int i = 0; i < R; ++i) dst[i] = gsh[i];
     }
@@ -296,8 +308,9 @@ __device__ __forceinline__ void store_sh_rows(float* stage, const float* gsh, in
         float* __restrict__ m = ad.m[4] + e0;
         float* __restrict__ v = ad.v[4] + e0;
         for (int i = lane; i < n; i += kWave) {
-          const float gr = stage[i];
-          const float lr = (i % R) < 3 ? ad.lr[4] : ad.lr[5];
+          const int row = i / R, col = i - row * R;
+          const float gr = stage[row * S + col];
+          const float lr = col < 3 ? ad.lr[4] : ad.lr[5];
           const float mm = fmaf(ad.beta1, m[i], (1.f - ad.beta1) * gr);
           const float vv = fmaf(ad.beta2, v[i], (1.f - ad.beta2) * gr * gr);
           p[i] -= lr * (mm * ad.inv_bc1) / (sqrtf(vv * ad.inv_bc2) + ad.eps);
@@ -305,20 +318,27 @@ __device__ __forceinline__ void store_sh_rows(float* stage, const float* gsh, in
           v[i] = vv;
         }
       } else {
-        // e0 * 4 bytes is a multiple of 128: float4 from an aligned base
-        float4* __restrict__ dst = reinterpret_cast<float4*>(v_sh + e0);
-        const float4* src = reinterpret_cast<const float4*>(stage);
-        const int n4 = n >> 2;
-        for (int q = lane; q < n4; q += kWave) {
-          float4 x = src[q];
-          if (accumulate) {
-            const float4 y = dst[q];
-            x.x += y.x, x.y += y.y, x.z += y.z, x.w += y.w;
+        if constexpr (R % 4 == 0) {
+          // e0 * 4 bytes is a multiple of 128: float4 from an aligned base
+          float4* __restrict__ dst = reinterpret_cast<float4*>(v_sh + e0);
+          constexpr int R4 = R / 4;
+          const int n4 = n >> 2;
+          for (int q = lane; q < n4; q += kWave) {
+            const int row = q / R4, col = q - row * R4;
+            float4 x = *reinterpret_cast<const float4*>(stage + row * S + 4 * col);
+            if (accumulate) {
+              const float4 y = dst[q];
+              x.x += y.x, x.y += y.y, x.z += y.z, x.w += y.w;
+            }
+            dst[q] = x;
           }
-          dst[q] = x;
+        } else {
+          for (int i = lane; i < n; i += kWave) {
+            const int row = i / R, col = i - row * R;
+            const float x = stage[row * S + col];
+            v_sh[e0 + i] = accumulate ? v_sh[e0 + i] + x : x;
+          }
         }
-        for (int i = (n4 << 2) + lane; i < n; i += kWave)
-          v_sh[e0 + i] = accumulate ? v_sh[e0 + i] + stage[i] : stage[i];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -334,7 +354,7 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_bwd(
     float* __restrict__ v_log_scales, float* __restrict__ v_opacity_logits,
     float* __restrict__ v_sh, int accumulate, AdamArgs ad) {
   constexpr int K = (DEG + 1) * (DEG + 1);
-  __shared__ __align__(16) float s_stage[2][32 * 3 * K];  // per wave: SH staging
+  __shared__ __align__(16) float s_stage[2][32 * sh_stage_stride<DEG>()];  // per wave: SH staging
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t g = int64_t(blockIdx.x) * kMaskGroup + tid;
   const bool valid = g < a.N;
@@ -443,7 +463,8 @@ __global__ __launch_bounds__(kWave) void k_project_bwd_pairs(
     float* __restrict__ v_sh, int accumulate, AdamArgs ad) {
   constexpr int K = (DEG + 1) * (DEG + 1);
   // per-Gaussian data and per-pair results; at the end, the SH staging
-  constexpr int kPool = (13 + kPbRes) * kWave > 32 * 3 * K ? (13 + kPbRes) * kWave : 32 * 3 * K;
+  constexpr int kStage = 32 * sh_stage_stride<DEG>();
+  constexpr int kPool = (13 + kPbRes) * kWave > kStage ? (13 + kPbRes) * kWave : kStage;
   __shared__ __align__(16) float s_pool[kPool];
   float(*s_mu)[kWave] = reinterpret_cast<float(*)[kWave]>(s_pool);
   float(*s_M)[kWave] = reinterpret_cast<float(*)[kWave]>(s_pool + 3 * kWave);
