@@ -48,7 +48,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 KERNELS = ["k_project_mask", "k_scan", "k_cam_offsets", "k_project_compact", "k_fill_u32",
            "k_isect_prep", "k_radix_count", "k_radix_scatter", "k_emit_count", "k_emit_write",
-           "k_tile_ranges", "k_tile_order_keys", "k_tile_order_rank", "k_raster_fwd", "k_raster_bwd", "k_project_bwd",
+           "k_tile_ranges", "k_row_chunks", "k_row_count", "k_row_colscan", "k_row_expand",
+           "k_tile_order_keys", "k_tile_order_rank", "k_raster_fwd", "k_raster_bwd", "k_project_bwd",
            "k_project_bwd_adam"]
 KERNEL_SOURCE = {"k_raster_fwd": "gs_raster.hip", "k_raster_bwd": "gs_raster.hip",
                  "k_project_mask": "gs_project.hip", "k_project_compact": "gs_project.hip",

@@ -80,13 +80,16 @@ ProjectWs carve_project(void* base, int64_t n_groups, int32_t C) {
 // ---- gs_intersect workspace ----
 // Layout: the words that must start at zero come first (one fill), then
 // every array the first phase needs (sized by nnz and the tile count),
-// then the entry arrays sized by n_isects.
+// then the arrays sized by n_isects (tile entries) or by the segment
+// count (row segments), whichever way the geometry sorts.
 struct IsectWs {
-  uint64_t* total;      // [1 + kPrepBlocks]: n_isects, then per-block depth key ranges (prep)
+  uint64_t* total;      // [2 + kPrepBlocks]: n_isects, per-block depth key ranges, segments
   int* err;
   uint32_t* ticket;     // scan of the emit count matrix
   uint64_t* scan_lb;    // its look-back words
   uint64_t* sort_grp;   // radix sort group totals
+  uint32_t *ticket_c, *ticket_t;  // row path: scans of the chunk and tile counts
+  uint64_t *lb_c, *lb_t;
   uint64_t zero_words;  // u32 words to clear, from the start
   int64_t* cam_off;     // [C+1]
   uint32_t *dkeys_a, *dkeys_b, *dvals_a, *dvals_b;
@@ -97,20 +100,35 @@ struct IsectWs {
   uint64_t* emit_off;   // their exclusive scan: first output position of each run
   uint64_t* emit_total;
   uint64_t phase1_bytes;  // enough to count (I still unknown)
-  uint32_t *tkeys_a, *tkeys_b, *tvals;
+  uint32_t *tkeys_a, *tkeys_b, *tvals;  // tile path
+  uint32_t *rkeys_a, *rkeys_b, *rvals;  // row path
+  RowScratch rows;
   uint64_t bytes;
 };
 
-IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects, uint64_t n_tiles) {
+// n_segments < 0: size the row path for every segment count up to
+// n_isects (a pair's segments never outnumber its entries).
+IsectWs carve_isect(void* base, int32_t C, int32_t W, int32_t H, int64_t nnz, int64_t n_isects,
+                    int64_t n_segments) {
   Carver cv{static_cast<char*>(base)};
   IsectWs w{};
   const uint64_t n = uint64_t(nnz);
   const uint64_t mat = emit_matrix_len(n);
-  w.total = cv.take<uint64_t>(1 + kPrepBlocks);
+  const uint64_t n_tiles = uint64_t(C) * uint64_t(tiles_x_of(W) * tiles_y_of(H));
+  const uint64_t R = uint64_t(C) * uint64_t(tiles_y_of(H));
+  RowKeys rk{};
+  const bool rows = row_keys_fit(C, W, H, &rk);
+  w.total = cv.take<uint64_t>(2 + kPrepBlocks);
   w.err = cv.take<int>(1);
   w.ticket = cv.take<uint32_t>(1);
   w.scan_lb = cv.take<uint64_t>((mat + kScanTile - 1) / kScanTile + 1);
   w.sort_grp = cv.take<uint64_t>(sort_groups_bytes() / sizeof(uint64_t));
+  if (rows) {
+    w.rows.ticket_c = cv.take<uint32_t>(1);
+    w.rows.ticket_t = cv.take<uint32_t>(1);
+    w.rows.lb_c = cv.take<uint64_t>((R + kScanTile - 1) / kScanTile + 1);
+    w.rows.lb_t = cv.take<uint64_t>((n_tiles + kScanTile - 1) / kScanTile + 1);
+  }
   w.zero_words = cv.off / 4;
   w.cam_off = cv.take<int64_t>(uint64_t(C) + 1);
   w.dkeys_a = cv.take<uint32_t>(n);
@@ -127,9 +145,22 @@ IsectWs carve_isect(void* base, int32_t C, int64_t nnz, int64_t n_isects, uint64
   w.emit_total = cv.take<uint64_t>(1);
   w.phase1_bytes = cv.off;
   const uint64_t I = n_isects > 0 ? uint64_t(n_isects) : 0;
-  w.tkeys_a = cv.take<uint32_t>(I);
-  w.tkeys_b = cv.take<uint32_t>(I);
-  w.tvals = cv.take<uint32_t>(I);
+  if (rows) {
+    const bool bound = n_segments < 0;
+    const uint64_t S = bound ? I : uint64_t(n_segments);
+    w.rkeys_a = cv.take<uint32_t>(S);
+    w.rkeys_b = cv.take<uint32_t>(S);
+    w.rvals = cv.take<uint32_t>(S);
+    w.rows.roff = cv.take<int64_t>(R + 1);
+    w.rows.cc = cv.take<uint32_t>(R);
+    w.rows.cq = cv.take<uint64_t>(R + 1);
+    w.rows.cm = cv.take<uint32_t>(row_matrix_len(S, C, W, H, bound));
+    w.rows.tcount = cv.take<uint32_t>(n_tiles);
+  } else {
+    w.tkeys_a = cv.take<uint32_t>(I);
+    w.tkeys_b = cv.take<uint32_t>(I);
+    w.tvals = cv.take<uint32_t>(I);
+  }
   w.bytes = cv.off;
   return w;
 }
@@ -271,8 +302,7 @@ uint64_t gs_project_workspace_bytes(int64_t N, int32_t C) {
 uint64_t gs_intersect_workspace_bytes(int32_t C, int32_t W, int32_t H, int64_t nnz,
                                       int64_t n_isects) {
   if (C < 1 || nnz < 0 || W < 1 || H < 1) return 0;
-  const uint64_t n_tiles = uint64_t(C) * uint64_t(tiles_x_of(W) * tiles_y_of(H));
-  return carve_isect(nullptr, C, nnz, n_isects, n_tiles).bytes;
+  return carve_isect(nullptr, C, W, H, nnz, n_isects, -1).bytes;
 }
 
 }  // extern "C"
@@ -438,15 +468,17 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   const uint64_t n_tiles = uint64_t(C) * uint64_t(tiles_x_of(W) * tiles_y_of(H));
   if (n_tiles >= (uint64_t(1) << 32)) return GS_E_OVERFLOW;
 
-  IsectWs ws = carve_isect(workspace, C, nnz, 0, n_tiles);
+  RowKeys rk{};
+  const bool rows = row_keys_fit(C, W, H, &rk);
+  IsectWs ws = carve_isect(workspace, C, W, H, nnz, 0, 0);
   *workspace_needed_out = ws.phase1_bytes;
   if (!workspace || workspace_bytes < ws.phase1_bytes) return GS_E_WORKSPACE;
   SortScratch sc;
   sc.cnt = ws.sort_cnt;
   sc.grp = ws.sort_grp;
   HostStage* hs = nullptr;
-  GS_TRY(host_stage(2 + kPrepBlocks, &hs));
-  hs->buf[1 + kPrepBlocks] = 0;  // receives the emit scan's error flag
+  GS_TRY(host_stage(3 + kPrepBlocks, &hs));
+  hs->buf[2 + kPrepBlocks] = 0;  // receives the scans' error flag
 
   // Phase 1: depth keys, per-slot tile counts and their exact 64-bit total.
   GS_TRY(launch_fill_u32(workspace, 0u, ws.zero_words, s));
@@ -454,7 +486,7 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
                         hipMemcpyHostToDevice, s));
   GS_TRY(launch_isect_prep(uint64_t(nnz), screen, aabb16, W, H, ws.dkeys_a, ws.dvals_a, ws.total,
                            s));
-  GS_TRY(hipMemcpyAsync(hs->buf, ws.total, (1 + kPrepBlocks) * sizeof(uint64_t),
+  GS_TRY(hipMemcpyAsync(hs->buf, ws.total, (2 + kPrepBlocks) * sizeof(uint64_t),
                         hipMemcpyDeviceToHost, s));
   GS_TRY(hipEventRecord(hs->ev, s));
   // Phase 2 needs only nnz-sized memory, so it is queued before the host
@@ -485,10 +517,11 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   }
   const uint32_t* order = in_b ? ws.dvals_b : ws.dvals_a;
   const uint64_t I = uint64_t(hs->buf[0]);
+  const uint64_t S = uint64_t(hs->buf[1 + kPrepBlocks]);  // tile-row segments
   bool flag_pending = false;
   *n_isects_out = int64_t(I);
   if (I >= (uint64_t(1) << 62)) return GS_E_OVERFLOW;
-  ws = carve_isect(workspace, C, nnz, int64_t(I), n_tiles);
+  ws = carve_isect(workspace, C, W, H, nnz, int64_t(I), int64_t(S));
   *workspace_needed_out = ws.bytes;
   if (int64_t(I) > isect_capacity) return GS_E_CAPACITY;
   if (workspace_bytes < ws.bytes) return GS_E_WORKSPACE;
@@ -496,6 +529,28 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
 
   if (I == 0) {
     GS_TRY(launch_fill_u32(tile_offsets, 0u, 2 * (n_tiles + 1), s));
+  } else if (rows) {
+    // Phase 3: (tile row, pair) segments in depth order, written already
+    // partitioned by the low digit of their row id (the first pass of a
+    // stable sort by row id); phase 4: the remaining digits. The pair ids
+    // start in flatten_ids when the pass count is odd, so that they end in
+    // the workspace, which the expansion reads while writing flatten_ids.
+    const int b1 = emit_digit_bits(rk.rb);
+    const int rest = rk.rb > b1 ? rk.rb - b1 : 0;
+    const int passes = rest ? sort_passes(rest) : 0;
+    uint32_t* v_first = (passes & 1) ? flatten_ids : ws.rvals;
+    uint32_t* v_second = (passes & 1) ? ws.rvals : flatten_ids;
+    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.cam_off, C, W, H, b1, &rk, S,
+                             ws.emit_cnt, ws.emit_rec, ws.emit_off, ws.emit_total, ws.scan_lb,
+                             ws.ticket, ws.err, ws.rkeys_a, v_first, s));
+    in_b = false;
+    if (passes)
+      GS_TRY(launch_sort_passes(ws.rkeys_a, v_first, ws.rkeys_b, v_second, S, b1, rest, sc,
+                                &in_b, s));
+    // Phase 5: tile offsets from the segments' counts, then the entries.
+    GS_TRY(launch_row_sort(in_b ? ws.rkeys_b : ws.rkeys_a, ws.rvals, S, C, W, H, rk, ws.rows,
+                           ws.err, screen, uint64_t(nnz), I, flatten_ids, tile_offsets,
+                           sorted_keys, s));
   } else {
     // Phase 3: (tile id, slot) entries in depth order, written already
     // partitioned by the low digit of the tile id (the first sort pass).
@@ -506,19 +561,10 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
     // the final pass must land its values in flatten_ids
     uint32_t* v_first = (passes & 1) ? ws.tvals : flatten_ids;
     uint32_t* v_second = (passes & 1) ? flatten_ids : ws.tvals;
-    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.cam_off, C, W, H, b1, I,
+    GS_TRY(launch_isect_emit(uint64_t(nnz), order, aabb16, ws.cam_off, C, W, H, b1, nullptr, I,
                              ws.emit_cnt, ws.emit_rec, ws.emit_off, ws.emit_total, ws.scan_lb,
                              ws.ticket,
                              ws.err, ws.tkeys_a, v_first, s));
-    // The emit's scan of its count matrix waits on predecessors with a
-    // bounded spin and raises ws.err when a wait times out (the emit
-    // offsets are then wrong). The flag is copied here, and the host waits
-    // for that copy only after every later kernel has been queued, so the
-    // device stays busy meanwhile.
-    GS_TRY(hipMemcpyAsync(hs->buf + 1 + kPrepBlocks, ws.err, sizeof(int), hipMemcpyDeviceToHost,
-                          s));
-    GS_TRY(hipEventRecord(hs->ev, s));
-    flag_pending = true;
     // Phase 4: the remaining digits of the stable sort by tile id.
     in_b = false;
     if (passes)
@@ -528,6 +574,17 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
     // Phase 5: per-tile ranges (and the composed 64-bit keys on request).
     GS_TRY(launch_tile_ranges(tkeys, I, n_tiles, tile_offsets, s));
     if (sorted_keys) GS_TRY(launch_compose_keys(tkeys, flatten_ids, screen, I, sorted_keys, s));
+  }
+  if (I > 0) {
+    // The scans above wait on predecessors with a bounded spin and raise
+    // ws.err when a wait times out (their offsets are then wrong). The
+    // flag is copied here, and the host waits for that copy only after
+    // the launch-order kernels have been queued, so the device stays busy
+    // meanwhile.
+    GS_TRY(hipMemcpyAsync(hs->buf + 2 + kPrepBlocks, ws.err, sizeof(int), hipMemcpyDeviceToHost,
+                          s));
+    GS_TRY(hipEventRecord(hs->ev, s));
+    flag_pending = true;
   }
   // Phase 6: launch order for the raster calls, longest tiles first (a
   // stable sort of 16-bit inverted counts): ranks of unique keys for small
@@ -544,7 +601,7 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
   if (!flag_pending) return GS_OK;
   GS_TRY(hipEventSynchronize(hs->ev));
   int flag = 0;
-  std::memcpy(&flag, hs->buf + 1 + kPrepBlocks, sizeof(int));
+  std::memcpy(&flag, hs->buf + 2 + kPrepBlocks, sizeof(int));
   return flag ? GS_E_DEVICE : GS_OK;
 }
 

@@ -98,9 +98,10 @@ hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys
                               SortScratch& sc, bool* in_b, hipStream_t s);
 
 // Intersection stages (gs_intersect.hip).
-// total[1 + kPrepBlocks] (zeroed): total[0] = intersection count; for
+// total[2 + kPrepBlocks] (zeroed): total[0] = intersection count; for
 // each block b, total[1 + b] = (largest depth key << 32) | complement of
-// its smallest depth key.
+// its smallest depth key; total[1 + kPrepBlocks] = tile-row segment count
+// (the sum over pairs of their rectangles' row counts).
 constexpr uint32_t kPrepBlocks = 1024;
 hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* aabb16, int W,
                              int H, uint32_t* dkeys, uint32_t* dvals, uint64_t* total,
@@ -112,16 +113,47 @@ hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* 
 // rec[2 * nnz] (uint32), the matrix scan mat_off (uint64) and its total,
 // and the scan's look-back words (ceil(emit_matrix_len / kScanTile)) and
 // ticket, which must be zero. Writes are clamped to `cap` entries.
+// With `rows` set, the emit writes (tile row, pair) segments instead, keyed
+// by global row id c * tiles_y + ty in bits [0, rb), first tile in the next
+// xb bits, width - 1 above; `bits` then splits the row id.
+struct RowKeys {
+  int rb, xb;
+};
+// Whether the segment keys of this geometry fit 32 bits (rb + 2 xb <= 32).
+bool row_keys_fit(int C, int W, int H, RowKeys* out);
 int emit_digit_bits(int tile_bits);
 uint64_t emit_matrix_len(uint64_t nnz);
 hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
                              const int64_t* cam_off, int C, int W, int H, int bits,
-                             uint64_t cap, uint32_t* mat, uint32_t* rec,
+                             const RowKeys* rows, uint64_t cap, uint32_t* mat, uint32_t* rec,
                              uint64_t* mat_off, uint64_t* mat_total,
                              uint64_t* lb, uint32_t* ticket, int* err, uint32_t* tkeys,
                              uint32_t* tvals, hipStream_t s);
+// Ranges of keys & kmask in a list sorted by them.
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
-                              hipStream_t s);
+                              hipStream_t s, uint32_t kmask = 0xFFFFFFFFu);
+// The sorted list from the segments sorted by row id (keys rkeys, pairs
+// rvals): tile offsets toff[C*T + 1], ids[n_isects] and, when keys_out is
+// not null, the 64-bit keys. Scratch (R = C * tiles_y rows): roff[R + 1],
+// cc[R], cq[R + 1], the count matrix cm[row_matrix_len], tcount[C*T], and
+// two scans' look-back words and tickets (zeroed): lb_c for R values,
+// lb_t for C*T values. Writes are clamped to `cap` entries.
+struct RowScratch {
+  int64_t* roff;
+  uint32_t* cc;
+  uint64_t* cq;
+  uint32_t* cm;
+  uint32_t* tcount;
+  uint64_t *lb_c, *lb_t;
+  uint32_t *ticket_c, *ticket_t;
+};
+// Count-matrix words for n_segments segments; with `bound`, an upper
+// bound valid for every smaller segment count.
+uint64_t row_matrix_len(uint64_t n_segments, int C, int W, int H, bool bound);
+hipError_t launch_row_sort(const uint32_t* rkeys, const uint32_t* rvals, uint64_t n_segments,
+                           int C, int W, int H, const RowKeys& rk, const RowScratch& w,
+                           int* err, const float* screen, uint64_t nnz, uint64_t cap,
+                           uint32_t* ids, int64_t* toff, uint64_t* keys_out, hipStream_t s);
 // Heavy-first launch order in one kernel for small tile counts.
 bool tile_order_small(uint64_t n_tiles);
 hipError_t launch_tile_order_small(const int64_t* toff, uint64_t n_tiles, uint32_t* order,

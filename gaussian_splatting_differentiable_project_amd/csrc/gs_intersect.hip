@@ -56,7 +56,8 @@ __device__ __forceinline__ uint32_t wave_incl_max_u32(uint32_t v) {
 }
 
 // Per slot: depth key bits and identity value for the depth sort, and
-// the exact 64-bit total of tile counts (one atomic per work-group).
+// the exact 64-bit totals of tile counts (total[0]) and of tile-row
+// counts (total[1 + kPrepBlocks]), one atomic each per work-group.
 // total[1 + b] receives block b's largest key (high word) and the
 // complement of its smallest key (low word): the host reduces them and
 // skips the depth passes over digits that every key shares. Words of
@@ -65,10 +66,10 @@ __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* _
                                                    const uint2* __restrict__ aabb16, uint32_t W,
                                                    uint32_t H, uint32_t* __restrict__ dkeys,
                                                    uint32_t* __restrict__ dvals, uint64_t* total) {
-  __shared__ uint64_t s_w[4];
+  __shared__ uint64_t s_w[4], s_wr[4];
   __shared__ uint32_t s_max[4], s_nmin[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  uint64_t n = 0;
+  uint64_t n = 0, nr = 0;
   uint32_t kmax = 0, knmin = 0;
   // grid-stride, so few blocks contend for the one 64-bit total
   const uint64_t stride = uint64_t(gridDim.x) * 256;
@@ -78,12 +79,17 @@ __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* _
     dvals[i] = uint32_t(i);
     kmax = k > kmax ? k : kmax;
     knmin = ~k > knmin ? ~k : knmin;
-    n += rect_count(rect_of(aabb16[i], W, H));
+    const TileRect r = rect_of(aabb16[i], W, H);
+    const uint32_t c = rect_count(r);
+    n += c;
+    nr += c ? r.ty1 - r.ty0 : 0u;
   }
   const uint64_t incl = wave_incl_scan_u64(n);
+  const uint64_t incl_r = wave_incl_scan_u64(nr);
   const uint32_t wmax = wave_incl_max_u32(kmax), wnmin = wave_incl_max_u32(knmin);
   if (lane == 63) {
     s_w[wave] = incl;
+    s_wr[wave] = incl_r;
     s_max[wave] = wmax;
     s_nmin[wave] = wnmin;
   }
@@ -91,6 +97,10 @@ __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* _
   if (tid == 0) {
     const uint64_t b = s_w[0] + s_w[1] + s_w[2] + s_w[3];
     if (b) atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)b);
+    const uint64_t br = s_wr[0] + s_wr[1] + s_wr[2] + s_wr[3];
+    if (br)
+      atomicAdd(reinterpret_cast<unsigned long long*>(total + 1 + kPrepBlocks),
+                (unsigned long long)br);
     uint32_t m = 0, nm = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -126,14 +136,22 @@ constexpr int kEmitSlots = 512;      // positions per sub-batch
 constexpr uint64_t kEmitBlocks = 8192;  // target block count (32 per CU; measured against 2048 and 16384)
 
 struct EmitGeom {
-  uint32_t W, H, tiles_x, T;
+  uint32_t W, H, tiles_x, tiles_y, T;
   int C;
   uint32_t bits;          // digit width, 1..kEmitBits
   uint64_t nnz, per_blk;  // positions per block (a multiple of kEmitSlots)
+  // Row mode: the entries are (tile row, pair) segments instead of
+  // (tile, pair) entries; their key is the global row id c * tiles_y + ty
+  // in bits [0, rb), with the segment's first tile in the next xb bits and
+  // its width minus one above those (rb + 2 xb <= 32).
+  int rows;
+  uint32_t rb, xb;
 };
 
 // Depth-order position i: its slot, the global id of the first tile of
 // its rectangle (camera tile base included) and the rectangle's size.
+// In row mode the "rectangle" is the run of its tile rows, one high: the
+// base is the segment key of its first row, the width its row count.
 __device__ __forceinline__ void emit_slot(uint64_t i, const uint32_t* __restrict__ order,
                                           const uint2* __restrict__ aabb16,
                                           const int64_t* __restrict__ cam_off,
@@ -149,7 +167,14 @@ __device__ __forceinline__ void emit_slot(uint64_t i, const uint32_t* __restrict
   const TileRect r = rect_of(aabb16[slot], g.W, g.H);
   wx = r.tx1 > r.tx0 ? r.tx1 - r.tx0 : 0u;
   wy = r.ty1 > r.ty0 ? r.ty1 - r.ty0 : 0u;
-  b0 = uint32_t(lo) * g.T + r.ty0 * g.tiles_x + r.tx0;
+  if (g.rows) {
+    const bool any = wx != 0u && wy != 0u;
+    b0 = any ? (uint32_t(lo) * g.tiles_y + r.ty0) | ((r.tx0 | ((wx - 1u) << g.xb)) << g.rb) : 0u;
+    wx = any ? wy : 0u;
+    wy = any ? 1u : 0u;
+  } else {
+    b0 = uint32_t(lo) * g.T + r.ty0 * g.tiles_x + r.tx0;
+  }
 }
 
 // mat[d * nblk + b] = entries of block b whose tile id has low digit d
@@ -441,13 +466,13 @@ __global__ __launch_bounds__(256) void k_emit_write(
   }
 }
 
-// tile_offsets[t] = first sorted position whose tile id is >= t.
-// Each lane takes four consecutive boundaries with one 16-byte load; the
-// key before its first one comes from the lane below (or, for lane 0, one
-// more load). Grid-stride over the n + 1 boundaries: a dispatch's
+// tile_offsets[t] = first sorted position whose tile id (key & kmask) is
+// >= t. Each lane takes four consecutive boundaries with one 16-byte load;
+// the key before its first one comes from the lane below (or, for lane 0,
+// one more load). Grid-stride over the n + 1 boundaries: a dispatch's
 // work-item count is a 32-bit quantity, and n_isects can exceed 2^32.
 __global__ __launch_bounds__(256) void k_tile_ranges(const uint32_t* __restrict__ tkeys,
-                                                    uint64_t n, uint64_t n_tiles,
+                                                    uint64_t n, uint64_t n_tiles, uint32_t kmask,
                                                     int64_t* __restrict__ toff) {
   const uint64_t groups = (n + 4) / 4;  // boundaries 0..n, four per lane
   const uint64_t stride = uint64_t(gridDim.x) * 256;
@@ -460,10 +485,10 @@ __global__ __launch_bounds__(256) void k_tile_ranges(const uint32_t* __restrict_
     uint32_t k[4];
     if (i0 + 3 < n) {
       const uint4 v = *reinterpret_cast<const uint4*>(tkeys + i0);
-      k[0] = v.x, k[1] = v.y, k[2] = v.z, k[3] = v.w;
+      k[0] = v.x & kmask, k[1] = v.y & kmask, k[2] = v.z & kmask, k[3] = v.w & kmask;
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) k[j] = i0 + j < n ? tkeys[i0 + j] : cap;
+      for (int j = 0; j < 4; ++j) k[j] = i0 + j < n ? (tkeys[i0 + j] & kmask) : cap;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) k[j] = k[j] < cap ? k[j] : cap;
@@ -471,7 +496,7 @@ __global__ __launch_bounds__(256) void k_tile_ranges(const uint32_t* __restrict_
     const uint32_t below = __shfl_up(k[3], 1, kWave);
     int64_t prev = -1;
     if (i0 > 0) {
-      const uint32_t p = lane == 0 ? tkeys[i0 - 1] : below;
+      const uint32_t p = lane == 0 ? (tkeys[i0 - 1] & kmask) : below;
       prev = int64_t(p < cap ? p : cap);
     }
 #pragma unroll
@@ -483,6 +508,376 @@ __global__ __launch_bounds__(256) void k_tile_ranges(const uint32_t* __restrict_
       prev = cur;
     }
   }
+}
+
+// ---- The sort by tile through tile rows ----
+// A pair's entries on one tile row are a run of consecutive tiles, so the
+// sorted list is built from (row, pair) segments instead of (tile, pair)
+// entries. The segments are emitted in depth order and sorted stably by
+// global row id (the emit and radix passes above, on segment keys); every
+// row's segment list is then in depth order. Each list is cut into chunks
+// of K segments. Per chunk, a difference array over the row's tiles counts
+// the segments covering every tile (k_row_count); an exclusive scan of
+// those counts over the row's chunks, per tile, gives each chunk its first
+// rank in every tile's list and the tile's total (k_row_colscan); a scan of
+// the totals gives the tile offsets. k_row_expand then walks each chunk in
+// order, one wave per 64 tiles of the row, one lane per tile: each segment
+// that covers a lane's tile is that tile's next entry. Within a tile the
+// entries so come in segment order, i.e. in depth order, which is the
+// stable sort of (tile << 32) | depth keys in slot order.
+struct RowGeom {
+  uint32_t tiles_x, R;  // tiles per row, rows (cameras x tile rows)
+  uint32_t rb, xb;      // segment key layout (see EmitGeom), rb < 32
+  uint32_t K;           // segments per chunk
+};
+
+// [x0, x1) of the segment with key k, clamped to the row.
+__device__ __forceinline__ void row_span(uint32_t k, const RowGeom& g, uint32_t& x0,
+                                         uint32_t& x1) {
+  const uint32_t xm = (1u << g.xb) - 1u;
+  const uint32_t a = (k >> g.rb) & xm;
+  const uint32_t b = a + ((k >> (g.rb + g.xb)) & xm) + 1u;
+  x0 = a < g.tiles_x ? a : g.tiles_x;
+  x1 = b < g.tiles_x ? b : g.tiles_x;
+}
+
+// Row of chunk q: the largest r < R with cq[r] <= q (cq is the exclusive
+// scan of the per-row chunk counts, so that row's chunks include q).
+__device__ __forceinline__ uint32_t chunk_row(const uint64_t* __restrict__ cq, uint32_t R,
+                                              uint64_t q) {
+  uint32_t lo = 0, hi = R - 1;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) >> 1;
+    if (cq[mid] <= q) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void k_row_chunks(const int64_t* __restrict__ roff, RowGeom g,
+                                                   uint32_t* __restrict__ cc) {
+  const uint32_t stride = gridDim.x * 256;
+  for (uint32_t r = blockIdx.x * 256 + threadIdx.x; r < g.R; r += stride) {
+    const int64_t len = roff[r + 1] - roff[r];
+    cc[r] = len > 0 ? uint32_t((uint64_t(len) + g.K - 1) / g.K) : 0u;
+  }
+}
+
+// cm[q][x] = segments of chunk q covering tile x of its row. One block per
+// chunk (the grid is an upper bound; blocks past the last chunk leave).
+constexpr uint32_t kRowMaxTiles = 4096;  // tiles per row: W <= 65535
+__global__ __launch_bounds__(256) void k_row_count(const uint32_t* __restrict__ rkeys,
+                                                  const int64_t* __restrict__ roff,
+                                                  const uint64_t* __restrict__ cq, RowGeom g,
+                                                  uint64_t qmax, uint32_t* __restrict__ cm) {
+  __shared__ uint32_t s_d[kRowMaxTiles + 1];
+  __shared__ uint32_t s_w[4];
+  const uint64_t q = blockIdx.x;
+  const uint64_t Q = cq[g.R] < qmax ? cq[g.R] : qmax;
+  if (q >= Q) return;
+  const int tid = threadIdx.x;
+  const uint32_t r = chunk_row(cq, g.R, q);
+  const uint64_t s0 = uint64_t(roff[r]) + (q - cq[r]) * g.K;
+  const uint64_t e = uint64_t(roff[r + 1]);
+  const uint64_t s1 = s0 + g.K < e ? s0 + g.K : e;
+  for (uint32_t x = tid; x <= g.tiles_x; x += 256) s_d[x] = 0;
+  __syncthreads();
+  for (uint64_t i = s0 + tid; i < s1; i += 256) {
+    uint32_t x0, x1;
+    row_span(rkeys[i], g, x0, x1);
+    if (x0 < x1) {
+      atomicAdd(&s_d[x0], 1u);
+      atomicAdd(&s_d[x1], 0xFFFFFFFFu);
+    }
+  }
+  __syncthreads();
+  // counts = inclusive prefix of the differences (modulo 2^32, exact for
+  // the true counts); each thread takes a run of consecutive tiles
+  const uint32_t per = (g.tiles_x + 255) / 256;
+  const uint32_t x0 = tid * per;
+  const uint32_t x1 = x0 + per < g.tiles_x ? x0 + per : g.tiles_x;
+  uint32_t sum = 0;
+  for (uint32_t x = x0; x < x1; ++x) sum += s_d[x];
+  uint32_t tot;
+  uint32_t run = block_excl_scan_u32(sum, s_w, &tot);
+  uint32_t* row = cm + q * g.tiles_x;
+  for (uint32_t x = x0; x < x1; ++x) {
+    run += s_d[x];
+    row[x] = run;
+  }
+}
+
+// Per (row, tile): the exclusive scan of cm over the row's chunks, in
+// place (each chunk's first rank in the tile's list), and the tile's
+// entry count.
+__global__ __launch_bounds__(256) void k_row_colscan(const uint64_t* __restrict__ cq, RowGeom g,
+                                                    uint64_t qmax, uint32_t* __restrict__ cm,
+                                                    uint32_t* __restrict__ tcount) {
+  const uint64_t n = uint64_t(g.R) * g.tiles_x;
+  const uint64_t stride = uint64_t(gridDim.x) * 256;
+  for (uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) {
+    const uint32_t r = uint32_t(i / g.tiles_x);
+    const uint32_t x = uint32_t(i - uint64_t(r) * g.tiles_x);
+    const uint64_t q0 = cq[r];
+    const uint64_t q1 = cq[r + 1] < qmax ? cq[r + 1] : qmax;
+    uint32_t run = 0;
+    uint64_t q = q0;
+    // eight loads in flight, then their stores
+    for (; q + 8 <= q1; q += 8) {
+      uint32_t c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = cm[(q + j) * g.tiles_x + x];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        cm[(q + j) * g.tiles_x + x] = run;
+        run += c[j];
+      }
+    }
+    for (; q < q1; ++q) {
+      const uint32_t c = cm[q * g.tiles_x + x];
+      cm[q * g.tiles_x + x] = run;
+      run += c;
+    }
+    tcount[i] = run;
+  }
+}
+
+// One wave per (chunk, 64-tile window of its row), one lane per tile. The
+// chunk's segments are read 64 at a time; those meeting the window are
+// queued in LDS, in order, as 64-bit masks of the window tiles they cover
+// (one bit per lane). Every 64 queued segments, the wave transposes the
+// 64 x 64 bit matrix (segment x tile) so that each lane holds the set of
+// queued segments covering its tile, and takes them lowest first (two per
+// step) as its tile's next entries. A lane stages its entries in LDS, in a
+// ring of two groups of 16 consecutive output positions (64 bytes); each
+// group is written out once complete, by 16 lanes at once, four groups
+// per store instruction, so the stores are whole contiguous runs instead
+// of one scattered word per entry. The groups at the two ends of a lane's
+// range are written in part. Writes are clamped to `cap` entries.
+constexpr int kGroup = 16;             // entries per written group
+constexpr int kRing = 2 * kGroup;      // staged entries per lane
+constexpr int kRingStride = kRing + 1;  // LDS words per lane: padded against bank conflicts
+constexpr int kQueue = 128;            // queued segments per wave (a ring)
+
+__device__ __forceinline__ void wave_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Lane l reads lane l ^ J's value (all lanes active). DPP inside rows of
+// 16 (J = 8 and 4 compose two of its fixed permutations), a swizzle
+// across the two 16-lane rows of each half, a permute across halves.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  const int v = int(x);
+  if constexpr (J == 1) return uint32_t(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));
+  if constexpr (J == 2) return uint32_t(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));
+  if constexpr (J == 4) {  // l ^ 7 (half-row mirror), then l ^ 3 (quad_perm [3,2,1,0])
+    const int y = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false);
+    return uint32_t(__builtin_amdgcn_update_dpp(0, y, 0x1B, 0xf, 0xf, false));
+  }
+  if constexpr (J == 8) {  // l ^ 15 (row mirror), then l ^ 7 (half-row mirror)
+    const int y = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);
+    return uint32_t(__builtin_amdgcn_update_dpp(0, y, 0x141, 0xf, 0xf, false));
+  }
+  if constexpr (J == 16) return uint32_t(__builtin_amdgcn_ds_swizzle(v, 0x401F));
+  return uint32_t(__shfl_xor(v, 32, kWave));
+}
+
+// One step of the 64 x 64 bit transpose at scale J: lanes with bit J clear
+// keep their bits b with (b & J) == 0 (mask M) and take the partner's
+// such bits shifted up into the others; lanes with bit J set keep the
+// other bits and take the partner's shifted down.
+template <int J>
+__device__ __forceinline__ void transpose_step(uint32_t& lo, uint32_t& hi, uint64_t M, int lane) {
+  const uint32_t plo = lane_xor<J>(lo), phi = lane_xor<J>(hi);
+  const uint64_t p = (uint64_t(phi) << 32) | plo;
+  const uint64_t v = (uint64_t(hi) << 32) | lo;
+  const bool up = (lane & J) != 0;
+  const uint64_t t = up ? (p >> J) : (p << J);
+  const uint64_t keep = up ? ~M : M;
+  const uint64_t r = (v & keep) | (t & ~keep);
+  lo = uint32_t(r);
+  hi = uint32_t(r >> 32);
+}
+
+// 64 x 64 bit-matrix transpose across the wave: lane l holds row l (bit b
+// is element (l, b)); afterwards lane l holds column l.
+__device__ __forceinline__ uint64_t wave_transpose64(uint64_t v) {
+  const int lane = __lane_id();
+  uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
+  transpose_step<32>(lo, hi, 0x00000000FFFFFFFFull, lane);
+  transpose_step<16>(lo, hi, 0x0000FFFF0000FFFFull, lane);
+  transpose_step<8>(lo, hi, 0x00FF00FF00FF00FFull, lane);
+  transpose_step<4>(lo, hi, 0x0F0F0F0F0F0F0F0Full, lane);
+  transpose_step<2>(lo, hi, 0x3333333333333333ull, lane);
+  transpose_step<1>(lo, hi, 0x5555555555555555ull, lane);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// Writes the group described by every lane in `lanes`: output positions
+// G + j for j in [vlo, vhi), from the lane's ring slots (G + j) mod kRing.
+// Four groups per store: lanes 16k .. 16k + 15 write the k-th lane's.
+__device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf, uint64_t G,
+                                             uint32_t vlohi, uint64_t cap,
+                                             uint32_t* __restrict__ ids) {
+  const int lane = __lane_id();
+  const int quarter = lane >> 4, j = lane & (kGroup - 1);
+  while (lanes) {
+    int L[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      L[k] = lanes ? __builtin_ctzll(lanes) : -1;
+      lanes &= lanes - 1;
+    }
+    const int src = quarter == 0 ? L[0] : quarter == 1 ? L[1] : quarter == 2 ? L[2] : L[3];
+    const int sl = src < 0 ? 0 : src;
+    const uint32_t glo = uint32_t(__builtin_amdgcn_ds_bpermute(sl * 4, int(uint32_t(G))));
+    const uint32_t ghi = uint32_t(__builtin_amdgcn_ds_bpermute(sl * 4, int(uint32_t(G >> 32))));
+    const uint32_t lh = uint32_t(__builtin_amdgcn_ds_bpermute(sl * 4, int(vlohi)));
+    const uint64_t g = ((uint64_t(ghi) << 32) | glo) + uint32_t(j);
+    const uint32_t v = buf[sl * kRingStride + ((glo + uint32_t(j)) & (kRing - 1))];
+    if (src >= 0 && uint32_t(j) >= (lh & 0xFFu) && uint32_t(j) < (lh >> 8) && g < cap) ids[g] = v;
+  }
+}
+
+template <bool KEYS>
+__global__ __launch_bounds__(256) void k_row_expand(
+    const uint32_t* __restrict__ rkeys, const uint32_t* __restrict__ rvals,
+    const int64_t* __restrict__ roff, const uint64_t* __restrict__ cq,
+    const uint32_t* __restrict__ cm, const int64_t* __restrict__ toff, RowGeom g, uint32_t nwin,
+    uint64_t qmax, uint64_t cap, const float* __restrict__ screen, uint64_t nnz,
+    uint32_t* __restrict__ ids, uint64_t* __restrict__ keys_out) {
+  __shared__ uint32_t s_buf[4][kWave * kRingStride];
+  __shared__ uint64_t s_qm[4][kQueue];
+  __shared__ uint32_t s_qv[4][kQueue];
+  const int lane = threadIdx.x & 63;
+  // wave-uniform: the chunk walk below runs on scalar registers
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wid = blockIdx.x * 4 + wv;
+  const uint32_t q = wid / nwin;  // the grid holds fewer than 2^26 waves
+  const uint32_t w = wid - q * nwin;
+  const uint64_t Q = cq[g.R] < qmax ? cq[g.R] : qmax;
+  if (q >= Q) return;  // the whole wave
+  uint32_t* buf = s_buf[wv];
+  uint32_t* mine = buf + lane * kRingStride;
+  uint64_t* qm = s_qm[wv];
+  uint32_t* qv = s_qv[wv];
+  const uint32_t r = chunk_row(cq, g.R, q);
+  const uint64_t s0 = uint64_t(roff[r]) + (q - cq[r]) * g.K;
+  const uint64_t e = uint64_t(roff[r + 1]);
+  const uint64_t s1 = s0 + g.K < e ? s0 + g.K : e;
+  const uint32_t x = w * 64 + uint32_t(lane);
+  const uint32_t t = r * g.tiles_x + x;  // global tile id (c * T + ty * tiles_x + x)
+  const uint64_t base =
+      x < g.tiles_x ? uint64_t(toff[t]) + cm[uint64_t(q) * g.tiles_x + x] : 0ull;
+  uint32_t sp = uint32_t(base);  // low word of the next output position
+  uint32_t off = 0;              // entries taken
+  const uint32_t lo = w * 64, hi = lo + 64;
+  const uint64_t lt = lanemask_lt();
+  uint32_t qh = 0, qt = 0;  // queue head and tail (uniform, modulo 2^32)
+
+  // The n (<= 64) queued segments from the head: transpose, then every
+  // lane takes the segments covering its tile, lowest first, two per step.
+  auto drain = [&](uint32_t n) {
+    wave_order();
+    const uint64_t m = uint32_t(lane) < n ? qm[(qh + lane) & (kQueue - 1)] : 0ull;
+    uint64_t c = wave_transpose64(m);
+    while (__ballot(c != 0ull)) {
+      uint32_t k = 0, v0 = 0, v1 = 0;
+      if (c) {
+        const int i0 = __builtin_ctzll(c);
+        c &= c - 1;
+        k = 1;
+        int i1 = i0;
+        if (c) {
+          i1 = __builtin_ctzll(c);
+          c &= c - 1;
+          k = 2;
+        }
+        v0 = qv[(qh + uint32_t(i0)) & (kQueue - 1)];
+        v1 = qv[(qh + uint32_t(i1)) & (kQueue - 1)];
+        mine[sp & (kRing - 1)] = v0;
+        if (k == 2) mine[(sp + 1) & (kRing - 1)] = v1;
+        if (KEYS) {
+          const uint64_t p0 = base + off;
+          if (p0 < cap && v0 < nnz)
+            keys_out[p0] = (uint64_t(t) << 32) | __float_as_uint(screen[uint64_t(v0) * kRow + 6]);
+          if (k == 2 && p0 + 1 < cap && v1 < nnz)
+            keys_out[p0 + 1] =
+                (uint64_t(t) << 32) | __float_as_uint(screen[uint64_t(v1) * kRow + 6]);
+        }
+      }
+      const uint32_t sp2 = sp + k;
+      // at most one group boundary is crossed per step
+      const bool done = ((sp2 ^ sp) & ~uint32_t(kGroup - 1)) != 0u;
+      sp = sp2;
+      off += k;
+      const uint64_t full = __ballot(done);
+      if (full) {
+        // the completed group: the 16 positions before the boundary crossed
+        const uint64_t pos = base + off;
+        const uint64_t G = (pos & ~uint64_t(kGroup - 1)) - kGroup;
+        const uint32_t vlo = G < base ? uint32_t(base - G) : 0u;
+        wave_order();
+        flush_groups(full, buf, G, vlo | (uint32_t(kGroup) << 8), cap, ids);
+        wave_order();
+      }
+    }
+    qh += n;
+  };
+
+  // Segments are loaded kAhead batches of 64 at a time, the next group
+  // while the current one is walked: a wait for loads also waits for every
+  // store issued before it, so it comes once per group of batches.
+  constexpr int kAhead = 4;
+  uint32_t nk[kAhead], nv[kAhead];
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j) {
+    const uint64_t i = s0 + j * 64 + lane;
+    nk[j] = i < s1 ? rkeys[i] : 0u;
+    nv[j] = i < s1 ? rvals[i] : 0u;
+  }
+  for (uint64_t sg = s0; sg < s1; sg += kAhead * 64) {
+    uint32_t ck[kAhead], cv[kAhead];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      ck[j] = nk[j];
+      cv[j] = nv[j];
+      const uint64_t i = sg + (kAhead + j) * 64 + lane;
+      nk[j] = i < s1 ? rkeys[i] : 0u;
+      nv[j] = i < s1 ? rvals[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      const bool in = sg + j * 64 + lane < s1;
+      uint32_t a, b;
+      row_span(ck[j], g, a, b);
+      a = a > lo ? a : lo;
+      b = b < hi ? b : hi;
+      const bool hit = in && a < b;
+      const uint64_t bal = __ballot(hit);
+      if (hit) {
+        // window tiles [a, b) as bits [a - lo, b - lo)
+        const uint32_t a0 = a - lo, b0 = b - lo;
+        const uint64_t upto = b0 >= 64 ? ~0ull : (1ull << b0) - 1ull;
+        const uint32_t slot = (qt + uint32_t(__popcll(bal & lt))) & (kQueue - 1);
+        qm[slot] = upto & ~((1ull << a0) - 1ull);
+        qv[slot] = cv[j];
+      }
+      qt += uint32_t(__popcll(bal));
+      if (qt - qh >= 64) drain(64);
+    }
+  }
+  if (qt != qh) drain(qt - qh);
+  // the partial last groups
+  const uint64_t pos = base + off;
+  const bool part = off != 0 && (uint32_t(pos) & (kGroup - 1)) != 0u;
+  const uint64_t G = pos & ~uint64_t(kGroup - 1);
+  const uint32_t vlo = G < base ? uint32_t(base - G) : 0u;
+  const uint64_t rest = __ballot(part);
+  wave_order();
+  flush_groups(rest, buf, G, vlo | ((uint32_t(pos) & (kGroup - 1)) << 8), cap, ids);
 }
 
 __global__ __launch_bounds__(256) void k_compose_keys(const uint32_t* __restrict__ tkeys,
@@ -633,7 +1028,7 @@ uint64_t emit_matrix_len(uint64_t nnz) {
 
 hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t* aabb16,
                              const int64_t* cam_off, int C, int W, int H, int bits,
-                             uint64_t cap, uint32_t* mat, uint32_t* rec,
+                             const RowKeys* rows, uint64_t cap, uint32_t* mat, uint32_t* rec,
                              uint64_t* mat_off, uint64_t* mat_total,
                              uint64_t* lb, uint32_t* ticket, int* err, uint32_t* tkeys,
                              uint32_t* tvals, hipStream_t s) {
@@ -642,8 +1037,12 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
   g.W = uint32_t(W);
   g.H = uint32_t(H);
   g.tiles_x = uint32_t((W + kTile - 1) / kTile);
-  g.T = g.tiles_x * uint32_t((H + kTile - 1) / kTile);
+  g.tiles_y = uint32_t((H + kTile - 1) / kTile);
+  g.T = g.tiles_x * g.tiles_y;
   g.C = C;
+  g.rows = rows != nullptr;
+  g.rb = rows ? uint32_t(rows->rb) : 0u;
+  g.xb = rows ? uint32_t(rows->xb) : 0u;
   g.bits = uint32_t(bits < 1 ? 1 : bits > kEmitBits ? kEmitBits : bits);
   g.nnz = nnz;
   g.per_blk = emit_per_block(nnz);
@@ -679,11 +1078,108 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
 }
 
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
-                              hipStream_t s) {
+                              hipStream_t s, uint32_t kmask) {
   ProfScope prof("k_tile_ranges", s);
   hipLaunchKernelGGL(k_tile_ranges, dim3(grid_stride_blocks((n + 4) / 4)), dim3(256), 0, s, tkeys, n,
-                     n_tiles, toff);
+                     n_tiles, kmask, toff);
   return hipGetLastError();
+}
+
+bool row_keys_fit(int C, int W, int H, RowKeys* out) {
+  const uint64_t tx = uint64_t((W + kTile - 1) / kTile), ty = uint64_t((H + kTile - 1) / kTile);
+  const uint64_t R = uint64_t(C) * ty;
+  int rb = 0, xb = 0;
+  while (rb < 64 && ((R - 1) >> rb)) ++rb;
+  while (xb < 64 && ((tx - 1) >> xb)) ++xb;
+  if (tx > kRowMaxTiles || rb > 30 || rb + 2 * xb > 32) return false;
+  out->rb = rb;
+  out->xb = xb;
+  return true;
+}
+
+// Chunk length: about 16K waves of the expansion for the count of
+// segments (between 512 and 4096 segments), and at least four times the
+// row's tile count so that the count matrix stays under a quarter of the
+// segment count (plus one chunk per row).
+uint32_t row_chunk(uint64_t n_segments, uint32_t tiles_x) {
+  const uint64_t nwin = (tiles_x + 63) / 64;
+  uint64_t k = 512;
+  while (k < 4096 && k * 16384 < n_segments * nwin) k <<= 1;
+  while (k < 4ull * tiles_x) k <<= 1;
+  return uint32_t(k);
+}
+
+uint64_t row_chunks_max(uint64_t n_segments, uint32_t R, uint32_t K) {
+  return (n_segments + K - 1) / K + R;
+}
+
+hipError_t launch_row_sort(const uint32_t* rkeys, const uint32_t* rvals, uint64_t n_segments,
+                           int C, int W, int H, const RowKeys& rk, const RowScratch& w,
+                           int* err, const float* screen, uint64_t nnz, uint64_t cap,
+                           uint32_t* ids, int64_t* toff, uint64_t* keys_out, hipStream_t s) {
+  RowGeom g;
+  g.tiles_x = uint32_t((W + kTile - 1) / kTile);
+  g.R = uint32_t(C) * uint32_t((H + kTile - 1) / kTile);
+  g.rb = uint32_t(rk.rb);
+  g.xb = uint32_t(rk.xb);
+  g.K = row_chunk(n_segments, g.tiles_x);
+  const uint64_t n_tiles = uint64_t(g.R) * g.tiles_x;
+  const uint64_t qmax = row_chunks_max(n_segments, g.R, g.K);
+  const uint32_t nwin = (g.tiles_x + 63) / 64;
+  const uint64_t waves = qmax * nwin;
+  if (!fits_dispatch(qmax, 256) || !fits_dispatch((waves + 3) / 4, 256))
+    return hipErrorInvalidConfiguration;
+  // row offsets of the sorted segment keys, then chunks per row and their scan
+  hipError_t e = launch_tile_ranges(rkeys, n_segments, g.R, w.roff, s,
+                                    g.rb ? (1u << g.rb) - 1u : 0u);
+  if (e != hipSuccess) return e;
+  {
+    ProfScope prof("k_row_chunks", s);
+    hipLaunchKernelGGL(k_row_chunks, dim3(grid_stride_blocks(g.R)), dim3(256), 0, s, w.roff, g,
+                       w.cc);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_scan_u32(w.cc, nullptr, nullptr, g.R, nullptr, w.cq, w.cq + g.R, w.lb_c, w.ticket_c,
+                      err, s);
+  if (e != hipSuccess) return e;
+  {
+    ProfScope prof("k_row_count", s);
+    hipLaunchKernelGGL(k_row_count, dim3(uint32_t(qmax)), dim3(256), 0, s, rkeys, w.roff, w.cq, g,
+                       qmax, w.cm);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    ProfScope prof("k_row_colscan", s);
+    hipLaunchKernelGGL(k_row_colscan, dim3(grid_stride_blocks(n_tiles)), dim3(256), 0, s, w.cq, g,
+                       qmax, w.cm, w.tcount);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // tile offsets: the exclusive scan of the tile counts, total at the end
+  e = launch_scan_u32(w.tcount, nullptr, nullptr, n_tiles, nullptr,
+                      reinterpret_cast<uint64_t*>(toff), reinterpret_cast<uint64_t*>(toff + n_tiles),
+                      w.lb_t, w.ticket_t, err, s);
+  if (e != hipSuccess) return e;
+  ProfScope prof("k_row_expand", s);
+  if (keys_out)
+    hipLaunchKernelGGL(k_row_expand<true>, dim3(uint32_t((waves + 3) / 4)), dim3(256), 0, s, rkeys,
+                       rvals, w.roff, w.cq, w.cm, toff, g, nwin, qmax, cap, screen, nnz, ids,
+                       keys_out);
+  else
+    hipLaunchKernelGGL(k_row_expand<false>, dim3(uint32_t((waves + 3) / 4)), dim3(256), 0, s,
+                       rkeys, rvals, w.roff, w.cq, w.cm, toff, g, nwin, qmax, cap, screen, nnz, ids,
+                       keys_out);
+  return hipGetLastError();
+}
+
+uint64_t row_matrix_len(uint64_t n_segments, int C, int W, int H, bool bound) {
+  const uint32_t tx = uint32_t((W + kTile - 1) / kTile);
+  const uint32_t R = uint32_t(C) * uint32_t((H + kTile - 1) / kTile);
+  // the bound takes the shortest chunk any segment count can get
+  const uint32_t K = bound ? row_chunk(0, tx) : row_chunk(n_segments, tx);
+  return row_chunks_max(n_segments, R, K) * tx;
 }
 
 bool tile_order_small(uint64_t n_tiles) { return n_tiles > 0 && n_tiles <= kOrderSmall; }

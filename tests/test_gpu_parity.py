@@ -103,8 +103,14 @@ def test_intersect_sort_bit_exact(lib, name):
 
 # Scenes with many tiles (over 2^16 tile ids), so that the sort by tile id
 # takes its wider first digit and, past 2^18 tiles, more than one further
-# pass. Only projection and intersection are compared.
+# pass. Only projection and intersection are compared. The 65520-pixel-wide
+# one has tile rows too long for a 32-bit (row, first tile, width) segment
+# key, so its entries are sorted by tile id directly; the others go through
+# tile-row segments.
 WIDE = {
+    "wide-tilepath-2cam-65520x4096": workloads.SceneSpec("sh0-2000-2cam-65520x4096", 2000, 0,
+                                                         2, 65520, 4096, 3547.0, 2.0, -3.5,
+                                                         0.5, 5.0, seed=2103),
     "wide-2cam-4096px": workloads.SceneSpec("sh0-3000-2cam-4096px", 3000, 0, 2, 4096, 4096,
                                             3547.0, 2.0, -3.5, 0.5, 5.0, seed=2101),
     "wide-5cam-4096x4000": workloads.SceneSpec("sh0-2000-5cam-4096x4000", 2000, 0, 5, 4096,
