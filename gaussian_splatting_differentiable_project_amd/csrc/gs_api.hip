@@ -115,7 +115,7 @@ IsectWs carve_isect(void* base, int32_t C, int32_t W, int32_t H, int64_t nnz, in
   const uint64_t n = uint64_t(nnz);
   const uint64_t mat = emit_matrix_len(n);
   const uint64_t n_tiles = uint64_t(C) * uint64_t(tiles_x_of(W) * tiles_y_of(H));
-  const uint64_t R = uint64_t(C) * uint64_t(tiles_y_of(H));
+  const uint64_t R = row_windows(C, W, H);  // segment lists of the row path
   RowKeys rk{};
   const bool rows = row_keys_fit(C, W, H, &rk);
   w.total = cv.take<uint64_t>(2 + kPrepBlocks);

@@ -100,8 +100,9 @@ hipError_t launch_sort_passes(uint32_t* keys_a, uint32_t* vals_a, uint32_t* keys
 // Intersection stages (gs_intersect.hip).
 // total[2 + kPrepBlocks] (zeroed): total[0] = intersection count; for
 // each block b, total[1 + b] = (largest depth key << 32) | complement of
-// its smallest depth key; total[1 + kPrepBlocks] = tile-row segment count
-// (the sum over pairs of their rectangles' row counts).
+// its smallest depth key; total[1 + kPrepBlocks] = segment count (the
+// sum over pairs of their rectangles' rows times the 64-tile windows each
+// row meets).
 constexpr uint32_t kPrepBlocks = 1024;
 hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* aabb16, int W,
                              int H, uint32_t* dkeys, uint32_t* dvals, uint64_t* total,
@@ -113,9 +114,11 @@ hipError_t launch_isect_prep(uint64_t nnz, const float* screen, const uint32_t* 
 // rec[2 * nnz] (uint32), the matrix scan mat_off (uint64) and its total,
 // and the scan's look-back words (ceil(emit_matrix_len / kScanTile)) and
 // ticket, which must be zero. Writes are clamped to `cap` entries.
-// With `rows` set, the emit writes (tile row, pair) segments instead, keyed
-// by global row id c * tiles_y + ty in bits [0, rb), first tile in the next
-// xb bits, width - 1 above; `bits` then splits the row id.
+// With `rows` set, the emit writes segments instead: the part of a pair's
+// tile row inside one window of 64 tiles, keyed by the window id
+// (c * tiles_y + ty) * ceil(tiles_x / 64) + tx / 64 in bits [0, rb), the
+// pair's first tile on the row in the next xb bits, its width - 1 above;
+// `bits` then splits the window id.
 struct RowKeys {
   int rb, xb;
 };
@@ -132,12 +135,13 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
 // Ranges of keys & kmask in a list sorted by them.
 hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tiles, int64_t* toff,
                               hipStream_t s, uint32_t kmask = 0xFFFFFFFFu);
-// The sorted list from the segments sorted by row id (keys rkeys, pairs
+// The sorted list from the segments sorted by window id (keys rkeys, pairs
 // rvals): tile offsets toff[C*T + 1], ids[n_isects] and, when keys_out is
-// not null, the 64-bit keys. Scratch (R = C * tiles_y rows): roff[R + 1],
-// cc[R], cq[R + 1], the count matrix cm[row_matrix_len], tcount[C*T], and
-// two scans' look-back words and tickets (zeroed): lb_c for R values,
-// lb_t for C*T values. Writes are clamped to `cap` entries.
+// not null, the 64-bit keys. Scratch (R = C * tiles_y * ceil(tiles_x / 64)
+// windows, row_windows()): roff[R + 1], cc[R], cq[R + 1], the count matrix
+// cm[row_matrix_len], tcount[C*T], and two scans' look-back words and
+// tickets (zeroed): lb_c for R values, lb_t for C*T values. Writes are
+// clamped to `cap` entries.
 struct RowScratch {
   int64_t* roff;
   uint32_t* cc;
@@ -150,6 +154,7 @@ struct RowScratch {
 // Count-matrix words for n_segments segments; with `bound`, an upper
 // bound valid for every smaller segment count.
 uint64_t row_matrix_len(uint64_t n_segments, int C, int W, int H, bool bound);
+uint64_t row_windows(int C, int W, int H);
 hipError_t launch_row_sort(const uint32_t* rkeys, const uint32_t* rvals, uint64_t n_segments,
                            int C, int W, int H, const RowKeys& rk, const RowScratch& w,
                            int* err, const float* screen, uint64_t nnz, uint64_t cap,

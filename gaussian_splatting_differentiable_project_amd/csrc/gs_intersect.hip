@@ -56,8 +56,9 @@ __device__ __forceinline__ uint32_t wave_incl_max_u32(uint32_t v) {
 }
 
 // Per slot: depth key bits and identity value for the depth sort, and
-// the exact 64-bit totals of tile counts (total[0]) and of tile-row
-// counts (total[1 + kPrepBlocks]), one atomic each per work-group.
+// the exact 64-bit totals of tile counts (total[0]) and of segment counts
+// (total[1 + kPrepBlocks]: rectangle rows times the 64-tile windows each
+// row meets), one atomic each per work-group.
 // total[1 + b] receives block b's largest key (high word) and the
 // complement of its smallest key (low word): the host reduces them and
 // skips the depth passes over digits that every key shares. Words of
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void k_isect_prep(uint64_t nnz, const float* _
     const TileRect r = rect_of(aabb16[i], W, H);
     const uint32_t c = rect_count(r);
     n += c;
-    nr += c ? r.ty1 - r.ty0 : 0u;
+    nr += c ? (r.ty1 - r.ty0) * (((r.tx1 - 1u) >> 6) - (r.tx0 >> 6) + 1u) : 0u;
   }
   const uint64_t incl = wave_incl_scan_u64(n);
   const uint64_t incl_r = wave_incl_scan_u64(nr);
@@ -137,21 +138,23 @@ constexpr uint64_t kEmitBlocks = 8192;  // target block count (32 per CU; measur
 
 struct EmitGeom {
   uint32_t W, H, tiles_x, tiles_y, T;
+  uint32_t pitch;         // key step between rectangle rows: tiles_x, or windows per row
   int C;
   uint32_t bits;          // digit width, 1..kEmitBits
   uint64_t nnz, per_blk;  // positions per block (a multiple of kEmitSlots)
-  // Row mode: the entries are (tile row, pair) segments instead of
-  // (tile, pair) entries; their key is the global row id c * tiles_y + ty
-  // in bits [0, rb), with the segment's first tile in the next xb bits and
+  // Row mode: the entries are segments, the part of a pair's tile row
+  // that falls in one window of 64 tiles, instead of (tile, pair) entries.
+  // Their key is the window id (c * tiles_y + ty) * nwin + tx / 64 in bits
+  // [0, rb), with the pair's first tile on the row in the next xb bits and
   // its width minus one above those (rb + 2 xb <= 32).
   int rows;
-  uint32_t rb, xb;
+  uint32_t rb, xb, nwin;
 };
 
 // Depth-order position i: its slot, the global id of the first tile of
 // its rectangle (camera tile base included) and the rectangle's size.
-// In row mode the "rectangle" is the run of its tile rows, one high: the
-// base is the segment key of its first row, the width its row count.
+// In row mode the rectangle is that of its windows (rows by windows per
+// row): the base is the segment key of its first one.
 __device__ __forceinline__ void emit_slot(uint64_t i, const uint32_t* __restrict__ order,
                                           const uint2* __restrict__ aabb16,
                                           const int64_t* __restrict__ cam_off,
@@ -169,9 +172,11 @@ __device__ __forceinline__ void emit_slot(uint64_t i, const uint32_t* __restrict
   wy = r.ty1 > r.ty0 ? r.ty1 - r.ty0 : 0u;
   if (g.rows) {
     const bool any = wx != 0u && wy != 0u;
-    b0 = any ? (uint32_t(lo) * g.tiles_y + r.ty0) | ((r.tx0 | ((wx - 1u) << g.xb)) << g.rb) : 0u;
-    wx = any ? wy : 0u;
-    wy = any ? 1u : 0u;
+    const uint32_t w0 = r.tx0 >> 6;
+    b0 = any ? ((uint32_t(lo) * g.tiles_y + r.ty0) * g.nwin + w0) |
+                   ((r.tx0 | ((wx - 1u) << g.xb)) << g.rb)
+             : 0u;
+    wx = any ? ((r.tx1 - 1u) >> 6) - w0 + 1u : 0u;
   } else {
     b0 = uint32_t(lo) * g.T + r.ty0 * g.tiles_x + r.tx0;
   }
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(256) void k_emit_count(const uint32_t* __restrict__
     const uint32_t rem = wx & M;
     if (rem == 0) continue;
     for (uint32_t dy = 0; dy < wy; ++dy) {
-      const uint32_t s = (b0 + dy * g.tiles_x) & M;
+      const uint32_t s = (b0 + dy * g.pitch) & M;
       const uint32_t e = s + rem;
       atomicAdd(&s_diff[s], 1u);
       if (e < R) {
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(256) void k_emit_write(
       dy = dy * w > k ? dy - 1 : dy;
       dy = (dy + 1) * w <= k ? dy + 1 : dy;
       dy = (dy + 1) * w <= k ? dy + 1 : dy;
-      const uint32_t t = valid ? s_base[own] + dy * g.tiles_x + (k - dy * w) : 0u;
+      const uint32_t t = valid ? s_base[own] + dy * g.pitch + (k - dy * w) : 0u;
       key[i] = t;
       val[i] = s_slot[own];
       // rank among the wave's earlier entries with the same digit (digits
@@ -510,28 +515,31 @@ __global__ __launch_bounds__(256) void k_tile_ranges(const uint32_t* __restrict_
   }
 }
 
-// ---- The sort by tile through tile rows ----
-// A pair's entries on one tile row are a run of consecutive tiles, so the
-// sorted list is built from (row, pair) segments instead of (tile, pair)
-// entries. The segments are emitted in depth order and sorted stably by
-// global row id (the emit and radix passes above, on segment keys); every
-// row's segment list is then in depth order. Each list is cut into chunks
-// of K segments. Per chunk, a difference array over the row's tiles counts
-// the segments covering every tile (k_row_count); an exclusive scan of
-// those counts over the row's chunks, per tile, gives each chunk its first
-// rank in every tile's list and the tile's total (k_row_colscan); a scan of
-// the totals gives the tile offsets. k_row_expand then walks each chunk in
-// order, one wave per 64 tiles of the row, one lane per tile: each segment
-// that covers a lane's tile is that tile's next entry. Within a tile the
-// entries so come in segment order, i.e. in depth order, which is the
-// stable sort of (tile << 32) | depth keys in slot order.
+// ---- The sort by tile through window segments ----
+// A pair's entries on one tile row are a run of consecutive tiles. Rows
+// are cut into windows of 64 tiles, and the sorted list is built from
+// segments, the part of a pair's row inside one window, instead of
+// (tile, pair) entries. The segments are emitted in depth order and sorted
+// stably by window id (the emit and radix passes above, on segment keys);
+// every window's segment list is then in depth order. Each list is cut
+// into chunks of K segments. Per chunk, a difference array over the
+// window's tiles counts the segments covering every tile (k_row_count); an
+// exclusive scan of those counts over the window's chunks, per tile, gives
+// each chunk its first rank in every tile's list and the tile's total
+// (k_row_colscan); a scan of the totals gives the tile offsets.
+// k_row_expand then walks each chunk in order, one wave per chunk, one
+// lane per tile of the window: each segment covering a lane's tile is that
+// tile's next entry. Within a tile the entries so come in segment order,
+// i.e. in depth order, which is the stable sort of (tile << 32) | depth
+// keys in slot order.
 struct RowGeom {
-  uint32_t tiles_x, R;  // tiles per row, rows (cameras x tile rows)
-  uint32_t rb, xb;      // segment key layout (see EmitGeom), rb < 32
-  uint32_t K;           // segments per chunk
+  uint32_t tiles_x, nwin, R;  // tiles per row, windows per row, windows (C * tiles_y * nwin)
+  uint32_t rb, xb;            // segment key layout (see EmitGeom), rb < 32
+  uint32_t K;                 // segments per chunk
 };
 
-// [x0, x1) of the segment with key k, clamped to the row.
+// [x0, x1) of the pair's run on the row for segment key k, clamped to the
+// row.
 __device__ __forceinline__ void row_span(uint32_t k, const RowGeom& g, uint32_t& x0,
                                          uint32_t& x1) {
   const uint32_t xm = (1u << g.xb) - 1u;
@@ -541,8 +549,26 @@ __device__ __forceinline__ void row_span(uint32_t k, const RowGeom& g, uint32_t&
   x1 = b < g.tiles_x ? b : g.tiles_x;
 }
 
-// Row of chunk q: the largest r < R with cq[r] <= q (cq is the exclusive
-// scan of the per-row chunk counts, so that row's chunks include q).
+// Bits [a, b) of a 64-bit word, 0 <= a < b <= 64.
+__device__ __forceinline__ uint64_t bit_range(uint32_t a, uint32_t b) {
+  const uint64_t upto = b >= 64 ? ~0ull : (1ull << b) - 1ull;
+  return upto & ~((1ull << a) - 1ull);
+}
+
+// The segment's tiles inside window w as bits of the window (tile
+// 64 w + i is bit i); zero for a key outside the window.
+__device__ __forceinline__ uint64_t segment_bits(uint32_t k, const RowGeom& g, uint32_t w) {
+  uint32_t a, b;
+  row_span(k, g, a, b);
+  const uint32_t lo = w * 64, hi = lo + 64;
+  a = a > lo ? a : lo;
+  b = b < hi ? b : hi;
+  return a < b ? bit_range(a - lo, b - lo) : 0ull;
+}
+
+// Window of chunk q: the largest r < R with cq[r] <= q (cq is the
+// exclusive scan of the per-window chunk counts, so that window's chunks
+// include q).
 __device__ __forceinline__ uint32_t chunk_row(const uint64_t* __restrict__ cq, uint32_t R,
                                               uint64_t q) {
   uint32_t lo = 0, hi = R - 1;
@@ -562,101 +588,101 @@ __global__ __launch_bounds__(256) void k_row_chunks(const int64_t* __restrict__ 
   }
 }
 
-// cm[q][x] = segments of chunk q covering tile x of its row. One block per
-// chunk (the grid is an upper bound; blocks past the last chunk leave).
-constexpr uint32_t kRowMaxTiles = 4096;  // tiles per row: W <= 65535
+// cm[q][i] = segments of chunk q covering tile i of its window. One wave
+// per chunk (the grid is an upper bound; waves past the last chunk
+// leave): every lane ORs the bit masks of its segments into 64 per-tile
+// counters kept as a difference array in LDS.
 __global__ __launch_bounds__(256) void k_row_count(const uint32_t* __restrict__ rkeys,
                                                   const int64_t* __restrict__ roff,
                                                   const uint64_t* __restrict__ cq, RowGeom g,
                                                   uint64_t qmax, uint32_t* __restrict__ cm) {
-  __shared__ uint32_t s_d[kRowMaxTiles + 1];
-  __shared__ uint32_t s_w[4];
-  const uint64_t q = blockIdx.x;
+  __shared__ uint32_t s_d[4][65];
+  const int lane = threadIdx.x & 63;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint64_t q = uint64_t(blockIdx.x) * 4 + wv;
   const uint64_t Q = cq[g.R] < qmax ? cq[g.R] : qmax;
-  if (q >= Q) return;
-  const int tid = threadIdx.x;
-  const uint32_t r = chunk_row(cq, g.R, q);
-  const uint64_t s0 = uint64_t(roff[r]) + (q - cq[r]) * g.K;
-  const uint64_t e = uint64_t(roff[r + 1]);
+  if (q >= Q) return;  // the whole wave
+  uint32_t* d = s_d[wv];
+  const uint32_t rw = chunk_row(cq, g.R, q);
+  const uint32_t w = rw % g.nwin;
+  const uint64_t s0 = uint64_t(roff[rw]) + (q - cq[rw]) * g.K;
+  const uint64_t e = uint64_t(roff[rw + 1]);
   const uint64_t s1 = s0 + g.K < e ? s0 + g.K : e;
-  for (uint32_t x = tid; x <= g.tiles_x; x += 256) s_d[x] = 0;
-  __syncthreads();
-  for (uint64_t i = s0 + tid; i < s1; i += 256) {
-    uint32_t x0, x1;
-    row_span(rkeys[i], g, x0, x1);
-    if (x0 < x1) {
-      atomicAdd(&s_d[x0], 1u);
-      atomicAdd(&s_d[x1], 0xFFFFFFFFu);
+  d[lane] = 0;
+  if (lane == 0) d[64] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (uint64_t i = s0 + lane; i < s1; i += 64) {
+    uint32_t a, b;
+    row_span(rkeys[i], g, a, b);
+    const uint32_t lo = w * 64, hi = lo + 64;
+    a = a > lo ? a : lo;
+    b = b < hi ? b : hi;
+    if (a < b) {
+      atomicAdd(&d[a - lo], 1u);
+      atomicAdd(&d[b - lo], 0xFFFFFFFFu);
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // counts = inclusive prefix of the differences (modulo 2^32, exact for
-  // the true counts); each thread takes a run of consecutive tiles
-  const uint32_t per = (g.tiles_x + 255) / 256;
-  const uint32_t x0 = tid * per;
-  const uint32_t x1 = x0 + per < g.tiles_x ? x0 + per : g.tiles_x;
-  uint32_t sum = 0;
-  for (uint32_t x = x0; x < x1; ++x) sum += s_d[x];
-  uint32_t tot;
-  uint32_t run = block_excl_scan_u32(sum, s_w, &tot);
-  uint32_t* row = cm + q * g.tiles_x;
-  for (uint32_t x = x0; x < x1; ++x) {
-    run += s_d[x];
-    row[x] = run;
-  }
+  // the true counts)
+  cm[q * 64 + lane] = wave_incl_scan_u32(d[lane]);
 }
 
-// Per (row, tile): the exclusive scan of cm over the row's chunks, in
-// place (each chunk's first rank in the tile's list), and the tile's
+// Per (window, tile): the exclusive scan of cm over the window's chunks,
+// in place (each chunk's first rank in the tile's list), and the tile's
 // entry count.
 __global__ __launch_bounds__(256) void k_row_colscan(const uint64_t* __restrict__ cq, RowGeom g,
                                                     uint64_t qmax, uint32_t* __restrict__ cm,
                                                     uint32_t* __restrict__ tcount) {
-  const uint64_t n = uint64_t(g.R) * g.tiles_x;
+  const uint64_t n = uint64_t(g.R) * 64;
   const uint64_t stride = uint64_t(gridDim.x) * 256;
   for (uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) {
-    const uint32_t r = uint32_t(i / g.tiles_x);
-    const uint32_t x = uint32_t(i - uint64_t(r) * g.tiles_x);
-    const uint64_t q0 = cq[r];
-    const uint64_t q1 = cq[r + 1] < qmax ? cq[r + 1] : qmax;
+    const uint32_t rw = uint32_t(i >> 6), l = uint32_t(i & 63);
+    const uint32_t w = rw % g.nwin, row = rw / g.nwin;
+    const uint32_t x = w * 64 + l;
+    const uint64_t q0 = cq[rw];
+    const uint64_t q1 = cq[rw + 1] < qmax ? cq[rw + 1] : qmax;
     uint32_t run = 0;
     uint64_t q = q0;
     // eight loads in flight, then their stores
     for (; q + 8 <= q1; q += 8) {
       uint32_t c[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = cm[(q + j) * g.tiles_x + x];
+      for (int j = 0; j < 8; ++j) c[j] = cm[(q + j) * 64 + l];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        cm[(q + j) * g.tiles_x + x] = run;
+        cm[(q + j) * 64 + l] = run;
         run += c[j];
       }
     }
     for (; q < q1; ++q) {
-      const uint32_t c = cm[q * g.tiles_x + x];
-      cm[q * g.tiles_x + x] = run;
+      const uint32_t c = cm[q * 64 + l];
+      cm[q * 64 + l] = run;
       run += c;
     }
-    tcount[i] = run;
+    if (x < g.tiles_x) tcount[uint64_t(row) * g.tiles_x + x] = run;
   }
 }
 
-// One wave per (chunk, 64-tile window of its row), one lane per tile. The
-// chunk's segments are read 64 at a time; those meeting the window are
-// queued in LDS, in order, as 64-bit masks of the window tiles they cover
-// (one bit per lane). Every 64 queued segments, the wave transposes the
-// 64 x 64 bit matrix (segment x tile) so that each lane holds the set of
-// queued segments covering its tile, and takes them lowest first (two per
-// step) as its tile's next entries. A lane stages its entries in LDS, in a
-// ring of two groups of 16 consecutive output positions (64 bytes); each
-// group is written out once complete, by 16 lanes at once, four groups
-// per store instruction, so the stores are whole contiguous runs instead
-// of one scattered word per entry. The groups at the two ends of a lane's
-// range are written in part. Writes are clamped to `cap` entries.
+// One wave per chunk, one lane per tile of the chunk's window. The chunk's
+// segments are read 64 at a time, one per lane, as 64-bit masks of the
+// window tiles they cover; the wave transposes the 64 x 64 bit matrix
+// (segment x tile) so that each lane holds the set of those segments
+// covering its tile, and takes them lowest first (four per step) as its
+// tile's next entries. A lane stages its entries in LDS, in a ring of two
+// groups of 16 consecutive output positions (64 bytes); each group is
+// written out once complete, by 16 lanes at once, four groups per store
+// instruction, so the stores are whole contiguous runs instead of one
+// scattered word per entry. The groups at the two ends of a lane's range
+// are written in part. Writes are clamped to `cap` entries.
 constexpr int kGroup = 16;             // entries per written group
 constexpr int kRing = 2 * kGroup;      // staged entries per lane
 constexpr int kRingStride = kRing + 1;  // LDS words per lane: padded against bank conflicts
-constexpr int kQueue = 128;            // queued segments per wave (a ring)
+constexpr int kTake = 4;               // entries a lane takes per step (< kGroup)
 
 __device__ __forceinline__ void wave_order() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -735,9 +761,9 @@ __device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf
     const uint32_t glo = uint32_t(__builtin_amdgcn_ds_bpermute(sl * 4, int(uint32_t(G))));
     const uint32_t ghi = uint32_t(__builtin_amdgcn_ds_bpermute(sl * 4, int(uint32_t(G >> 32))));
     const uint32_t lh = uint32_t(__builtin_amdgcn_ds_bpermute(sl * 4, int(vlohi)));
-    const uint64_t g = ((uint64_t(ghi) << 32) | glo) + uint32_t(j);
+    const uint64_t gp = ((uint64_t(ghi) << 32) | glo) + uint32_t(j);
     const uint32_t v = buf[sl * kRingStride + ((glo + uint32_t(j)) & (kRing - 1))];
-    if (src >= 0 && uint32_t(j) >= (lh & 0xFFu) && uint32_t(j) < (lh >> 8) && g < cap) ids[g] = v;
+    if (src >= 0 && uint32_t(j) >= (lh & 0xFFu) && uint32_t(j) < (lh >> 8) && gp < cap) ids[gp] = v;
   }
 }
 
@@ -745,87 +771,28 @@ template <bool KEYS>
 __global__ __launch_bounds__(256) void k_row_expand(
     const uint32_t* __restrict__ rkeys, const uint32_t* __restrict__ rvals,
     const int64_t* __restrict__ roff, const uint64_t* __restrict__ cq,
-    const uint32_t* __restrict__ cm, const int64_t* __restrict__ toff, RowGeom g, uint32_t nwin,
-    uint64_t qmax, uint64_t cap, const float* __restrict__ screen, uint64_t nnz,
-    uint32_t* __restrict__ ids, uint64_t* __restrict__ keys_out) {
+    const uint32_t* __restrict__ cm, const int64_t* __restrict__ toff, RowGeom g, uint64_t qmax,
+    uint64_t cap, const float* __restrict__ screen, uint64_t nnz, uint32_t* __restrict__ ids,
+    uint64_t* __restrict__ keys_out) {
   __shared__ uint32_t s_buf[4][kWave * kRingStride];
-  __shared__ uint64_t s_qm[4][kQueue];
-  __shared__ uint32_t s_qv[4][kQueue];
   const int lane = threadIdx.x & 63;
   // wave-uniform: the chunk walk below runs on scalar registers
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t wid = blockIdx.x * 4 + wv;
-  const uint32_t q = wid / nwin;  // the grid holds fewer than 2^26 waves
-  const uint32_t w = wid - q * nwin;
+  const uint64_t q = uint64_t(blockIdx.x) * 4 + wv;
   const uint64_t Q = cq[g.R] < qmax ? cq[g.R] : qmax;
   if (q >= Q) return;  // the whole wave
   uint32_t* buf = s_buf[wv];
   uint32_t* mine = buf + lane * kRingStride;
-  uint64_t* qm = s_qm[wv];
-  uint32_t* qv = s_qv[wv];
-  const uint32_t r = chunk_row(cq, g.R, q);
-  const uint64_t s0 = uint64_t(roff[r]) + (q - cq[r]) * g.K;
-  const uint64_t e = uint64_t(roff[r + 1]);
+  const uint32_t rw = chunk_row(cq, g.R, q);
+  const uint32_t w = rw % g.nwin, row = rw / g.nwin;
+  const uint64_t s0 = uint64_t(roff[rw]) + (q - cq[rw]) * g.K;
+  const uint64_t e = uint64_t(roff[rw + 1]);
   const uint64_t s1 = s0 + g.K < e ? s0 + g.K : e;
   const uint32_t x = w * 64 + uint32_t(lane);
-  const uint32_t t = r * g.tiles_x + x;  // global tile id (c * T + ty * tiles_x + x)
-  const uint64_t base =
-      x < g.tiles_x ? uint64_t(toff[t]) + cm[uint64_t(q) * g.tiles_x + x] : 0ull;
+  const uint32_t t = row * g.tiles_x + x;  // global tile id (c * T + ty * tiles_x + x)
+  const uint64_t base = x < g.tiles_x ? uint64_t(toff[t]) + cm[q * 64 + lane] : 0ull;
   uint32_t sp = uint32_t(base);  // low word of the next output position
   uint32_t off = 0;              // entries taken
-  const uint32_t lo = w * 64, hi = lo + 64;
-  const uint64_t lt = lanemask_lt();
-  uint32_t qh = 0, qt = 0;  // queue head and tail (uniform, modulo 2^32)
-
-  // The n (<= 64) queued segments from the head: transpose, then every
-  // lane takes the segments covering its tile, lowest first, two per step.
-  auto drain = [&](uint32_t n) {
-    wave_order();
-    const uint64_t m = uint32_t(lane) < n ? qm[(qh + lane) & (kQueue - 1)] : 0ull;
-    uint64_t c = wave_transpose64(m);
-    while (__ballot(c != 0ull)) {
-      uint32_t k = 0, v0 = 0, v1 = 0;
-      if (c) {
-        const int i0 = __builtin_ctzll(c);
-        c &= c - 1;
-        k = 1;
-        int i1 = i0;
-        if (c) {
-          i1 = __builtin_ctzll(c);
-          c &= c - 1;
-          k = 2;
-        }
-        v0 = qv[(qh + uint32_t(i0)) & (kQueue - 1)];
-        v1 = qv[(qh + uint32_t(i1)) & (kQueue - 1)];
-        mine[sp & (kRing - 1)] = v0;
-        if (k == 2) mine[(sp + 1) & (kRing - 1)] = v1;
-        if (KEYS) {
-          const uint64_t p0 = base + off;
-          if (p0 < cap && v0 < nnz)
-            keys_out[p0] = (uint64_t(t) << 32) | __float_as_uint(screen[uint64_t(v0) * kRow + 6]);
-          if (k == 2 && p0 + 1 < cap && v1 < nnz)
-            keys_out[p0 + 1] =
-                (uint64_t(t) << 32) | __float_as_uint(screen[uint64_t(v1) * kRow + 6]);
-        }
-      }
-      const uint32_t sp2 = sp + k;
-      // at most one group boundary is crossed per step
-      const bool done = ((sp2 ^ sp) & ~uint32_t(kGroup - 1)) != 0u;
-      sp = sp2;
-      off += k;
-      const uint64_t full = __ballot(done);
-      if (full) {
-        // the completed group: the 16 positions before the boundary crossed
-        const uint64_t pos = base + off;
-        const uint64_t G = (pos & ~uint64_t(kGroup - 1)) - kGroup;
-        const uint32_t vlo = G < base ? uint32_t(base - G) : 0u;
-        wave_order();
-        flush_groups(full, buf, G, vlo | (uint32_t(kGroup) << 8), cap, ids);
-        wave_order();
-      }
-    }
-    qh += n;
-  };
 
   // Segments are loaded kAhead batches of 64 at a time, the next group
   // while the current one is walked: a wait for loads also waits for every
@@ -850,26 +817,57 @@ __global__ __launch_bounds__(256) void k_row_expand(
     }
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) {
+      if (sg + j * 64 >= s1) break;  // uniform
       const bool in = sg + j * 64 + lane < s1;
-      uint32_t a, b;
-      row_span(ck[j], g, a, b);
-      a = a > lo ? a : lo;
-      b = b < hi ? b : hi;
-      const bool hit = in && a < b;
-      const uint64_t bal = __ballot(hit);
-      if (hit) {
-        // window tiles [a, b) as bits [a - lo, b - lo)
-        const uint32_t a0 = a - lo, b0 = b - lo;
-        const uint64_t upto = b0 >= 64 ? ~0ull : (1ull << b0) - 1ull;
-        const uint32_t slot = (qt + uint32_t(__popcll(bal & lt))) & (kQueue - 1);
-        qm[slot] = upto & ~((1ull << a0) - 1ull);
-        qv[slot] = cv[j];
+      const uint64_t m = in ? segment_bits(ck[j], g, w) : 0ull;
+      const uint32_t val = cv[j];
+      // lane i now holds the set of this batch's segments covering tile i
+      uint64_t c = wave_transpose64(m);
+      while (__ballot(c != 0ull)) {
+        // up to kTake segments per lane and step; their pairs are read
+        // from their lanes together
+        int idx[kTake];
+        uint32_t k = 0;
+#pragma unroll
+        for (int u = 0; u < kTake; ++u) {
+          idx[u] = c ? __builtin_ctzll(c) : 0;
+          k += c ? 1u : 0u;
+          c &= c - 1;
+        }
+        uint32_t v[kTake];
+#pragma unroll
+        for (int u = 0; u < kTake; ++u)
+          v[u] = uint32_t(__builtin_amdgcn_ds_bpermute(idx[u] * 4, int(val)));
+#pragma unroll
+        for (int u = 0; u < kTake; ++u) {
+          if (uint32_t(u) < k) {
+            mine[(sp + u) & (kRing - 1)] = v[u];
+            if (KEYS) {
+              const uint64_t p = base + off + u;
+              if (p < cap && v[u] < nnz)
+                keys_out[p] =
+                    (uint64_t(t) << 32) | __float_as_uint(screen[uint64_t(v[u]) * kRow + 6]);
+            }
+          }
+        }
+        const uint32_t sp2 = sp + k;
+        // at most one group boundary is crossed per step
+        const bool done = ((sp2 ^ sp) & ~uint32_t(kGroup - 1)) != 0u;
+        sp = sp2;
+        off += k;
+        const uint64_t full = __ballot(done);
+        if (full) {
+          // the completed group: the 16 positions before the boundary crossed
+          const uint64_t pos = base + off;
+          const uint64_t G = (pos & ~uint64_t(kGroup - 1)) - kGroup;
+          const uint32_t vlo = G < base ? uint32_t(base - G) : 0u;
+          wave_order();
+          flush_groups(full, buf, G, vlo | (uint32_t(kGroup) << 8), cap, ids);
+          wave_order();
+        }
       }
-      qt += uint32_t(__popcll(bal));
-      if (qt - qh >= 64) drain(64);
     }
   }
-  if (qt != qh) drain(qt - qh);
   // the partial last groups
   const uint64_t pos = base + off;
   const bool part = off != 0 && (uint32_t(pos) & (kGroup - 1)) != 0u;
@@ -1043,6 +1041,8 @@ hipError_t launch_isect_emit(uint64_t nnz, const uint32_t* order, const uint32_t
   g.rows = rows != nullptr;
   g.rb = rows ? uint32_t(rows->rb) : 0u;
   g.xb = rows ? uint32_t(rows->xb) : 0u;
+  g.nwin = (g.tiles_x + 63) / 64;
+  g.pitch = rows ? g.nwin : g.tiles_x;
   g.bits = uint32_t(bits < 1 ? 1 : bits > kEmitBits ? kEmitBits : bits);
   g.nnz = nnz;
   g.per_blk = emit_per_block(nnz);
@@ -1087,31 +1087,38 @@ hipError_t launch_tile_ranges(const uint32_t* tkeys, uint64_t n, uint64_t n_tile
 
 bool row_keys_fit(int C, int W, int H, RowKeys* out) {
   const uint64_t tx = uint64_t((W + kTile - 1) / kTile), ty = uint64_t((H + kTile - 1) / kTile);
-  const uint64_t R = uint64_t(C) * ty;
+  const uint64_t R = uint64_t(C) * ty * ((tx + 63) / 64);
   int rb = 0, xb = 0;
   while (rb < 64 && ((R - 1) >> rb)) ++rb;
   while (xb < 64 && ((tx - 1) >> xb)) ++xb;
-  if (tx > kRowMaxTiles || rb > 30 || rb + 2 * xb > 32) return false;
+  if (rb > 30 || rb + 2 * xb > 32) return false;
   out->rb = rb;
   out->xb = xb;
   return true;
 }
 
-// Chunk length: about 16K waves of the expansion for the count of
-// segments (between 512 and 4096 segments), and at least four times the
-// row's tile count so that the count matrix stays under a quarter of the
-// segment count (plus one chunk per row).
-uint32_t row_chunk(uint64_t n_segments, uint32_t tiles_x) {
-  const uint64_t nwin = (tiles_x + 63) / 64;
-  uint64_t k = 512;
-  while (k < 4096 && k * 16384 < n_segments * nwin) k <<= 1;
-  while (k < 4ull * tiles_x) k <<= 1;
+uint64_t row_windows(int C, int W, int H) {
+  const uint64_t tx = uint64_t((W + kTile - 1) / kTile), ty = uint64_t((H + kTile - 1) / kTile);
+  return uint64_t(C) * ty * ((tx + 63) / 64);
+}
+
+namespace {
+
+// Chunk length: about 16K chunks (one wave each) for the count of
+// segments, between 256 and 4096 segments, so that the count matrix (64
+// words per chunk) stays under a quarter of the segment count plus one
+// chunk per window.
+uint32_t row_chunk(uint64_t n_segments) {
+  uint64_t k = 256;
+  while (k < 4096 && k * 16384 < n_segments) k <<= 1;
   return uint32_t(k);
 }
 
-uint64_t row_chunks_max(uint64_t n_segments, uint32_t R, uint32_t K) {
+uint64_t row_chunks_max(uint64_t n_segments, uint64_t R, uint32_t K) {
   return (n_segments + K - 1) / K + R;
 }
+
+}  // namespace
 
 hipError_t launch_row_sort(const uint32_t* rkeys, const uint32_t* rvals, uint64_t n_segments,
                            int C, int W, int H, const RowKeys& rk, const RowScratch& w,
@@ -1119,17 +1126,16 @@ hipError_t launch_row_sort(const uint32_t* rkeys, const uint32_t* rvals, uint64_
                            uint32_t* ids, int64_t* toff, uint64_t* keys_out, hipStream_t s) {
   RowGeom g;
   g.tiles_x = uint32_t((W + kTile - 1) / kTile);
-  g.R = uint32_t(C) * uint32_t((H + kTile - 1) / kTile);
+  g.nwin = (g.tiles_x + 63) / 64;
+  g.R = uint32_t(row_windows(C, W, H));
   g.rb = uint32_t(rk.rb);
   g.xb = uint32_t(rk.xb);
-  g.K = row_chunk(n_segments, g.tiles_x);
-  const uint64_t n_tiles = uint64_t(g.R) * g.tiles_x;
+  g.K = row_chunk(n_segments);
+  const uint64_t n_tiles = uint64_t(C) * uint64_t((H + kTile - 1) / kTile) * g.tiles_x;
   const uint64_t qmax = row_chunks_max(n_segments, g.R, g.K);
-  const uint32_t nwin = (g.tiles_x + 63) / 64;
-  const uint64_t waves = qmax * nwin;
-  if (!fits_dispatch(qmax, 256) || !fits_dispatch((waves + 3) / 4, 256))
-    return hipErrorInvalidConfiguration;
-  // row offsets of the sorted segment keys, then chunks per row and their scan
+  if (!fits_dispatch((qmax + 3) / 4, 256)) return hipErrorInvalidConfiguration;
+  // window offsets of the sorted segment keys, then chunks per window and
+  // their scan
   hipError_t e = launch_tile_ranges(rkeys, n_segments, g.R, w.roff, s,
                                     g.rb ? (1u << g.rb) - 1u : 0u);
   if (e != hipSuccess) return e;
@@ -1143,17 +1149,17 @@ hipError_t launch_row_sort(const uint32_t* rkeys, const uint32_t* rvals, uint64_
   e = launch_scan_u32(w.cc, nullptr, nullptr, g.R, nullptr, w.cq, w.cq + g.R, w.lb_c, w.ticket_c,
                       err, s);
   if (e != hipSuccess) return e;
+  const dim3 grid{uint32_t((qmax + 3) / 4)};
   {
     ProfScope prof("k_row_count", s);
-    hipLaunchKernelGGL(k_row_count, dim3(uint32_t(qmax)), dim3(256), 0, s, rkeys, w.roff, w.cq, g,
-                       qmax, w.cm);
+    hipLaunchKernelGGL(k_row_count, grid, dim3(256), 0, s, rkeys, w.roff, w.cq, g, qmax, w.cm);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     ProfScope prof("k_row_colscan", s);
-    hipLaunchKernelGGL(k_row_colscan, dim3(grid_stride_blocks(n_tiles)), dim3(256), 0, s, w.cq, g,
-                       qmax, w.cm, w.tcount);
+    hipLaunchKernelGGL(k_row_colscan, dim3(grid_stride_blocks(uint64_t(g.R) * 64)), dim3(256), 0,
+                       s, w.cq, g, qmax, w.cm, w.tcount);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1164,22 +1170,18 @@ hipError_t launch_row_sort(const uint32_t* rkeys, const uint32_t* rvals, uint64_
   if (e != hipSuccess) return e;
   ProfScope prof("k_row_expand", s);
   if (keys_out)
-    hipLaunchKernelGGL(k_row_expand<true>, dim3(uint32_t((waves + 3) / 4)), dim3(256), 0, s, rkeys,
-                       rvals, w.roff, w.cq, w.cm, toff, g, nwin, qmax, cap, screen, nnz, ids,
-                       keys_out);
+    hipLaunchKernelGGL(k_row_expand<true>, grid, dim3(256), 0, s, rkeys, rvals, w.roff, w.cq, w.cm,
+                       toff, g, qmax, cap, screen, nnz, ids, keys_out);
   else
-    hipLaunchKernelGGL(k_row_expand<false>, dim3(uint32_t((waves + 3) / 4)), dim3(256), 0, s,
-                       rkeys, rvals, w.roff, w.cq, w.cm, toff, g, nwin, qmax, cap, screen, nnz, ids,
-                       keys_out);
+    hipLaunchKernelGGL(k_row_expand<false>, grid, dim3(256), 0, s, rkeys, rvals, w.roff, w.cq,
+                       w.cm, toff, g, qmax, cap, screen, nnz, ids, keys_out);
   return hipGetLastError();
 }
 
 uint64_t row_matrix_len(uint64_t n_segments, int C, int W, int H, bool bound) {
-  const uint32_t tx = uint32_t((W + kTile - 1) / kTile);
-  const uint32_t R = uint32_t(C) * uint32_t((H + kTile - 1) / kTile);
   // the bound takes the shortest chunk any segment count can get
-  const uint32_t K = bound ? row_chunk(0, tx) : row_chunk(n_segments, tx);
-  return row_chunks_max(n_segments, R, K) * tx;
+  const uint32_t K = bound ? row_chunk(0) : row_chunk(n_segments);
+  return row_chunks_max(n_segments, row_windows(C, W, H), K) * 64;
 }
 
 bool tile_order_small(uint64_t n_tiles) { return n_tiles > 0 && n_tiles <= kOrderSmall; }
