@@ -54,7 +54,7 @@ KERNELS = ["k_project_mask", "k_scan", "k_cam_offsets", "k_project_compact", "k_
 KERNEL_SOURCE = {"k_raster_fwd": "gs_raster.hip", "k_raster_bwd": "gs_raster.hip",
                  "k_project_mask": "gs_project.hip", "k_project_compact": "gs_project.hip",
                  "k_project_bwd": "gs_project_bwd.hip", "k_radix_scatter": "gs_sort.hip",
-                 "k_emit_write": "gs_intersect.hip"}
+                 "k_emit_write": "gs_intersect.hip", "k_row_expand": "gs_intersect.hip"}
 
 # Flops of one (pixel, entry) evaluation in the raster kernels: the alpha
 # test every evaluation needs (dx, dy, three products, the quadratic form,
@@ -105,15 +105,46 @@ def source_sha(kernel: str) -> str | None:
     return h.hexdigest()[:16]
 
 
-def tile_sort_digits(spec):
-    """(bits of the emit's fused first digit, radix passes after it) of the
-    sort by tile id, as the library chooses them."""
-    n_tiles = spec.n_cams * ((spec.width + 15) // 16) * ((spec.height + 15) // 16)
-    bits = max(0, int(n_tiles - 1).bit_length())
+def _bits(n_values: int) -> int:
+    return max(0, int(n_values - 1).bit_length())
+
+
+def _emit_digit_bits(bits: int) -> int:
     total = 1 if bits <= 8 else (bits + 7) // 8
-    b1 = max(1, (bits + total - 1) // total)
+    return max(1, (bits + total - 1) // total)
+
+
+def sort_model(spec, aabb16, n_isects):
+    """How the library sorts the entries by tile for this geometry, and the
+    elements its passes move: through window segments (the part of a
+    pair's tile row inside one window of 64 tiles; the emit's first digit
+    and radix passes over the segments, then the expansion writes the
+    entries) when the segment key fits 32 bits, else the entries
+    themselves sorted by tile id."""
+    import torch
+    tx = (spec.width + 15) // 16
+    ty = (spec.height + 15) // 16
+    windows = spec.n_cams * ty * ((tx + 63) // 64)
+    rb, xb = _bits(windows), _bits(tx)
+    if rb <= 30 and rb + 2 * xb <= 32:
+        b = aabb16.to(torch.int64)
+        D = 16 * 65535
+        x0 = (b[:, 0] & 0xFFFF) * spec.width // D
+        y0 = ((b[:, 0] >> 16) & 0xFFFF) * spec.height // D
+        x1 = ((b[:, 1] & 0xFFFF) * spec.width + D - 1) // D
+        y1 = (((b[:, 1] >> 16) & 0xFFFF) * spec.height + D - 1) // D
+        ok = (x1 > x0) & (y1 > y0)
+        segs = ((y1 - y0) * (((x1 - 1) >> 6) - (x0 >> 6) + 1)).clamp(min=0)
+        S = int(segs[ok].sum().item()) if b.numel() else 0
+        b1 = _emit_digit_bits(rb)
+        rest = max(0, rb - b1)
+        return {"rows": True, "segments": S, "passes": (rest + 7) // 8 if rest else 0,
+                "elems": S}
+    bits = _bits(spec.n_cams * tx * ty)
+    b1 = _emit_digit_bits(bits)
     rest = max(0, bits - b1)
-    return b1, (rest + 7) // 8
+    return {"rows": False, "segments": None, "passes": (rest + 7) // 8 if rest else 0,
+            "elems": n_isects}
 
 
 def order_passes(spec):
@@ -123,8 +154,9 @@ def order_passes(spec):
     return 0 if 0 < n_tiles <= 16384 else 2
 
 
-def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes, depth_passes=4):
-    """Algorithmic HBM bytes of one launch of an HBM-bound kernel."""
+def hbm_bytes(kernel, spec, nnz, n_isects, V, sm, depth_passes=4):
+    """Algorithmic HBM bytes of one launch of an HBM-bound kernel; sm is
+    sort_model()."""
     N, C, K = spec.n, spec.n_cams, spec.K
     Np = ((N + 127) // 128) * 128
     pairs = C * Np
@@ -139,10 +171,12 @@ def hbm_bytes(kernel, spec, nnz, n_isects, V, tile_passes, depth_passes=4):
     if kernel == "k_radix_scatter":  # mean over the step's passes: 8 B read + 8 B written per key
         tiles = C * ((spec.width + 15) // 16) * ((spec.height + 15) // 16)
         op = order_passes(spec)
-        return (16 * (depth_passes * nnz + tile_passes * n_isects + op * tiles)
-                / (depth_passes + tile_passes + op))
-    if kernel == "k_emit_write":     # order + box per pair; 8 B per entry
-        return 12 * nnz + 8 * n_isects
+        return (16 * (depth_passes * nnz + sm["passes"] * sm["elems"] + op * tiles)
+                / (depth_passes + sm["passes"] + op))
+    if kernel == "k_emit_write":     # order + rectangle per pair; 8 B per entry or segment
+        return 12 * nnz + 8 * sm["elems"]
+    if kernel == "k_row_expand":     # 8 B per segment read, 4 B per entry written
+        return 8 * sm["segments"] + 4 * n_isects if sm["rows"] else None
     return None
 
 
@@ -486,7 +520,8 @@ def run_config(cid, a, cpu_baseline_on, mode="train"):
     V = int(vis[: spec.n_cams * Np].reshape(spec.n_cams, Np).any(0).sum())
     del vis
     tx, ty = gsd.tiles(spec.width, spec.height)
-    _, tile_passes = tile_sort_digits(spec)
+    sm = sort_model(spec, p.aabb16[:nnz] if p.aabb16 is not None else
+                    torch.empty(0, 2, dtype=torch.int32, device="cuda"), it.n_isects)
     # the depth sort runs its top 8-bit pass only when the keys differ there
     depth_passes = 3
     if nnz:
@@ -504,7 +539,7 @@ def run_config(cid, a, cpu_baseline_on, mode="train"):
                 "flops_per_launch": work, "evaluations": evals,
                 "flops_per_evaluation": FLOPS_EVAL + per_comp, "launch_ms": dom_ms}
     else:
-        byt = hbm_bytes(dom, spec, nnz, n_is, V, tile_passes, depth_passes)
+        byt = hbm_bytes(dom, spec, nnz, n_is, V, sm, depth_passes)
         achieved = byt / (dom_ms * 1e-3) / 1e9 if byt else None
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
@@ -539,6 +574,7 @@ def run_config(cid, a, cpu_baseline_on, mode="train"):
         "m_visible_pairs_per_s": nnz * steps_s / 1e6,
         "nnz": nnz,
         "n_isects": n_is,
+        "segments": sm["segments"],
         "visible_gaussians": V,
         "raster_evaluations": evals,
         "stage_ms": stage_ms,
@@ -551,17 +587,17 @@ def run_config(cid, a, cpu_baseline_on, mode="train"):
         out["arena"] = {"alias": arena.alias, "MiB": arena.buf.numel() / 2**20}
     hb = {}
     for kn, ms in kernel_ms.items():
-        byt = hbm_bytes(kn, spec, nnz, n_is, V, tile_passes, depth_passes)
+        byt = hbm_bytes(kn, spec, nnz, n_is, V, sm, depth_passes)
         if byt:
             if kn == "k_radix_scatter":   # per-launch mean; ms is the step's sum
-                byt *= depth_passes + tile_passes + order_passes(spec)
+                byt *= depth_passes + sm["passes"] + order_passes(spec)
             hb[kn] = byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     # the whole sort (depth passes over the pairs, tile passes over the
     # entries, launch-order passes over the tiles if any; each pass reads and
     # writes a 4 B key and a 4 B value per element) against the time of all
     # its kernels: counting and scatter
     sort_ms = sum(kernel_ms.get(k, 0.0) for k in ("k_radix_count", "k_radix_scatter"))
-    sort_bytes = 16 * (depth_passes * nnz + tile_passes * n_is
+    sort_bytes = 16 * (depth_passes * nnz + sm["passes"] * sm["elems"]
                        + order_passes(spec) * spec.n_cams * tx * ty)
     if sort_ms > 0:
         hb["sort (all radix kernels)"] = sort_bytes / (sort_ms * 1e-3) / 1e9 / HBM_PEAK_GBS

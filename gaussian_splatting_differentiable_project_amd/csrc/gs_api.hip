@@ -451,7 +451,8 @@ int gs_intersect(void* stream, int32_t C, int32_t W, int32_t H, int64_t nnz, con
       !tile_offsets || !cam_offsets || isect_capacity < 0)
     return GS_E_INVALID;
   if (nnz > 0 && (!screen || !aabb16)) return GS_E_INVALID;
-  if (!aligned(aabb16, 8) || !aligned(workspace, kAlign)) return GS_E_INVALID;
+  if (!aligned(aabb16, 8) || !aligned(workspace, kAlign) || !aligned(flatten_ids, 16))
+    return GS_E_INVALID;
   *n_isects_out = -1;
   if (nnz >= (int64_t(1) << 31)) return GS_E_OVERFLOW;
   int64_t widest = 0;  // most pairs of any one camera

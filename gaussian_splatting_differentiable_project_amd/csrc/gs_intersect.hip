@@ -672,17 +672,18 @@ __global__ __launch_bounds__(256) void k_row_colscan(const uint64_t* __restrict_
 // segments are read 64 at a time, one per lane, as 64-bit masks of the
 // window tiles they cover; the wave transposes the 64 x 64 bit matrix
 // (segment x tile) so that each lane holds the set of those segments
-// covering its tile, and takes them lowest first (four per step) as its
-// tile's next entries. A lane stages its entries in LDS, in a ring of two
-// groups of 16 consecutive output positions (64 bytes); each group is
-// written out once complete, by 16 lanes at once, four groups per store
-// instruction, so the stores are whole contiguous runs instead of one
-// scattered word per entry. The groups at the two ends of a lane's range
-// are written in part. Writes are clamped to `cap` entries.
-constexpr int kGroup = 16;             // entries per written group
-constexpr int kRing = 2 * kGroup;      // staged entries per lane
-constexpr int kRingStride = kRing + 1;  // LDS words per lane: padded against bank conflicts
-constexpr int kTake = 4;               // entries a lane takes per step (< kGroup)
+// covering its tile, and takes them lowest first (up to eight per step) as
+// its tile's next entries. A lane stages its entries in LDS, in a ring of
+// two groups of 16 consecutive output positions (64 bytes, aligned); a
+// group completed in a step is written out at the end of that step, by
+// four lanes with one 16-byte store each, sixteen groups per store
+// instruction. The groups at the two ends of a lane's range are written in
+// part, word by word. Writes are clamped to `cap` entries; ids must be
+// 16-byte aligned.
+constexpr int kGroup = 16;         // entries per written group
+constexpr int kRing = 2 * kGroup;  // staged entries per lane
+constexpr int kRingStride = kRing + 4;  // LDS words per lane: rows stay 16-byte aligned
+constexpr int kTake = 8;           // entries a lane takes per step (< kGroup)
 
 __device__ __forceinline__ void wave_order() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -729,42 +730,54 @@ __device__ __forceinline__ void transpose_step(uint32_t& lo, uint32_t& hi, uint6
 
 // 64 x 64 bit-matrix transpose across the wave: lane l holds row l (bit b
 // is element (l, b)); afterwards lane l holds column l.
-__device__ __forceinline__ uint64_t wave_transpose64(uint64_t v) {
+__device__ __forceinline__ void wave_transpose64(uint32_t& lo, uint32_t& hi) {
   const int lane = __lane_id();
-  uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
   transpose_step<32>(lo, hi, 0x00000000FFFFFFFFull, lane);
   transpose_step<16>(lo, hi, 0x0000FFFF0000FFFFull, lane);
   transpose_step<8>(lo, hi, 0x00FF00FF00FF00FFull, lane);
   transpose_step<4>(lo, hi, 0x0F0F0F0F0F0F0F0Full, lane);
   transpose_step<2>(lo, hi, 0x3333333333333333ull, lane);
   transpose_step<1>(lo, hi, 0x5555555555555555ull, lane);
-  return (uint64_t(hi) << 32) | lo;
 }
 
-// Writes the group described by every lane in `lanes`: output positions
-// G + j for j in [vlo, vhi), from the lane's ring slots (G + j) mod kRing.
-// Four groups per store: lanes 16k .. 16k + 15 write the k-th lane's.
-__device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf, uint64_t G,
-                                             uint32_t vlohi, uint64_t cap,
+// Writes the groups of the lanes in `lanes`: lane l's group covers output
+// positions G_l + j, j in [vlo_l, vhi_l), staged in its ring slots
+// (G_l + j) mod kRing. Each such lane posts (G, vlo | vhi << 8, lane) in
+// LDS in lane order; four lanes then write each posted group, 16 bytes
+// each (word by word for a partial group).
+__device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf, uint4* desc,
+                                             uint64_t G, uint32_t vlohi, uint64_t cap,
                                              uint32_t* __restrict__ ids) {
+  if (!lanes) return;
   const int lane = __lane_id();
-  const int quarter = lane >> 4, j = lane & (kGroup - 1);
-  while (lanes) {
-    int L[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      L[k] = lanes ? __builtin_ctzll(lanes) : -1;
-      lanes &= lanes - 1;
-    }
-    const int src = quarter == 0 ? L[0] : quarter == 1 ? L[1] : quarter == 2 ? L[2] : L[3];
-    const int sl = src < 0 ? 0 : src;
-    const uint32_t glo = uint32_t(__builtin_amdgcn_ds_bpermute(sl * 4, int(uint32_t(G))));
-    const uint32_t ghi = uint32_t(__builtin_amdgcn_ds_bpermute(sl * 4, int(uint32_t(G >> 32))));
-    const uint32_t lh = uint32_t(__builtin_amdgcn_ds_bpermute(sl * 4, int(vlohi)));
-    const uint64_t gp = ((uint64_t(ghi) << 32) | glo) + uint32_t(j);
-    const uint32_t v = buf[sl * kRingStride + ((glo + uint32_t(j)) & (kRing - 1))];
-    if (src >= 0 && uint32_t(j) >= (lh & 0xFFu) && uint32_t(j) < (lh >> 8) && gp < cap) ids[gp] = v;
+  if ((lanes >> lane) & 1ull) {
+    const uint32_t rank = uint32_t(__popcll(lanes & lanemask_lt()));
+    desc[rank] = make_uint4(uint32_t(G), uint32_t(G >> 32), vlohi, uint32_t(lane));
   }
+  wave_order();
+  const uint32_t n = uint32_t(__popcll(lanes));
+  const uint32_t sub = uint32_t(lane) & 3u;
+  for (uint32_t g0 = 0; g0 < n; g0 += 16) {
+    const uint32_t gi = g0 + (uint32_t(lane) >> 2);
+    if (gi < n) {
+      const uint4 d = desc[gi];
+      const uint64_t gs = (uint64_t(d.y) << 32) | d.x;
+      const uint32_t vlo = d.z & 0xFFu, vhi = d.z >> 8;
+      const uint32_t j0 = 4 * sub;
+      const uint4 v = *reinterpret_cast<const uint4*>(
+          buf + d.w * kRingStride + ((d.x + j0) & (kRing - 1)));
+      const uint64_t p = gs + j0;
+      if (vlo == 0 && vhi == uint32_t(kGroup) && p + 3 < cap) {
+        *reinterpret_cast<uint4*>(ids + p) = v;
+      } else {
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (uint32_t u = 0; u < 4; ++u)
+          if (j0 + u >= vlo && j0 + u < vhi && p + u < cap) ids[p + u] = vv[u];
+      }
+    }
+  }
+  wave_order();
 }
 
 template <bool KEYS>
@@ -774,7 +787,8 @@ __global__ __launch_bounds__(256) void k_row_expand(
     const uint32_t* __restrict__ cm, const int64_t* __restrict__ toff, RowGeom g, uint64_t qmax,
     uint64_t cap, const float* __restrict__ screen, uint64_t nnz, uint32_t* __restrict__ ids,
     uint64_t* __restrict__ keys_out) {
-  __shared__ uint32_t s_buf[4][kWave * kRingStride];
+  __shared__ __align__(16) uint32_t s_buf[4][kWave * kRingStride];
+  __shared__ uint4 s_desc[4][kWave];
   const int lane = threadIdx.x & 63;
   // wave-uniform: the chunk walk below runs on scalar registers
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -783,6 +797,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
   if (q >= Q) return;  // the whole wave
   uint32_t* buf = s_buf[wv];
   uint32_t* mine = buf + lane * kRingStride;
+  uint4* desc = s_desc[wv];
   const uint32_t rw = chunk_row(cq, g.R, q);
   const uint32_t w = rw % g.nwin, row = rw / g.nwin;
   const uint64_t s0 = uint64_t(roff[rw]) + (q - cq[rw]) * g.K;
@@ -793,6 +808,48 @@ __global__ __launch_bounds__(256) void k_row_expand(
   const uint64_t base = x < g.tiles_x ? uint64_t(toff[t]) + cm[q * 64 + lane] : 0ull;
   uint32_t sp = uint32_t(base);  // low word of the next output position
   uint32_t off = 0;              // entries taken
+
+  // Takes the segments of one 32-bit word of the transposed set (segment
+  // indices i0 + bit) in order, kTake per step.
+  auto take = [&](uint32_t cw, int i0, uint32_t val) {
+    while (__ballot(cw != 0u)) {
+      int idx[kTake];
+      uint32_t k = 0;
+#pragma unroll
+      for (int u = 0; u < kTake; ++u) {
+        idx[u] = i0 + (cw ? __builtin_ctz(cw) : 0);
+        k += cw ? 1u : 0u;
+        cw &= cw - 1u;
+      }
+      // the pairs of those segments, read from their lanes; slots past the
+      // k taken ones receive values that later entries overwrite before
+      // any group holding them is written out
+#pragma unroll
+      for (int u = 0; u < kTake; ++u) {
+        const uint32_t v = uint32_t(__builtin_amdgcn_ds_bpermute(idx[u] * 4, int(val)));
+        mine[(sp + u) & (kRing - 1)] = v;
+        if (KEYS && uint32_t(u) < k) {
+          const uint64_t p = base + off + u;
+          if (p < cap && v < nnz)
+            keys_out[p] = (uint64_t(t) << 32) | __float_as_uint(screen[uint64_t(v) * kRow + 6]);
+        }
+      }
+      const uint32_t sp2 = sp + k;
+      // at most one group boundary is crossed per step
+      const bool done = ((sp2 ^ sp) & ~uint32_t(kGroup - 1)) != 0u;
+      sp = sp2;
+      off += k;
+      const uint64_t full = __ballot(done);
+      if (full) {
+        // the completed group: the 16 positions before the boundary crossed
+        const uint64_t pos = base + off;
+        const uint64_t G = (pos & ~uint64_t(kGroup - 1)) - kGroup;
+        const uint32_t vlo = G < base ? uint32_t(base - G) : 0u;
+        wave_order();
+        flush_groups(full, buf, desc, G, vlo | (uint32_t(kGroup) << 8), cap, ids);
+      }
+    }
+  };
 
   // Segments are loaded kAhead batches of 64 at a time, the next group
   // while the current one is walked: a wait for loads also waits for every
@@ -820,52 +877,11 @@ __global__ __launch_bounds__(256) void k_row_expand(
       if (sg + j * 64 >= s1) break;  // uniform
       const bool in = sg + j * 64 + lane < s1;
       const uint64_t m = in ? segment_bits(ck[j], g, w) : 0ull;
-      const uint32_t val = cv[j];
       // lane i now holds the set of this batch's segments covering tile i
-      uint64_t c = wave_transpose64(m);
-      while (__ballot(c != 0ull)) {
-        // up to kTake segments per lane and step; their pairs are read
-        // from their lanes together
-        int idx[kTake];
-        uint32_t k = 0;
-#pragma unroll
-        for (int u = 0; u < kTake; ++u) {
-          idx[u] = c ? __builtin_ctzll(c) : 0;
-          k += c ? 1u : 0u;
-          c &= c - 1;
-        }
-        uint32_t v[kTake];
-#pragma unroll
-        for (int u = 0; u < kTake; ++u)
-          v[u] = uint32_t(__builtin_amdgcn_ds_bpermute(idx[u] * 4, int(val)));
-#pragma unroll
-        for (int u = 0; u < kTake; ++u) {
-          if (uint32_t(u) < k) {
-            mine[(sp + u) & (kRing - 1)] = v[u];
-            if (KEYS) {
-              const uint64_t p = base + off + u;
-              if (p < cap && v[u] < nnz)
-                keys_out[p] =
-                    (uint64_t(t) << 32) | __float_as_uint(screen[uint64_t(v[u]) * kRow + 6]);
-            }
-          }
-        }
-        const uint32_t sp2 = sp + k;
-        // at most one group boundary is crossed per step
-        const bool done = ((sp2 ^ sp) & ~uint32_t(kGroup - 1)) != 0u;
-        sp = sp2;
-        off += k;
-        const uint64_t full = __ballot(done);
-        if (full) {
-          // the completed group: the 16 positions before the boundary crossed
-          const uint64_t pos = base + off;
-          const uint64_t G = (pos & ~uint64_t(kGroup - 1)) - kGroup;
-          const uint32_t vlo = G < base ? uint32_t(base - G) : 0u;
-          wave_order();
-          flush_groups(full, buf, G, vlo | (uint32_t(kGroup) << 8), cap, ids);
-          wave_order();
-        }
-      }
+      uint32_t clo = uint32_t(m), chi = uint32_t(m >> 32);
+      wave_transpose64(clo, chi);
+      take(clo, 0, cv[j]);
+      take(chi, 32, cv[j]);
     }
   }
   // the partial last groups
@@ -875,7 +891,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
   const uint32_t vlo = G < base ? uint32_t(base - G) : 0u;
   const uint64_t rest = __ballot(part);
   wave_order();
-  flush_groups(rest, buf, G, vlo | ((uint32_t(pos) & (kGroup - 1)) << 8), cap, ids);
+  flush_groups(rest, buf, desc, G, vlo | ((uint32_t(pos) & (kGroup - 1)) << 8), cap, ids);
 }
 
 __global__ __launch_bounds__(256) void k_compose_keys(const uint32_t* __restrict__ tkeys,

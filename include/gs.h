@@ -205,7 +205,7 @@ int gs_project_noalloc(void* stream, int64_t N, int32_t C, int32_t W, int32_t H,
  * Inputs: screen[nnz][10], aabb16[nnz][2] from gs_project, and (host)
  * cam_offsets[C+1] (first slot of every camera).
  * Outputs: flatten_ids[n_isects] (uint32 slot of every sorted entry,
- * capacity isect_capacity); tile_offsets[C*T+1] int64 (entries of global
+ * capacity isect_capacity, 16-byte aligned); tile_offsets[C*T+1] int64 (entries of global
  * tile t are flatten_ids[tile_offsets[t] .. tile_offsets[t+1]));
  * sorted_keys[n_isects] (nullable: the sorted 64-bit keys);
  * tile_order[C*T] (nullable: every global tile id once, ordered by
