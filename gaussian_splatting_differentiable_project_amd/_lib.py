@@ -89,8 +89,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         [c_vp] * 3 + [ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), ctypes.POINTER(ctypes.c_float),
                       ctypes.c_float, ctypes.c_float, ctypes.c_float, c_i32]
     lib.gs_arena_plan.restype = ctypes.c_int
-    lib.gs_arena_plan.argtypes = [c_i64, c_i32, c_i32, c_i32, c_i64, c_i64, c_i32, P_u64, P_u64,
-                                  P_u64]
+    lib.gs_arena_plan.argtypes = [c_i64, c_i32, c_i32, c_i32, c_i64, c_i64, c_u64, c_i32, P_u64,
+                                  P_u64, P_u64]
     lib.gs_project_bwd.restype = ctypes.c_int
     lib.gs_project_bwd.argtypes = [c_vp, c_i64, c_i32, c_i32, c_i32, c_i32] + [c_vp] * 7 + \
         [c_vp] * 3 + [c_vp] * 5 + [c_i32]
@@ -237,14 +237,15 @@ def gs_project_bwd(N, C, W, H, sh_degree, means, quats, log_scales, opacity_logi
                                  int(accumulate))
 
 
-def gs_arena_plan(N, C, W, H, nnz, n_isects, alias=True):
-    """(status, {slot: (offset, bytes)}, arena_bytes)."""
+def gs_arena_plan(N, C, W, H, nnz, n_isects, alias=True, isect_ws_bytes=0):
+    """(status, {slot: (offset, bytes)}, arena_bytes). isect_ws_bytes = 0
+    sizes the intersection workspace by its bound for the capacities."""
     n = len(ARENA_SLOTS)
     off = (ctypes.c_uint64 * n)()
     sz = (ctypes.c_uint64 * n)()
     tot = ctypes.c_uint64(0)
-    st = load().gs_arena_plan(N, C, W, H, nnz, n_isects, 1 if alias else 0, off, sz,
-                              ctypes.byref(tot))
+    st = load().gs_arena_plan(N, C, W, H, nnz, n_isects, int(isect_ws_bytes), 1 if alias else 0,
+                              off, sz, ctypes.byref(tot))
     return st, {k: (off[i], sz[i]) for i, k in enumerate(ARENA_SLOTS)}, tot.value
 
 
@@ -352,17 +353,23 @@ class PhaseArena:
         self.buf = None
         self.cap_nnz = 0
         self.cap_isects = 0
+        self.cap_ws = 0
         self.slots = {}
 
-    def plan(self, s: "Scene", nnz: int, n_isects: int) -> bool:
-        """Lay out capacities >= (nnz, n_isects); grows (and returns True) when
-        the planned arena is larger than the current allocation."""
+    def plan(self, s: "Scene", nnz: int, n_isects: int, isect_ws: int = 0) -> bool:
+        """Lay out capacities >= (nnz, n_isects) and an intersection
+        workspace of at least isect_ws bytes (the need gs_intersect reports;
+        its lower bound for counting until one is seen); grows (and returns
+        True) when the planned arena is larger than the current allocation."""
         if nnz > self.cap_nnz:
             self.cap_nnz = int(nnz * self.slack) + 1
         if n_isects > self.cap_isects:
             self.cap_isects = int(n_isects * self.slack) + 1
+        floor = int(load().gs_intersect_workspace_bytes(s.C, s.W, s.H, self.cap_nnz, 0))
+        if max(isect_ws, floor) > self.cap_ws:
+            self.cap_ws = int(max(isect_ws, floor) * self.slack) + 1
         st, self.slots, total = gs_arena_plan(s.N, s.C, s.W, s.H, self.cap_nnz, self.cap_isects,
-                                              self.alias)
+                                              self.alias, self.cap_ws)
         if st != GS_OK:
             raise GsError(st, "gs_arena_plan")
         if self.buf is None or self.buf.numel() < total:
@@ -524,9 +531,9 @@ class Rasterizer:
         Np = pad_n(s.N)
         tx, ty = tiles(s.W, s.H)
         n_tiles = s.C * tx * ty
-        nnz_need, is_need = A.cap_nnz, A.cap_isects
+        nnz_need, is_need, ws_need = A.cap_nnz, A.cap_isects, A.cap_ws
         for _ in range(4):
-            A.plan(s, nnz_need, is_need)
+            A.plan(s, nnz_need, is_need, ws_need)
             mask = A.view("mask", torch.int64, (max(s.C * Np // 64, 1),))
             wgc = A.view("wg_count", torch.int32, (max(s.C * Np // MASK_GROUP, 1),))
             wgs = A.view("wg_scan", torch.int32, (max(s.C * Np // MASK_GROUP, 1),))
@@ -550,6 +557,7 @@ class Rasterizer:
                                           ids, A.cap_isects, toff, None, order)
             if st in (GS_E_CAPACITY, GS_E_WORKSPACE):
                 is_need = max(n_is, is_need)
+                ws_need = max(need, ws_need)
                 continue
             self._check(st, "gs_intersect")
             ids = ids[:n_is]

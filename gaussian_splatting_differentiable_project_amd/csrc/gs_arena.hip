@@ -29,8 +29,8 @@ uint64_t up(uint64_t x) { return (x + kArenaAlign - 1) & ~(kArenaAlign - 1); }
 }  // namespace
 
 extern "C" int gs_arena_plan(int64_t N, int32_t C, int32_t W, int32_t H, int64_t nnz,
-                             int64_t n_isects, int32_t alias, uint64_t* offsets,
-                             uint64_t* sizes, uint64_t* arena_bytes) {
+                             int64_t n_isects, uint64_t isect_ws_bytes, int32_t alias,
+                             uint64_t* offsets, uint64_t* sizes, uint64_t* arena_bytes) {
   if (N < 0 || C < 1 || W < 1 || H < 1 || W > 65535 || H > 65535 || nnz < 0 || n_isects < 0 ||
       !offsets || !sizes || !arena_bytes)
     return GS_E_INVALID;
@@ -47,7 +47,9 @@ extern "C" int gs_arena_plan(int64_t N, int32_t C, int32_t W, int32_t H, int64_t
   s[GS_SLOT_PROJECT_WS] = {gs_project_workspace_bytes(N, C), 0, 0};
   s[GS_SLOT_SCREEN] = {40 * n, 0, 3};
   s[GS_SLOT_AABB16] = {8 * n, 0, 1};
-  s[GS_SLOT_ISECT_WS] = {gs_intersect_workspace_bytes(C, W, H, nnz, n_isects), 1, 1};
+  s[GS_SLOT_ISECT_WS] = {isect_ws_bytes ? isect_ws_bytes
+                                        : gs_intersect_workspace_bytes(C, W, H, nnz, n_isects),
+                         1, 1};
   s[GS_SLOT_FLATTEN_IDS] = {4 * I, 1, 3};
   s[GS_SLOT_TILE_OFFSETS] = {8 * (tiles + 1), 1, 3};
   s[GS_SLOT_TILE_ORDER] = {4 * tiles, 1, 3};

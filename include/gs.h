@@ -357,7 +357,11 @@ int gs_project_bwd_adam(void* stream, int64_t N, int32_t C, int32_t W, int32_t H
  * not the sum; SS_POOL_ALIAS=0 there turns the sharing off).
  *
  * Host arithmetic only. For a step with N Gaussians, C cameras of W x H,
- * capacities nnz (visible pairs) and n_isects (intersections), writes for
+ * capacities nnz (visible pairs) and n_isects (intersections), and an
+ * intersection workspace of isect_ws_bytes (0 = the bound
+ * gs_intersect_workspace_bytes(C, W, H, nnz, n_isects), which holds for any
+ * scene of those capacities; a caller that has seen the bytes gs_intersect
+ * reports as needed may pass those, with a margin, instead), writes for
  * each slot below (host arrays of GS_ARENA_SLOTS) its byte offset in the
  * arena (256-byte aligned) and its size, and (host) *arena_bytes. Phases:
  * 0 gs_project, 1 gs_intersect, 2 gs_rasterize_fwd, 3 gs_rasterize_bwd,
@@ -386,8 +390,8 @@ int gs_project_bwd_adam(void* stream, int64_t N, int32_t C, int32_t W, int32_t H
 #define GS_SLOT_LAST_IDS 12
 #define GS_SLOT_V_SCREEN 13
 int gs_arena_plan(int64_t N, int32_t C, int32_t W, int32_t H, int64_t nnz,
-                  int64_t n_isects, int32_t alias, uint64_t* offsets,
-                  uint64_t* sizes, uint64_t* arena_bytes);
+                  int64_t n_isects, uint64_t isect_ws_bytes, int32_t alias,
+                  uint64_t* offsets, uint64_t* sizes, uint64_t* arena_bytes);
 
 /* ---------------------------------------------------------------------
  * Per-kernel timing (opt-in; a HIP event pair around each launch of a
@@ -403,8 +407,8 @@ int gs_arena_plan(int64_t N, int32_t C, int32_t W, int32_t H, int64_t nnz,
  *   count and summed duration in milliseconds (host out-params).
  * Kernel names: k_project_mask, k_scan, k_cam_offsets, k_project_compact,
  * k_fill_u32, k_isect_prep, k_radix_count, k_radix_scatter, k_emit_count,
- * k_emit_write, k_tile_ranges, k_tile_order_keys, k_tile_order_rank,
- * k_compose_keys,
+ * k_emit_write, k_tile_ranges, k_row_chunks, k_row_count, k_row_colscan,
+ * k_row_expand, k_tile_order_keys, k_tile_order_rank, k_compose_keys,
  * k_raster_fwd, k_raster_bwd, k_project_bwd, k_project_bwd_adam.
  * Recording adds host overhead per launch
  * and is not meant to stay on in production.

@@ -234,8 +234,11 @@ def test_arena_plan_properties(lib, shape):
     Np = (N + 127) // 128 * 128
     assert plain["mask"][1] == C * Np // 8 and plain["v_screen"][1] == 40 * nnz
     assert plain["isect_ws"][1] == lib.gs_intersect_workspace_bytes(C, W, H, nnz, I)
+    # an explicit intersection workspace (the need a call reported) replaces the bound
+    st2, given, _ = gsd.gs_arena_plan(N, C, W, H, nnz, I, alias=True, isect_ws_bytes=123_457)
+    assert st2 == gsd.GS_OK and given["isect_ws"][1] == 123_457
     if nnz > 1000:
         o_i, s_i = al["isect_ws"]
         o_v, s_v = al["v_screen"]
         assert o_i < o_v + s_v and o_v < o_i + s_i   # they share bytes
-    assert lib.gs_arena_plan(-1, 1, 1, 1, 0, 0, 1, None, None, None) == gsd.GS_E_INVALID
+    assert lib.gs_arena_plan(-1, 1, 1, 1, 0, 0, 0, 1, None, None, None) == gsd.GS_E_INVALID
