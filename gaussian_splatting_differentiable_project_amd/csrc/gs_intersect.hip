@@ -672,7 +672,7 @@ __global__ __launch_bounds__(256) void k_row_colscan(const uint64_t* __restrict_
 // segments are read 64 at a time, one per lane, as 64-bit masks of the
 // window tiles they cover; the wave transposes the 64 x 64 bit matrix
 // (segment x tile) so that each lane holds the set of those segments
-// covering its tile, and takes them lowest first (up to eight per step) as
+// covering its tile, and takes them lowest first (up to four per step) as
 // its tile's next entries. A lane stages its entries in LDS, in a ring of
 // two groups of 16 consecutive output positions (64 bytes, aligned); a
 // group completed in a step is written out at the end of that step, by
@@ -682,8 +682,16 @@ __global__ __launch_bounds__(256) void k_row_colscan(const uint64_t* __restrict_
 // 16-byte aligned.
 constexpr int kGroup = 16;         // entries per written group
 constexpr int kRing = 2 * kGroup;  // staged entries per lane
-constexpr int kRingStride = kRing + 4;  // LDS words per lane: rows stay 16-byte aligned
-constexpr int kTake = 8;           // entries a lane takes per step (< kGroup)
+constexpr int kTake = 4;           // entries a lane takes per step (< kGroup)
+// steps between flushes of the completed groups: a lane's writes reach a
+// completed group's slots again only after kGroup - kTake + 1 more entries
+constexpr uint32_t kFlushEvery = (kGroup - kTake) / kTake;
+static_assert(kFlushEvery >= 1, "a completed group must survive until the flush");
+// LDS words per lane: the ring, then kTake overflow slots (a step writes
+// its entries contiguously from its first slot; entries past the ring's
+// end are copied to its start), rows 16-byte aligned
+constexpr int kRingStride = kRing + kTake;
+static_assert(kRingStride % 4 == 0, "16-byte aligned ring rows");
 
 __device__ __forceinline__ void wave_order() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -811,43 +819,61 @@ __global__ __launch_bounds__(256) void k_row_expand(
 
   // Takes the segments of one 32-bit word of the transposed set (segment
   // indices i0 + bit) in order, kTake per step.
+  bool pend = false;      // a completed group awaits writing
+  uint64_t pend_g = 0;    // its first position
+  uint32_t steps = 0;     // steps since the last flush (uniform)
+  auto flush_pending = [&]() {
+    const uint64_t lanes = __ballot(pend);
+    if (lanes) {
+      const uint32_t vlo = pend_g < base ? uint32_t(base - pend_g) : 0u;
+      wave_order();
+      flush_groups(lanes, buf, desc, pend_g, vlo | (uint32_t(kGroup) << 8), cap, ids);
+    }
+    pend = false;
+    steps = 0;
+  };
+
   auto take = [&](uint32_t cw, int i0, uint32_t val) {
     while (__ballot(cw != 0u)) {
-      int idx[kTake];
-      uint32_t k = 0;
+      // up to kTake entries into consecutive slots from this step's first
+      // one; slots past the k taken ones receive values that later entries
+      // overwrite before any group holding them is written out
+      const uint32_t slot0 = sp & (kRing - 1);
+      uint32_t* wp = mine + slot0;
+      const uint32_t n = uint32_t(__popc(cw));
+      const uint32_t k = n < uint32_t(kTake) ? n : uint32_t(kTake);
 #pragma unroll
       for (int u = 0; u < kTake; ++u) {
-        idx[u] = i0 + (cw ? __builtin_ctz(cw) : 0);
-        k += cw ? 1u : 0u;
+        // the lowest remaining segment (32 once none remain: a harmless
+        // lane), its pair read from its lane
+        const int i = i0 + int(__builtin_ctzg(cw, 32));
+        const uint32_t v = uint32_t(__builtin_amdgcn_ds_bpermute(i * 4, int(val)));
+        wp[u] = v;
         cw &= cw - 1u;
-      }
-      // the pairs of those segments, read from their lanes; slots past the
-      // k taken ones receive values that later entries overwrite before
-      // any group holding them is written out
-#pragma unroll
-      for (int u = 0; u < kTake; ++u) {
-        const uint32_t v = uint32_t(__builtin_amdgcn_ds_bpermute(idx[u] * 4, int(val)));
-        mine[(sp + u) & (kRing - 1)] = v;
         if (KEYS && uint32_t(u) < k) {
           const uint64_t p = base + off + u;
           if (p < cap && v < nnz)
             keys_out[p] = (uint64_t(t) << 32) | __float_as_uint(screen[uint64_t(v) * kRow + 6]);
         }
       }
+      if (slot0 + k > uint32_t(kRing)) {  // wrapped: the overflow slots belong at the ring's start
+        const uint4 w = *reinterpret_cast<const uint4*>(mine + kRing);
+        *reinterpret_cast<uint4*>(mine) = w;
+      }
       const uint32_t sp2 = sp + k;
-      // at most one group boundary is crossed per step
-      const bool done = ((sp2 ^ sp) & ~uint32_t(kGroup - 1)) != 0u;
+      // at most one group boundary is crossed per step: the group of the
+      // 16 positions before it is complete, and waits for the next flush
+      if (((sp2 ^ sp) & ~uint32_t(kGroup - 1)) != 0u) {
+        const uint64_t pos = base + off + k;
+        pend_g = (pos & ~uint64_t(kGroup - 1)) - kGroup;
+        pend = true;
+      }
       sp = sp2;
       off += k;
-      const uint64_t full = __ballot(done);
-      if (full) {
-        // the completed group: the 16 positions before the boundary crossed
-        const uint64_t pos = base + off;
-        const uint64_t G = (pos & ~uint64_t(kGroup - 1)) - kGroup;
-        const uint32_t vlo = G < base ? uint32_t(base - G) : 0u;
-        wave_order();
-        flush_groups(full, buf, desc, G, vlo | (uint32_t(kGroup) << 8), cap, ids);
-      }
+      // A lane writes at most kTake entries, kTake - 1 slots ahead, per
+      // step, so a completed group's slots stay untouched for kFlushEvery
+      // more steps; a lane completes at most one group between flushes.
+      if (++steps == kFlushEvery) flush_pending();
     }
   };
 
@@ -884,6 +910,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
       take(chi, 32, cv[j]);
     }
   }
+  flush_pending();
   // the partial last groups
   const uint64_t pos = base + off;
   const bool part = off != 0 && (uint32_t(pos) & (kGroup - 1)) != 0u;
