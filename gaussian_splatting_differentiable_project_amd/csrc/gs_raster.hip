@@ -55,18 +55,31 @@ __device__ __forceinline__ Staged stage_row(const float* __restrict__ screen, ui
   return e;
 }
 
-struct Eval {
-  float dx, dy, dxx, dyy, dxy, raw, alpha;
+// sigma = a' dx^2 + (c' dy + b dx) dy with dx = u - px, dy = v - py (a', c'
+// the halved conic). A lane's pixels share their column, so the dx terms
+// are formed once per entry and lane; both raster kernels evaluate sigma
+// in this same order, so they take the same alpha decisions bit for bit.
+struct ColTerms {
+  float dx, bdx, adxx;  // dx, b dx, a' dx^2
 };
 
-__device__ __forceinline__ Eval eval_splat(const float4& A, const float4& Bv, float px, float py) {
+__device__ __forceinline__ ColTerms col_terms(const float4& A, const float4& Bv, float px) {
+  ColTerms t;
+  t.dx = A.x - px;
+  t.bdx = Bv.x * t.dx;
+  t.adxx = (A.z * t.dx) * t.dx;
+  return t;
+}
+
+struct Eval {
+  float dy, raw, alpha;
+};
+
+__device__ __forceinline__ Eval eval_splat(const ColTerms& t, const float4& A, const float4& Bv,
+                                           float py) {
   Eval e;
-  e.dx = A.x - px;
   e.dy = A.y - py;
-  e.dxx = e.dx * e.dx;
-  e.dyy = e.dy * e.dy;
-  e.dxy = e.dx * e.dy;
-  const float sig = fmaf(A.z, e.dxx, fmaf(A.w, e.dyy, Bv.x * e.dxy));
+  const float sig = fmaf(fmaf(A.w, e.dy, t.bdx), e.dy, t.adxx);
   e.raw = __builtin_amdgcn_exp2f(fmaf(-sig, kLog2e, Bv.y));
   e.alpha = fminf(kAlphaMax, e.raw);
   return e;
@@ -153,6 +166,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
     int tiles_x, int T, const float* __restrict__ background, float* __restrict__ out_rgb,
     float* __restrict__ out_T, float* __restrict__ out_depth, int32_t* __restrict__ last_ids) {
   constexpr int NT = kTilePix / PPT;
+  static_assert(NT % kTile == 0, "a lane's pixels share one column");
   constexpr int B = NT;
   __shared__ float4 s_a[B];
   __shared__ float4 s_b[B];
@@ -216,11 +230,12 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
       const float cblue = s_c[j];
       const float zj = DEPTH ? s_z[j] : 0.f;
       const int lid = s_lid[j];
+      const ColTerms ct = col_terms(A, Bv, px[0]);  // the lane's pixels share px
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
         // pixel k of this wave lies in strip wave + k * (waves per tile)
         if (!((rm >> (wave + k * (NT / kWave))) & 1u)) continue;
-        const Eval e = eval_splat(A, Bv, px[k], py[k]);
+        const Eval e = eval_splat(ct, A, Bv, py[k]);
         const float Tn = Tr[k] * (1.f - e.alpha);
         const bool use = live[k] && e.alpha >= kAlphaMin;
         const bool stop = use && Tn < kTStop;
@@ -335,6 +350,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
     const float* __restrict__ v_T, const float* __restrict__ v_depth,
     float* __restrict__ v_screen, float* __restrict__ v_background) {
   constexpr int NT = kTilePix / PPT;
+  static_assert(NT % kTile == 0, "a lane's pixels share one column");
   constexpr int B = NT;
   __shared__ float4 s_a[B];
   __shared__ float4 s_b[B];
@@ -442,15 +458,16 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
       const float2 Cv = s_c[j];
       const float zj = DEPTH ? s_z[j] : 0.f;
       const int lid = s_lid[j];
-      // per-lane sums over its pixels: first moments and second moments of
-      // (dx, dy) weighted by dL/dsigma, sum of dL/dalpha raw, colour and
-      // depth grads
-      float mx = 0.f, my = 0.f, mxx = 0.f, mxy = 0.f, myy = 0.f, mo = 0.f;
+      // per-lane sums over its pixels, which share dx: the weights
+      // dL/dsigma and their first and second moments in dy (the dx moments
+      // follow from dx), sum of dL/dalpha raw, colour and depth grads
+      const ColTerms ct = col_terms(A, Bv, px[0]);
+      float s0 = 0.f, sy = 0.f, syy = 0.f, mo = 0.f;
       float gr = 0.f, gg = 0.f, gbl = 0.f, gz = 0.f;
       bool any = false;
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
-        const Eval e = eval_splat(A, Bv, px[k], py[k]);
+        const Eval e = eval_splat(ct, A, Bv, py[k]);
         if (lid <= last[k] && e.alpha >= kAlphaMin) {
           any = true;
           const float om = __builtin_amdgcn_rcpf(1.f - e.alpha);
@@ -468,15 +485,16 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_bwd(
           if (e.raw <= kAlphaMax) {
             const float vs = -va * e.alpha;
             mo = fmaf(va, e.raw, mo);
-            mx = fmaf(vs, e.dx, mx);
-            my = fmaf(vs, e.dy, my);
-            mxx = fmaf(vs, e.dxx, mxx);
-            mxy = fmaf(vs, e.dxy, mxy);
-            myy = fmaf(vs, e.dyy, myy);
+            const float vy = vs * e.dy;
+            s0 += vs;
+            sy += vy;
+            syy = fmaf(vy, e.dy, syy);
           }
         }
       }
       if (__ballot(any) != 0ull) {
+        const float mx = ct.dx * s0, my = sy, mxx = (ct.dx * ct.dx) * s0, mxy = ct.dx * sy,
+                    myy = syy;
         // dsigma/du = a dx + b dy, dsigma/dv = b dx + c dy, dsigma/da = dx^2/2,
         // dsigma/db = dx dy, dsigma/dc = dy^2/2, dalpha/do = exp(-sigma)
         const float a2 = A.z + A.z, c2 = A.w + A.w;
