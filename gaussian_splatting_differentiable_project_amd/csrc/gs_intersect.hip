@@ -674,12 +674,13 @@ __global__ __launch_bounds__(256) void k_row_colscan(const uint64_t* __restrict_
 // (segment x tile) so that each lane holds the set of those segments
 // covering its tile, and takes them lowest first (up to four per step) as
 // its tile's next entries. A lane stages its entries in LDS, in a ring of
-// two groups of 16 consecutive output positions (64 bytes, aligned); a
-// group completed in a step is written out at the end of that step, by
-// four lanes with one 16-byte store each, sixteen groups per store
-// instruction. The groups at the two ends of a lane's range are written in
-// part, word by word. Writes are clamped to `cap` entries; ids must be
-// 16-byte aligned.
+// two groups of 16 consecutive output positions (64 bytes, aligned),
+// slot-major (slot s of lane l at word s * 64 + l, so the lanes' writes of
+// one step fall in distinct banks whatever their slots); completed groups
+// are written out every few steps, kGroup / 4 lanes with one 16-byte
+// store each per group, 64 / (kGroup / 4) groups per store instruction. The groups at the two ends
+// of a lane's range are written in part, word by word. Writes are clamped
+// to `cap` entries; ids must be 16-byte aligned.
 constexpr int kGroup = 16;         // entries per written group
 constexpr int kRing = 2 * kGroup;  // staged entries per lane
 constexpr int kTake = 4;           // entries a lane takes per step (< kGroup)
@@ -687,11 +688,10 @@ constexpr int kTake = 4;           // entries a lane takes per step (< kGroup)
 // completed group's slots again only after kGroup - kTake + 1 more entries
 constexpr uint32_t kFlushEvery = (kGroup - kTake) / kTake;
 static_assert(kFlushEvery >= 1, "a completed group must survive until the flush");
-// LDS words per lane: the ring, then kTake overflow slots (a step writes
-// its entries contiguously from its first slot; entries past the ring's
-// end are copied to its start), rows 16-byte aligned
-constexpr int kRingStride = kRing + kTake;
-static_assert(kRingStride % 4 == 0, "16-byte aligned ring rows");
+// slots per lane: the ring, then kTake overflow slots (a step writes its
+// entries to consecutive slots from its first; entries past the ring's
+// end are copied to its start)
+constexpr int kRingSlots = kRing + kTake;
 
 __device__ __forceinline__ void wave_order() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -750,7 +750,7 @@ __device__ __forceinline__ void wave_transpose64(uint32_t& lo, uint32_t& hi) {
 
 // Writes the groups of the lanes in `lanes`: lane l's group covers output
 // positions G_l + j, j in [vlo_l, vhi_l), staged in its ring slots
-// (G_l + j) mod kRing. Each such lane posts (G, vlo | vhi << 8, lane) in
+// (G_l + j) mod kRing (word slot * 64 + l). Each such lane posts (G, vlo | vhi << 8, lane) in
 // LDS in lane order; four lanes then write each posted group, 16 bytes
 // each (word by word for a partial group).
 __device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf, uint4* desc,
@@ -763,17 +763,20 @@ __device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf
     desc[rank] = make_uint4(uint32_t(G), uint32_t(G >> 32), vlohi, uint32_t(lane));
   }
   wave_order();
+  constexpr uint32_t kLanesPerGroup = kGroup / 4, kGroupsPerStore = kWave / kLanesPerGroup;
   const uint32_t n = uint32_t(__popcll(lanes));
-  const uint32_t sub = uint32_t(lane) & 3u;
-  for (uint32_t g0 = 0; g0 < n; g0 += 16) {
-    const uint32_t gi = g0 + (uint32_t(lane) >> 2);
+  const uint32_t sub = uint32_t(lane) % kLanesPerGroup;
+  for (uint32_t g0 = 0; g0 < n; g0 += kGroupsPerStore) {
+    const uint32_t gi = g0 + uint32_t(lane) / kLanesPerGroup;
     if (gi < n) {
       const uint4 d = desc[gi];
       const uint64_t gs = (uint64_t(d.y) << 32) | d.x;
       const uint32_t vlo = d.z & 0xFFu, vhi = d.z >> 8;
       const uint32_t j0 = 4 * sub;
-      const uint4 v = *reinterpret_cast<const uint4*>(
-          buf + d.w * kRingStride + ((d.x + j0) & (kRing - 1)));
+      const uint32_t* src = buf + d.w;
+      const uint32_t s0 = (d.x + j0) & (kRing - 1);  // four slots, no wrap (s0 % 4 == 0)
+      const uint4 v = make_uint4(src[(s0 + 0) * kWave], src[(s0 + 1) * kWave],
+                                 src[(s0 + 2) * kWave], src[(s0 + 3) * kWave]);
       const uint64_t p = gs + j0;
       if (vlo == 0 && vhi == uint32_t(kGroup) && p + 3 < cap) {
         *reinterpret_cast<uint4*>(ids + p) = v;
@@ -795,7 +798,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
     const uint32_t* __restrict__ cm, const int64_t* __restrict__ toff, RowGeom g, uint64_t qmax,
     uint64_t cap, const float* __restrict__ screen, uint64_t nnz, uint32_t* __restrict__ ids,
     uint64_t* __restrict__ keys_out) {
-  __shared__ __align__(16) uint32_t s_buf[4][kWave * kRingStride];
+  __shared__ uint32_t s_buf[4][kRingSlots * kWave];
   __shared__ uint4 s_desc[4][kWave];
   const int lane = threadIdx.x & 63;
   // wave-uniform: the chunk walk below runs on scalar registers
@@ -804,7 +807,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
   const uint64_t Q = cq[g.R] < qmax ? cq[g.R] : qmax;
   if (q >= Q) return;  // the whole wave
   uint32_t* buf = s_buf[wv];
-  uint32_t* mine = buf + lane * kRingStride;
+  uint32_t* mine = buf + lane;  // slot s at mine[s * kWave]
   uint4* desc = s_desc[wv];
   const uint32_t rw = chunk_row(cq, g.R, q);
   const uint32_t w = rw % g.nwin, row = rw / g.nwin;
@@ -839,7 +842,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
       // one; slots past the k taken ones receive values that later entries
       // overwrite before any group holding them is written out
       const uint32_t slot0 = sp & (kRing - 1);
-      uint32_t* wp = mine + slot0;
+      uint32_t* wp = mine + slot0 * kWave;
       const uint32_t n = uint32_t(__popc(cw));
       const uint32_t k = n < uint32_t(kTake) ? n : uint32_t(kTake);
 #pragma unroll
@@ -848,7 +851,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
         // lane), its pair read from its lane
         const int i = i0 + int(__builtin_ctzg(cw, 32));
         const uint32_t v = uint32_t(__builtin_amdgcn_ds_bpermute(i * 4, int(val)));
-        wp[u] = v;
+        wp[u * kWave] = v;
         cw &= cw - 1u;
         if (KEYS && uint32_t(u) < k) {
           const uint64_t p = base + off + u;
@@ -857,8 +860,8 @@ __global__ __launch_bounds__(256) void k_row_expand(
         }
       }
       if (slot0 + k > uint32_t(kRing)) {  // wrapped: the overflow slots belong at the ring's start
-        const uint4 w = *reinterpret_cast<const uint4*>(mine + kRing);
-        *reinterpret_cast<uint4*>(mine) = w;
+#pragma unroll
+        for (int u = 0; u < kTake; ++u) mine[u * kWave] = mine[(kRing + u) * kWave];
       }
       const uint32_t sp2 = sp + k;
       // at most one group boundary is crossed per step: the group of the
