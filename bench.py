@@ -626,7 +626,7 @@ def run_config(cid, a, cpu_baseline_on, mode="train"):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "one GPU only: this build has no multi-GPU path; use --gpus 1"}))
+        print(json.dumps({"error": "one GPU only: the library has no multi-GPU path; use --gpus 1"}))
         sys.exit(2)
     import torch
 
