@@ -13,6 +13,8 @@
 // stably by tile id alone. Because each slot meets a tile at most once,
 // the result is exactly the stable sort of (tile << 32) | depth keys in
 // slot order, with a fraction of the bytes moved per intersection.
+#include <cstdlib>
+
 #include "gs_internal.h"
 
 namespace gs {
@@ -677,21 +679,29 @@ __global__ __launch_bounds__(256) void k_row_colscan(const uint64_t* __restrict_
 // two groups of 16 consecutive output positions (64 bytes, aligned),
 // slot-major (slot s of lane l at word s * 64 + l, so the lanes' writes of
 // one step fall in distinct banks whatever their slots); completed groups
-// are written out every few steps, kGroup / 4 lanes with one 16-byte
-// store each per group, 64 / (kGroup / 4) groups per store instruction. The groups at the two ends
-// of a lane's range are written in part, word by word. Writes are clamped
-// to `cap` entries; ids must be 16-byte aligned.
-constexpr int kGroup = 16;         // entries per written group
-constexpr int kRing = 2 * kGroup;  // staged entries per lane
-constexpr int kTake = 4;           // entries a lane takes per step (< kGroup)
-// steps between flushes of the completed groups: a lane's writes reach a
-// completed group's slots again only after kGroup - kTake + 1 more entries
-constexpr uint32_t kFlushEvery = (kGroup - kTake) / kTake;
-static_assert(kFlushEvery >= 1, "a completed group must survive until the flush");
+// are written out, GROUP / 4 lanes with one 16-byte store each per group,
+// 64 / (GROUP / 4) groups per store instruction. The groups at the two
+// ends of a lane's range are written in part, word by word. Writes are
+// clamped to `cap` entries; ids must be 16-byte aligned.
+// GROUP (entries per written group) is 16 (64 bytes, two groups in the
+// ring, completed groups written every kFlushEvery steps) or 32 (a whole
+// 128-byte line, one group filling the ring, written in the step that
+// completes it): 32 halves the write requests where a chunk's run per tile
+// is long, 16 writes fewer partial groups where it is short.
+constexpr int kRing = 32;  // staged entries per lane
+constexpr int kTake = 4;   // entries a lane takes per step
 // slots per lane: the ring, then kTake overflow slots (a step writes its
 // entries to consecutive slots from its first; entries past the ring's
-// end are copied to its start)
+// end are copied to its start once any group they complete is written)
 constexpr int kRingSlots = kRing + kTake;
+// steps between flushes of the completed groups: with two groups in the
+// ring a lane's writes reach a completed group's slots again only after
+// GROUP - kTake + 1 more entries; with one, the group goes in its step
+template <int GROUP>
+__host__ __device__ constexpr uint32_t flush_every() {
+  return GROUP >= kRing ? 1u : uint32_t(GROUP - kTake) / kTake;
+}
+static_assert(flush_every<16>() >= 1 && flush_every<32>() == 1, "");
 
 __device__ __forceinline__ void wave_order() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -753,6 +763,7 @@ __device__ __forceinline__ void wave_transpose64(uint32_t& lo, uint32_t& hi) {
 // (G_l + j) mod kRing (word slot * 64 + l). Each such lane posts (G, vlo | vhi << 8, lane) in
 // LDS in lane order; four lanes then write each posted group, 16 bytes
 // each (word by word for a partial group).
+template <int GROUP>
 __device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf, uint4* desc,
                                              uint64_t G, uint32_t vlohi, uint64_t cap,
                                              uint32_t* __restrict__ ids) {
@@ -763,7 +774,7 @@ __device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf
     desc[rank] = make_uint4(uint32_t(G), uint32_t(G >> 32), vlohi, uint32_t(lane));
   }
   wave_order();
-  constexpr uint32_t kLanesPerGroup = kGroup / 4, kGroupsPerStore = kWave / kLanesPerGroup;
+  constexpr uint32_t kLanesPerGroup = GROUP / 4, kGroupsPerStore = kWave / kLanesPerGroup;
   const uint32_t n = uint32_t(__popcll(lanes));
   const uint32_t sub = uint32_t(lane) % kLanesPerGroup;
   for (uint32_t g0 = 0; g0 < n; g0 += kGroupsPerStore) {
@@ -778,7 +789,7 @@ __device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf
       const uint4 v = make_uint4(src[(s0 + 0) * kWave], src[(s0 + 1) * kWave],
                                  src[(s0 + 2) * kWave], src[(s0 + 3) * kWave]);
       const uint64_t p = gs + j0;
-      if (vlo == 0 && vhi == uint32_t(kGroup) && p + 3 < cap) {
+      if (vlo == 0 && vhi == uint32_t(GROUP) && p + 3 < cap) {
         *reinterpret_cast<uint4*>(ids + p) = v;
       } else {
         const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
@@ -791,7 +802,7 @@ __device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf
   wave_order();
 }
 
-template <bool KEYS>
+template <bool KEYS, int GROUP>
 __global__ __launch_bounds__(256) void k_row_expand(
     const uint32_t* __restrict__ rkeys, const uint32_t* __restrict__ rvals,
     const int64_t* __restrict__ roff, const uint64_t* __restrict__ cq,
@@ -830,7 +841,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
     if (lanes) {
       const uint32_t vlo = pend_g < base ? uint32_t(base - pend_g) : 0u;
       wave_order();
-      flush_groups(lanes, buf, desc, pend_g, vlo | (uint32_t(kGroup) << 8), cap, ids);
+      flush_groups<GROUP>(lanes, buf, desc, pend_g, vlo | (uint32_t(GROUP) << 8), cap, ids);
     }
     pend = false;
     steps = 0;
@@ -859,24 +870,27 @@ __global__ __launch_bounds__(256) void k_row_expand(
             keys_out[p] = (uint64_t(t) << 32) | __float_as_uint(screen[uint64_t(v) * kRow + 6]);
         }
       }
-      if (slot0 + k > uint32_t(kRing)) {  // wrapped: the overflow slots belong at the ring's start
-#pragma unroll
-        for (int u = 0; u < kTake; ++u) mine[u * kWave] = mine[(kRing + u) * kWave];
-      }
       const uint32_t sp2 = sp + k;
       // at most one group boundary is crossed per step: the group of the
-      // 16 positions before it is complete, and waits for the next flush
-      if (((sp2 ^ sp) & ~uint32_t(kGroup - 1)) != 0u) {
+      // GROUP positions before it is complete, and waits for the next flush
+      if (((sp2 ^ sp) & ~uint32_t(GROUP - 1)) != 0u) {
         const uint64_t pos = base + off + k;
-        pend_g = (pos & ~uint64_t(kGroup - 1)) - kGroup;
+        pend_g = (pos & ~uint64_t(GROUP - 1)) - GROUP;
         pend = true;
       }
       sp = sp2;
       off += k;
       // A lane writes at most kTake entries, kTake - 1 slots ahead, per
-      // step, so a completed group's slots stay untouched for kFlushEvery
-      // more steps; a lane completes at most one group between flushes.
-      if (++steps == kFlushEvery) flush_pending();
+      // step, so a completed group's slots stay untouched for
+      // flush_every() more steps; a lane completes at most one group
+      // between flushes. Entries in the overflow slots belong to the group
+      // after any completed one, so they move to the ring's start after
+      // the flush.
+      if (++steps == flush_every<GROUP>()) flush_pending();
+      if (slot0 + k > uint32_t(kRing)) {  // wrapped: the overflow slots belong at the ring's start
+#pragma unroll
+        for (int u = 0; u < kTake; ++u) mine[u * kWave] = mine[(kRing + u) * kWave];
+      }
     }
   };
 
@@ -916,12 +930,12 @@ __global__ __launch_bounds__(256) void k_row_expand(
   flush_pending();
   // the partial last groups
   const uint64_t pos = base + off;
-  const bool part = off != 0 && (uint32_t(pos) & (kGroup - 1)) != 0u;
-  const uint64_t G = pos & ~uint64_t(kGroup - 1);
+  const bool part = off != 0 && (uint32_t(pos) & (GROUP - 1)) != 0u;
+  const uint64_t G = pos & ~uint64_t(GROUP - 1);
   const uint32_t vlo = G < base ? uint32_t(base - G) : 0u;
   const uint64_t rest = __ballot(part);
   wave_order();
-  flush_groups(rest, buf, desc, G, vlo | ((uint32_t(pos) & (kGroup - 1)) << 8), cap, ids);
+  flush_groups<GROUP>(rest, buf, desc, G, vlo | ((uint32_t(pos) & (GROUP - 1)) << 8), cap, ids);
 }
 
 __global__ __launch_bounds__(256) void k_compose_keys(const uint32_t* __restrict__ tkeys,
@@ -1214,13 +1228,26 @@ hipError_t launch_row_sort(const uint32_t* rkeys, const uint32_t* rvals, uint64_
                       reinterpret_cast<uint64_t*>(toff), reinterpret_cast<uint64_t*>(toff + n_tiles),
                       w.lb_t, w.ticket_t, err, s);
   if (e != hipSuccess) return e;
+  // 128-byte groups where a chunk's run per tile averages at least
+  // kLongRun entries (cap is the entry count here); GS_EXPAND_GROUP (16
+  // or 32) overrides the choice for sweeps
+  static const int group_env = [] {
+    const char* v = std::getenv("GS_EXPAND_GROUP");
+    const int x = v ? std::atoi(v) : 0;
+    return x == 16 || x == 32 ? x : 0;
+  }();
+  constexpr uint64_t kLongRun = 512;
+  const bool wide = group_env ? group_env == 32 : cap >= kLongRun * 64 * qmax;
   ProfScope prof("k_row_expand", s);
-  if (keys_out)
-    hipLaunchKernelGGL(k_row_expand<true>, grid, dim3(256), 0, s, rkeys, rvals, w.roff, w.cq, w.cm,
-                       toff, g, qmax, cap, screen, nnz, ids, keys_out);
-  else
-    hipLaunchKernelGGL(k_row_expand<false>, grid, dim3(256), 0, s, rkeys, rvals, w.roff, w.cq,
-                       w.cm, toff, g, qmax, cap, screen, nnz, ids, keys_out);
+#define GS_EXPAND(KEYS, GRP)                                                                    \
+  hipLaunchKernelGGL((k_row_expand<KEYS, GRP>), grid, dim3(256), 0, s, rkeys, rvals, w.roff,    \
+                     w.cq, w.cm, toff, g, qmax, cap, screen, nnz, ids, keys_out)
+  if (keys_out) {
+    if (wide) GS_EXPAND(true, 32); else GS_EXPAND(true, 16);
+  } else {
+    if (wide) GS_EXPAND(false, 32); else GS_EXPAND(false, 16);
+  }
+#undef GS_EXPAND
   return hipGetLastError();
 }
 
