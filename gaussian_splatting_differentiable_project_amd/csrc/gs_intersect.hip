@@ -615,15 +615,27 @@ __global__ __launch_bounds__(256) void k_row_count(const uint32_t* __restrict__ 
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  for (uint64_t i = s0 + lane; i < s1; i += 64) {
-    uint32_t a, b;
-    row_span(rkeys[i], g, a, b);
-    const uint32_t lo = w * 64, hi = lo + 64;
-    a = a > lo ? a : lo;
-    b = b < hi ? b : hi;
-    if (a < b) {
-      atomicAdd(&d[a - lo], 1u);
-      atomicAdd(&d[b - lo], 0xFFFFFFFFu);
+  // eight keys per lane in flight, then their counts
+  constexpr int kLoads = 8;
+  for (uint64_t i0 = s0 + lane; i0 < s1; i0 += 64 * kLoads) {
+    uint32_t kk[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const uint64_t i = i0 + uint64_t(j) * 64;
+      kk[j] = i < s1 ? rkeys[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      if (i0 + uint64_t(j) * 64 >= s1) break;
+      uint32_t a, b;
+      row_span(kk[j], g, a, b);
+      const uint32_t lo = w * 64, hi = lo + 64;
+      a = a > lo ? a : lo;
+      b = b < hi ? b : hi;
+      if (a < b) {
+        atomicAdd(&d[a - lo], 1u);
+        atomicAdd(&d[b - lo], 0xFFFFFFFFu);
+      }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
