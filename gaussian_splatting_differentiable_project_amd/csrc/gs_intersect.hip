@@ -1242,12 +1242,9 @@ hipError_t launch_row_sort(const uint32_t* rkeys, const uint32_t* rvals, uint64_
   if (e != hipSuccess) return e;
   // 128-byte groups where a chunk's run per tile averages at least
   // kLongRun entries (cap is the entry count here); GS_EXPAND_GROUP (16
-  // or 32) overrides the choice for sweeps
-  static const int group_env = [] {
-    const char* v = std::getenv("GS_EXPAND_GROUP");
-    const int x = v ? std::atoi(v) : 0;
-    return x == 16 || x == 32 ? x : 0;
-  }();
+  // or 32, read at each call) overrides the choice for sweeps and tests
+  const char* genv = std::getenv("GS_EXPAND_GROUP");
+  const int group_env = genv && (std::atoi(genv) == 16 || std::atoi(genv) == 32) ? std::atoi(genv) : 0;
   constexpr uint64_t kLongRun = 512;
   const bool wide = group_env ? group_env == 32 : cap >= kLongRun * 64 * qmax;
   ProfScope prof("k_row_expand", s);

@@ -428,14 +428,15 @@ int gs_profile_reset(void);
 int gs_profile_query(const char* kernel, int64_t* launches, double* total_ms);
 
 /* ---------------------------------------------------------------------
- * Launch-shape overrides for sweeps (environment, read once per process;
- * unset or any other value keeps the library's choice; results are the
- * same either way):
- *   GS_RASTER_PPT_FWD, GS_RASTER_PPT_BWD = 1, 2 or 4: pixels per lane of
- *     the raster kernels (4, 2 or 1 waves per tile).
- *   GS_EXPAND_GROUP = 16 or 32: entries per group the list expansion
- *     writes at once (64 or 128 bytes); by default 32 where a chunk's run
- *     per tile averages at least 512 entries.
+ * Launch-shape overrides for sweeps (environment; unset or any other
+ * value keeps the library's choice; results are the same either way):
+ *   GS_RASTER_PPT_FWD, GS_RASTER_PPT_BWD = 1, 2 or 4 (read once per
+ *     process): pixels per lane of the raster kernels (4, 2 or 1 waves
+ *     per tile).
+ *   GS_EXPAND_GROUP = 16 or 32 (read at each gs_intersect call): entries
+ *     per group the list expansion writes at once (64 or 128 bytes); by
+ *     default 32 where a chunk's run per tile averages at least 512
+ *     entries.
  * ------------------------------------------------------------------- */
 
 #ifdef __cplusplus

@@ -107,6 +107,26 @@ def test_intersect_sort_bit_exact(lib, name):
     check_intersect(sc, ref["proj"], ref["isect"])
 
 
+@pytest.mark.parametrize("with_keys", [False, True], ids=["ids", "ids+keys"])
+@pytest.mark.parametrize("group", [16, 32])
+@pytest.mark.parametrize("name", ["sh2-dense", "wide-2cam-4096px"])
+def test_intersect_expand_groups(lib, name, group, with_keys, monkeypatch):
+    """Both group sizes of the list expansion (64- and 128-byte groups;
+    the library takes 128 only for long runs per chunk and tile, which
+    only scenes of over 8M segments reach), forced through its override,
+    with and without the 64-bit keys: the same lists as the oracle."""
+    if name in WIDE:
+        sc = workloads.make_scene(WIDE[name])
+        proj = oracle.project(sc)
+        proj.screen = proj.screen.astype(np.float32).astype(np.float64)
+        isect = oracle.intersect(proj, sc["W"], sc["H"])
+    else:
+        sc, _, ref = reference(name)
+        proj, isect = ref["proj"], ref["isect"]
+    monkeypatch.setenv("GS_EXPAND_GROUP", str(group))
+    check_intersect(sc, proj, isect, with_keys=with_keys)
+
+
 # Scenes with many tiles (over 2^16 tile ids), so that the sort by tile id
 # takes its wider first digit and, past 2^18 tiles, more than one further
 # pass. Only projection and intersection are compared. The 65520-pixel-wide
@@ -200,7 +220,7 @@ def test_intersect_launch_order_sizes(lib, name):
     check_intersect(sc, proj, isect)
 
 
-def check_intersect(sc, proj, isect):
+def check_intersect(sc, proj, isect, with_keys=True):
     screen = P.to_dev(proj.screen.astype(np.float32))
     aabb = P.to_dev(P.u32_as_i32(proj.aabb16))
     cam = [0] + [int(np.searchsorted(proj.cam, c)) for c in range(1, sc["C"])] + [proj.nnz]
@@ -213,13 +233,14 @@ def check_intersect(sc, proj, isect):
     toff = torch.empty(n_tiles + 1, dtype=torch.int64, device="cuda")
     order = torch.empty(n_tiles, dtype=torch.int32, device="cuda")
     st, n_is, need = gsd.gs_intersect(C, W, H, proj.nnz, screen, aabb, cam, ws, ws_bytes, ids,
-                                      ids.numel(), toff, keys, order)
+                                      ids.numel(), toff, keys if with_keys else None, order)
     torch.cuda.synchronize()
     assert st == 0, gsd.status_str(st)
     assert n_is == isect.n_isects
     np.testing.assert_array_equal(toff.cpu().numpy(), isect.tile_offsets)
     np.testing.assert_array_equal(ids.cpu().numpy()[:n_is].view(np.uint32), isect.flatten_ids)
-    np.testing.assert_array_equal(keys.cpu().numpy()[:n_is].view(np.uint64), isect.sorted_keys)
+    if with_keys:
+        np.testing.assert_array_equal(keys.cpu().numpy()[:n_is].view(np.uint64), isect.sorted_keys)
     np.testing.assert_array_equal(order.cpu().numpy(), launch_order(isect.tile_offsets))
 
 
