@@ -715,6 +715,14 @@ __host__ __device__ constexpr uint32_t flush_every() {
 }
 static_assert(flush_every<16>() >= 1 && flush_every<32>() == 1, "");
 
+// Index of the lowest set bit of x, 0xFFFFFFFF for x == 0 (the hardware
+// instruction, without a clamp to 32).
+__device__ __forceinline__ uint32_t lowest_bit(uint32_t x) {
+  uint32_t r;
+  asm("v_ffbl_b32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 __device__ __forceinline__ void wave_order() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -845,12 +853,15 @@ __global__ __launch_bounds__(256) void k_row_expand(
 
   // Takes the segments of one 32-bit word of the transposed set (segment
   // indices i0 + bit) in order, kTake per step.
-  bool pend = false;      // a completed group awaits writing
-  uint64_t pend_g = 0;    // its first position
+  // a completed group awaits writing: at most one per lane between
+  // flushes, so it is the group before the one holding the lane's next
+  // position
+  bool pend = false;
   uint32_t steps = 0;     // steps since the last flush (uniform)
   auto flush_pending = [&]() {
     const uint64_t lanes = __ballot(pend);
     if (lanes) {
+      const uint64_t pend_g = ((base + off) & ~uint64_t(GROUP - 1)) - GROUP;
       const uint32_t vlo = pend_g < base ? uint32_t(base - pend_g) : 0u;
       wave_order();
       flush_groups<GROUP>(lanes, buf, desc, pend_g, vlo | (uint32_t(GROUP) << 8), cap, ids);
@@ -870,9 +881,10 @@ __global__ __launch_bounds__(256) void k_row_expand(
       const uint32_t k = n < uint32_t(kTake) ? n : uint32_t(kTake);
 #pragma unroll
       for (int u = 0; u < kTake; ++u) {
-        // the lowest remaining segment (32 once none remain: a harmless
-        // lane), its pair read from its lane
-        const int i = i0 + int(__builtin_ctzg(cw, 32));
+        // the lowest remaining segment, its pair read from its lane (once
+        // none remain, the lane below i0, a slot value later entries
+        // overwrite)
+        const int i = i0 + int(lowest_bit(cw));
         const uint32_t v = uint32_t(__builtin_amdgcn_ds_bpermute(i * 4, int(val)));
         wp[u * kWave] = v;
         cw &= cw - 1u;
@@ -885,11 +897,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
       const uint32_t sp2 = sp + k;
       // at most one group boundary is crossed per step: the group of the
       // GROUP positions before it is complete, and waits for the next flush
-      if (((sp2 ^ sp) & ~uint32_t(GROUP - 1)) != 0u) {
-        const uint64_t pos = base + off + k;
-        pend_g = (pos & ~uint64_t(GROUP - 1)) - GROUP;
-        pend = true;
-      }
+      pend = pend || ((sp2 ^ sp) & ~uint32_t(GROUP - 1)) != 0u;
       sp = sp2;
       off += k;
       // A lane writes at most kTake entries, kTake - 1 slots ahead, per
