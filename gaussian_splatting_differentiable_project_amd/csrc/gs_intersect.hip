@@ -735,47 +735,70 @@ __device__ __forceinline__ void wave_order() {
 template <int J>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
   const int v = int(x);
-  if constexpr (J == 1) return uint32_t(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));
-  if constexpr (J == 2) return uint32_t(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));
+  if constexpr (J == 1) return uint32_t(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, true));
+  if constexpr (J == 2) return uint32_t(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, true));
   if constexpr (J == 4) {  // l ^ 7 (half-row mirror), then l ^ 3 (quad_perm [3,2,1,0])
-    const int y = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false);
-    return uint32_t(__builtin_amdgcn_update_dpp(0, y, 0x1B, 0xf, 0xf, false));
+    const int y = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, true);
+    return uint32_t(__builtin_amdgcn_update_dpp(0, y, 0x1B, 0xf, 0xf, true));
   }
   if constexpr (J == 8) {  // l ^ 15 (row mirror), then l ^ 7 (half-row mirror)
-    const int y = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);
-    return uint32_t(__builtin_amdgcn_update_dpp(0, y, 0x141, 0xf, 0xf, false));
+    const int y = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, true);
+    return uint32_t(__builtin_amdgcn_update_dpp(0, y, 0x141, 0xf, 0xf, true));
   }
   if constexpr (J == 16) return uint32_t(__builtin_amdgcn_ds_swizzle(v, 0x401F));
   return uint32_t(__shfl_xor(v, 32, kWave));
 }
 
-// One step of the 64 x 64 bit transpose at scale J: lanes with bit J clear
-// keep their bits b with (b & J) == 0 (mask M) and take the partner's
-// such bits shifted up into the others; lanes with bit J set keep the
-// other bits and take the partner's shifted down.
-template <int J>
-__device__ __forceinline__ void transpose_step(uint32_t& lo, uint32_t& hi, uint64_t M, int lane) {
-  const uint32_t plo = lane_xor<J>(lo), phi = lane_xor<J>(hi);
-  const uint64_t p = (uint64_t(phi) << 32) | plo;
-  const uint64_t v = (uint64_t(hi) << 32) | lo;
-  const bool up = (lane & J) != 0;
-  const uint64_t t = up ? (p >> J) : (p << J);
-  const uint64_t keep = up ? ~M : M;
-  const uint64_t r = (v & keep) | (t & ~keep);
-  lo = uint32_t(r);
-  hi = uint32_t(r >> 32);
+// The 64 x 64 bit-matrix transpose across the wave: lane l holds row l
+// (bit b is element (l, b)); afterwards lane l holds column l. At each
+// scale J the lanes l and l ^ J swap their off-diagonal J x J blocks: the
+// lane with bit J clear keeps its bits b with (b & J) == 0 and sends the
+// others moved down by J; its partner keeps those others and sends its
+// bits with (b & J) == 0 moved up by J. For J <= 16 a moved bit stays in
+// its 2J-bit block, so inside one 32-bit word the move is a rotation, and
+// the bits received fill exactly the positions sent. `out[k]` and `rot[k]`
+// are the lane's sent bits and rotation for J = 16 >> k.
+struct TransposeLane {
+  uint32_t out[5], rot[5];
+};
+
+__device__ __forceinline__ TransposeLane transpose_lane(int lane) {
+  constexpr uint32_t kLow[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
+  TransposeLane c;
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const uint32_t J = 16u >> k;
+    const bool up = (uint32_t(lane) & J) != 0u;
+    c.out[k] = up ? kLow[k] : ~kLow[k];
+    c.rot[k] = up ? 32u - J : J;  // rotate right: up by J, or down by J
+  }
+  return c;
 }
 
-// 64 x 64 bit-matrix transpose across the wave: lane l holds row l (bit b
-// is element (l, b)); afterwards lane l holds column l.
-__device__ __forceinline__ void wave_transpose64(uint32_t& lo, uint32_t& hi) {
-  const int lane = __lane_id();
-  transpose_step<32>(lo, hi, 0x00000000FFFFFFFFull, lane);
-  transpose_step<16>(lo, hi, 0x0000FFFF0000FFFFull, lane);
-  transpose_step<8>(lo, hi, 0x00FF00FF00FF00FFull, lane);
-  transpose_step<4>(lo, hi, 0x0F0F0F0F0F0F0F0Full, lane);
-  transpose_step<2>(lo, hi, 0x3333333333333333ull, lane);
-  transpose_step<1>(lo, hi, 0x5555555555555555ull, lane);
+template <int J, int K>
+__device__ __forceinline__ uint32_t transpose_word(uint32_t w, const TransposeLane& c) {
+  const uint32_t sent = w & c.out[K];
+  const uint32_t got = lane_xor<J>(__builtin_amdgcn_alignbit(sent, sent, c.rot[K]));
+  return (w & ~c.out[K]) | got;
+}
+
+__device__ __forceinline__ void wave_transpose64(uint32_t& lo, uint32_t& hi,
+                                                 const TransposeLane& c) {
+  // J = 32: the lower half's high words trade with the upper half's low words
+  const bool up = __lane_id() >= 32;
+  const uint32_t got = lane_xor<32>(up ? lo : hi);
+  lo = up ? got : lo;
+  hi = up ? hi : got;
+  lo = transpose_word<16, 0>(lo, c);
+  hi = transpose_word<16, 0>(hi, c);
+  lo = transpose_word<8, 1>(lo, c);
+  hi = transpose_word<8, 1>(hi, c);
+  lo = transpose_word<4, 2>(lo, c);
+  hi = transpose_word<4, 2>(hi, c);
+  lo = transpose_word<2, 3>(lo, c);
+  hi = transpose_word<2, 3>(hi, c);
+  lo = transpose_word<1, 4>(lo, c);
+  hi = transpose_word<1, 4>(hi, c);
 }
 
 // Writes the groups of the lanes in `lanes`: lane l's group covers output
@@ -914,6 +937,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
     }
   };
 
+  const TransposeLane tl = transpose_lane(lane);
   // Segments are loaded kAhead batches of 64 at a time, the next group
   // while the current one is walked: a wait for loads also waits for every
   // store issued before it, so it comes once per group of batches.
@@ -942,7 +966,7 @@ __global__ __launch_bounds__(256) void k_row_expand(
       const uint64_t m = in ? segment_bits(ck[j], g, w) : 0ull;
       // lane i now holds the set of this batch's segments covering tile i
       uint32_t clo = uint32_t(m), chi = uint32_t(m >> 32);
-      wave_transpose64(clo, chi);
+      wave_transpose64(clo, chi, tl);
       take(clo, 0, cv[j]);
       take(chi, 32, cv[j]);
     }
