@@ -20,7 +20,7 @@ constexpr int kTile = GS_TILE;             // 16 x 16 pixels
 constexpr int kTilePix = kTile * kTile;
 constexpr int kRow = GS_ROW;               // floats per screen row
 constexpr float kNear = 0.01f;
-constexpr float kBlur = 0.3f;              // px^2 added to the 2D covariance
+constexpr double kBlur = 0.3;              // px^2 added to the 2D covariance (0.3 in the evaluating precision)
 constexpr float kAlphaMax = 0.99f;
 constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kTStop = 1e-4f;

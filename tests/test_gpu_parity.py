@@ -18,6 +18,17 @@ gsd = pytest.importorskip("gaussian_splatting_differentiable_project_amd")
 
 SCENES = list(workloads.SMALL.keys())
 
+# More than 64 cameras: the compaction reads the mask words 64 cameras at a
+# time. A wide view (every pair visible: dense waves, each lane walking the
+# cameras) and a narrow one (about a quarter visible: sparse waves, pairs
+# queued camera by camera).
+MANY_CAMS = {
+    "ring-70cam-wide": workloads.SceneSpec("sh1-1500-70cam-40x32-wide", 1500, 1, 70, 40, 32, 30.0,
+                                           1.0, -2.8, 0.4, 5.0, seed=2006),
+    "ring-70cam-narrow": workloads.SceneSpec("sh1-3000-70cam-40x32-narrow", 3000, 1, 70, 40, 32,
+                                             120.0, 2.0, -3.0, 0.4, 5.0, seed=2007),
+}
+
 
 @pytest.fixture(scope="module")
 def lib():
@@ -33,7 +44,8 @@ def reference(name):
     """Oracle results for one small scene (computed once per session), with
     the screen rows stored in fp32 as the method stores them."""
     if name not in _cache:
-        sc = workloads.make_scene(workloads.SMALL[name])
+        sc = workloads.make_scene(workloads.SMALL[name] if name in workloads.SMALL
+                                  else MANY_CAMS[name])
         L, grads, ref = oracle.loss_and_grads(sc, rows32=True)
         _cache[name] = (sc, grads, ref)
     return _cache[name]
@@ -43,7 +55,7 @@ def gpu_scene(sc):
     return gsd.Scene.from_numpy(sc, "cuda")
 
 
-@pytest.mark.parametrize("name", SCENES)
+@pytest.mark.parametrize("name", SCENES + list(MANY_CAMS))
 def test_project_mask_and_rows(lib, name):
     sc, _, ref = reference(name)
     proj = ref["proj"]
@@ -373,7 +385,7 @@ def test_project_bwd_stage(lib, name):
                                    atol=1e-30)
 
 
-@pytest.mark.parametrize("name", SCENES)
+@pytest.mark.parametrize("name", SCENES + list(MANY_CAMS))
 def test_end_to_end(lib, name):
     """Whole step on the GPU vs the whole oracle step."""
     sc, grads_o, ref = reference(name)
