@@ -272,11 +272,12 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
   }
 }
 
-// DPP lane permutations inside 16-lane rows (all lanes active).
+// DPP lane permutations inside 16-lane rows (all lanes active, every
+// source lane valid, so no old value is needed).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
 constexpr int kDppRowMirror = 0x140;      // lane reads 15 - l within its row
 constexpr int kDppRowHalfMirror = 0x141;  // lane reads 7 - l within its half-row
