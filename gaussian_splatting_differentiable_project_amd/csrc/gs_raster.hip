@@ -202,6 +202,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
   const float tx0 = float(tx * kTile) + 0.5f, ty0 = float(ty * kTile) + 0.5f;
   const float tx1 = fminf(tx0 + 15.f, float(W) - 0.5f), ylast = float(H) - 0.5f;
   const int wave = tid >> 6;
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(uint32_t(wave));
   for (int64_t b0 = start; b0 < end; b0 += B) {
     bool any_live = false;
 #pragma unroll
@@ -225,7 +226,8 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
     }
     __syncthreads();
     for (int j = 0; j < nb; ++j) {
-      const uint32_t rm = s_reach[j];
+      // the entry's strips, the same for every lane: tested on the scalar unit
+      const uint32_t rm = __builtin_amdgcn_readfirstlane(s_reach[j]);
       const float4 A = s_a[j], Bv = s_b[j];
       const float cblue = s_c[j];
       const float zj = DEPTH ? s_z[j] : 0.f;
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(kTilePix / PPT) void k_raster_fwd(
 #pragma unroll
       for (int k = 0; k < PPT; ++k) {
         // pixel k of this wave lies in strip wave + k * (waves per tile)
-        if (!((rm >> (wave + k * (NT / kWave))) & 1u)) continue;
+        if (!((rm >> (wave_u + k * (NT / kWave))) & 1u)) continue;
         const Eval e = eval_splat(ct, A, Bv, py[k]);
         const float Tn = Tr[k] * (1.f - e.alpha);
         const bool use = live[k] && e.alpha >= kAlphaMin;
