@@ -688,23 +688,24 @@ __global__ __launch_bounds__(256) void k_row_colscan(const uint64_t* __restrict_
 // (segment x tile) so that each lane holds the set of those segments
 // covering its tile, and takes them lowest first (up to four per step) as
 // its tile's next entries. A lane stages its entries in LDS, in a ring of
-// two groups of 16 consecutive output positions (64 bytes, aligned),
-// slot-major (slot s of lane l at word s * 64 + l, so the lanes' writes of
-// one step fall in distinct banks whatever their slots); completed groups
-// are written out, GROUP / 4 lanes with one 16-byte store each per group,
-// 64 / (GROUP / 4) groups per store instruction. The groups at the two
-// ends of a lane's range are written in part, word by word. Writes are
-// clamped to `cap` entries; ids must be 16-byte aligned.
-// GROUP (entries per written group) is 16 (64 bytes, two groups in the
-// ring, completed groups written every kFlushEvery steps) or 32 (a whole
-// 128-byte line, one group filling the ring, written in the step that
-// completes it): 32 halves the write requests where a chunk's run per tile
-// is long, 16 writes fewer partial groups where it is short.
+// 32 consecutive output positions (slot = position mod 32), slot-major
+// (slot s of lane l at word s * 64 + l, so the lanes' writes of one step
+// fall in distinct banks whatever their slots); completed aligned groups of
+// GROUP positions are written out, GROUP / 4 lanes with one 16-byte store
+// each per group, 64 / (GROUP / 4) groups per store instruction. The
+// groups at the two ends of a lane's range are written in part, word by
+// word. Writes are clamped to `cap` entries; ids must be 16-byte aligned.
+// GROUP is 16 (64 bytes, two groups in the ring, completed groups written
+// every flush_every<16>() steps) or 32 (a whole 128-byte line, one group
+// filling the ring, written in the step that completes it): 32 halves the
+// write requests where a chunk's run per tile is long, 16 writes fewer
+// partial groups where it is short.
 constexpr int kRing = 32;  // staged entries per lane
 constexpr int kTake = 4;   // entries a lane takes per step
 // slots per lane: the ring, then kTake overflow slots (a step writes its
 // entries to consecutive slots from its first; entries past the ring's
-// end are copied to its start once any group they complete is written)
+// end belong to the group after any completed one and move to the ring's
+// start after that group is written)
 constexpr int kRingSlots = kRing + kTake;
 // steps between flushes of the completed groups: with two groups in the
 // ring a lane's writes reach a completed group's slots again only after
