@@ -47,6 +47,14 @@ __device__ __forceinline__ uint32_t rect_count(const TileRect& r) {
 }
 
 // Inclusive running maximum over the 64 lanes.
+// All ones when bit b of x is set, else zero (a signed one-bit extract,
+// kept opaque so that a test of it stays one compare).
+__device__ __forceinline__ uint32_t bit_as_mask(uint32_t x, int b) {
+  uint32_t r;
+  asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(r) : "v"(x), "i"(b));
+  return r;
+}
+
 __device__ __forceinline__ uint32_t wave_incl_max_u32(uint32_t v) {
   const int l = __lane_id();
 #pragma unroll
@@ -402,26 +410,40 @@ __global__ __launch_bounds__(256) void k_emit_write(
       const uint32_t own = s_own[le] % WIN;  // window slot of the owner
       const uint32_t k = uint32_t(rb + le - s_off[own]);
       const uint32_t w = s_wx[own];
-      // k < 2^24 and w <= 4096: the fp32 quotient is within one of
-      // floor(k / w); two corrections each way make it exact
+      // k < w * wy with w, wy <= 4096: k / w is below 4096 and the fp32
+      // estimate (exact operands, reciprocal and product within 2^-22
+      // relative) is within 2^-10 of it, so its truncation is within one
+      // of floor(k / w); one correction each way makes it exact. Every
+      // product here is of values below 2^24 and stays below 2^32.
       uint32_t dy = uint32_t(float(k) * __builtin_amdgcn_rcpf(float(w)));
-      dy = dy * w > k ? dy - 1 : dy;
-      dy = dy * w > k ? dy - 1 : dy;
-      dy = (dy + 1) * w <= k ? dy + 1 : dy;
-      dy = (dy + 1) * w <= k ? dy + 1 : dy;
-      const uint32_t t = valid ? s_base[own] + dy * g.pitch + (k - dy * w) : 0u;
+      uint32_t dw = __umul24(dy, w);
+      const bool over = dw > k, under = dw + w <= k;
+      dy = over ? dy - 1 : under ? dy + 1 : dy;
+      dw = over ? dw - w : under ? dw + w : dw;
+      const uint32_t t = valid ? s_base[own] + __umul24(dy, g.pitch) + (k - dw) : 0u;
       key[i] = t;
       val[i] = s_slot[own];
       // rank among the wave's earlier entries with the same digit (digits
       // are below 2^bits, so the ballots of higher bits agree everywhere)
       const uint32_t d = t & M;
-      uint64_t peers = __ballot(valid);
+      const uint64_t vb = __ballot(valid);
+      uint32_t plo = uint32_t(vb), phi = uint32_t(vb >> 32);
+      // per bit, all ones where this lane's bit is set, else zero: a lane
+      // keeps the peers whose ballot bit equals its own (all ballots first,
+      // so the compares do not wait on each other's results)
+      uint32_t sm[DB];
+      uint64_t bb[DB];
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t bb = __ballot(bit);
-        peers &= bit ? bb : ~bb;
+        sm[b] = bit_as_mask(d, b);
+        bb[b] = __ballot(sm[b] != 0u);
       }
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        plo &= ~(uint32_t(bb[b]) ^ sm[b]);
+        phi &= ~(uint32_t(bb[b] >> 32) ^ sm[b]);
+      }
+      const uint64_t peers = (uint64_t(phi) << 32) | plo;
       const uint32_t before = s_whist[wave][d];
       const uint32_t r = uint32_t(__popcll(peers & lt));
       if (valid && r == 0) s_whist[wave][d] = uint16_t(before + uint32_t(__popcll(peers)));
