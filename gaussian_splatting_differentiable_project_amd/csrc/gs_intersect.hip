@@ -614,13 +614,16 @@ __global__ __launch_bounds__(256) void k_row_chunks(const int64_t* __restrict__ 
 
 // cm[q][i] = segments of chunk q covering tile i of its window. One wave
 // per chunk (the grid is an upper bound; waves past the last chunk
-// leave): every lane ORs the bit masks of its segments into 64 per-tile
-// counters kept as a difference array in LDS.
+// leave): every lane adds its segments into 64 per-tile counters kept as
+// a difference array in LDS. Only interior bounds go through LDS atomics:
+// a segment ending at the window's end needs no decrement (the counts
+// stop at tile 63), and those starting at the window's first tile, which
+// would all hit one word, are counted in a register and added once.
 __global__ __launch_bounds__(256) void k_row_count(const uint32_t* __restrict__ rkeys,
                                                   const int64_t* __restrict__ roff,
                                                   const uint64_t* __restrict__ cq, RowGeom g,
                                                   uint64_t qmax, uint32_t* __restrict__ cm) {
-  __shared__ uint32_t s_d[4][65];
+  __shared__ uint32_t s_d[4][64];
   const int lane = threadIdx.x & 63;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint64_t q = uint64_t(blockIdx.x) * 4 + wv;
@@ -633,7 +636,7 @@ __global__ __launch_bounds__(256) void k_row_count(const uint32_t* __restrict__ 
   const uint64_t e = uint64_t(roff[rw + 1]);
   const uint64_t s1 = s0 + g.K < e ? s0 + g.K : e;
   d[lane] = 0;
-  if (lane == 0) d[64] = 0;
+  uint32_t nf = 0;  // this lane's segments starting at tile 0 of the window
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -655,17 +658,19 @@ __global__ __launch_bounds__(256) void k_row_count(const uint32_t* __restrict__ 
       a = a > lo ? a : lo;
       b = b < hi ? b : hi;
       if (a < b) {
-        atomicAdd(&d[a - lo], 1u);
-        atomicAdd(&d[b - lo], 0xFFFFFFFFu);
+        if (a > lo) atomicAdd(&d[a - lo], 1u);
+        else ++nf;
+        if (b < hi) atomicAdd(&d[b - lo], 0xFFFFFFFFu);
       }
     }
   }
+  const uint32_t n_first = __builtin_amdgcn_readlane(wave_incl_scan_u32(nf), 63);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // counts = inclusive prefix of the differences (modulo 2^32, exact for
   // the true counts)
-  cm[q * 64 + lane] = wave_incl_scan_u32(d[lane]);
+  cm[q * 64 + lane] = wave_incl_scan_u32(d[lane] + (lane == 0 ? n_first : 0u));
 }
 
 // Per (window, tile): the exclusive scan of cm over the window's chunks,
