@@ -99,6 +99,179 @@ __global__ __launch_bounds__(kMaskGroup) void k_project_mask(ProjectArgs a, uint
   }
 }
 
+// Mask pass for 2 to kMaskFastCams cameras. A bound test settles most
+// pairs in fp32 from the Gaussian's position and largest scale alone;
+// only the others run the full projection of k_project_mask, queued per
+// block so that every lane of a pass has a pair. (With one camera there is
+// nothing to share the Gaussian's loads across, and the camera-walking
+// kernel is faster.)
+//
+// The bounds are those of the fp64 projection, for any input:
+//  - each fp64 camera-space coordinate lies within e = 2^-21 (max|R|
+//    (|mx| + |my| + |mz|) + max|t|) of its fp32 value (three fused
+//    roundings, each at most 2^-24 of that sum);
+//  - for z > e the fp64 ratio x / z lies within da = e (z + |x|) /
+//    (z (z - e)) of the fp32 one (plus that ratio's own rounding), so the
+//    fp64 centre lies within tu = |fx| da (plus rounding margins) of the
+//    fp32 centre u;
+//  - the radius is 3 sqrt(lambda_max) and lambda_max is at most the trace
+//    of the 2D covariance, |J R_cam M|_F^2 + 2 blur, with |J R_cam M|_F at
+//    most |J R_cam|_F max(s); the rows of J R_cam are (f / z) (R_i - (x /
+//    z) R_2), bounded through the row norms with |x / z| <= |x / z| + da
+//    and 1 / z <= 1 / (z - e).
+// A pair past the near test is visible in fp64 when its centre is inside
+// the image: the radius is then positive, and a radius that is not finite
+// also leaves the clamped box non-empty. It is invisible when the centre
+// lies farther outside than the bounded radius, which is taken only when
+// the fp64 radius is sure to be finite: a finite, non-zero squared
+// quaternion norm and finite scales in fp32 (no log scale NaN). The
+// largest scale is exp of the largest log scale (exp is monotonic; the
+// fp32 value is within 2 ulp). All other pairs are queued.
+constexpr int kMaskFastCams = 64;
+constexpr int kMaskCam = 24;  // floats per staged camera: R, t, fx, fy, cx, cy, 2^-21 max|R|,
+                              // 2^-21 max|t|, row norms of R, fx^2, fy^2, pad
+
+size_t mask_fast_lds(int C) {
+  return size_t(C) * (2 * sizeof(uint64_t) + kMaskCam * sizeof(float) +
+                      kMaskGroup * sizeof(uint16_t));
+}
+
+__device__ __forceinline__ Camera mask_camera(const float* sc) {
+  Camera k;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) k.R[i] = sc[i];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) k.t[i] = sc[9 + i];
+  k.fx = sc[12], k.fy = sc[13], k.cx = sc[14], k.cy = sc[15];
+  k.cc[0] = k.cc[1] = k.cc[2] = 0.f;  // not read by the projection
+  return k;
+}
+
+__global__ __launch_bounds__(kMaskGroup) void k_project_mask_fast(ProjectArgs a, uint64_t* mask) {
+  extern __shared__ __align__(16) uint64_t s_mdyn[];
+  const int C = a.C;
+  uint64_t* s_vis = s_mdyn;                                           // [C][2] mask words
+  float* s_cam = reinterpret_cast<float*>(s_mdyn + 2 * C);            // [C][kMaskCam]
+  uint16_t* s_q = reinterpret_cast<uint16_t*>(s_cam + kMaskCam * C);  // queued camera << 7 | lane
+  __shared__ uint32_t s_qn;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t g = int64_t(blockIdx.x) * kMaskGroup + tid;
+  const bool valid = g < a.N;
+  if (tid < C) {
+    const Camera k = load_camera(a.viewmats, a.Ks, tid);
+    float* sc = s_cam + tid * kMaskCam;
+    float rm = 0.f, tm = 0.f;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      sc[i] = k.R[i];
+      rm = fmaxf(rm, fabsf(k.R[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      sc[9 + i] = k.t[i];
+      tm = fmaxf(tm, fabsf(k.t[i]));
+      sc[18 + i] = sqrtf(k.R[3 * i] * k.R[3 * i] + k.R[3 * i + 1] * k.R[3 * i + 1] +
+                         k.R[3 * i + 2] * k.R[3 * i + 2]) * (1.f + 1e-6f);
+    }
+    sc[12] = k.fx, sc[13] = k.fy, sc[14] = k.cx, sc[15] = k.cy;
+    sc[16] = 0x1p-21f * rm;
+    sc[17] = 0x1p-21f * tm;
+    sc[21] = k.fx * k.fx, sc[22] = k.fy * k.fy, sc[23] = 0.f;
+  }
+  if (tid == 0) s_qn = 0;
+  float mx = 0.f, my = 0.f, mz = 0.f, smax2 = 0.f;
+  bool finite_r = false;
+  if (valid) {
+    mx = a.means[3 * g + 0], my = a.means[3 * g + 1], mz = a.means[3 * g + 2];
+    const float4 q = reinterpret_cast<const float4*>(a.quats)[g];
+    const float l0 = a.log_scales[3 * g + 0], l1 = a.log_scales[3 * g + 1],
+                l2 = a.log_scales[3 * g + 2];
+    const float smax = expf(fmaxf(fmaxf(l0, l1), l2));
+    smax2 = smax * smax;
+    const float qn2 = q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w;
+    const float lsum = l0 + l1 + l2;
+    finite_r = qn2 > 0.f && qn2 < 3e38f && smax2 < 3e38f && lsum == lsum;
+  }
+  const float m1 = fabsf(mx) + fabsf(my) + fabsf(mz);
+  const float Wf = float(a.W), Hf = float(a.H);
+  const uint64_t lt = lanemask_lt();
+  __syncthreads();
+
+  for (int c = 0; c < C; ++c) {
+    const float* sc = s_cam + c * kMaskCam;
+    const Camera k = mask_camera(sc);
+    const float ra = sc[16], ta = sc[17], n0 = sc[18], n1 = sc[19], n2 = sc[20];
+    const float fx2 = sc[21], fy2 = sc[22];
+    const float z32 = depth_z32(k, mx, my, mz);
+    bool sure_vis = false, need = false;
+    if (valid && z32 > kNear) {
+      const float x = fmaf(k.R[0], mx, fmaf(k.R[1], my, fmaf(k.R[2], mz, k.t[0])));
+      const float y = fmaf(k.R[3], mx, fmaf(k.R[4], my, fmaf(k.R[5], mz, k.t[1])));
+      const float z = fmaf(k.R[6], mx, fmaf(k.R[7], my, fmaf(k.R[8], mz, k.t[2])));
+      const float e = fmaf(ra, m1, ta);
+      const float zl = z - e;
+      bool sure_inv = false;
+      if (zl > 0.f) {
+        const float iz = __builtin_amdgcn_rcpf(z), izl = __builtin_amdgcn_rcpf(zl);
+        const float q = e * iz * izl;
+        const float ax = x * iz, ay = y * iz;
+        const float dax = fmaf(q, z + fabsf(x), 2.5e-7f * fabsf(ax)) * 1.01f;
+        const float day = fmaf(q, z + fabsf(y), 2.5e-7f * fabsf(ay)) * 1.01f;
+        const float u = fmaf(k.fx, ax, k.cx), v = fmaf(k.fy, ay, k.cy);
+        const float tu = fmaf(fabsf(k.fx), dax, 1e-6f * (fabsf(u) + fabsf(k.cx) + 1.f));
+        const float tv = fmaf(fabsf(k.fy), day, 1e-6f * (fabsf(v) + fabsf(k.cy) + 1.f));
+        sure_vis = u - tu > 0.f && u + tu < Wf && v - tv > 0.f && v + tv < Hf;
+        const float r0 = fmaf(fabsf(ax) + dax, n2, n0), r1 = fmaf(fabsf(ay) + day, n2, n1);
+        const float j2 = (fx2 * r0 * r0 + fy2 * r1 * r1) * (izl * izl);
+        const float rup = 3.f * __builtin_amdgcn_sqrtf(fmaf(j2, smax2, 0.6f) * 1.01f);
+        sure_inv = finite_r && (u + tu + rup < 0.f || u - tu - rup > Wf || v + tv + rup < 0.f ||
+                                v - tv - rup > Hf);
+      }
+      need = !(sure_vis || sure_inv);
+    }
+    const uint64_t nb = __ballot(need);
+    if (nb) {  // wave-uniform
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&s_qn, uint32_t(__popcll(nb)));
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (need) s_q[base + uint32_t(__popcll(nb & lt))] = uint16_t((c << 7) | tid);
+    }
+    const uint64_t word = __ballot(sure_vis);
+    if (lane == 0) s_vis[2 * c + wave] = word;
+  }
+  __syncthreads();
+
+  // the queued pairs, one per lane: the camera-walking kernel's test
+  const uint32_t qn = s_qn;
+  for (uint32_t i = uint32_t(tid); i < qn; i += kMaskGroup) {
+    const uint32_t it = s_q[i];
+    const int c = int(it >> 7), t = int(it & 127u);
+    const int64_t gt = int64_t(blockIdx.x) * kMaskGroup + t;
+    GaussLocal<float> G1;
+    gauss_local(a.means, a.quats, a.log_scales, gt, G1);
+    const Camera k = mask_camera(s_cam + c * kMaskCam);
+    PairFwd<float> Pf;
+    pair_fwd(k, G1, Wf, Hf, Pf);
+    bool unsure;
+    bool vis = visible_fp32(Pf, k.cx, k.cy, Wf, Hf, &unsure);
+    if (unsure) {
+      GaussLocal<double> G;
+      gauss_local(a.means, a.quats, a.log_scales, gt, G);
+      PairFwd<double> P;
+      pair_fwd(k, G, double(a.W), double(a.H), P);
+      vis = P.visible;
+    }
+    if (vis)
+      atomicOr(reinterpret_cast<unsigned long long*>(&s_vis[2 * c + (t >> 6)]),
+               1ull << (t & 63));
+  }
+  __syncthreads();
+  for (int i = tid; i < 2 * C; i += kMaskGroup) {
+    const int64_t p0 = int64_t(i >> 1) * a.N_pad + int64_t(blockIdx.x) * kMaskGroup;
+    mask[p0 / 64 + (i & 1)] = s_vis[i];
+  }
+}
+
 // One visible pair: its fp32 screen row and 16-bit box at slot `slot`.
 // fp64 arithmetic, rounded once into the fp32 row (see the mask pass).
 // G carries the Gaussian's position and M = Rq diag(s), the only parts
@@ -465,7 +638,11 @@ hipError_t launch_project_mask(const ProjectArgs& a, uint64_t* mask, hipStream_t
   if (blocks == 0) return hipSuccess;
   if (!fits_dispatch(uint64_t(blocks), kMaskGroup)) return hipErrorInvalidConfiguration;
   ProfScope prof("k_project_mask", s);
-  hipLaunchKernelGGL(k_project_mask, dim3(uint32_t(blocks)), dim3(kMaskGroup), 0, s, a, mask);
+  if (a.C >= 2 && a.C <= kMaskFastCams)
+    hipLaunchKernelGGL(k_project_mask_fast, dim3(uint32_t(blocks)), dim3(kMaskGroup),
+                       mask_fast_lds(a.C), s, a, mask);
+  else
+    hipLaunchKernelGGL(k_project_mask, dim3(uint32_t(blocks)), dim3(kMaskGroup), 0, s, a, mask);
   return hipGetLastError();
 }
 

@@ -21,8 +21,11 @@ SCENES = list(workloads.SMALL.keys())
 # More than 64 cameras: the compaction reads the mask words 64 cameras at a
 # time. A wide view (every pair visible: dense waves, each lane walking the
 # cameras) and a narrow one (about a quarter visible: sparse waves, pairs
-# queued camera by camera).
+# queued camera by camera). 64 cameras: the most the bound-test mask pass
+# takes (its queue entries hold the camera in 6 bits).
 MANY_CAMS = {
+    "ring-64cam-narrow": workloads.SceneSpec("sh1-3000-64cam-40x32-narrow", 3000, 1, 64, 40, 32,
+                                             120.0, 2.0, -3.0, 0.4, 5.0, seed=2008),
     "ring-70cam-wide": workloads.SceneSpec("sh1-1500-70cam-40x32-wide", 1500, 1, 70, 40, 32, 30.0,
                                            1.0, -2.8, 0.4, 5.0, seed=2006),
     "ring-70cam-narrow": workloads.SceneSpec("sh1-3000-70cam-40x32-narrow", 3000, 1, 70, 40, 32,
