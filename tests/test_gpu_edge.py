@@ -195,3 +195,65 @@ def test_forward_and_sort_are_deterministic(lib):
                                                       it.sorted_keys, it.tile_offsets, rgb, T, last)])
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_mask_bound_adversarial(lib):
+    """The visibility mask on inputs chosen against the bound test of the
+    2-64-camera mask pass (three cameras here): a scaled and sheared camera
+    rotation, a camera a thousand units from the origin (large world
+    coordinates), centres within a pixel of the image edges, depths about
+    the near plane with large lateral offsets, splats from 1e-6 to 55
+    units, elongated ones, and quaternion norms from 1e-15 to 1e15. The
+    mask must equal the fp64 oracle's outside fragile pairs."""
+    rng = np.random.default_rng(77)
+    W, H, f = 96, 64, 80.0
+    K = intrinsics(f, f, W, H)
+    V0 = workloads.lookat_viewmat((0.0, 0.0, 5.0))
+    V1 = V0.copy()
+    V1[:3, :3] *= 2.5
+    V1[0, 1] += 0.7
+    V2 = workloads.lookat_viewmat((900.0, -400.0, 1200.0), target=(880.0, -390.0, 1170.0))
+    views = [V0, V1, V2]
+
+    def to_world(V, p):  # camera-space points -> world, through the (maybe skewed) view
+        return np.linalg.solve(V[:3, :3], (p - V[:3, 3]).T).T
+
+    def cam_points(n, z_lo, z_hi, u, v):
+        z = rng.uniform(z_lo, z_hi, n)
+        return np.stack([(u - K[0, 2]) * z / f, (v - K[1, 2]) * z / f, z], 1)
+
+    groups = []
+    n = 600
+    groups.append(rng.uniform(-1.5, 1.5, (n, 3)))                          # a cloud at the origin
+    for V in views:
+        # centres within a pixel of each edge
+        u = np.concatenate([rng.uniform(-1, 1, n // 4), W + rng.uniform(-1, 1, n // 4),
+                            rng.uniform(0, W, n // 2)])
+        v = np.concatenate([rng.uniform(0, H, n // 2), rng.uniform(-1, 1, n // 4),
+                            H + rng.uniform(-1, 1, n // 4)])
+        groups.append(to_world(V, cam_points(n, 0.5, 50.0, u, v)))
+        # about the near plane, centres anywhere from far outside to inside
+        groups.append(to_world(V, cam_points(n, 0.0099, 0.03, rng.uniform(-3 * W, 4 * W, n),
+                                             rng.uniform(-3 * H, 4 * H, n))))
+    means = np.concatenate(groups)
+    N = means.shape[0]
+    q = rng.normal(size=(N, 4))
+    q *= (10.0 ** rng.uniform(-15, 15, N))[:, None] / np.linalg.norm(q, axis=1, keepdims=True)
+    ls = rng.uniform(-14.0, 4.0, (N, 1)) + np.zeros((N, 3))
+    elong = rng.random(N) < 0.3
+    ls[elong, 1:] -= 8.0
+    sc = make_scene_from(means, q, ls, rng.normal(size=N), rng.normal(size=(N, 1, 3)) * 0.1,
+                         np.stack(views), np.stack([K] * 3), W, H, 0)
+    proj = oracle.project(sc)
+    r = gsd.Rasterizer()
+    p = r.project(gsd.Scene.from_numpy(sc))
+    torch.cuda.synchronize()
+    n_pairs = sc["C"] * proj.N_pad
+    vis_gpu = P.unpack_mask(p.mask.cpu().numpy(), n_pairs)
+    frag = P.fragile_pairs(sc, proj)
+    diff = vis_gpu != proj.visible_pairs
+    print(f"adversarial: N={N} nnz gpu={p.nnz} oracle={proj.nnz} fragile={int(frag.sum())} "
+          f"mask diffs={int(diff.sum())} (fragile among them={int((diff & frag).sum())})")
+    assert not (diff & ~frag).any(), np.flatnonzero(diff & ~frag)[:10]
+    # the scene reaches both verdicts, and most pairs are not fragile
+    assert N // 2 < proj.nnz < sc["C"] * N - N // 2 and int(frag.sum()) < N // 10
