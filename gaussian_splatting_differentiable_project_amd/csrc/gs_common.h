@@ -89,6 +89,27 @@ __device__ __forceinline__ uint64_t lookback_prefix(const uint64_t* lb, int64_t 
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Non-temporal vector stores, for outputs written once and not read again
+// by the kernel that writes them (the sorted list's lines, the gradient
+// rows): they stream past the caches instead of taking lines from data
+// the kernel still reads.
+__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) {
+  __builtin_nontemporal_store(v, p);
+}
+__device__ __forceinline__ void store_stream(float* p, float v) {
+  __builtin_nontemporal_store(v, p);
+}
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(float4* p, float4 v) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = __lane_id();
   return l == 0 ? 0ull : (~0ull >> (64 - l));

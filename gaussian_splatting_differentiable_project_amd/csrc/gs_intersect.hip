@@ -833,7 +833,7 @@ __device__ __forceinline__ void wave_transpose64(uint32_t& lo, uint32_t& hi,
 // positions G_l + j, j in [vlo_l, vhi_l), staged in its ring slots
 // (G_l + j) mod kRing (word slot * 64 + l). Each such lane posts (G, vlo | vhi << 8, lane) in
 // LDS in lane order; four lanes then write each posted group, 16 bytes
-// each (word by word for a partial group).
+// each (word by word for a partial group), as non-temporal stores.
 template <int GROUP>
 __device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf, uint4* desc,
                                              uint64_t G, uint32_t vlohi, uint64_t cap,
@@ -861,12 +861,12 @@ __device__ __forceinline__ void flush_groups(uint64_t lanes, const uint32_t* buf
                                  src[(s0 + 2) * kWave], src[(s0 + 3) * kWave]);
       const uint64_t p = gs + j0;
       if (vlo == 0 && vhi == uint32_t(GROUP) && p + 3 < cap) {
-        *reinterpret_cast<uint4*>(ids + p) = v;
+        store_stream(reinterpret_cast<uint4*>(ids + p), v);
       } else {
         const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (uint32_t u = 0; u < 4; ++u)
-          if (j0 + u >= vlo && j0 + u < vhi && p + u < cap) ids[p + u] = vv[u];
+          if (j0 + u >= vlo && j0 + u < vhi && p + u < cap) store_stream(ids + p + u, vv[u]);
       }
     }
   }

@@ -253,11 +253,11 @@ __device__ __forceinline__ void finish_gaussian(int64_t g, bool any, const Gauss
   } else {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      v_means[3 * g + j] = gmu[j];
-      v_log_scales[3 * g + j] = gls[j];
+      store_stream(v_means + 3 * g + j, gmu[j]);
+      store_stream(v_log_scales + 3 * g + j, gls[j]);
     }
-    reinterpret_cast<float4*>(v_quats)[g] = make_float4(gq[0], gq[1], gq[2], gq[3]);
-    v_opacity_logits[g] = glogit;
+    store_stream(reinterpret_cast<float4*>(v_quats) + g, make_float4(gq[0], gq[1], gq[2], gq[3]));
+    store_stream(v_opacity_logits + g, glogit);
   }
 }
 
@@ -329,8 +329,10 @@ __device__ __forceinline__ void store_sh_rows(float* stage, const float* gsh, in
             if (accumulate) {
               const float4 y = dst[q];
               x.x += y.x, x.y += y.y, x.z += y.z, x.w += y.w;
+              dst[q] = x;
+            } else {
+              store_stream(dst + q, x);
             }
-            dst[q] = x;
           }
         } else {
           for (int i = lane; i < n; i += kWave) {
