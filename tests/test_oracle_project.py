@@ -106,6 +106,46 @@ def test_visibility_cases():
     assert (pc["u"][0] - pc["r"][0] < W) == bool(pc["visible"][0])
 
 
+def test_radius_bound_and_centre_rule():
+    """Two facts a visibility test may use to settle pairs early, checked on
+    the fp64 projection: the screen radius 3 sqrt(lambda_max) is at most
+    3 sqrt(|J R_cam|_F^2 max(s)^2 + 2 blur) (lambda_max is at most the 2D
+    covariance's trace, |J R_cam M|_F^2 + 2 blur, and |J R_cam M|_F is at
+    most |J R_cam|_F |M|_2 with |M|_2 = max(s) for a rotation times a
+    diagonal), including for a camera matrix that is not a rotation; and a
+    pair past the near plane whose centre lies inside the image is visible
+    whatever its size."""
+    rng = np.random.default_rng(11)
+    W, H = 160, 120
+    n = 20000
+    for skew in (False, True):
+        vm = workloads.lookat_viewmat((0.3, -0.2, 4.0))
+        if skew:
+            vm[:3, :3] *= 1.7
+            vm[0, 1] += 0.6
+            vm[2, 0] -= 0.3
+        means = rng.uniform(-3, 3, (n, 3))
+        quats = rng.normal(size=(n, 4)) * (10.0 ** rng.uniform(-6, 6, n))[:, None]
+        ls = rng.uniform(-9, 2, (n, 3))
+        K = intrinsics(rng.uniform(60, 400), rng.uniform(60, 400), W, H)
+        pc = project_camera(means, quats, ls, np.zeros(n), np.zeros((n, 1, 3)), vm, K, W, H, 0)
+        front = pc["z"] > 0.05
+        R = np.asarray(vm, np.float64)[:3, :3]
+        x, y, z = pc["x"], pc["y"], pc["z"]
+        JR0 = (K[0, 0] / z)[:, None] * (R[0][None, :] - (x / z)[:, None] * R[2][None, :])
+        JR1 = (K[1, 1] / z)[:, None] * (R[1][None, :] - (y / z)[:, None] * R[2][None, :])
+        jr2 = (JR0 ** 2).sum(1) + (JR1 ** 2).sum(1)
+        smax = np.exp(np.asarray(ls, np.float64).max(1))
+        bound = 3.0 * np.sqrt(jr2 * smax ** 2 + 2 * 0.3)
+        r = pc["r"]
+        assert np.all(r[front] <= bound[front] * (1 + 1e-12)), np.max(r[front] / bound[front])
+        # the bound is not vacuous: within a factor 3 for most pairs
+        assert np.median(bound[front] / r[front]) < 3.0
+        inside = front & (pc["z32"] > 0.01) & (pc["u"] > 0) & (pc["u"] < W) & (pc["v"] > 0) & (pc["v"] < H)
+        assert inside.sum() > 1000 and np.all(pc["visible"][inside])
+
+
+
 @pytest.mark.parametrize("name", ["tiny", "multicam", "sh1-odd-n"])
 def test_compaction_invariants(name):
     sc = workloads.make_scene(workloads.SMALL[name])
