@@ -534,13 +534,19 @@ int ppt_from_env(const char* name, int dflt) {
 // 15M 5-camera (21,730) 0.72 -> 0.58 ms, 7680x7680 (230,400) 4.10 ->
 // 3.49 ms; 1920x1080 (8,160) even; 128x128 (64) 0.14 -> 0.20 ms.
 constexpr int64_t kFwdManyTiles = 16384;
-constexpr int kBwdPPT = 4;
+
+// Backward: one wave per tile (four pixels per lane: the per-entry
+// reduction and atomics are paid once per 256 pixels) once there are
+// enough tiles to fill the chip; with few tiles, more waves per tile.
+// Measured: 1920x1080 (8,160 tiles) 0.43 ms at four pixels per lane, 0.49
+// at two, 0.59 at one; 128x128 (64 tiles) 0.50, 0.37, 0.25 ms.
+inline int bwd_ppt(int64_t tiles) { return tiles >= 2048 ? 4 : tiles >= 512 ? 2 : 1; }
 
 hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uint32_t* ids,
                              const int64_t* toff, const uint32_t* order, const float* background,
                              float* out_rgb, float* out_T, float* out_depth, int32_t* last_ids,
                              hipStream_t s) {
-  static const int ppt_env = ppt_from_env("GS_RASTER_PPT_FWD", 0);
+  const int ppt_env = ppt_from_env("GS_RASTER_PPT_FWD", 0);
   const int tiles_x = (W + kTile - 1) / kTile, tiles_y = (H + kTile - 1) / kTile;
   const int T = tiles_x * tiles_y;
   const int64_t blocks = int64_t(C) * T;
@@ -566,11 +572,12 @@ hipError_t launch_raster_bwd(int C, int W, int H, const float* screen, const uin
                              const float* out_T, const int32_t* last_ids, const float* v_rgb,
                              const float* v_T, const float* v_depth, float* v_screen,
                              float* v_background, hipStream_t s) {
-  static const int ppt = ppt_from_env("GS_RASTER_PPT_BWD", kBwdPPT);
+  const int ppt_env = ppt_from_env("GS_RASTER_PPT_BWD", 0);
   const int tiles_x = (W + kTile - 1) / kTile, tiles_y = (H + kTile - 1) / kTile;
   const int T = tiles_x * tiles_y;
   const int64_t blocks = int64_t(C) * T;
   if (blocks == 0) return hipSuccess;
+  const int ppt = ppt_env ? ppt_env : bwd_ppt(blocks);
   if (!fits_dispatch(uint64_t(blocks), kTilePix)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)};
 #define GS_BWD(P, D)                                                                           \

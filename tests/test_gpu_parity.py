@@ -333,6 +333,19 @@ def test_raster_fwd_stage_many_tiles(lib):
 @pytest.mark.parametrize("ordered", [False, True], ids=["id-order", "heavy-first"])
 @pytest.mark.parametrize("name", SCENES)
 def test_raster_bwd_stage(lib, name, ordered):
+    check_raster_bwd(name, ordered)
+
+
+# Every width of the backward kernel (the library picks one by tile count:
+# these scenes alone would only reach one pixel per lane).
+@pytest.mark.parametrize("ppt", [1, 2, 4])
+@pytest.mark.parametrize("name", ["tiny", "multicam", "sh2-dense"])
+def test_raster_bwd_widths(lib, name, ppt, monkeypatch):
+    monkeypatch.setenv("GS_RASTER_PPT_BWD", str(ppt))
+    check_raster_bwd(name, True)
+
+
+def check_raster_bwd(name, ordered):
     sc, _, ref = reference(name)
     proj, isect = ref["proj"], ref["isect"]
     C, W, H = sc["C"], sc["W"], sc["H"]
