@@ -528,12 +528,14 @@ int ppt_from_env(const char* name, int dflt) {
   return (p == 1 || p == 2 || p == 4) ? p : dflt;
 }
 
-// Forward: four waves per tile while tiles are few, two (two pixels per
-// lane, half the staging and barrier work per pixel) from kFwdManyTiles
-// tiles on. Measured: 5-camera 1600x1064 (33,500 tiles) 1.11 -> 0.92 ms,
-// 15M 5-camera (21,730) 0.72 -> 0.58 ms, 7680x7680 (230,400) 4.10 ->
-// 3.49 ms; 1920x1080 (8,160) even; 128x128 (64) 0.14 -> 0.20 ms.
-constexpr int64_t kFwdManyTiles = 16384;
+// Forward: four waves per tile while tiles are few, then two (two pixels
+// per lane, half the staging and barrier work per pixel), then one. Measured
+// (ms at 1 / 2 / 4 pixels per lane): 640x480, 1,200 tiles, 0.106 / 0.110 /
+// 0.166; 1024x512, 2,048 tiles, 0.105 / 0.096 / 0.117; 1920x1080, 8,160
+// tiles, 0.234 / 0.192 / 0.196; 5-camera 1600x1064, 33,500 tiles, 1.09 /
+// 0.76 / 0.70; 15M 5-camera, 21,730 tiles, 0.72 / 0.49 / 0.45; 7680x7680,
+// 230,400 tiles, 3.81 / 2.85 / 2.38.
+inline int fwd_ppt(int64_t tiles) { return tiles >= 16384 ? 4 : tiles >= 2048 ? 2 : 1; }
 
 // Backward: one wave per tile (four pixels per lane: the per-entry
 // reduction and atomics are paid once per 256 pixels) once there are
@@ -551,7 +553,7 @@ hipError_t launch_raster_fwd(int C, int W, int H, const float* screen, const uin
   const int T = tiles_x * tiles_y;
   const int64_t blocks = int64_t(C) * T;
   if (blocks == 0) return hipSuccess;
-  const int ppt = ppt_env ? ppt_env : (blocks >= kFwdManyTiles ? 2 : 1);
+  const int ppt = ppt_env ? ppt_env : fwd_ppt(blocks);
   if (!fits_dispatch(uint64_t(blocks), kTilePix)) return hipErrorInvalidConfiguration;
   const dim3 grid{uint32_t(blocks)};
 #define GS_FWD(P, D)                                                                           \

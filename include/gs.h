@@ -432,8 +432,9 @@ int gs_profile_query(const char* kernel, int64_t* launches, double* total_ms);
  * value keeps the library's choice; results are the same either way):
  *   GS_RASTER_PPT_FWD, GS_RASTER_PPT_BWD = 1, 2 or 4 (read at each
  *     raster call): pixels per lane of the raster kernels (4, 2 or 1
- *     waves per tile). By default the forward takes 1, and 2 from 16,384
- *     tiles; the backward 1 below 512 tiles, 2 below 2,048, else 4.
+ *     waves per tile). By default the forward takes 1 below 2,048 tiles,
+ *     2 below 16,384, else 4; the backward 1 below 512 tiles, 2 below
+ *     2,048, else 4.
  *   GS_EXPAND_GROUP = 16 or 32 (read at each gs_intersect call): entries
  *     per group the list expansion writes at once (64 or 128 bytes); by
  *     default 32 where a chunk's run per tile averages at least 512

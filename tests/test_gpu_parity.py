@@ -271,6 +271,19 @@ def launch_order(tile_offsets):
 def test_raster_fwd_stage(lib, name, ordered):
     """Stage-isolated forward: oracle rows (fp32) and oracle tile lists in,
     tiles launched in id order or in the heavy-first order."""
+    check_raster_fwd(name, ordered)
+
+
+# Every width of the forward kernel (these scenes alone take one pixel per
+# lane).
+@pytest.mark.parametrize("ppt", [1, 2, 4])
+@pytest.mark.parametrize("name", ["tiny", "multicam", "sh2-dense"])
+def test_raster_fwd_widths(lib, name, ppt, monkeypatch):
+    monkeypatch.setenv("GS_RASTER_PPT_FWD", str(ppt))
+    check_raster_fwd(name, True)
+
+
+def check_raster_fwd(name, ordered):
     sc, _, ref = reference(name)
     proj, isect = ref["proj"], ref["isect"]
     C, W, H = sc["C"], sc["W"], sc["H"]
@@ -296,8 +309,8 @@ def test_raster_fwd_stage(lib, name, ordered):
     np.testing.assert_array_equal(lg[ok], last_o[ok])
 
 
-# 32,768 tiles: past the tile count from which the forward runs two pixels
-# per lane (two waves per tile) instead of one.
+# 32,768 tiles: past the tile count from which the forward runs four pixels
+# per lane (one wave per tile).
 MANY_TILES = workloads.SceneSpec("sh0-4000-2cam-2048px", 4000, 0, 2, 2048, 2048, 1773.0, 2.0,
                                  -3.5, 0.5, 5.0, seed=2106)
 
