@@ -255,5 +255,5 @@ def test_mask_bound_adversarial(lib):
     print(f"adversarial: N={N} nnz gpu={p.nnz} oracle={proj.nnz} fragile={int(frag.sum())} "
           f"mask diffs={int(diff.sum())} (fragile among them={int((diff & frag).sum())})")
     assert not (diff & ~frag).any(), np.flatnonzero(diff & ~frag)[:10]
-    # the scene reaches both verdicts, and most pairs are not fragile
+    # the scene reaches both outcomes, and most pairs are not fragile
     assert N // 2 < proj.nnz < sc["C"] * N - N // 2 and int(frag.sum()) < N // 10
